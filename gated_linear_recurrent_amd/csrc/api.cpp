@@ -1,0 +1,208 @@
+// C ABI of the Liger Attention library: argument validation, workspace
+// sizing, launch configuration and HIP error mapping. Every check runs before
+// the first HIP call, so an invalid call launches nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+#include "liger_attn.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+liger_status fail(liger_status st, const std::string& msg) {
+    g_last_error = msg;
+    return st;
+}
+
+liger_status ok() {
+    g_last_error.clear();
+    return LIGER_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared shape checks. `need_T` is false for decode (T is ignored there).
+liger_status check_shape(const liger_shape* s, bool need_T) {
+    if (!s) return fail(LIGER_E_INVALID_ARG, "shape is NULL");
+    if (s->B < 1 || s->B > 65535) return fail(LIGER_E_INVALID_ARG, "B must be in 1..65535");
+    if (need_T && (s->T < 1 || s->T > (int64_t(1) << 31)))
+        return fail(LIGER_E_INVALID_ARG, "T must be in 1..2^31");
+    if (s->H_kv < 1 || s->H_kv > 65535) return fail(LIGER_E_INVALID_ARG, "H_kv must be in 1..65535");
+    if (s->H_q < 1 || s->H_q % s->H_kv != 0) return fail(LIGER_E_INVALID_ARG, "H_q must be a positive multiple of H_kv");
+    if (s->dtype != LIGER_F32 && s->dtype != LIGER_BF16) return fail(LIGER_E_INVALID_ARG, "dtype must be LIGER_F32 or LIGER_BF16");
+    if (s->d < 1) return fail(LIGER_E_INVALID_ARG, "d must be positive");
+    if (s->d != 64 && s->d != 128) return fail(LIGER_E_UNSUPPORTED, "d must be 64 or 128");
+    return LIGER_OK;
+}
+
+liger_status check_common(int32_t gate_mode, float alpha) {
+    if (gate_mode != LIGER_GATE_SCALAR_MEAN && gate_mode != LIGER_GATE_VECTOR_AVGPOOL4)
+        return fail(LIGER_E_INVALID_ARG, "gate_mode must be LIGER_GATE_SCALAR_MEAN or LIGER_GATE_VECTOR_AVGPOOL4");
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return fail(LIGER_E_INVALID_ARG, "alpha must be in [0, 1]");
+    return LIGER_OK;
+}
+
+liger_status check_ptr(const void* p, const char* name) {
+    if (!p) return fail(LIGER_E_INVALID_ARG, std::string(name) + " is NULL");
+    if (!aligned16(p)) return fail(LIGER_E_INVALID_ARG, std::string(name) + " is not 16-byte aligned");
+    return LIGER_OK;
+}
+
+liger_status map_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(LIGER_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define LIGER_TRY(expr)                    \
+    do {                                   \
+        liger_status st_ = (expr);         \
+        if (st_ != LIGER_OK) return st_;   \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* liger_last_error(void) { return g_last_error.c_str(); }
+
+size_t liger_attn_prefill_workspace_size_ex(const liger_shape* shape, int32_t chunks_per_segment) {
+    if (check_shape(shape, true) != LIGER_OK || chunks_per_segment < 0) return 0;
+    const liger::PrefillPlan pl = liger::make_prefill_plan(shape->B, shape->T, shape->H_kv, shape->d,
+                                                           shape->dtype == LIGER_BF16, chunks_per_segment);
+    return pl.workspace_bytes;
+}
+
+size_t liger_attn_prefill_workspace_size(const liger_shape* shape) {
+    return liger_attn_prefill_workspace_size_ex(shape, 0);
+}
+
+liger_status liger_attn_prefill_ex(const void* q, const void* k, const void* v, int32_t gate_mode,
+                                   int32_t window, float alpha, const liger_shape* shape, void* o,
+                                   float* S_T, void* workspace, size_t workspace_bytes,
+                                   int32_t chunks_per_segment, void* stream) {
+    LIGER_TRY(check_shape(shape, true));
+    LIGER_TRY(check_common(gate_mode, alpha));
+    if (window < 1 || window > 64) return fail(LIGER_E_INVALID_ARG, "window must be in 1..64");
+    if (chunks_per_segment < 0) return fail(LIGER_E_INVALID_ARG, "chunks_per_segment must be >= 0");
+    if (shape->dtype == LIGER_F32 && shape->d != 64)
+        return fail(LIGER_E_UNSUPPORTED, "fp32 prefill is built for d = 64 only");
+    LIGER_TRY(check_ptr(q, "q"));
+    LIGER_TRY(check_ptr(k, "k"));
+    LIGER_TRY(check_ptr(v, "v"));
+    LIGER_TRY(check_ptr(o, "o"));
+    LIGER_TRY(check_ptr(S_T, "S_T"));
+    if (o == q || o == k || o == v) return fail(LIGER_E_INVALID_ARG, "o must not alias q, k or v");
+    const liger::PrefillPlan pl = liger::make_prefill_plan(shape->B, shape->T, shape->H_kv, shape->d,
+                                                           shape->dtype == LIGER_BF16, chunks_per_segment);
+    if (pl.workspace_bytes > 0) {
+        if (!workspace) return fail(LIGER_E_WORKSPACE, "workspace is NULL but " + std::to_string(pl.workspace_bytes) + " bytes are needed");
+        if (!aligned16(workspace)) return fail(LIGER_E_INVALID_ARG, "workspace is not 16-byte aligned");
+        if (workspace_bytes < pl.workspace_bytes)
+            return fail(LIGER_E_WORKSPACE, "workspace too small: " + std::to_string(workspace_bytes) + " < " +
+                                               std::to_string(pl.workspace_bytes) + " bytes");
+    }
+    liger::PrefillArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.S_T = S_T;
+    a.workspace = static_cast<float*>(workspace);
+    a.B = shape->B;
+    a.T = shape->T;
+    a.H_kv = shape->H_kv;
+    a.n_rep = shape->H_q / shape->H_kv;
+    a.d = shape->d;
+    a.window = window;
+    a.gate = gate_mode;
+    a.bf16 = shape->dtype == LIGER_BF16;
+    a.alpha = alpha;
+    a.plan = pl;
+    a.stream = stream;
+    return map_hip(liger::launch_prefill(a), "prefill launch");
+}
+
+liger_status liger_attn_prefill(const void* q, const void* k, const void* v, int32_t gate_mode, int32_t window,
+                                float alpha, const liger_shape* shape, void* o, float* S_T, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    return liger_attn_prefill_ex(q, k, v, gate_mode, window, alpha, shape, o, S_T, workspace, workspace_bytes, 0,
+                                 stream);
+}
+
+liger_status liger_attn_decode_step(const void* q, const void* k, const void* v, float* S,
+                                    const liger_kv_ring* kv_ring, int32_t gate_mode, float alpha,
+                                    const liger_shape* shape, void* o, void* stream) {
+    LIGER_TRY(check_shape(shape, false));
+    LIGER_TRY(check_common(gate_mode, alpha));
+    if (!kv_ring) return fail(LIGER_E_INVALID_ARG, "kv_ring is NULL");
+    if (kv_ring->window < 1 || kv_ring->window > 64) return fail(LIGER_E_INVALID_ARG, "ring window must be in 1..64");
+    const int n_rep = shape->H_q / shape->H_kv;
+    if (n_rep != 1 && n_rep != 2 && n_rep != 4 && n_rep != 8)
+        return fail(LIGER_E_UNSUPPORTED, "decode is built for H_q / H_kv in {1, 2, 4, 8}");
+    LIGER_TRY(check_ptr(q, "q"));
+    LIGER_TRY(check_ptr(k, "k"));
+    LIGER_TRY(check_ptr(v, "v"));
+    LIGER_TRY(check_ptr(S, "S"));
+    LIGER_TRY(check_ptr(o, "o"));
+    LIGER_TRY(check_ptr(kv_ring->k, "kv_ring->k"));
+    LIGER_TRY(check_ptr(kv_ring->v, "kv_ring->v"));
+    if (!kv_ring->pos) return fail(LIGER_E_INVALID_ARG, "kv_ring->pos is NULL");
+    if (!kv_ring->sync) return fail(LIGER_E_INVALID_ARG, "kv_ring->sync is NULL");
+    if (o == q || o == k || o == v) return fail(LIGER_E_INVALID_ARG, "o must not alias q, k or v");
+    liger::DecodeArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.S = S;
+    a.ring_k = kv_ring->k;
+    a.ring_v = kv_ring->v;
+    a.pos = kv_ring->pos;
+    a.sync = kv_ring->sync;
+    a.o = o;
+    a.N = shape->B;
+    a.H_kv = shape->H_kv;
+    a.n_rep = n_rep;
+    a.d = shape->d;
+    a.window = kv_ring->window;
+    a.gate = gate_mode;
+    a.bf16 = shape->dtype == LIGER_BF16;
+    a.alpha = alpha;
+    a.stream = stream;
+    return map_hip(liger::launch_decode_step(a), "decode launch");
+}
+
+liger_status liger_kv_ring_fill(const void* k, const void* v, const liger_shape* shape,
+                                const liger_kv_ring* kv_ring, void* stream) {
+    LIGER_TRY(check_shape(shape, true));
+    if (!kv_ring) return fail(LIGER_E_INVALID_ARG, "kv_ring is NULL");
+    if (kv_ring->window < 1 || kv_ring->window > 64) return fail(LIGER_E_INVALID_ARG, "ring window must be in 1..64");
+    LIGER_TRY(check_ptr(k, "k"));
+    LIGER_TRY(check_ptr(v, "v"));
+    LIGER_TRY(check_ptr(kv_ring->k, "kv_ring->k"));
+    LIGER_TRY(check_ptr(kv_ring->v, "kv_ring->v"));
+    if (!kv_ring->pos) return fail(LIGER_E_INVALID_ARG, "kv_ring->pos is NULL");
+    if (!kv_ring->sync) return fail(LIGER_E_INVALID_ARG, "kv_ring->sync is NULL");
+    liger::RingFillArgs a;
+    a.k = k;
+    a.v = v;
+    a.ring_k = kv_ring->k;
+    a.ring_v = kv_ring->v;
+    a.pos = kv_ring->pos;
+    a.sync = kv_ring->sync;
+    a.B = shape->B;
+    a.T = shape->T;
+    a.H_kv = shape->H_kv;
+    a.d = shape->d;
+    a.window = kv_ring->window;
+    a.bf16 = shape->dtype == LIGER_BF16;
+    a.stream = stream;
+    return map_hip(liger::launch_ring_fill(a), "ring fill launch");
+}
+
+}  // extern "C"

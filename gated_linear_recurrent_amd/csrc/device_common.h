@@ -1,0 +1,126 @@
+// Device helpers for the Liger Attention kernels on gfx950 (CDNA4, wave64).
+//
+// MFMA fragment conventions used throughout (16x16 output tiles):
+//   accumulator (D) : lane L holds column (L & 15), rows 4*(L >> 4) + r, r = 0..3
+//   operand (A or B): lane L holds row/column (L & 15) and KPL consecutive
+//                     k-elements starting at KPL * (L >> 4) of a KSTEP-wide k-step
+// so an MFMA computes D[m][n] += sum_k X[m][k] * Y[n][k] for two matrices that are
+// both stored k-contiguous ("NT" form). bf16 uses v_mfma_f32_16x16x32_bf16
+// (KSTEP 32, KPL 8); fp32 uses v_mfma_f32_16x16x4_f32 (KSTEP 4, KPL 1).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace liger {
+
+typedef uint16_t bf16_t;  // bfloat16 storage (bit pattern)
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even conversion (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    __bf16 h = static_cast<__bf16>(f);
+    return __builtin_bit_cast(bf16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// 2^x on the hardware exponential unit (inputs are already in log2 units).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// log2(sigmoid(x)) = min(x, 0)*log2(e) - log2(1 + 2^(-|x| log2(e))), never overflows.
+__device__ __forceinline__ float log2_sigmoid(float x) {
+    float ax = fabsf(x) * kLog2e;
+    return fminf(x, 0.0f) * kLog2e - fast_log2(1.0f + fast_exp2(-ax));
+}
+
+__device__ __forceinline__ float sigmoidf_stable(float x) {
+    float e = __expf(-fabsf(x));
+    float s = 1.0f / (1.0f + e);
+    return x >= 0.0f ? s : e * s;
+}
+
+// Storage type -> float.
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t x) { return bf16_to_f32(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f32_to_bf16(x); }
+
+// Wave-wide (64 lanes) butterfly reductions.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+// Reduction over the four lane groups (L >> 4) that share a fragment row.
+__device__ __forceinline__ float group4_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ __forceinline__ float group4_sum(float v) {
+    v += __shfl_xor(v, 16, 64);
+    return v + __shfl_xor(v, 32, 64);
+}
+
+// ---------------------------------------------------------------- MFMA traits
+template <typename OT> struct Mfma;
+
+template <> struct Mfma<bf16_t> {
+    static constexpr int KSTEP = 32;
+    static constexpr int KPL = 8;
+    typedef bf16x8_t frag;
+    __device__ static __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    // KPL contiguous elements from LDS (16 bytes).
+    __device__ static __forceinline__ frag load(const bf16_t* p) {
+        return *reinterpret_cast<const bf16x8_t*>(p);
+    }
+    __device__ static __forceinline__ frag zero() {
+        uint4 z = make_uint4(0, 0, 0, 0);
+        return __builtin_bit_cast(frag, z);
+    }
+    // Pack KPL floats (rounded to nearest even).
+    __device__ static __forceinline__ frag pack(const float* x) {
+        uint4 u;
+        u.x = pack_bf16x2(x[0], x[1]);
+        u.y = pack_bf16x2(x[2], x[3]);
+        u.z = pack_bf16x2(x[4], x[5]);
+        u.w = pack_bf16x2(x[6], x[7]);
+        return __builtin_bit_cast(frag, u);
+    }
+};
+
+template <> struct Mfma<float> {
+    static constexpr int KSTEP = 4;
+    static constexpr int KPL = 1;
+    typedef float frag;
+    __device__ static __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ frag load(const float* p) { return *p; }
+    __device__ static __forceinline__ frag zero() { return 0.0f; }
+    __device__ static __forceinline__ frag pack(const float* x) { return x[0]; }
+};
+
+__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace liger

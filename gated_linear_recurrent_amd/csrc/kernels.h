@@ -1,0 +1,87 @@
+// Internal launch interface between the C ABI (api.cpp) and the HIP kernels.
+// Arguments arrive here already validated; these functions only configure
+// and enqueue kernels on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace liger {
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    float* S;
+    void* ring_k;
+    void* ring_v;
+    int64_t* pos;
+    uint32_t* sync;
+    void* o;
+    int64_t N;
+    int H_kv;
+    int n_rep;
+    int d;
+    int window;
+    int gate;   // 0 scalar mean, 1 vector avg-pool-4
+    bool bf16;
+    float alpha;
+    void* stream;
+};
+
+struct RingFillArgs {
+    const void* k;
+    const void* v;
+    void* ring_k;
+    void* ring_v;
+    int64_t* pos;
+    uint32_t* sync;
+    int64_t B;
+    int64_t T;
+    int H_kv;
+    int d;
+    int window;
+    bool bf16;
+    void* stream;
+};
+
+// Segment plan of the chunked prefill: chunks of 64 tokens grouped into
+// n_seg segments of cps chunks (the last segment may be shorter).
+struct PrefillPlan {
+    int64_t n_chunks;  // ceil(T / 64)
+    int64_t cps;       // chunks per segment
+    int64_t n_seg;     // ceil(n_chunks / cps)
+    size_t carry_floats;     // floats per carry record: d*d + d
+    size_t workspace_bytes;  // B * H_kv * (n_seg - 1) * carry_floats * 4
+};
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* S_T;
+    float* workspace;
+    int64_t B;
+    int64_t T;
+    int H_kv;
+    int n_rep;
+    int d;
+    int window;
+    int gate;
+    bool bf16;
+    float alpha;
+    PrefillPlan plan;
+    void* stream;
+};
+
+constexpr int kChunk = 64;
+
+PrefillPlan make_prefill_plan(int64_t B, int64_t T, int H_kv, int d, bool bf16, int64_t chunks_per_segment);
+
+hipError_t launch_decode_step(const DecodeArgs& a);
+hipError_t launch_ring_fill(const RingFillArgs& a);
+hipError_t launch_prefill(const PrefillArgs& a);
+
+}  // namespace liger

@@ -1,0 +1,166 @@
+/*
+ * liger_attn.h - C ABI of the Liger Attention layer for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The layer (paper-notes page "Liger: Linearizing Large Language Models to
+ * Gated Recurrent Structures", sections on the unified gated linear
+ * recurrence and on Liger Attention) mixes two token mixers inside one
+ * attention layer:
+ *
+ *   GRM  S_t = G_t (.) S_{t-1} + phi(k_t)^T v_t ,   o_t = phi(q_t) S_t
+ *   SWA  softmax attention of q_t over the last `window` keys (self included)
+ *   out  o_t = alpha * GRM + (1 - alpha) * SWA
+ *
+ * phi is a softmax over the head dimension applied to q and k separately;
+ * G_t is a parameter-free pooling of the raw key k_t squashed by a sigmoid
+ * (the key projection reused as the gate, section on the gate built from the
+ * key projection). The pages say only "pooling, e.g. mean"; the two pooled
+ * gates offered here are:
+ *   LIGER_GATE_SCALAR_MEAN     g_t = sigmoid(mean_c k_t[c]) on every entry of S
+ *   LIGER_GATE_VECTOR_AVGPOOL4 g_t[c] = sigmoid(mean of k_t[c-1 .. c+2] over the
+ *                              in-range channels), applied to row c (d_k) of S
+ * The state starts at zero for prefill. The GRM output of token t uses the
+ * state that already holds token t. SWA uses the raw q and k, scale 1/sqrt(d).
+ * Query head h reads key/value head h / (H_q / H_kv).
+ *
+ * Layouts (row-major, contiguous, device memory unless stated otherwise):
+ *   q, o   [B, T, H_q,  d]          dtype of the shape (fp32 or bf16)
+ *   k, v   [B, T, H_kv, d]          same dtype
+ *   S, S_T [B, H_kv, d, d]          float32, row index d_k, column index d_v
+ *   ring   k, v [N, H_kv, window, d] input dtype; token t in slot t mod window
+ *          pos  [N] int64: tokens consumed so far
+ *          sync [N] uint32: arrival counters, zero between calls
+ *
+ * Conventions for every call:
+ *   - Returns LIGER_OK (0) or a negative liger_status. liger_last_error()
+ *     then returns a message (thread-local; valid until the next call on the
+ *     same thread).
+ *   - All arguments are validated before any HIP call; an invalid call
+ *     launches nothing and touches no memory.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL means the default
+ *     stream). The library never synchronises: results are valid once the
+ *     caller has synchronised with the stream.
+ *   - The caller owns every buffer. The library keeps no pointer after
+ *     returning, allocates nothing and frees nothing. Device pointers must be
+ *     16-byte aligned. Outputs must not alias inputs.
+ *   - No global mutable state: calls on different streams may run
+ *     concurrently as long as their buffers do not overlap.
+ *   - Floating-point inputs are not sanitised: NaN or Inf propagate.
+ */
+#ifndef LIGER_ATTN_H
+#define LIGER_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum liger_status {
+    LIGER_OK = 0,
+    LIGER_E_INVALID_ARG = -1, /* bad pointer, size, enum or range            */
+    LIGER_E_UNSUPPORTED = -2, /* valid but not built (e.g. d not in {64,128}) */
+    LIGER_E_HIP = -3,         /* a HIP call or kernel launch failed           */
+    LIGER_E_WORKSPACE = -4    /* workspace missing or too small               */
+} liger_status;
+
+typedef enum liger_gate_mode {
+    LIGER_GATE_SCALAR_MEAN = 0,
+    LIGER_GATE_VECTOR_AVGPOOL4 = 1
+} liger_gate_mode;
+
+typedef enum liger_dtype {
+    LIGER_F32 = 0,
+    LIGER_BF16 = 1
+} liger_dtype;
+
+/* Problem shape. B is the batch (number of sequences; N for decode), T the
+ * sequence length (prefill; ignored by decode), d the head size (64 or 128),
+ * dtype a liger_dtype for q, k, v, o and the ring. */
+typedef struct liger_shape {
+    int64_t B;
+    int64_t T;
+    int32_t H_q;
+    int32_t H_kv;
+    int32_t d;
+    int32_t dtype;
+} liger_shape;
+
+/* Sliding-window KV ring of the decode state (all device pointers). */
+typedef struct liger_kv_ring {
+    void* k;        /* [N, H_kv, window, d], input dtype                     */
+    void* v;        /* [N, H_kv, window, d], input dtype                     */
+    int64_t* pos;   /* [N] tokens consumed; advanced by one per decode step  */
+    uint32_t* sync; /* [N] arrival counters; zero before and after each call */
+    int32_t window; /* 1 .. 64                                               */
+} liger_kv_ring;
+
+/*
+ * Bytes of device workspace liger_attn_prefill needs for `shape` (the
+ * per-segment state carries of the chunked scan). Returns 0 when the shape
+ * needs none or is invalid. `chunks_per_segment` selects the segment length
+ * in 64-token chunks; 0 picks it from the shape (the same choice the
+ * prefill call makes when given 0).
+ */
+size_t liger_attn_prefill_workspace_size(const liger_shape* shape);
+size_t liger_attn_prefill_workspace_size_ex(const liger_shape* shape,
+                                            int32_t chunks_per_segment);
+
+/*
+ * Prefill: whole sequences from a zero state.
+ * Inputs q, k, v (layouts above). Outputs o [B, T, H_q, d] (dtype of q) and
+ * S_T [B, H_kv, d, d] float32, the state after the last token.
+ * window in 1..64, alpha in [0, 1] (beta = 1 - alpha).
+ * workspace: device memory of at least liger_attn_prefill_workspace_size
+ * bytes (may be NULL when that size is 0); its contents on entry are
+ * ignored and on return are unspecified.
+ * Supported: d in {64, 128} for bf16, d = 64 for fp32.
+ */
+liger_status liger_attn_prefill(const void* q, const void* k, const void* v,
+                                int32_t gate_mode, int32_t window, float alpha,
+                                const liger_shape* shape, void* o, float* S_T,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* As liger_attn_prefill with an explicit segment length (0 = automatic);
+ * every segment length gives the same result up to float32 rounding. */
+liger_status liger_attn_prefill_ex(const void* q, const void* k, const void* v,
+                                   int32_t gate_mode, int32_t window, float alpha,
+                                   const liger_shape* shape, void* o, float* S_T,
+                                   void* workspace, size_t workspace_bytes,
+                                   int32_t chunks_per_segment, void* stream);
+
+/*
+ * Decode step: one new token for each of N = shape->B sequences.
+ * q [N, H_q, d], k, v [N, H_kv, d] (dtype of the shape); o [N, H_q, d].
+ * S [N, H_kv, d, d] float32 is updated in place to G (.) S + phi(k)^T v.
+ * The ring is updated in place: the new k, v go to slot pos mod window, the
+ * window of `window` most recent tokens (the new one included) is attended
+ * to, and pos advances by one. gate_mode and alpha must be those of the
+ * prefill that produced the state. shape->T is ignored.
+ */
+liger_status liger_attn_decode_step(const void* q, const void* k, const void* v,
+                                    float* S, const liger_kv_ring* kv_ring,
+                                    int32_t gate_mode, float alpha,
+                                    const liger_shape* shape, void* o,
+                                    void* stream);
+
+/*
+ * Ring set-up after a prompt: copies the last min(T, window) tokens of
+ * k, v [B, T, H_kv, d] to slots t mod window, zeroes the other slots,
+ * sets pos = T and sync = 0. (Together with S_T from the prefill this is the
+ * complete decode state.)
+ */
+liger_status liger_kv_ring_fill(const void* k, const void* v,
+                                const liger_shape* shape,
+                                const liger_kv_ring* kv_ring, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* liger_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIGER_ATTN_H */

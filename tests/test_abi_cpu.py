@@ -1,0 +1,170 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the header
+declares, and rejects invalid arguments before making any HIP call.
+
+No kernel runs here. Pointers handed to the library are fake but 16-byte
+aligned; every call below fails validation, so they are never dereferenced.
+The one call that passes validation (no-GPU error path) runs only where no
+GPU is visible.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_linear_recurrent_amd as gla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gla.LIB_PATH):
+        from gated_linear_recurrent_amd import build_lib
+        build_lib.build()
+    return gla.load_library()
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "liger_attn.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|size_t|liger_status)\s+(liger_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _header_functions()
+    assert set(declared) == set(gla.EXPORTED), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_exports_are_plain_c_symbols():
+    out = os.popen(f"nm -D --defined-only {gla.LIB_PATH}").read()
+    for name in gla.EXPORTED:
+        assert re.search(rf"\bT {name}$", out, re.M), name
+
+
+def _shape(**kw):
+    base = dict(B=1, T=128, H_q=4, H_kv=1, d=128, dtype=gla.LIGER_BF16)
+    base.update(kw)
+    return gla.liger_shape(**base)
+
+
+def _prefill(lib, shape, gate=1, window=64, alpha=0.5, q=FAKE, k=FAKE, v=FAKE, o=FAKE + 4096,
+             S=FAKE + 8192, ws=None, ws_bytes=0, cps=0):
+    return lib.liger_attn_prefill_ex(q, k, v, gate, window, alpha, ctypes.byref(shape), o, S, ws,
+                                     ws_bytes, cps, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), gla.LIGER_E_INVALID_ARG),
+    (dict(T=0), gla.LIGER_E_INVALID_ARG),
+    (dict(H_kv=0), gla.LIGER_E_INVALID_ARG),
+    (dict(H_q=6, H_kv=4), gla.LIGER_E_INVALID_ARG),
+    (dict(d=96), gla.LIGER_E_UNSUPPORTED),
+    (dict(d=256), gla.LIGER_E_UNSUPPORTED),
+    (dict(dtype=7), gla.LIGER_E_INVALID_ARG),
+    (dict(dtype=gla.LIGER_F32, d=128), gla.LIGER_E_UNSUPPORTED),
+])
+def test_prefill_rejects_bad_shapes(lib, kw, code):
+    assert _prefill(lib, _shape(**kw)) == code
+    assert gla.liger_last_error() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(gate=2), gla.LIGER_E_INVALID_ARG),
+    (dict(window=0), gla.LIGER_E_INVALID_ARG),
+    (dict(window=65), gla.LIGER_E_INVALID_ARG),
+    (dict(alpha=-0.1), gla.LIGER_E_INVALID_ARG),
+    (dict(alpha=1.5), gla.LIGER_E_INVALID_ARG),
+    (dict(alpha=float("nan")), gla.LIGER_E_INVALID_ARG),
+    (dict(q=None), gla.LIGER_E_INVALID_ARG),
+    (dict(k=FAKE + 8), gla.LIGER_E_INVALID_ARG),
+    (dict(o=FAKE), gla.LIGER_E_INVALID_ARG),      # aliases q
+    (dict(S=None), gla.LIGER_E_INVALID_ARG),
+    (dict(cps=-1), gla.LIGER_E_INVALID_ARG),
+])
+def test_prefill_rejects_bad_arguments(lib, kw, code):
+    assert _prefill(lib, _shape(T=4096), **kw) == code
+
+
+def test_prefill_workspace_checks(lib):
+    shp = _shape(T=8192, H_q=32, H_kv=8)
+    need = lib.liger_attn_prefill_workspace_size(ctypes.byref(shp))
+    assert need > 0 and need % 16 == 0
+    assert _prefill(lib, shp, ws=None) == gla.LIGER_E_WORKSPACE
+    assert _prefill(lib, shp, ws=FAKE + 1 << 20, ws_bytes=need - 1) == gla.LIGER_E_WORKSPACE
+    assert _prefill(lib, shp, ws=(FAKE + 1 << 20) + 4, ws_bytes=need) == gla.LIGER_E_INVALID_ARG
+
+
+def test_workspace_size_formula(lib):
+    # carries of every segment but the last: (d*d + d) fp32 per (b, kv head, segment)
+    for T, cps in [(64, 1), (65, 1), (8192, 4), (8192, 0), (1000, 3)]:
+        shp = _shape(B=2, T=T, H_q=8, H_kv=2)
+        n_chunks = -(-T // 64)
+        size = lib.liger_attn_prefill_workspace_size_ex(ctypes.byref(shp), cps)
+        if cps > 0:
+            n_seg = -(-n_chunks // min(cps, n_chunks))
+            assert size == 2 * 2 * (n_seg - 1) * (128 * 128 + 128) * 4
+        assert size % ((128 * 128 + 128) * 4 * 4) == 0
+    assert lib.liger_attn_prefill_workspace_size(ctypes.byref(_shape(d=96))) == 0
+    assert lib.liger_attn_prefill_workspace_size(None) == 0
+
+
+def _ring(window=64, k=FAKE, v=FAKE + 4096, pos=FAKE + 8192, sync=FAKE + 12288):
+    return gla.liger_kv_ring(k, v, pos, sync, window)
+
+
+def _decode(lib, shape, ring, gate=1, alpha=0.5, q=FAKE + 65536, k=FAKE + 69632, v=FAKE + 73728,
+            S=FAKE + 77824, o=FAKE + 81920):
+    return lib.liger_attn_decode_step(q, k, v, S, ctypes.byref(ring) if ring is not None else None,
+                                      gate, alpha, ctypes.byref(shape), o, None)
+
+
+@pytest.mark.parametrize("kw,rkw,code", [
+    (dict(), dict(window=0), gla.LIGER_E_INVALID_ARG),
+    (dict(), dict(window=65), gla.LIGER_E_INVALID_ARG),
+    (dict(), dict(pos=None), gla.LIGER_E_INVALID_ARG),
+    (dict(), dict(sync=None), gla.LIGER_E_INVALID_ARG),
+    (dict(), dict(k=FAKE + 2), gla.LIGER_E_INVALID_ARG),
+    (dict(H_q=12, H_kv=1), dict(), gla.LIGER_E_UNSUPPORTED),
+    (dict(d=32), dict(), gla.LIGER_E_UNSUPPORTED),
+    (dict(B=0), dict(), gla.LIGER_E_INVALID_ARG),
+])
+def test_decode_rejects_bad_arguments(lib, kw, rkw, code):
+    assert _decode(lib, _shape(**kw), _ring(**rkw)) == code
+
+
+def test_decode_rejects_null_ring_and_alias(lib):
+    assert _decode(lib, _shape(), None) == gla.LIGER_E_INVALID_ARG
+    assert _decode(lib, _shape(), _ring(), o=FAKE + 65536) == gla.LIGER_E_INVALID_ARG
+    assert _decode(lib, _shape(), _ring(), gate=-1) == gla.LIGER_E_INVALID_ARG
+
+
+def test_ring_fill_rejects_bad_arguments(lib):
+    shp = _shape()
+    assert lib.liger_kv_ring_fill(FAKE, FAKE, ctypes.byref(shp), None, None) == gla.LIGER_E_INVALID_ARG
+    r = _ring(window=100)
+    assert lib.liger_kv_ring_fill(FAKE, FAKE, ctypes.byref(shp), ctypes.byref(r), None) == gla.LIGER_E_INVALID_ARG
+    r = _ring()
+    assert lib.liger_kv_ring_fill(None, FAKE, ctypes.byref(shp), ctypes.byref(r), None) == gla.LIGER_E_INVALID_ARG
+
+
+def test_no_gpu_returns_hip_error_instead_of_aborting(lib):
+    """A valid call on a machine without a GPU fails with LIGER_E_HIP."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: the fake pointers of this test must not reach a kernel")
+    st = _prefill(lib, _shape(T=64))
+    assert st == gla.LIGER_E_HIP, gla.liger_last_error()
+    assert "launch" in gla.liger_last_error()
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 64, 4, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 64, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(gla.LigerError):
+        gla.liger_attn_prefill(q, k, k, 1, 64, 0.5, o=q.clone(), S_T=torch.zeros(1, 1, 128, 128),
+                               workspace=None)
