@@ -30,6 +30,9 @@ LIGER_GATE_SCALAR_MEAN = 0
 LIGER_GATE_VECTOR_AVGPOOL4 = 1
 LIGER_F32 = 0
 LIGER_BF16 = 1
+LIGER_STAGE_SEGMENT_STATES = 1
+LIGER_STAGE_CARRY_SCAN = 2
+LIGER_STAGE_OUTPUT = 4
 
 # Every symbol the header declares (checked by the CPU tests).
 EXPORTED = (
@@ -37,6 +40,7 @@ EXPORTED = (
     "liger_attn_prefill_workspace_size_ex",
     "liger_attn_prefill",
     "liger_attn_prefill_ex",
+    "liger_attn_prefill_stages",
     "liger_attn_decode_step",
     "liger_kv_ring_fill",
     "liger_last_error",
@@ -81,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.liger_attn_prefill.restype = i32
     lib.liger_attn_prefill_ex.argtypes = [vp, vp, vp, i32, i32, f32, shp, vp, vp, vp, sz, i32, vp]
     lib.liger_attn_prefill_ex.restype = i32
+    lib.liger_attn_prefill_stages.argtypes = [vp, vp, vp, i32, i32, f32, shp, vp, vp, vp, sz, i32, i32, vp]
+    lib.liger_attn_prefill_stages.restype = i32
     lib.liger_attn_decode_step.argtypes = [vp, vp, vp, vp, ring, i32, f32, shp, vp, vp]
     lib.liger_attn_decode_step.restype = i32
     lib.liger_kv_ring_fill.argtypes = [vp, vp, shp, ring, vp]
@@ -141,8 +147,10 @@ def liger_attn_prefill_workspace_size(B: int, T: int, H_q: int, H_kv: int, d: in
 
 
 def liger_attn_prefill(q, k, v, gate_mode: int, window: int, alpha: float, *, o=None, S_T=None,
-                       workspace=None, chunks_per_segment: int = 0, stream=None):
-    """Prefill from a zero state. q [B,T,H_q,d], k/v [B,T,H_kv,d] -> (o, S_T fp32 [B,H_kv,d,d])."""
+                       workspace=None, chunks_per_segment: int = 0, stage_mask: int = 7, stream=None):
+    """Prefill from a zero state. q [B,T,H_q,d], k/v [B,T,H_kv,d] -> (o, S_T fp32 [B,H_kv,d,d]).
+
+    stage_mask < 7 enqueues only some kernels (liger_attn_prefill_stages)."""
     torch = _torch()
     lib = load_library()
     B, T, H_q, d = q.shape
@@ -156,9 +164,9 @@ def liger_attn_prefill(q, k, v, gate_mode: int, window: int, alpha: float, *, o=
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.liger_attn_prefill_ex(_ptr(q), _ptr(k), _ptr(v), gate_mode, window, alpha,
-                                     ctypes.byref(shp), _ptr(o), _ptr(S_T), _ptr(workspace),
-                                     ws_bytes, chunks_per_segment, _stream(stream)))
+    _check(lib.liger_attn_prefill_stages(_ptr(q), _ptr(k), _ptr(v), gate_mode, window, alpha,
+                                         ctypes.byref(shp), _ptr(o), _ptr(S_T), _ptr(workspace),
+                                         ws_bytes, chunks_per_segment, stage_mask, _stream(stream)))
     return o, S_T
 
 

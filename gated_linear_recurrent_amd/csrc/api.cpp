@@ -82,10 +82,11 @@ size_t liger_attn_prefill_workspace_size(const liger_shape* shape) {
     return liger_attn_prefill_workspace_size_ex(shape, 0);
 }
 
-liger_status liger_attn_prefill_ex(const void* q, const void* k, const void* v, int32_t gate_mode,
-                                   int32_t window, float alpha, const liger_shape* shape, void* o,
-                                   float* S_T, void* workspace, size_t workspace_bytes,
-                                   int32_t chunks_per_segment, void* stream) {
+liger_status liger_attn_prefill_stages(const void* q, const void* k, const void* v, int32_t gate_mode,
+                                       int32_t window, float alpha, const liger_shape* shape, void* o,
+                                       float* S_T, void* workspace, size_t workspace_bytes,
+                                       int32_t chunks_per_segment, int32_t stage_mask, void* stream) {
+    if (stage_mask < 1 || stage_mask > 7) return fail(LIGER_E_INVALID_ARG, "stage_mask must be in 1..7");
     LIGER_TRY(check_shape(shape, true));
     LIGER_TRY(check_common(gate_mode, alpha));
     if (window < 1 || window > 64) return fail(LIGER_E_INVALID_ARG, "window must be in 1..64");
@@ -124,8 +125,17 @@ liger_status liger_attn_prefill_ex(const void* q, const void* k, const void* v, 
     a.bf16 = shape->dtype == LIGER_BF16;
     a.alpha = alpha;
     a.plan = pl;
+    a.stage_mask = stage_mask;
     a.stream = stream;
     return map_hip(liger::launch_prefill(a), "prefill launch");
+}
+
+liger_status liger_attn_prefill_ex(const void* q, const void* k, const void* v, int32_t gate_mode,
+                                   int32_t window, float alpha, const liger_shape* shape, void* o,
+                                   float* S_T, void* workspace, size_t workspace_bytes,
+                                   int32_t chunks_per_segment, void* stream) {
+    return liger_attn_prefill_stages(q, k, v, gate_mode, window, alpha, shape, o, S_T, workspace,
+                                     workspace_bytes, chunks_per_segment, 7, stream);
 }
 
 liger_status liger_attn_prefill(const void* q, const void* k, const void* v, int32_t gate_mode, int32_t window,

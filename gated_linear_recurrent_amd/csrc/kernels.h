@@ -73,6 +73,7 @@ struct PrefillArgs {
     bool bf16;
     float alpha;
     PrefillPlan plan;
+    int stage_mask;  // 1 segment states, 2 carry scan, 4 outputs
     void* stream;
 };
 

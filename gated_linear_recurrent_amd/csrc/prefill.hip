@@ -883,19 +883,24 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     p.window = a.window;
     p.alpha = a.alpha;
     hipStream_t st = static_cast<hipStream_t>(a.stream);
-    if (p.n_seg > 1) {
+    if (p.n_seg > 1 && (a.stage_mask & 1)) {
         hipLaunchKernelGGL((segment_state_kernel<T, D, GATE>), dim3(unsigned(p.n_seg - 1), a.H_kv, unsigned(a.B)),
                            dim3(kPThreads), 0, st, p);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((carry_scan_kernel<D>), dim3((D * D / 4 + 255) / 256, a.H_kv, unsigned(a.B)), dim3(256), 0, st,
-                           p.carry, p.n_seg, p.H_kv);
-        e = hipGetLastError();
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((prefill_output_kernel<T, D, GATE>), dim3(unsigned(p.n_seg), a.H_kv, unsigned(a.B)),
-                       dim3(kPThreads), 0, st, p);
-    return hipGetLastError();
+    if (p.n_seg > 1 && (a.stage_mask & 2)) {
+        hipLaunchKernelGGL((carry_scan_kernel<D>), dim3((D * D / 4 + 255) / 256, a.H_kv, unsigned(a.B)), dim3(256), 0, st,
+                           p.carry, p.n_seg, p.H_kv);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (a.stage_mask & 4) {
+        hipLaunchKernelGGL((prefill_output_kernel<T, D, GATE>), dim3(unsigned(p.n_seg), a.H_kv, unsigned(a.B)),
+                           dim3(kPThreads), 0, st, p);
+        return hipGetLastError();
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {

@@ -132,6 +132,25 @@ liger_status liger_attn_prefill_ex(const void* q, const void* k, const void* v,
                                    int32_t chunks_per_segment, void* stream);
 
 /*
+ * Profiling aid: enqueue only the prefill kernels chosen by stage_mask, in
+ * pipeline order: LIGER_STAGE_SEGMENT_STATES (local end state of every
+ * segment but the last), LIGER_STAGE_CARRY_SCAN (states entering each
+ * segment, in the workspace) and LIGER_STAGE_OUTPUT (o and S_T). Enqueuing
+ * mask 3 and then mask 4 on one stream with the same workspace is the same
+ * work as one liger_attn_prefill_ex call. Other arguments as for
+ * liger_attn_prefill_ex; stage_mask must be in 1..7.
+ */
+#define LIGER_STAGE_SEGMENT_STATES 1
+#define LIGER_STAGE_CARRY_SCAN 2
+#define LIGER_STAGE_OUTPUT 4
+liger_status liger_attn_prefill_stages(const void* q, const void* k, const void* v,
+                                       int32_t gate_mode, int32_t window, float alpha,
+                                       const liger_shape* shape, void* o, float* S_T,
+                                       void* workspace, size_t workspace_bytes,
+                                       int32_t chunks_per_segment, int32_t stage_mask,
+                                       void* stream);
+
+/*
  * Decode step: one new token for each of N = shape->B sequences.
  * q [N, H_q, d], k, v [N, H_kv, d] (dtype of the shape); o [N, H_q, d].
  * S [N, H_kv, d, d] float32 is updated in place to G (.) S + phi(k)^T v.
