@@ -30,9 +30,19 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(bf16_t, h);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32), lo in bits 0..15.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    bf16x2_t v;
+    v[0] = static_cast<__bf16>(lo);
+    v[1] = static_cast<__bf16>(hi);
+    return __builtin_bit_cast(uint32_t, v);
 }
+
+// Hardware reciprocal (about 1 ulp); used where a correctly rounded division
+// is not needed.
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // 2^x on the hardware exponential unit (inputs are already in log2 units).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -58,6 +68,39 @@ template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t x) { return b
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f32_to_bf16(x); }
+
+// DPP lane exchanges (no LDS traffic). Row = 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16 lanes
+constexpr int kDppRowShr1 = 0x111;
+
+// All-reduce over aligned groups of 8 lanes.
+__device__ __forceinline__ float group8_max(float v) {
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    return fmaxf(v, dpp<kDppHalfMirror>(v));
+}
+__device__ __forceinline__ float group8_sum(float v) {
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    return v + dpp<kDppHalfMirror>(v);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(v, o, 64);
+        if (lane >= o) v += y;
+    }
+    return v;
+}
 
 // Wave-wide (64 lanes) butterfly reductions.
 __device__ __forceinline__ float wave_max(float v) {

@@ -48,12 +48,16 @@ struct RingFillArgs {
 
 // Segment plan of the chunked prefill: chunks of 64 tokens grouped into
 // n_seg segments of cps chunks (the last segment may be shorter).
+// Workspace: carry records (state entering each segment but the first, plus
+// the segment's total log2 decay), then one private d*d fp32 slot per output
+// workgroup that holds the running state between chunks.
 struct PrefillPlan {
-    int64_t n_chunks;  // ceil(T / 64)
-    int64_t cps;       // chunks per segment
-    int64_t n_seg;     // ceil(n_chunks / cps)
+    int64_t n_chunks;        // ceil(T / 64)
+    int64_t cps;             // chunks per segment
+    int64_t n_seg;           // ceil(n_chunks / cps)
     size_t carry_floats;     // floats per carry record: d*d + d
-    size_t workspace_bytes;  // B * H_kv * (n_seg - 1) * carry_floats * 4
+    size_t state_offset;     // floats before the state slots: B * H_kv * (n_seg - 1) * carry_floats
+    size_t workspace_bytes;  // (state_offset + B * H_kv * n_seg * d*d) * 4
 };
 
 struct PrefillArgs {

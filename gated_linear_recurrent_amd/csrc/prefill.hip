@@ -43,6 +43,16 @@ __device__ __forceinline__ int ltid() {
     return t;
 }
 
+// Channel-major tiles ([c][64 keys]: V^T and the transposed state key operand)
+// store key j at position key_pos(j): inside each 32-key group the two
+// 16-key halves are interleaved in units of 4, so positions 8g .. 8g+7 of a
+// group hold keys 4g..4g+3 and 16+4g..16+4g+3. One 16-byte read then yields
+// the operand of a key-tile pair in the MFMA order used for the score
+// matrices, and two consecutive keys (2m, 2m+1) stay adjacent.
+__device__ __forceinline__ int key_pos(int j) {
+    return (j & 32) | (((j & 15) >> 2) << 3) | (((j >> 4) & 1) << 2) | (j & 3);
+}
+
 // ------------------------------------------------------------- LDS layout
 template <typename T, int D, int GATE, bool FULL>
 struct Layout {
@@ -67,7 +77,7 @@ struct Layout {
     static constexpr size_t TMP_FLOATS = size_t(kPThreads) + 3 * D;
     static constexpr bool TMP_ALIASED = FULL && (ST_BYTES >= TMP_FLOATS * 4);
     static constexpr size_t SMALL_OFF = TMP_ALIASED ? TMP_OFF : TMP_OFF + TMP_FLOATS * 4;
-    // small persistent arrays: kmax[64] kinv[64] b2s[64] dec[D] mref[D] badlist[D] badmask[D/32] nbad
+    // small persistent arrays: kmax[64] kinv[64] b2s[64] dec[D] mref[D] badlist[D] badmask[D/32] nbad, exact
     static constexpr size_t SMALL_WORDS = 64 * 3 + D * 3 + D / 32 + 4;
     static constexpr size_t TOTAL = SMALL_OFF + SMALL_WORDS * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS budget of a gfx950 workgroup exceeded");
@@ -93,6 +103,7 @@ struct Smem {
     int* badlist; // [D]
     uint32_t* badmask;  // [D/32]
     int* nbad;
+    int* exact;  // scalar gate: this chunk's decay range needs the exact per-pair path
 
     __device__ explicit Smem(char* base) {
         K = reinterpret_cast<T*>(base + L::K_OFF);
@@ -114,6 +125,7 @@ struct Smem {
         badlist = reinterpret_cast<int*>(mref + D);
         badmask = reinterpret_cast<uint32_t*>(badlist + D);
         nbad = reinterpret_cast<int*>(badmask + D / 32);
+        exact = nbad + 1;
     }
 };
 
@@ -124,6 +136,7 @@ struct PrefillParams {
     void* o;
     float* S_T;
     float* carry;
+    float* state_slots;
     int64_t T;
     int64_t n_chunks;
     int64_t cps;
@@ -135,31 +148,90 @@ struct PrefillParams {
 };
 
 // ------------------------------------------------------------ chunk loading
-// K rows go to LDS as they are; V rows are written transposed (V^T[c][j]).
-// Rows past the end of the sequence are zero.
+// K rows go to LDS as they are; V is written transposed (V^T[c][key_pos(j)]),
+// two keys per 32-bit (bf16) or 64-bit (fp32) store so that the lanes of a
+// wave write one contiguous row segment. Rows past the end are zero.
+// The global loads (issue) and the LDS stores (commit) are separate steps so
+// that other loads can be issued in between.
+template <typename T, int D>
+struct ChunkRegs {
+    static constexpr int VPL = 16 / sizeof(T);
+    static constexpr int PPR = D / VPL;                                  // 16-byte pieces per row
+    static constexpr int NK = (64 * PPR + kPThreads - 1) / kPThreads;    // K pieces per thread
+    static constexpr int NV = (32 * PPR + kPThreads - 1) / kPThreads;    // V row pairs per thread
+    uint4 k[NK];
+    uint4 v0[NV], v1[NV];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void load_chunk_issue(ChunkRegs<T, D>& cr, const T* kbase, const T* vbase,
+                                                 int64_t row_stride, int64_t t0, int nvalid) {
+    typedef ChunkRegs<T, D> CR;
+    const int tid = ltid();
+#pragma unroll
+    for (int n = 0; n < CR::NK; ++n) {
+        const int idx = tid + n * kPThreads;
+        const int j = idx / CR::PPR;
+        const int c0 = (idx % CR::PPR) * CR::VPL;
+        cr.k[n] = make_uint4(0, 0, 0, 0);
+        if (idx < 64 * CR::PPR && j < nvalid)
+            cr.k[n] = *reinterpret_cast<const uint4*>(kbase + (t0 + j) * row_stride + c0);
+    }
+#pragma unroll
+    for (int n = 0; n < CR::NV; ++n) {
+        const int idx = tid + n * kPThreads;
+        const int j0 = 2 * (idx & 31);
+        const int c0 = (idx >> 5) * CR::VPL;
+        cr.v0[n] = make_uint4(0, 0, 0, 0);
+        cr.v1[n] = make_uint4(0, 0, 0, 0);
+        if (idx < 32 * CR::PPR) {
+            if (j0 < nvalid) cr.v0[n] = *reinterpret_cast<const uint4*>(vbase + (t0 + j0) * row_stride + c0);
+            if (j0 + 1 < nvalid) cr.v1[n] = *reinterpret_cast<const uint4*>(vbase + (t0 + j0 + 1) * row_stride + c0);
+        }
+    }
+}
+
+template <typename T, int D, int GATE, bool FULL>
+__device__ __forceinline__ void load_chunk_commit(const Smem<T, D, GATE, FULL>& sm, int slot, const ChunkRegs<T, D>& cr) {
+    typedef Layout<T, D, GATE, FULL> L;
+    typedef ChunkRegs<T, D> CR;
+    T* Ks = sm.K + slot * 64 * L::DP;
+    T* Vts = sm.Vt + slot * D * L::JP;
+    const int tid = ltid();
+#pragma unroll
+    for (int n = 0; n < CR::NK; ++n) {
+        const int idx = tid + n * kPThreads;
+        if (idx < 64 * CR::PPR)
+            *reinterpret_cast<uint4*>(Ks + (idx / CR::PPR) * L::DP + (idx % CR::PPR) * CR::VPL) = cr.k[n];
+    }
+#pragma unroll
+    for (int n = 0; n < CR::NV; ++n) {
+        const int idx = tid + n * kPThreads;
+        if (idx >= 32 * CR::PPR) continue;
+        const int j0 = 2 * (idx & 31);
+        const int c0 = (idx >> 5) * CR::VPL;
+        const T* e0 = reinterpret_cast<const T*>(&cr.v0[n]);
+        const T* e1 = reinterpret_cast<const T*>(&cr.v1[n]);
+        T* dst = Vts + c0 * L::JP + key_pos(j0);
+#pragma unroll
+        for (int e = 0; e < CR::VPL; ++e) {
+            if constexpr (sizeof(T) == 2) {
+                *reinterpret_cast<uint32_t*>(dst + e * L::JP) =
+                    static_cast<uint32_t>(e0[e]) | (static_cast<uint32_t>(e1[e]) << 16);
+            } else {
+                *reinterpret_cast<float2*>(dst + e * L::JP) = make_float2(e0[e], e1[e]);
+            }
+        }
+    }
+}
+
 template <typename T, int D, int GATE, bool FULL>
 __device__ __forceinline__ void load_chunk(const Smem<T, D, GATE, FULL>& sm, int slot,
                                            const T* kbase, const T* vbase, int64_t row_stride,
                                            int64_t t0, int nvalid) {
-    typedef Layout<T, D, GATE, FULL> L;
-    constexpr int VPL = 16 / sizeof(T);
-    constexpr int PPR = D / VPL;
-    T* Ks = sm.K + slot * 64 * L::DP;
-    T* Vts = sm.Vt + slot * D * L::JP;
-    for (int idx = ltid(); idx < 64 * PPR; idx += kPThreads) {
-        const int j = idx / PPR;
-        const int c0 = (idx % PPR) * VPL;
-        uint4 kk = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-        if (j < nvalid) {
-            const int64_t off = (t0 + j) * row_stride + c0;
-            kk = *reinterpret_cast<const uint4*>(kbase + off);
-            vv = *reinterpret_cast<const uint4*>(vbase + off);
-        }
-        *reinterpret_cast<uint4*>(Ks + j * L::DP + c0) = kk;
-        const T* ve = reinterpret_cast<const T*>(&vv);
-#pragma unroll
-        for (int e = 0; e < VPL; ++e) Vts[(c0 + e) * L::JP + j] = ve[e];
-    }
+    ChunkRegs<T, D> cr;
+    load_chunk_issue<T, D>(cr, kbase, vbase, row_stride, t0, nvalid);
+    load_chunk_commit(sm, slot, cr);
 }
 
 template <typename T, int D, int GATE, bool FULL>
@@ -173,35 +245,43 @@ __device__ __forceinline__ void zero_slot(const Smem<T, D, GATE, FULL>& sm, int 
 
 // ------------------------------------------------------- per-chunk gate work
 // B1: softmax statistics of every key row (max, 1/sum) and, for the scalar
-// gate, ell2_j = log2 sigmoid(mean_c k_j[c]). Rows past the end get 1/sum = 0
-// so phi(k) vanishes there, and ell2 = 0.
+// gate, ell2_j = log2 sigmoid(mean_c k_j[c]). Eight lanes share a row (DPP
+// reductions); rows past the end get 1/sum = 0 so phi(k) vanishes there, and
+// ell2 = 0.
 template <typename T, int D, int GATE, bool FULL>
 __device__ __forceinline__ void key_row_stats(const Smem<T, D, GATE, FULL>& sm, int slot, int nvalid) {
     typedef Layout<T, D, GATE, FULL> L;
-    constexpr int EPL = D / 64;
-    const int lane = ltid() & 63, wave = ltid() >> 6;
-    const T* Ks = sm.K + slot * 64 * L::DP;
-    for (int j = wave; j < 64; j += kPWaves) {
-        float x[EPL];
-        float mx = -INFINITY, s = 0.f;
+    static_assert(kPThreads == 64 * 8, "eight lanes per key row");
+    constexpr int VPL = 16 / sizeof(T);
+    constexpr int NLD = D / (8 * VPL);  // 16-byte loads per lane
+    const int tid = ltid();
+    const int j = tid >> 3, part = tid & 7;
+    const T* row = sm.K + slot * 64 * L::DP + j * L::DP + part * VPL;
+    float x[NLD * VPL];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            x[e] = to_f32(Ks[j * L::DP + lane + 64 * e]);
-            mx = fmaxf(mx, x[e]);
-            s += x[e];
-        }
-        mx = wave_max(mx);
-        float se = 0.f;
+    for (int q = 0; q < NLD; ++q) {
+        const uint4 u = *reinterpret_cast<const uint4*>(row + q * 8 * VPL);
+        const T* e = reinterpret_cast<const T*>(&u);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) se += fast_exp2((x[e] - mx) * kLog2e);
-        se = wave_sum(se);
-        if (GATE == 0) s = wave_sum(s);
-        if (lane == 0) {
-            const bool ok = j < nvalid;
-            sm.kmax[j] = mx;
-            sm.kinv[j] = ok ? 1.0f / se : 0.0f;
-            if (GATE == 0) sm.b2s[j] = ok ? log2_sigmoid(s * (1.0f / D)) : 0.0f;
-        }
+        for (int i = 0; i < VPL; ++i) x[q * VPL + i] = to_f32(e[i]);
+    }
+    float mx = -INFINITY, sraw = 0.f;
+#pragma unroll
+    for (int i = 0; i < NLD * VPL; ++i) {
+        mx = fmaxf(mx, x[i]);
+        sraw += x[i];
+    }
+    mx = group8_max(mx);
+    float se = 0.f;
+#pragma unroll
+    for (int i = 0; i < NLD * VPL; ++i) se += fast_exp2((x[i] - mx) * kLog2e);
+    se = group8_sum(se);
+    if (GATE == 0) sraw = group8_sum(sraw);
+    if (part == 0) {
+        const bool ok = j < nvalid;
+        sm.kmax[j] = mx;
+        sm.kinv[j] = ok ? fast_rcp(se) : 0.0f;
+        if (GATE == 0) sm.b2s[j] = ok ? log2_sigmoid(sraw * (1.0f / D)) : 0.0f;
     }
 }
 
@@ -351,6 +431,30 @@ __device__ __forceinline__ void load_state(const float* src, f32x4_t (&acc)[Stat
     }
 }
 
+// Private state slot of an output workgroup, in accumulator order: every
+// lane moves one float4 per tile, so each access is a contiguous 1 KiB per wave.
+template <int D>
+__device__ __forceinline__ void load_slot(const float* slot, f32x4_t (&acc)[StateTiles<D>::TPW]) {
+    typedef StateTiles<D> ST;
+    const int tid = ltid();
+    const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+    for (int u = 0; u < ST::TPW; ++u) {
+        const float4 v = *reinterpret_cast<const float4*>(slot + (size_t((wave * ST::TPW + u) * 64 + lane)) * 4);
+        acc[u] = f32x4_t{v.x, v.y, v.z, v.w};
+    }
+}
+template <int D>
+__device__ __forceinline__ void store_slot(float* slot, const f32x4_t (&acc)[StateTiles<D>::TPW]) {
+    typedef StateTiles<D> ST;
+    const int tid = ltid();
+    const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+    for (int u = 0; u < ST::TPW; ++u)
+        *reinterpret_cast<float4*>(slot + (size_t((wave * ST::TPW + u) * 64 + lane)) * 4) =
+            make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+}
+
 // -------------------------------------------- gate prep shared by P1 and P3
 // After this: dec, mref, badlist/badmask/nbad, F (P3, vector) and the
 // transposed state key operand Kb[c][j] = phik_j[c] 2^(b_last[c] - b_j[c]).
@@ -366,16 +470,37 @@ __device__ __forceinline__ void gate_prep(const Smem<T, D, GATE, FULL>& sm, int 
         scalar_gate_scan(sm);
         __syncthreads();
         const float bl = sm.b2s[nvalid - 1];
-        for (int idx = ltid(); idx < 64 * D; idx += kPThreads) {
-            const int j = idx & 63, c = idx >> 6;
-            const float kv = to_f32(Ks[j * L::DP + c]);
-            sm.Kb[c * L::JP + j] =
-                from_f32<T>(sm.kinv[j] * fast_exp2((kv - sm.kmax[j]) * kLog2e + bl - sm.b2s[j]));
+        constexpr int VPL = 16 / sizeof(T);
+        for (int idx = ltid(); idx < 32 * (D / VPL); idx += kPThreads) {
+            const int j0 = 2 * (idx & 31);
+            const int c0 = (idx >> 5) * VPL;
+            const uint4 u0 = *reinterpret_cast<const uint4*>(Ks + j0 * L::DP + c0);
+            const uint4 u1 = *reinterpret_cast<const uint4*>(Ks + (j0 + 1) * L::DP + c0);
+            const T* e0 = reinterpret_cast<const T*>(&u0);
+            const T* e1 = reinterpret_cast<const T*>(&u1);
+            const float m0 = sm.kmax[j0], m1 = sm.kmax[j0 + 1];
+            const float f0 = bl - sm.b2s[j0], f1 = bl - sm.b2s[j0 + 1];
+            const float s0 = sm.kinv[j0], s1 = sm.kinv[j0 + 1];
+            T* dst = sm.Kb + c0 * L::JP + key_pos(j0);
+#pragma unroll
+            for (int e = 0; e < VPL; ++e) {
+                const float a = s0 * fast_exp2((to_f32(e0[e]) - m0) * kLog2e + f0);
+                const float b = s1 * fast_exp2((to_f32(e1[e]) - m1) * kLog2e + f1);
+                if constexpr (sizeof(T) == 2) {
+                    *reinterpret_cast<uint32_t*>(dst + e * L::JP) = pack_bf16x2(a, b);
+                } else {
+                    *reinterpret_cast<float2*>(dst + e * L::JP) = make_float2(a, b);
+                }
+            }
         }
+        // reference for the factorised intra-chunk decay: the middle token
+        const float m = sm.b2s[nvalid - 1 < 31 ? nvalid - 1 : 31];
+        const bool ex = fmaxf(sm.b2s[0] - m, m - bl) > kEmax2;
         if (ltid() < D) {
             sm.dec[ltid()] = fast_exp2(bl);
-            sm.mref[ltid()] = 0.0f;
+            sm.mref[ltid()] = ex ? 0.0f : m;
         }
+        if (ltid() == 0) *sm.exact = ex ? 1 : 0;
     } else {
         vector_gate_scan<T, D, GATE, FULL, TPT>(sm, slot, nvalid, b2);
         __syncthreads();
@@ -398,7 +523,7 @@ __device__ __forceinline__ void gate_prep(const Smem<T, D, GATE, FULL>& sm, int 
         for (int jj = 0; jj < TPT; ++jj) {
             const int j = part * TPT + jj;
             const float kv = to_f32(Ks[j * L::DP + c]);
-            sm.Kb[c * L::JP + j] =
+            sm.Kb[c * L::JP + key_pos(j)] =
                 from_f32<T>(sm.kinv[j] * fast_exp2((kv - sm.kmax[j]) * kLog2e + bl - b2[jj]));
             if (FULL) sm.F[j * L::FP + c] = bad ? b2[jj] : alpha * fast_exp2(b2[jj] - mref);
         }
@@ -413,10 +538,24 @@ __device__ __forceinline__ void intra_key_operand(const Smem<T, D, GATE, FULL>& 
     typedef Layout<T, D, GATE, FULL> L;
     const T* Ks = sm.K + slot * 64 * L::DP;
     if (GATE == 0) {
-        for (int idx = ltid(); idx < 64 * D; idx += kPThreads) {
-            const int j = idx / D, c = idx % D;
-            const float kv = to_f32(Ks[j * L::DP + c]);
-            sm.Kb[j * L::DP + c] = from_f32<T>(sm.kinv[j] * fast_exp2((kv - sm.kmax[j]) * kLog2e));
+        constexpr int VPL = 16 / sizeof(T);
+        for (int idx = ltid(); idx < 64 * (D / VPL); idx += kPThreads) {
+            const int j = idx / (D / VPL);
+            const int c0 = (idx % (D / VPL)) * VPL;
+            const uint4 u = *reinterpret_cast<const uint4*>(Ks + j * L::DP + c0);
+            const T* e = reinterpret_cast<const T*>(&u);
+            const float m = sm.kmax[j];
+            const float sc = sm.kinv[j] * (*sm.exact ? 1.0f : fast_exp2(sm.mref[0] - sm.b2s[j]));
+            float y[VPL];
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) y[i] = sc * fast_exp2((to_f32(e[i]) - m) * kLog2e);
+            if constexpr (sizeof(T) == 2) {
+                *reinterpret_cast<uint4*>(sm.Kb + j * L::DP + c0) =
+                    make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                               pack_bf16x2(y[6], y[7]));
+            } else {
+                *reinterpret_cast<float4*>(sm.Kb + j * L::DP + c0) = make_float4(y[0], y[1], y[2], y[3]);
+            }
         }
     } else {
         const int c = ltid() % D;
@@ -453,10 +592,13 @@ __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams 
     float lg = 0.f;  // total log2 decay of the segment for channel threadIdx.x (< D)
     const int64_t c_begin = int64_t(s) * p.cps;
     const int64_t c_end = c_begin + p.cps;  // never the last segment: always whole chunks
+    ChunkRegs<T, D> cr;
+    load_chunk_issue<T, D>(cr, kbase, vbase, row_stride, c_begin * kChunk, kChunk);
     for (int64_t c = c_begin; c < c_end; ++c) {
-        const int64_t t0 = c * kChunk;
-        load_chunk(sm, 0, kbase, vbase, row_stride, t0, kChunk);
+        load_chunk_commit(sm, 0, cr);
         __syncthreads();
+        // the next chunk's K/V are in flight while this one is processed
+        if (c + 1 < c_end) load_chunk_issue<T, D>(cr, kbase, vbase, row_stride, (c + 1) * kChunk, kChunk);
         float b2[TPT];
         gate_prep<T, D, GATE, false, TPT>(sm, 0, kChunk, p.alpha, b2);
         __syncthreads();
@@ -516,7 +658,6 @@ struct ItemCtx {
     int64_t row0;      // b * T + t0 (token row of the chunk start)
     int H_q;
     int hq;
-    int I;             // 16-row query tile inside the chunk
     int nvalid;
     int window;
     bool have_prev;    // a previous chunk exists (chunk index > 0)
@@ -524,9 +665,47 @@ struct ItemCtx {
     int cur;
 };
 
-template <typename T, int D, int GATE, int I>
-__device__ __forceinline__ void output_item(const Smem<T, D, GATE, true>& sm, const ItemCtx<T, D, GATE>& x,
-                                            int lane) {
+// One wave computes the outputs of 32 query rows (query tiles I0 = 2 IB and
+// I0 + 1) of one query head over all of d_v. Every LDS operand fragment it
+// reads (key tiles, K~, S'^T, V^T) feeds both query tiles.
+// Scores are kept per (query tile s, key tile kt) in the accumulator layout:
+// lane (col, g) holds keys 16 kt + 4 g + r for query 16 (I0 + s) + col.
+// The intra-chunk scores (keys of this chunk, j <= i) and the window weights
+// (keys i-w < j <= i) multiply the same V rows, so they are added into one
+// operand per key tile before the product with V.
+// Raw query fragments of a 32-row block: lane (col, g) holds row 16 (I0 + s) + col,
+// elements KSTEP k + KPL g .. + KPL - 1. Rows past the end are zero.
+template <typename T, int D>
+struct QFrags {
+    typename Mfma<T>::frag f[2][D / Mfma<T>::KSTEP];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void load_q_block(QFrags<T, D>& qf, const T* q, int64_t row0, int H_q, int hq, int i0,
+                                             int nvalid, int lane) {
+    typedef Mfma<T> M;
+    const int col = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int i = i0 + 16 * s + col;
+        const bool ok = i < nvalid;
+        const T* qrow = q + ((row0 + (ok ? i : 0)) * H_q + hq) * D;
+#pragma unroll
+        for (int k = 0; k < D / M::KSTEP; ++k) {
+            if constexpr (sizeof(T) == 2) {
+                const uint4 u = ok ? *reinterpret_cast<const uint4*>(qrow + M::KSTEP * k + M::KPL * g)
+                                   : make_uint4(0, 0, 0, 0);
+                qf.f[s][k] = __builtin_bit_cast(typename M::frag, u);
+            } else {
+                qf.f[s][k] = ok ? reinterpret_cast<const float*>(qrow)[M::KSTEP * k + g] : 0.0f;
+            }
+        }
+    }
+}
+
+template <typename T, int D, int GATE, int IB>
+__device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, const ItemCtx<T, D, GATE>& x,
+                                             int lane, const QFrags<T, D>& qin) {
     typedef Layout<T, D, GATE, true> L;
     typedef Mfma<T> M;
     typedef typename M::frag Frag;
@@ -534,238 +713,311 @@ __device__ __forceinline__ void output_item(const Smem<T, D, GATE, true>& sm, co
     constexpr int KPL = M::KPL;
     constexpr int NT = D / 16;
     constexpr bool BF = sizeof(T) == 2;
+    constexpr int I0 = 2 * IB;          // first query tile of the block
+    constexpr int KT0 = I0 - 4;         // first key tile (relative to the chunk start)
+    constexpr int NKT = 6;              // key tiles KT0 .. I0 + 1
     const int col = lane & 15, g = lane >> 4;
-    const int i_loc = 16 * I + col;
-    const bool row_ok = i_loc < x.nvalid;
-    const T* qrow = x.q + ((x.row0 + (row_ok ? i_loc : 0)) * x.H_q + x.hq) * D;
+    const int dl = col - 4 * g;         // i - j = 16 (I - kt) + dl - r inside a tile pair
     const T* Kcur = sm.K + x.cur * 64 * L::DP;
     const T* Kprv = sm.K + (x.cur ^ 1) * 64 * L::DP;
     const T* Vcur = sm.Vt + x.cur * D * L::JP;
     const T* Vprv = sm.Vt + (x.cur ^ 1) * D * L::JP;
     const int nbad = GATE ? *sm.nbad : 0;
+    const bool exact = GATE ? false : (*sm.exact != 0);
+    const bool full_window = x.window >= 64;
 
-    // ---- query row. qr: raw fragment (window operand). qt: unnormalised
-    // e^(q - max) times the gate factor (recurrence operand); the softmax
-    // normaliser qinv is applied to the products, which are linear in phi(q).
-    Frag qr[KS];
+    int i_loc[2];
+    bool row_ok[2];
+    const T* qrow[2];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        if constexpr (BF) {
-            const uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qrow + M::KSTEP * s + KPL * g)
-                                   : make_uint4(0, 0, 0, 0);
-            qr[s] = __builtin_bit_cast(Frag, u);
-        } else {
-            qr[s] = row_ok ? reinterpret_cast<const float*>(qrow)[M::KSTEP * s + g] : 0.0f;
-        }
+    for (int s = 0; s < 2; ++s) {
+        i_loc[s] = 16 * (I0 + s) + col;
+        row_ok[s] = i_loc[s] < x.nvalid;
+        qrow[s] = x.q + ((x.row0 + (row_ok[s] ? i_loc[s] : 0)) * x.H_q + x.hq) * D;
     }
-    auto qval = [&](int s, int i) -> float {
+
+    // ---- query rows: raw fragments (window operand). The recurrence operand
+    // (built below) is e^(q - max) times the gate factor; the softmax
+    // normaliser of phi(q) and alpha are applied to the products instead.
+    Frag qr[2][KS], qt[2][KS];
+    float qmax[2], qinv[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int k = 0; k < KS; ++k) qr[s][k] = qin.f[s][k];
+    auto qval = [&](int s, int k, int i) -> float {
         if constexpr (BF) {
-            const uint4 u = __builtin_bit_cast(uint4, qr[s]);
+            const uint4 u = __builtin_bit_cast(uint4, qr[s][k]);
             const uint32_t w = (i >> 1) == 0 ? u.x : (i >> 1) == 1 ? u.y : (i >> 1) == 2 ? u.z : u.w;
             return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
         } else {
-            return __builtin_bit_cast(float, qr[s]);
+            return __builtin_bit_cast(float, qr[s][k]);
         }
     };
-    float qmax = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+    for (int s = 0; s < 2; ++s) {
+        float m = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < KPL; ++i) qmax = fmaxf(qmax, qval(s, i));
-    qmax = group4_max(qmax);
-    Frag qt[KS];
-    float qsum = 0.f;
+        for (int k = 0; k < KS; ++k)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        float tmp[KPL];
-#pragma unroll
-        for (int i = 0; i < KPL; ++i) {
-            const float e = fast_exp2((qval(s, i) - qmax) * kLog2e);
-            qsum += e;
-            if (GATE) {
-                const int ch = M::KSTEP * s + KPL * g + i;
-                float f = sm.F[i_loc * L::FP + ch];
-                if (nbad && ((sm.badmask[ch >> 5] >> (ch & 31)) & 1u)) f = 0.0f;
-                tmp[i] = e * f;
-            } else {
-                tmp[i] = e;
-            }
-        }
-        qt[s] = M::pack(tmp);
+            for (int i = 0; i < KPL; ++i) m = fmaxf(m, qval(s, k, i));
+        qmax[s] = group4_max(m);
     }
-    // alpha folded here; for the vector gate F already carries alpha
-    const float qinv = (GATE ? 1.0f : x.alpha) / group4_sum(qsum);
 
-    // ---- sliding-window scores over key tiles kt = I-4 .. I (relative to
-    // the chunk start; negative tiles live in the previous chunk's slot)
-    constexpr int U0 = I - 4;
-    bool live[5];
-    float pw[5][4];
+    // ---- window scores over key tiles KT0 .. I0+1; query tile s uses
+    // u = s .. s + 4. A key is valid when 0 <= i - j < window. With the full
+    // 64-key window only the diagonal tile (u = s + 4) and the window's first
+    // tile (u = s) are partial.
+    float sc[2][NKT][4];
     {
         const float lscale = kLog2e * rsqrtf(static_cast<float>(D));
-        float lmax = -INFINITY;
+        float lmax[2] = {-INFINITY, -INFINITY};
+        const unsigned w = static_cast<unsigned>(x.window);
 #pragma unroll
-        for (int u = 0; u < 5; ++u) {
-            const int kt = U0 + u;
-            live[u] = (kt >= 0 || x.have_prev) && (16 * kt + 15 > 16 * I - x.window);
+        for (int u = 0; u < NKT; ++u) {
+            const int kt = KT0 + u;
+            bool live[2];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pw[u][r] = -INFINITY;
-            if (live[u]) {
+            for (int s = 0; s < 2; ++s) {
+                live[s] = u >= s && u <= s + 4 && (kt >= 0 || x.have_prev) &&
+                          (16 * kt + 15 > 16 * (I0 + s) - x.window);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sc[s][u][r] = -INFINITY;
+            }
+            if (live[0] || live[1]) {
                 const T* krow = kt >= 0 ? Kcur + (16 * kt + col) * L::DP : Kprv + (16 * kt + 64 + col) * L::DP;
-                f32x4_t d4 = zero4();
+                f32x4_t d4[2] = {zero4(), zero4()};
 #pragma unroll
-                for (int s = 0; s < KS; ++s) d4 = M::mma(M::load(krow + M::KSTEP * s + KPL * g), qr[s], d4);
+                for (int k = 0; k < KS; ++k) {
+                    const Frag a = M::load(krow + M::KSTEP * k + KPL * g);
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+                        if (live[s]) d4[s] = M::mma(a, qr[s][k], d4[s]);
+                }
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    if (!live[s]) continue;
+                    const int dt = 16 * (I0 + s - kt);  // 16 (I - kt), compile-time
+                    const bool partial = (u == s) || (u == s + 4) || !full_window;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float v = d4[s][r] * lscale;
+                        if (partial) v = static_cast<unsigned>(dt + dl - r) < w ? v : -INFINITY;
+                        sc[s][u][r] = v;
+                        lmax[s] = fmaxf(lmax[s], v);
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);  // bound the number of key fragments in flight
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const float m = group4_max(lmax[s]);
+            float sum = 0.f;
+#pragma unroll
+            for (int u = 0; u < NKT; ++u)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int j = 16 * kt + 4 * g + r;
-                    const bool ok = (j <= i_loc) && (j > i_loc - x.window);
-                    pw[u][r] = ok ? d4[r] * lscale : -INFINITY;
-                    lmax = fmaxf(lmax, pw[u][r]);
+                    const float e = fast_exp2(sc[s][u][r] - m);  // exp2(-inf) = 0 for masked keys
+                    sc[s][u][r] = e;
+                    sum += e;
+                }
+            const float ps = (1.0f - x.alpha) * fast_rcp(group4_sum(sum));
+#pragma unroll
+            for (int u = 0; u < NKT; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sc[s][u][r] *= ps;
+        }
+    }
+
+    // recurrence operand (built after the window scores so qr can retire)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        float sum = 0.f;
+        const float mq = qmax[s] * kLog2e;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            float tmp[KPL];
+            float f[KPL];
+            if (GATE) {
+                const float* fr = sm.F + i_loc[s] * L::FP + M::KSTEP * k + KPL * g;
+#pragma unroll
+                for (int i = 0; i < KPL; i += 4) {
+                    const float4 f4 = *reinterpret_cast<const float4*>(fr + i);
+                    f[i] = f4.x;
+                    if (i + 1 < KPL) f[i + 1] = f4.y;
+                    if (i + 2 < KPL) f[i + 2] = f4.z;
+                    if (i + 3 < KPL) f[i + 3] = f4.w;
                 }
             }
-        }
-        lmax = group4_max(lmax);
-        float lsum = 0.f;
 #pragma unroll
-        for (int u = 0; u < 5; ++u)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float e = live[u] ? fast_exp2(pw[u][r] - lmax) : 0.0f;
-                pw[u][r] = e;
-                lsum += e;
+            for (int i = 0; i < KPL; ++i) {
+                const float e = fast_exp2(fmaf(qval(s, k, i), kLog2e, -mq));
+                sum += e;
+                if (GATE) {
+                    const int ch = M::KSTEP * k + KPL * g + i;
+                    float fi = f[i];
+                    if (nbad && ((sm.badmask[ch >> 5] >> (ch & 31)) & 1u)) fi = 0.0f;
+                    tmp[i] = e * fi;
+                } else {
+                    tmp[i] = e;
+                }
             }
-        const float pscale = (1.0f - x.alpha) / group4_sum(lsum);
-#pragma unroll
-        for (int u = 0; u < 5; ++u)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) pw[u][r] *= pscale;
+            qt[s][k] = M::pack(tmp);
+        }
+        qinv[s] = (GATE ? 1.0f : x.alpha) * fast_rcp(group4_sum(sum));
     }
 
-    // ---- intra-chunk scores A[i][j] = Q~_i . K~_j, causal; lane holds
-    // j = 16J + 4g + r for query i = i_loc
-    float aw[I + 1][4];
+    // ---- intra-chunk scores on key tiles J = 0 .. I0+s, added into the same
+    // per-key-tile operand. Tiles below the diagonal are whole; the diagonal
+    // tile keeps j <= i. Scalar gate: the decay 2^(b_i - b_j) is split into
+    // 2^(b_i - m) (here) and 2^(m - b_j) (in the key operand), or applied per
+    // pair when the chunk's decay range is too wide to split.
+    float bq[2] = {0.f, 0.f};
+    float qsc[2];
+    float4 bk[I0 + 2];
 #pragma unroll
-    for (int J = 0; J <= I; ++J) {
-        f32x4_t a4 = zero4();
+    for (int s = 0; s < 2; ++s) {
+        if (GATE == 0) bq[s] = sm.b2s[i_loc[s]];
+        qsc[s] = qinv[s] * ((GATE == 0 && !exact) ? fast_exp2(bq[s] - sm.mref[0]) : 1.0f);
+    }
+    if (GATE == 0 && exact) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-            a4 = M::mma(M::load(sm.Kb + (16 * J + col) * L::DP + M::KSTEP * s + KPL * g), qt[s], a4);
+        for (int J = 0; J <= I0 + 1; ++J) bk[J] = *reinterpret_cast<const float4*>(sm.b2s + 16 * J + 4 * g);
+    }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) a4[r] *= qinv;
-        for (int nb = 0; nb < nbad; ++nb) {
-            const int c = sm.badlist[nb];
-            const float qc = row_ok ? to_f32(qrow[c]) : 0.0f;
-            const float coef = x.alpha * fast_exp2((qc - qmax) * kLog2e) * qinv;
-            const float b2i = sm.F[i_loc * L::FP + c];
+    for (int J = 0; J <= I0 + 1; ++J) {
+        f32x4_t d4[2] = {zero4(), zero4()};
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            const Frag a = M::load(sm.Kb + (16 * J + col) * L::DP + M::KSTEP * k + KPL * g);
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                if (J <= I0 + s) d4[s] = M::mma(a, qt[s][k], d4[s]);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if (J > I0 + s) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) d4[s][r] *= qsc[s];
+            for (int nb = 0; nb < nbad; ++nb) {
+                const int c = sm.badlist[nb];
+                const float qc = row_ok[s] ? to_f32(qrow[s][c]) : 0.0f;
+                const float coef = x.alpha * fast_exp2((qc - qmax[s]) * kLog2e) * qinv[s];
+                const float b2i = sm.F[i_loc[s] * L::FP + c];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * J + 4 * g + r;
+                    const float phik = sm.kinv[j] * fast_exp2((to_f32(Kcur[j * L::DP + c]) - sm.kmax[j]) * kLog2e);
+                    const float term = coef * phik * fast_exp2(fminf(b2i - sm.F[j * L::FP + c], 0.0f));
+                    d4[s][r] += j <= i_loc[s] ? term : 0.0f;
+                }
+            }
+            if (GATE == 0 && exact) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float bj = r == 0 ? bk[J].x : r == 1 ? bk[J].y : r == 2 ? bk[J].z : bk[J].w;
+                    d4[s][r] *= fast_exp2(fminf(bq[s] - bj, 0.0f));
+                }
+            }
+            const int u = J - KT0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int j = 16 * J + 4 * g + r;
-                const float phik = sm.kinv[j] * fast_exp2((to_f32(Kcur[j * L::DP + c]) - sm.kmax[j]) * kLog2e);
-                const float term = coef * phik * fast_exp2(fminf(b2i - sm.F[j * L::FP + c], 0.0f));
-                a4[r] += j <= i_loc ? term : 0.0f;
+                float val = d4[s][r];
+                if (J == I0 + s) val = dl >= r ? val : 0.0f;  // diagonal tile: j <= i
+                sc[s][u][r] += val;
             }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int j = 16 * J + 4 * g + r;
-            float val = a4[r];
-            if (GATE == 0) val *= fast_exp2(fminf(sm.b2s[i_loc] - sm.b2s[j], 0.0f));
-            aw[J][r] = j <= i_loc ? val : 0.0f;
-        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- operand fragments of the score matrices. bf16: a k-step of 32 keys
-    // takes two 16-key tiles; the V^T operand below reads the same key order.
-    constexpr int NA = (I + 2) / 2;
-    Frag af[NA], pf[3];
+    // ---- bf16: pack the combined scores of the aligned key-tile pairs
+    // (u = 2G, 2G + 1); tiles outside query tile s's range u in [s, s+4] are 0.
+    Frag pf[2][3];
     if constexpr (BF) {
 #pragma unroll
-        for (int pj = 0; pj < NA; ++pj) {
-            float v8[8];
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                v8[r] = aw[2 * pj][r];
-                v8[4 + r] = 2 * pj + 1 <= I ? aw[2 * pj + 1 <= I ? 2 * pj + 1 : 0][r] : 0.0f;
+            for (int G = 0; G < 3; ++G) {
+                float v8[8];
+                const int u0 = 2 * G, u1 = 2 * G + 1;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    v8[r] = (u0 >= s && u0 <= s + 4) ? sc[s][u0][r] : 0.0f;
+                    v8[4 + r] = (u1 >= s && u1 <= s + 4) ? sc[s][u1][r] : 0.0f;
+                }
+                pf[s][G] = M::pack(v8);
             }
-            af[pj] = M::pack(v8);
-        }
-#pragma unroll
-        for (int pu = 0; pu < 3; ++pu) {
-            float v8[8];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                v8[r] = pw[2 * pu][r];
-                v8[4 + r] = 2 * pu + 1 < 5 ? pw[2 * pu + 1 < 5 ? 2 * pu + 1 : 0][r] : 0.0f;
-            }
-            pf[pu] = M::pack(v8);
-        }
     }
-    const float inter_scale = GATE == 0 ? qinv * fast_exp2(sm.b2s[i_loc]) : qinv;
-    float bad_coef = 0.0f;
+    float inter_scale[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) inter_scale[s] = GATE == 0 ? qinv[s] * fast_exp2(bq[s]) : qinv[s];
 
-    // ---- one 16-wide slice of d_v at a time: inter + intra + window, store
-    T* orow = x.o + ((x.row0 + i_loc) * x.H_q + x.hq) * D;
-#pragma unroll 2
+    // ---- one 16-wide slice of d_v at a time: inter + (intra + window), store
+    T* orow[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) orow[s] = x.o + ((x.row0 + i_loc[s]) * x.H_q + x.hq) * D + 4 * g;
+#pragma unroll 1
     for (int t = 0; t < NT; ++t) {
-        f32x4_t acc = zero4();
+        f32x4_t acc[2] = {zero4(), zero4()};
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-            acc = M::mma(M::load(sm.St + (16 * t + col) * L::DP + M::KSTEP * s + KPL * g), qt[s], acc);
-        acc *= inter_scale;
-        for (int nb = 0; nb < nbad; ++nb) {
-            const int c = sm.badlist[nb];
-            const float qc = row_ok ? to_f32(qrow[c]) : 0.0f;
-            bad_coef = x.alpha * fast_exp2((qc - qmax) * kLog2e) * qinv * fast_exp2(sm.F[i_loc * L::FP + c]);
+        for (int k = 0; k < KS; ++k) {
+            const Frag a = M::load(sm.St + (16 * t + col) * L::DP + M::KSTEP * k + KPL * g);
+            acc[0] = M::mma(a, qt[0][k], acc[0]);
+            acc[1] = M::mma(a, qt[1][k], acc[1]);
+        }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] += bad_coef * to_f32(sm.St[(16 * t + 4 * g + r) * L::DP + c]);
+        for (int s = 0; s < 2; ++s) {
+            acc[s] *= inter_scale[s];
+            for (int nb = 0; nb < nbad; ++nb) {
+                const int c = sm.badlist[nb];
+                const float qc = row_ok[s] ? to_f32(qrow[s][c]) : 0.0f;
+                const float bad_q =
+                    x.alpha * fast_exp2((qc - qmax[s]) * kLog2e) * qinv[s] * fast_exp2(sm.F[i_loc[s] * L::FP + c]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[s][r] += bad_q * to_f32(sm.St[(16 * t + 4 * g + r) * L::DP + c]);
+            }
         }
         const T* vrow_c = Vcur + (16 * t + col) * L::JP;
-        const T* vrow_p = Vprv + (16 * t + col) * L::JP + 64;
+        const T* vrow_p = Vprv + (16 * t + col) * L::JP;
         if constexpr (BF) {
+            // key tiles (KT0 + 2G, KT0 + 2G + 1) form one aligned 32-key group
 #pragma unroll
-            for (int pj = 0; pj < NA; ++pj) {
-                const uint2 lo = *reinterpret_cast<const uint2*>(vrow_c + 32 * pj + 4 * g);
-                const uint2 hi = *reinterpret_cast<const uint2*>(vrow_c + 32 * pj + 16 + 4 * g);
-                acc = M::mma(__builtin_bit_cast(Frag, make_uint4(lo.x, lo.y, hi.x, hi.y)), af[pj], acc);
-            }
-#pragma unroll
-            for (int pu = 0; pu < 3; ++pu) {
-                const int u0 = 2 * pu, u1 = 2 * pu + 1;
-                const bool l1 = u1 < 5 && live[u1 < 5 ? u1 : 0];
-                if (live[u0] || l1) {
-                    const int kt0 = U0 + u0;
-                    const int kt1 = u1 < 5 ? U0 + u1 : kt0;
-                    const T* p0 = kt0 >= 0 ? vrow_c + 16 * kt0 : vrow_p + 16 * kt0;
-                    const T* p1 = kt1 >= 0 ? vrow_c + 16 * kt1 : vrow_p + 16 * kt1;
-                    const uint2 lo = *reinterpret_cast<const uint2*>(p0 + 4 * g);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(p1 + 4 * g);
-                    acc = M::mma(__builtin_bit_cast(Frag, make_uint4(lo.x, lo.y, hi.x, hi.y)), pf[pu], acc);
-                }
+            for (int G = 0; G < 3; ++G) {
+                const int kt = KT0 + 2 * G;
+                const T* grp = kt >= 0 ? vrow_c + 16 * kt : vrow_p + 16 * (kt + 4);
+                const Frag a = M::load(grp + 8 * g);
+                acc[0] = M::mma(a, pf[0][G], acc[0]);
+                acc[1] = M::mma(a, pf[1][G], acc[1]);
             }
         } else {
 #pragma unroll
-            for (int J = 0; J <= I; ++J)
+            for (int u = 0; u < NKT; ++u) {
+                const int kt = KT0 + u;
+                const int kk = kt >= 0 ? kt : kt + 4;
+                const T* base = kt >= 0 ? vrow_c : vrow_p;
+                const float4 pv = *reinterpret_cast<const float4*>(base + 32 * (kk >> 1) + 8 * g + 4 * (kk & 1));
+                const float pr[4] = {pv.x, pv.y, pv.z, pv.w};
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc = M::mma(M::load(vrow_c + 16 * J + 4 * g + r), __builtin_bit_cast(Frag, aw[J][r]), acc);
+                for (int s = 0; s < 2; ++s)
+                    if (u >= s && u <= s + 4) {
 #pragma unroll
-            for (int u = 0; u < 5; ++u)
-                if (live[u]) {
-                    const int kt = U0 + u;
-                    const T* pr = kt >= 0 ? vrow_c + 16 * kt : vrow_p + 16 * kt;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        acc = M::mma(M::load(pr + 4 * g + r), __builtin_bit_cast(Frag, pw[u][r]), acc);
-                }
-        }
-        if (row_ok) {
-            T* dst = orow + 16 * t + 4 * g;
-            if constexpr (BF) {
-                *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
-            } else {
-                *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                        for (int r = 0; r < 4; ++r)
+                            acc[s] = M::mma(__builtin_bit_cast(Frag, pr[r]), __builtin_bit_cast(Frag, sc[s][u][r]), acc[s]);
+                    }
             }
         }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            if (row_ok[s]) {
+                T* dst = orow[s] + 16 * t;
+                if constexpr (BF) {
+                    *reinterpret_cast<uint2*>(dst) =
+                        make_uint2(pack_bf16x2(acc[s][0], acc[s][1]), pack_bf16x2(acc[s][2], acc[s][3]));
+                } else {
+                    *reinterpret_cast<float4*>(dst) = make_float4(acc[s][0], acc[s][1], acc[s][2], acc[s][3]);
+                }
+            }
     }
 }
 
@@ -786,8 +1038,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
     const int H_q = p.H_kv * p.n_rep;
     const size_t rec = size_t(D) * D + D;
 
-    f32x4_t acc[StateTiles<D>::TPW];
-    load_state<D>(s == 0 ? nullptr : p.carry + ((size_t(b) * p.H_kv + h) * size_t(p.n_seg - 1) + (s - 1)) * rec, acc);
+    float* slot = p.state_slots + ((size_t(b) * p.H_kv + h) * size_t(p.n_seg) + s) * size_t(D) * D;
+    const float* carry_in = s == 0 ? nullptr : p.carry + ((size_t(b) * p.H_kv + h) * size_t(p.n_seg - 1) + (s - 1)) * rec;
+    const bool last_seg = s == p.n_seg - 1;
 
     const int64_t c_begin = int64_t(s) * p.cps;
     const int64_t c_end = c_begin + p.cps < p.n_chunks ? c_begin + p.cps : p.n_chunks;
@@ -796,13 +1049,34 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
     } else {
         zero_slot(sm, int((c_begin + 1) & 1));
     }
+    // K/V of the chunk about to be processed: the first one is loaded here,
+    // the following ones are issued before the previous chunk's output phase
+    ChunkRegs<T, D> cr;
+    load_chunk_issue<T, D>(cr, kbase, vbase, row_stride, c_begin * kChunk,
+                           p.T - c_begin * kChunk < kChunk ? int(p.T - c_begin * kChunk) : kChunk);
     for (int64_t c = c_begin; c < c_end; ++c) {
         const int cur = int(c & 1);
         const int64_t t0 = c * kChunk;
         const int nvalid = p.T - t0 < kChunk ? int(p.T - t0) : kChunk;
+        // running state (entering this chunk) and the query fragments of this
+        // wave's first output block, loaded now so their latency overlaps the
+        // gate and state phases
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4_t acc[StateTiles<D>::TPW];
+        if (c == c_begin) load_state<D>(carry_in, acc);
+        else load_slot<D>(slot, acc);
+        const int n_items = p.n_rep * 2;
+        QFrags<T, D> qpre;
+        if (wave < n_items) {
+            int lane = threadIdx.x & 63;
+            asm volatile("" : "+v"(lane));
+            load_q_block<T, D>(qpre, static_cast<const T*>(p.q), b * p.T + t0, H_q, h * p.n_rep + (wave % p.n_rep),
+                               32 * (wave / p.n_rep), nvalid, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         if (threadIdx.x == 0) *sm.nbad = 0;
         if (threadIdx.x < D / 32) sm.badmask[threadIdx.x] = 0u;
-        load_chunk(sm, cur, kbase, vbase, row_stride, t0, nvalid);
+        load_chunk_commit(sm, cur, cr);
         __syncthreads();
         float b2[TPT];
         gate_prep<T, D, GATE, true, TPT>(sm, cur, nvalid, p.alpha, b2);
@@ -810,6 +1084,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
         // state operand for this chunk (S entering it), then advance the state
         publish_state(sm, acc);
         state_advance(sm, cur, acc);
+        if (c + 1 < c_end) store_slot<D>(slot, acc);
+        else if (last_seg) store_state<D>(p.S_T + (size_t(b) * p.H_kv + h) * D * D, acc);
         __syncthreads();
         intra_key_operand<T, D, GATE, true, TPT>(sm, cur, b2);
         __syncthreads();
@@ -823,23 +1099,22 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
         x.have_prev = c > 0;
         x.alpha = p.alpha;
         x.cur = cur;
-        const int n_items = p.n_rep * 4;
+        // next chunk's K/V: in flight during the output phase, stored after it
+        if (c + 1 < c_end) {
+            const int64_t t1 = t0 + kChunk;
+            load_chunk_issue<T, D>(cr, kbase, vbase, row_stride, t1, p.T - t1 < kChunk ? int(p.T - t1) : kChunk);
+        }
         for (int it = wave; it < n_items; it += kPWaves) {
-            const int ti = it / p.n_rep;
             x.hq = h * p.n_rep + (it % p.n_rep);
             int lane = threadIdx.x & 63;
             asm volatile("" : "+v"(lane));  // keep lane-derived addresses inside the loop
-            // pairs query tiles {0,3} and {1,2} on the waves of the two halves
-            switch (ti) {
-                case 0: output_item<T, D, GATE, 0>(sm, x, lane); break;
-                case 1: output_item<T, D, GATE, 1>(sm, x, lane); break;
-                case 2: output_item<T, D, GATE, 3>(sm, x, lane); break;
-                default: output_item<T, D, GATE, 2>(sm, x, lane); break;
-            }
+            if (it != wave)
+                load_q_block<T, D>(qpre, x.q, x.row0, H_q, x.hq, 32 * (it / p.n_rep), nvalid, lane);
+            if (it / p.n_rep == 0) output_block<T, D, GATE, 0>(sm, x, lane, qpre);
+            else output_block<T, D, GATE, 1>(sm, x, lane, qpre);
         }
         __syncthreads();
     }
-    if (s == p.n_seg - 1) store_state<D>(p.S_T + (size_t(b) * p.H_kv + h) * D * D, acc);
 }
 
 // ------------------------------------------------------------------ host side
@@ -861,7 +1136,8 @@ PrefillPlan make_prefill_plan(int64_t B, int64_t T, int H_kv, int d, bool bf16, 
     pl.cps = cps;
     pl.n_seg = (pl.n_chunks + cps - 1) / cps;
     pl.carry_floats = size_t(d) * d + d;
-    pl.workspace_bytes = size_t(B) * H_kv * size_t(pl.n_seg - 1) * pl.carry_floats * sizeof(float);
+    pl.state_offset = size_t(B) * H_kv * size_t(pl.n_seg - 1) * pl.carry_floats;
+    pl.workspace_bytes = (pl.state_offset + size_t(B) * H_kv * size_t(pl.n_seg) * d * d) * sizeof(float);
     return pl;
 }
 
@@ -874,6 +1150,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     p.o = a.o;
     p.S_T = a.S_T;
     p.carry = a.workspace;
+    p.state_slots = a.workspace + a.plan.state_offset;
     p.T = a.T;
     p.n_chunks = a.plan.n_chunks;
     p.cps = a.plan.cps;

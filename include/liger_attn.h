@@ -97,9 +97,9 @@ typedef struct liger_kv_ring {
 } liger_kv_ring;
 
 /*
- * Bytes of device workspace liger_attn_prefill needs for `shape` (the
- * per-segment state carries of the chunked scan). Returns 0 when the shape
- * needs none or is invalid. `chunks_per_segment` selects the segment length
+ * Bytes of device workspace liger_attn_prefill needs for `shape`: the state
+ * carried into each segment of the chunked scan and a running-state slot per
+ * segment. Returns 0 when the shape is invalid. `chunks_per_segment` selects the segment length
  * in 64-token chunks; 0 picks it from the shape (the same choice the
  * prefill call makes when given 0).
  */

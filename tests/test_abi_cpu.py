@@ -99,15 +99,16 @@ def test_prefill_workspace_checks(lib):
 
 
 def test_workspace_size_formula(lib):
-    # carries of every segment but the last: (d*d + d) fp32 per (b, kv head, segment)
-    for T, cps in [(64, 1), (65, 1), (8192, 4), (8192, 0), (1000, 3)]:
+    # carries of every segment but the last, (d*d + d) fp32 per (b, kv head,
+    # segment), then one d*d fp32 running-state slot per (b, kv head, segment)
+    for T, cps in [(64, 1), (65, 1), (8192, 4), (1000, 3)]:
         shp = _shape(B=2, T=T, H_q=8, H_kv=2)
         n_chunks = -(-T // 64)
         size = lib.liger_attn_prefill_workspace_size_ex(ctypes.byref(shp), cps)
-        if cps > 0:
-            n_seg = -(-n_chunks // min(cps, n_chunks))
-            assert size == 2 * 2 * (n_seg - 1) * (128 * 128 + 128) * 4
-        assert size % ((128 * 128 + 128) * 4 * 4) == 0
+        n_seg = -(-n_chunks // min(cps, n_chunks))
+        assert size == 2 * 2 * ((n_seg - 1) * (128 * 128 + 128) + n_seg * 128 * 128) * 4
+    size0 = lib.liger_attn_prefill_workspace_size(ctypes.byref(_shape(T=8192, H_q=32, H_kv=8)))
+    assert size0 > 0 and size0 % 16 == 0
     assert lib.liger_attn_prefill_workspace_size(ctypes.byref(_shape(d=96))) == 0
     assert lib.liger_attn_prefill_workspace_size(None) == 0
 
@@ -156,7 +157,9 @@ def test_no_gpu_returns_hip_error_instead_of_aborting(lib):
     import torch
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is visible: the fake pointers of this test must not reach a kernel")
-    st = _prefill(lib, _shape(T=64))
+    shp = _shape(T=64)
+    need = lib.liger_attn_prefill_workspace_size(ctypes.byref(shp))
+    st = _prefill(lib, shp, ws=FAKE << 8, ws_bytes=need)
     assert st == gla.LIGER_E_HIP, gla.liger_last_error()
     assert "launch" in gla.liger_last_error()
 
