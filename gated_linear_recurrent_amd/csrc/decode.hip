@@ -13,6 +13,8 @@
 //   - and the last workgroup of the sequence to finish advances pos.
 // The state row-major read-modify-write is the dominant HBM traffic
 // (2 * d * d * 4 bytes per (n, h)); every float4 of S is touched once.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -20,8 +22,26 @@ namespace liger {
 
 constexpr int kDecThreads = 256;
 
+// 64-lane reductions: DPP inside rows of 16, then two cross-row exchanges.
+__device__ __forceinline__ float dec_wave_max(float v) {
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp<kDppMirror>(v));
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ __forceinline__ float dec_wave_sum(float v) {
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    v += dpp<kDppMirror>(v);
+    v += __shfl_xor(v, 16, 64);
+    return v + __shfl_xor(v, 32, 64);
+}
+
 template <typename T, int D, int GATE, int NREP>
-__global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
+__global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2) void decode_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     float* __restrict__ S, T* __restrict__ ring_k, T* __restrict__ ring_v,
     int64_t* __restrict__ pos, uint32_t* __restrict__ sync, T* __restrict__ o,
@@ -29,13 +49,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     constexpr int CG = D / 4;             // float4 column groups of a state row
     constexpr int RG = kDecThreads / CG;  // row groups
     constexpr int RPT = D / RG;           // state rows per thread
-    constexpr int SPT = 64 / RG;          // ring slots per thread (<= 64 slots)
+    constexpr int SPT = 64 / RG;          // ring slots per thread in the value pass
+    constexpr int VPL = 16 / sizeof(T);   // elements per 16-byte load
+    constexpr int KPT = (D / 4) / VPL;    // 16-byte key loads per thread in the logit pass
+    constexpr int NR4 = (NREP + 3) / 4;   // float4 groups of the per-head values
+    constexpr int NRP = 4 * NR4;          // per-head values padded to a float4 multiple
+    static_assert(kDecThreads == 256, "four lanes per ring slot");
 
     __shared__ float s_k[D], s_v[D], s_phik[D], s_g[D];
-    __shared__ float s_q[NREP][D];
-    __shared__ float s_phiq[NREP][D];
-    __shared__ float s_p[NREP][64];
-    __shared__ float s_red[RG][NREP][D];
+    __shared__ __align__(16) float s_q[D][NRP];      // raw q, head-minor
+    __shared__ __align__(16) float s_phiq[D][NRP];   // phi(q), head-minor
+    __shared__ __align__(16) float s_p[64][NRP];     // window weights, head-minor
+    __shared__ __align__(16) float s_red[RG][NREP][D];
 
     const int h = blockIdx.x;
     const int n = blockIdx.y;
@@ -43,49 +68,101 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int H_q = H_kv * NREP;
-
-    const int64_t p = pos[n];
-    const int slot = static_cast<int>(p % window);
-    const int nvalid = static_cast<int>(p + 1 < window ? p + 1 : window);
+    const int cg = tid % CG;
+    const int rg = tid / CG;
 
     const size_t kv_off = (static_cast<size_t>(n) * H_kv + h) * D;
     const T* kp = k + kv_off;
     const T* vp = v + kv_off;
     const T* qp = q + (static_cast<size_t>(n) * H_q + static_cast<size_t>(h) * NREP) * D;
+    float* Sp = S + (static_cast<size_t>(n) * H_kv + h) * D * D;
+    const T* rk = ring_k + (static_cast<size_t>(n) * H_kv + h) * window * D;
+    const T* rv = ring_v + (static_cast<size_t>(n) * H_kv + h) * window * D;
 
-    for (int i = tid; i < D; i += kDecThreads) {
-        s_k[i] = to_f32(kp[i]);
-        s_v[i] = to_f32(vp[i]);
+    // ---- loads, smallest first (memory returns in issue order): the new
+    // token, then the state rows and this thread's ring key and value slices.
+    // None of them depends on pos.
+    float kin = 0.f, vin = 0.f;
+    if (tid < D) {
+        kin = to_f32(kp[tid]);
+        vin = to_f32(vp[tid]);
     }
-    for (int i = tid; i < NREP * D; i += kDecThreads) s_q[i / D][i % D] = to_f32(qp[i]);
+    float qin[(NREP * D + kDecThreads - 1) / kDecThreads];
+#pragma unroll
+    for (int i = 0; i < (NREP * D + kDecThreads - 1) / kDecThreads; ++i) {
+        const int idx = tid + i * kDecThreads;
+        qin[i] = idx < NREP * D ? to_f32(qp[idx]) : 0.f;
+    }
+    float4 sv[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        sv[i] = *reinterpret_cast<const float4*>(Sp + static_cast<size_t>(rg + i * RG) * D + cg * 4);
+    const int ks = tid >> 2;    // ring slot of the logit pass
+    const int kpart = tid & 3;  // quarter of the head dimension
+    uint4 kr[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+        kr[i] = ks < window
+                    ? *reinterpret_cast<const uint4*>(rk + static_cast<size_t>(ks) * D + kpart * (D / 4) + i * VPL)
+                    : make_uint4(0, 0, 0, 0);
+    // ring values stay packed in registers until they are used
+    typedef typename std::conditional<sizeof(T) == 2, uint2, float4>::type VRaw;
+    VRaw vraw[SPT];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        const int s = rg + i * RG;
+        if (s < window) {
+            vraw[i] = *reinterpret_cast<const VRaw*>(rv + static_cast<size_t>(s) * D + cg * 4);
+        } else {
+            if constexpr (sizeof(T) == 2) vraw[i] = make_uint2(0, 0);
+            else vraw[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+
+    const int64_t p = pos[n];
+    const int slot = static_cast<int>(p % window);
+    const int nvalid = static_cast<int>(p + 1 < window ? p + 1 : window);
+
+    if (tid < D) {
+        s_k[tid] = kin;
+        s_v[tid] = vin;
+    }
+#pragma unroll
+    for (int i = 0; i < (NREP * D + kDecThreads - 1) / kDecThreads; ++i) {
+        const int idx = tid + i * kDecThreads;
+        if (idx < NREP * D) s_q[idx % D][idx / D] = qin[i];
+    }
     __syncthreads();
 
-    // softmax over d of k (row 0) and of each query head (rows 1..NREP); gate.
+    // ---- softmax over d of k (row 0) and of each query head; the gate
     constexpr int EPL = D / 64;
     for (int row = wave; row <= NREP; row += kDecThreads / 64) {
-        const float* src = row == 0 ? s_k : s_q[row - 1];
         float x[EPL];
         float mx = -INFINITY, sum_raw = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-            x[e] = src[lane + 64 * e];
+            const int c = lane + 64 * e;
+            x[e] = row == 0 ? s_k[c] : s_q[c][row - 1];
             mx = fmaxf(mx, x[e]);
             sum_raw += x[e];
         }
-        mx = wave_max(mx);
+        mx = dec_wave_max(mx);
         float se = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             x[e] = fast_exp2((x[e] - mx) * kLog2e);
             se += x[e];
         }
-        const float inv = 1.0f / wave_sum(se);
-        float* dst = row == 0 ? s_phik : s_phiq[row - 1];
+        const float inv = 1.0f / dec_wave_sum(se);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) dst[lane + 64 * e] = x[e] * inv;
+        for (int e = 0; e < EPL; ++e) {
+            const int c = lane + 64 * e;
+            if (row == 0) s_phik[c] = x[e] * inv;
+            else s_phiq[c][row - 1] = x[e] * inv;
+        }
         if (row == 0) {
             if (GATE == 0) {
-                const float g = sigmoidf_stable(wave_sum(sum_raw) * (1.0f / D));
+                const float g = sigmoidf_stable(dec_wave_sum(sum_raw) * (1.0f / D));
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) s_g[lane + 64 * e] = g;
             } else {
@@ -94,96 +171,90 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
                     const int c = lane + 64 * e;
                     const int lo = c > 0 ? c - 1 : 0;
                     const int hi = c + 3 < D ? c + 3 : D;
-                    float s = 0.f;
-                    for (int m = lo; m < hi; ++m) s += s_k[m];
-                    s_g[c] = sigmoidf_stable(s / static_cast<float>(hi - lo));
+                    float sm = 0.f;
+                    for (int m = lo; m < hi; ++m) sm += s_k[m];
+                    s_g[c] = sigmoidf_stable(sm / static_cast<float>(hi - lo));
                 }
             }
         }
     }
     __syncthreads();
 
-    // ---- state read-modify-write and GRM output phi(q) S_t
-    const int cg = tid % CG;
-    const int rg = tid / CG;
-    float* Sp = S + (static_cast<size_t>(n) * H_kv + h) * D * D;
-    float4 sv[RPT];
+    // ---- window logits: q . k_s for this thread's slot and quarter
+    {
+        float dot[NRP];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
-        sv[i] = *reinterpret_cast<const float4*>(Sp + static_cast<size_t>(rg + i * RG) * D + cg * 4);
+        for (int j = 0; j < NRP; ++j) dot[j] = 0.f;
+        const int c0 = kpart * (D / 4);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const T* e = reinterpret_cast<const T*>(&kr[i]);
+#pragma unroll
+            for (int t = 0; t < VPL; ++t) {
+                const int c = c0 + i * VPL + t;
+                const float kv = ks == slot ? s_k[c] : to_f32(e[t]);
+#pragma unroll
+                for (int j4 = 0; j4 < NR4; ++j4) {
+                    const float4 q4 = *reinterpret_cast<const float4*>(&s_q[c][4 * j4]);
+                    dot[4 * j4 + 0] += q4.x * kv;
+                    dot[4 * j4 + 1] += q4.y * kv;
+                    dot[4 * j4 + 2] += q4.z * kv;
+                    dot[4 * j4 + 3] += q4.w * kv;
+                }
+            }
+        }
+        const float scale = kLog2e * rsqrtf(static_cast<float>(D));
+#pragma unroll
+        for (int j = 0; j < NREP; ++j) {
+            dot[j] += dpp<kDppXor1>(dot[j]);
+            dot[j] += dpp<kDppXor2>(dot[j]);
+        }
+        if (kpart == 0) {
+#pragma unroll
+            for (int j = 0; j < NREP; ++j) s_p[ks][j] = ks < nvalid ? dot[j] * scale : -INFINITY;
+        }
+    }
+
+    // ---- state read-modify-write and phi(q) S_t (state rows already loaded)
     const float4 v4 = *reinterpret_cast<const float4*>(s_v + cg * 4);
-    float acc[NREP][4];
+    float acc[NRP][4];
 #pragma unroll
-    for (int j = 0; j < NREP; ++j) acc[j][0] = acc[j][1] = acc[j][2] = acc[j][3] = 0.f;
+    for (int j = 0; j < NRP; ++j) acc[j][0] = acc[j][1] = acc[j][2] = acc[j][3] = 0.f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = rg + i * RG;
         const float g = s_g[r];
         const float pk = s_phik[r];
-        float4 s = sv[i];
-        s.x = g * s.x + pk * v4.x;
-        s.y = g * s.y + pk * v4.y;
-        s.z = g * s.z + pk * v4.z;
-        s.w = g * s.w + pk * v4.w;
-        *reinterpret_cast<float4*>(Sp + static_cast<size_t>(r) * D + cg * 4) = s;
+        float4 st = sv[i];
+        st.x = g * st.x + pk * v4.x;
+        st.y = g * st.y + pk * v4.y;
+        st.z = g * st.z + pk * v4.z;
+        st.w = g * st.w + pk * v4.w;
+        *reinterpret_cast<float4*>(Sp + static_cast<size_t>(r) * D + cg * 4) = st;
 #pragma unroll
-        for (int j = 0; j < NREP; ++j) {
-            const float pq = s_phiq[j][r];
-            acc[j][0] += pq * s.x;
-            acc[j][1] += pq * s.y;
-            acc[j][2] += pq * s.z;
-            acc[j][3] += pq * s.w;
-        }
-    }
-
-    // ---- sliding-window logits over the ring (current token from registers)
-    const float scale = kLog2e * rsqrtf(static_cast<float>(D));
-    const T* rk = ring_k + (static_cast<size_t>(n) * H_kv + h) * window * D;
-    const T* rv = ring_v + (static_cast<size_t>(n) * H_kv + h) * window * D;
-    {
-        const int s = tid >> 2;       // ring slot
-        const int part = tid & 3;     // quarter of the head dimension
-        float dot[NREP];
+        for (int j4 = 0; j4 < NR4; ++j4) {
+            const float4 pq = *reinterpret_cast<const float4*>(&s_phiq[r][4 * j4]);
+            const float pqs[4] = {pq.x, pq.y, pq.z, pq.w};
 #pragma unroll
-        for (int j = 0; j < NREP; ++j) dot[j] = 0.f;
-        if (s < nvalid) {
-            const int c0 = part * (D / 4);
-            if (s == slot) {
-                for (int c = c0; c < c0 + D / 4; ++c) {
-                    const float kv = s_k[c];
-#pragma unroll
-                    for (int j = 0; j < NREP; ++j) dot[j] += s_q[j][c] * kv;
-                }
-            } else {
-                const T* kr = rk + static_cast<size_t>(s) * D;
-                for (int c = c0; c < c0 + D / 4; ++c) {
-                    const float kv = to_f32(kr[c]);
-#pragma unroll
-                    for (int j = 0; j < NREP; ++j) dot[j] += s_q[j][c] * kv;
-                }
+            for (int jj = 0; jj < 4; ++jj) {
+                acc[4 * j4 + jj][0] += pqs[jj] * st.x;
+                acc[4 * j4 + jj][1] += pqs[jj] * st.y;
+                acc[4 * j4 + jj][2] += pqs[jj] * st.z;
+                acc[4 * j4 + jj][3] += pqs[jj] * st.w;
             }
-        }
-#pragma unroll
-        for (int j = 0; j < NREP; ++j) {
-            dot[j] += __shfl_xor(dot[j], 1, 64);
-            dot[j] += __shfl_xor(dot[j], 2, 64);
-        }
-        if (part == 0) {
-#pragma unroll
-            for (int j = 0; j < NREP; ++j) s_p[j][s] = s < nvalid ? dot[j] * scale : -INFINITY;
         }
     }
     __syncthreads();
     for (int j = wave; j < NREP; j += kDecThreads / 64) {
-        const float l = s_p[j][lane];
-        const float m = wave_max(l);
+        const float l = s_p[lane][j];
+        const float m = dec_wave_max(l);
         const float e = lane < nvalid ? fast_exp2(l - m) : 0.f;
-        const float inv = 1.0f / wave_sum(e);
-        s_p[j][lane] = e * inv * (1.0f - alpha);
+        const float inv = 1.0f / dec_wave_sum(e);
+        s_p[lane][j] = e * inv * (1.0f - alpha);
     }
     __syncthreads();
 
-    // ---- mix: alpha * GRM + sum_s p_s v_s
+    // ---- mix: alpha * GRM + sum_s p_s v_s (the new token's value from LDS)
 #pragma unroll
     for (int j = 0; j < NREP; ++j) {
         acc[j][0] *= alpha;
@@ -194,22 +265,30 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
         const int s = rg + i * RG;
-        if (s < nvalid) {
-            float vv[4];
-            if (s == slot) {
+        float vr[4];
+        if constexpr (sizeof(T) == 2) {
+            vr[0] = __uint_as_float(vraw[i].x << 16);
+            vr[1] = __uint_as_float(vraw[i].x & 0xffff0000u);
+            vr[2] = __uint_as_float(vraw[i].y << 16);
+            vr[3] = __uint_as_float(vraw[i].y & 0xffff0000u);
+        } else {
+            vr[0] = vraw[i].x;
+            vr[1] = vraw[i].y;
+            vr[2] = vraw[i].z;
+            vr[3] = vraw[i].w;
+        }
+        if (s == slot) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) vv[e] = s_v[cg * 4 + e];
-            } else {
-                const T* vr = rv + static_cast<size_t>(s) * D + cg * 4;
+            for (int e = 0; e < 4; ++e) vr[e] = s_v[cg * 4 + e];
+        }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) vv[e] = to_f32(vr[e]);
-            }
+        for (int j4 = 0; j4 < NR4; ++j4) {
+            const float4 p4 = *reinterpret_cast<const float4*>(&s_p[s][4 * j4]);  // 0 outside the window
+            const float ps[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
-            for (int j = 0; j < NREP; ++j) {
-                const float pj = s_p[j][s];
+            for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[j][e] += pj * vv[e];
-            }
+                for (int e = 0; e < 4; ++e) acc[4 * j4 + jj][e] += ps[jj] * vr[e];
         }
     }
 #pragma unroll
@@ -234,11 +313,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     }
 
     // ---- the last of the H_kv workgroups of sequence n advances pos[n].
-    // Every workgroup has read pos before it arrives, so the write is safe.
-    __syncthreads();
+    // Every wave of every workgroup consumed pos before its first barrier, so
+    // the counter needs atomicity only: a relaxed atomic does not wait for
+    // this workgroup's state stores to complete.
     if (tid == 0) {
-        __threadfence();
-        const uint32_t prev = __hip_atomic_fetch_add(&sync[n], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t prev = __hip_atomic_fetch_add(&sync[n], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (prev == static_cast<uint32_t>(H_kv - 1)) {
             sync[n] = 0u;
             pos[n] = p + 1;
