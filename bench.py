@@ -118,7 +118,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the Liger Attention layer here is built and "
-              "measured on a single MI355X (see DESIGN.md for how it would shard).", file=sys.stderr)
+              "measured on a single MI355X; multi-GPU runs are not supported.", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -240,11 +240,12 @@ def main() -> int:
         log(f"[bench] decode kernel {k_ms * 1e3:.1f} us/step ({dach:.0f} GB/s); wall {dwall * 1e6 / nsteps:.1f} us/step")
 
     if args.copy_probe_mib > 0:
+        # an elementwise kernel that reads and writes exactly n bytes each
         n = args.copy_probe_mib * (1 << 20)
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
         log(f"[bench] copy probe {args.copy_probe_mib} MiB x3 done")
 

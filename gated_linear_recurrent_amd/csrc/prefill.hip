@@ -53,6 +53,23 @@ __device__ __forceinline__ int key_pos(int j) {
     return (j & 32) | (((j & 15) >> 2) << 3) | (((j >> 4) & 1) << 2) | (j & 3);
 }
 
+// bf16 operand fragment over keys (the contraction index) from a token-major
+// [key][channel] tile, read with two transposing LDS loads (ds_read_b64_tr_b16:
+// in each 16-lane group, lane i supplies 4 consecutive elements of a row and
+// lane 4a+b receives element b of the rows supplied by lanes a, a+4, a+8, a+12).
+// Lane (n, g) gets channel c0 + n of keys kb + 4g + 0..3 and kb + 16 + 4g + 0..3,
+// the key_pos order of a 32-key group used by the score operands.
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+__device__ __forceinline__ bf16x8_t load_key_frag(const bf16_t* tile, int pitch, int kb, int c0, int lane) {
+    const int i = lane & 15, g = lane >> 4;
+    const bf16_t* p0 = tile + (kb + 4 * g + (i >> 2)) * pitch + c0 + 4 * (i & 3);
+    const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p0));
+    const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p0 + 16 * pitch));
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
+}
+
 // ------------------------------------------------------------- LDS layout
 template <typename T, int D, int GATE, bool FULL>
 struct Layout {
@@ -63,10 +80,15 @@ struct Layout {
     static constexpr int FP = D + 4;     // pitch of the fp32 gate-factor tile
     static constexpr int NSLOT = FULL ? 2 : 1;
     static constexpr int KB_ELEMS = (64 * DP > D * JP) ? 64 * DP : D * JP;
+    // bf16 keeps V token-major ([64][VP], rows 8 banks apart) and reads it with
+    // transposing loads; fp32 stores V^T ([D][JP], keys at key_pos).
+    static constexpr bool VNAT = (E == 2);
+    static constexpr int VP = D + 16;
+    static constexpr int V_ELEMS = VNAT ? 64 * VP : D * JP;
 
     static constexpr size_t K_OFF = 0;                                        // raw K [slot][64][DP]
-    static constexpr size_t VT_OFF = K_OFF + size_t(NSLOT) * 64 * DP * E;     // V^T [slot][D][JP]
-    static constexpr size_t KB_OFF = VT_OFF + size_t(NSLOT) * D * JP * E;     // K~ (state^T or intra)
+    static constexpr size_t VT_OFF = K_OFF + size_t(NSLOT) * 64 * DP * E;     // V [slot][V_ELEMS]
+    static constexpr size_t KB_OFF = VT_OFF + size_t(NSLOT) * V_ELEMS * E;    // K~ (state^T or intra)
     static constexpr size_t ST_OFF = KB_OFF + size_t(KB_ELEMS) * E;           // S'^T [D][DP]
     static constexpr size_t ST_BYTES = FULL ? size_t(D) * DP * E : 0;
     static constexpr size_t F_OFF = ST_OFF + ST_BYTES;                        // fp32 [64][FP]
@@ -87,7 +109,7 @@ template <typename T, int D, int GATE, bool FULL>
 struct Smem {
     typedef Layout<T, D, GATE, FULL> L;
     T* K;      // [NSLOT][64][DP]
-    T* Vt;     // [NSLOT][D][JP]
+    T* Vt;     // [NSLOT][V_ELEMS]: [64][VP] (bf16) or [D][JP] (fp32)
     T* Kb;     // [D][JP] (K~ state, transposed) then [64][DP] (K~ intra)
     T* St;     // [D][DP]
     float* F;  // [64][FP]
@@ -158,8 +180,10 @@ struct ChunkRegs {
     static constexpr int VPL = 16 / sizeof(T);
     static constexpr int PPR = D / VPL;                                  // 16-byte pieces per row
     static constexpr int NK = (64 * PPR + kPThreads - 1) / kPThreads;    // K pieces per thread
-    static constexpr int NV = (32 * PPR + kPThreads - 1) / kPThreads;    // V row pairs per thread
+    static constexpr bool VNAT = sizeof(T) == 2;
+    static constexpr int NV = VNAT ? 1 : (32 * PPR + kPThreads - 1) / kPThreads;  // V row pairs per thread (fp32)
     uint4 k[NK];
+    uint4 v[VNAT ? NK : 1];  // bf16: V pieces, same mapping as K
     uint4 v0[NV], v1[NV];
 };
 
@@ -176,6 +200,18 @@ __device__ __forceinline__ void load_chunk_issue(ChunkRegs<T, D>& cr, const T* k
         cr.k[n] = make_uint4(0, 0, 0, 0);
         if (idx < 64 * CR::PPR && j < nvalid)
             cr.k[n] = *reinterpret_cast<const uint4*>(kbase + (t0 + j) * row_stride + c0);
+    }
+    if constexpr (CR::VNAT) {
+#pragma unroll
+        for (int n = 0; n < CR::NK; ++n) {
+            const int idx = tid + n * kPThreads;
+            const int j = idx / CR::PPR;
+            const int c0 = (idx % CR::PPR) * CR::VPL;
+            cr.v[n] = make_uint4(0, 0, 0, 0);
+            if (idx < 64 * CR::PPR && j < nvalid)
+                cr.v[n] = *reinterpret_cast<const uint4*>(vbase + (t0 + j) * row_stride + c0);
+        }
+        return;
     }
 #pragma unroll
     for (int n = 0; n < CR::NV; ++n) {
@@ -196,13 +232,22 @@ __device__ __forceinline__ void load_chunk_commit(const Smem<T, D, GATE, FULL>& 
     typedef Layout<T, D, GATE, FULL> L;
     typedef ChunkRegs<T, D> CR;
     T* Ks = sm.K + slot * 64 * L::DP;
-    T* Vts = sm.Vt + slot * D * L::JP;
+    T* Vts = sm.Vt + slot * L::V_ELEMS;
     const int tid = ltid();
 #pragma unroll
     for (int n = 0; n < CR::NK; ++n) {
         const int idx = tid + n * kPThreads;
         if (idx < 64 * CR::PPR)
             *reinterpret_cast<uint4*>(Ks + (idx / CR::PPR) * L::DP + (idx % CR::PPR) * CR::VPL) = cr.k[n];
+    }
+    if constexpr (CR::VNAT) {
+#pragma unroll
+        for (int n = 0; n < CR::NK; ++n) {
+            const int idx = tid + n * kPThreads;
+            if (idx < 64 * CR::PPR)
+                *reinterpret_cast<uint4*>(Vts + (idx / CR::PPR) * L::VP + (idx % CR::PPR) * CR::VPL) = cr.v[n];
+        }
+        return;
     }
 #pragma unroll
     for (int n = 0; n < CR::NV; ++n) {
@@ -239,8 +284,8 @@ __device__ __forceinline__ void zero_slot(const Smem<T, D, GATE, FULL>& sm, int 
     typedef Layout<T, D, GATE, FULL> L;
     uint32_t* kz = reinterpret_cast<uint32_t*>(sm.K + slot * 64 * L::DP);
     for (int i = ltid(); i < 64 * L::DP * int(sizeof(T)) / 4; i += kPThreads) kz[i] = 0u;
-    uint32_t* vz = reinterpret_cast<uint32_t*>(sm.Vt + slot * D * L::JP);
-    for (int i = ltid(); i < D * L::JP * int(sizeof(T)) / 4; i += kPThreads) vz[i] = 0u;
+    uint32_t* vz = reinterpret_cast<uint32_t*>(sm.Vt + slot * L::V_ELEMS);
+    for (int i = ltid(); i < L::V_ELEMS * int(sizeof(T)) / 4; i += kPThreads) vz[i] = 0u;
 }
 
 // ------------------------------------------------------- per-chunk gate work
@@ -361,7 +406,7 @@ __device__ __forceinline__ void state_advance(const Smem<T, D, GATE, FULL>& sm, 
     typedef StateTiles<D> ST;
     const int lane = ltid() & 63, wave = ltid() >> 6;
     const int col = lane & 15, g = lane >> 4;
-    const T* Vts = sm.Vt + slot * D * L::JP;
+    const T* Vts = sm.Vt + slot * L::V_ELEMS;
 #pragma unroll
     for (int u = 0; u < ST::TPW; ++u) {
         const int rt = ST::rt(wave, u), t = ST::ct(wave, u);
@@ -369,7 +414,9 @@ __device__ __forceinline__ void state_advance(const Smem<T, D, GATE, FULL>& sm, 
 #pragma unroll
         for (int ks = 0; ks < 64 / M::KSTEP; ++ks) {
             const typename M::frag a = M::load(sm.Kb + (16 * rt + col) * L::JP + M::KSTEP * ks + M::KPL * g);
-            const typename M::frag b = M::load(Vts + (16 * t + col) * L::JP + M::KSTEP * ks + M::KPL * g);
+            typename M::frag b;
+            if constexpr (L::VNAT) b = load_key_frag(Vts, L::VP, M::KSTEP * ks, 16 * t, lane);
+            else b = M::load(Vts + (16 * t + col) * L::JP + M::KSTEP * ks + M::KPL * g);
             d = M::mma(a, b, d);
         }
         const int r0 = 16 * rt + 4 * g;
@@ -613,38 +660,33 @@ __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams 
 }
 
 // ------------------------------------------------------------------ P2
+// One thread per state element; the carries of up to BATCH segments are
+// loaded before the first multiply-add so their latencies overlap.
 template <int D>
 __global__ __launch_bounds__(256) void carry_scan_kernel(float* __restrict__ carry, int64_t n_seg, int H_kv) {
-    constexpr int NV4 = D * D / 4;
-    const int e4 = blockIdx.x * 256 + threadIdx.x;
-    if (e4 >= NV4) return;
+    constexpr int BATCH = 32;
+    const int e = blockIdx.x * 256 + threadIdx.x;  // D*D is a multiple of 256
     const int h = blockIdx.y;
     const int64_t b = blockIdx.z;
     const size_t rec = size_t(D) * D + D;
     float* base = carry + (size_t(b) * H_kv + h) * size_t(n_seg - 1) * rec;
-    const int r = (e4 * 4) / D;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    constexpr int BATCH = 8;
+    const int r = e / D;
+    float acc = 0.f;
     for (int64_t s0 = 0; s0 < n_seg - 1; s0 += BATCH) {
-        float4 Ls[BATCH];
-        float lg[BATCH];
+        float Ls[BATCH], lg[BATCH];
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
             if (s0 + u < n_seg - 1) {
                 const float* recp = base + (s0 + u) * rec;
-                Ls[u] = *reinterpret_cast<const float4*>(recp + e4 * 4);
+                Ls[u] = recp[e];
                 lg[u] = recp[size_t(D) * D + r];
             }
         }
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
             if (s0 + u < n_seg - 1) {
-                const float f = fast_exp2(lg[u]);
-                acc.x = f * acc.x + Ls[u].x;
-                acc.y = f * acc.y + Ls[u].y;
-                acc.z = f * acc.z + Ls[u].z;
-                acc.w = f * acc.w + Ls[u].w;
-                *reinterpret_cast<float4*>(base + (s0 + u) * rec + e4 * 4) = acc;
+                acc = fast_exp2(lg[u]) * acc + Ls[u];
+                base[(s0 + u) * rec + e] = acc;
             }
         }
     }
@@ -720,8 +762,8 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
     const int dl = col - 4 * g;         // i - j = 16 (I - kt) + dl - r inside a tile pair
     const T* Kcur = sm.K + x.cur * 64 * L::DP;
     const T* Kprv = sm.K + (x.cur ^ 1) * 64 * L::DP;
-    const T* Vcur = sm.Vt + x.cur * D * L::JP;
-    const T* Vprv = sm.Vt + (x.cur ^ 1) * D * L::JP;
+    const T* Vcur = sm.Vt + x.cur * L::V_ELEMS;
+    const T* Vprv = sm.Vt + (x.cur ^ 1) * L::V_ELEMS;
     const int nbad = GATE ? *sm.nbad : 0;
     const bool exact = GATE ? false : (*sm.exact != 0);
     const bool full_window = x.window >= 64;
@@ -978,19 +1020,19 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
                 for (int r = 0; r < 4; ++r) acc[s][r] += bad_q * to_f32(sm.St[(16 * t + 4 * g + r) * L::DP + c]);
             }
         }
-        const T* vrow_c = Vcur + (16 * t + col) * L::JP;
-        const T* vrow_p = Vprv + (16 * t + col) * L::JP;
         if constexpr (BF) {
             // key tiles (KT0 + 2G, KT0 + 2G + 1) form one aligned 32-key group
 #pragma unroll
             for (int G = 0; G < 3; ++G) {
                 const int kt = KT0 + 2 * G;
-                const T* grp = kt >= 0 ? vrow_c + 16 * kt : vrow_p + 16 * (kt + 4);
-                const Frag a = M::load(grp + 8 * g);
+                const Frag a = kt >= 0 ? load_key_frag(Vcur, L::VP, 16 * kt, 16 * t, lane)
+                                       : load_key_frag(Vprv, L::VP, 16 * (kt + 4), 16 * t, lane);
                 acc[0] = M::mma(a, pf[0][G], acc[0]);
                 acc[1] = M::mma(a, pf[1][G], acc[1]);
             }
         } else {
+            const T* vrow_c = Vcur + (16 * t + col) * L::JP;
+            const T* vrow_p = Vprv + (16 * t + col) * L::JP;
 #pragma unroll
             for (int u = 0; u < NKT; ++u) {
                 const int kt = KT0 + u;
@@ -1049,11 +1091,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
     } else {
         zero_slot(sm, int((c_begin + 1) & 1));
     }
-    // K/V of the chunk about to be processed: the first one is loaded here,
-    // the following ones are issued before the previous chunk's output phase
+    // K/V of the chunk about to be processed: the first one is loaded here;
+    // each following one is issued before the previous chunk's output phase
+    // and stored to LDS right after it
     ChunkRegs<T, D> cr;
     load_chunk_issue<T, D>(cr, kbase, vbase, row_stride, c_begin * kChunk,
                            p.T - c_begin * kChunk < kChunk ? int(p.T - c_begin * kChunk) : kChunk);
+    load_chunk_commit(sm, int(c_begin & 1), cr);
+    __syncthreads();
     for (int64_t c = c_begin; c < c_end; ++c) {
         const int cur = int(c & 1);
         const int64_t t0 = c * kChunk;
@@ -1076,7 +1121,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
         __builtin_amdgcn_sched_barrier(0);
         if (threadIdx.x == 0) *sm.nbad = 0;
         if (threadIdx.x < D / 32) sm.badmask[threadIdx.x] = 0u;
-        load_chunk_commit(sm, cur, cr);
         __syncthreads();
         float b2[TPT];
         gate_prep<T, D, GATE, true, TPT>(sm, cur, nvalid, p.alpha, b2);
@@ -1114,6 +1158,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
             else output_block<T, D, GATE, 1>(sm, x, lane, qpre);
         }
         __syncthreads();
+        if (c + 1 < c_end) {
+            load_chunk_commit(sm, cur ^ 1, cr);  // the previous chunk's slot is free now
+            __syncthreads();
+        }
     }
 }
 
@@ -1167,7 +1215,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
         if (e != hipSuccess) return e;
     }
     if (p.n_seg > 1 && (a.stage_mask & 2)) {
-        hipLaunchKernelGGL((carry_scan_kernel<D>), dim3((D * D / 4 + 255) / 256, a.H_kv, unsigned(a.B)), dim3(256), 0, st,
+        hipLaunchKernelGGL((carry_scan_kernel<D>), dim3(D * D / 256, a.H_kv, unsigned(a.B)), dim3(256), 0, st,
                            p.carry, p.n_seg, p.H_kv);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
