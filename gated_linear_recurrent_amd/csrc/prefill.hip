@@ -86,23 +86,37 @@ struct Layout {
     static constexpr int VP = D + 16;
     static constexpr int V_ELEMS = VNAT ? 64 * VP : D * JP;
 
+    static constexpr int SP = D + 4;     // pitch of the resident fp32 state [D][SP]
+
     static constexpr size_t K_OFF = 0;                                        // raw K [slot][64][DP]
     static constexpr size_t VT_OFF = K_OFF + size_t(NSLOT) * 64 * DP * E;     // V [slot][V_ELEMS]
     static constexpr size_t KB_OFF = VT_OFF + size_t(NSLOT) * V_ELEMS * E;    // K~ (state^T or intra)
-    static constexpr size_t ST_OFF = KB_OFF + size_t(KB_ELEMS) * E;           // S'^T [D][DP]
-    static constexpr size_t ST_BYTES = FULL ? size_t(D) * DP * E : 0;
-    static constexpr size_t F_OFF = ST_OFF + ST_BYTES;                        // fp32 [64][FP]
+    static constexpr size_t ST_OFF = KB_OFF + size_t(KB_ELEMS) * E;           // state region
+    // small persistent arrays: kmax[64] kinv[64] b2s[64] dec[D] mref[D] emref[D]
+    // blast[D] badlist[D] badmask[D/32] nbad, exact
+    static constexpr size_t SMALL_WORDS = 64 * 3 + D * 5 + D / 32 + 4;
     static constexpr size_t F_BYTES = (FULL && GATE) ? size_t(64) * FP * 4 : 0;
-    static constexpr size_t TMP_OFF = F_OFF + F_BYTES;                        // gate-scan scratch
-    // The scan scratch (part sums, raw references) lives inside the S'^T
-    // region when there is one: that region is free until the state phase.
     static constexpr size_t TMP_FLOATS = size_t(kPThreads) + 3 * D;
-    static constexpr bool TMP_ALIASED = FULL && (ST_BYTES >= TMP_FLOATS * 4);
-    static constexpr size_t SMALL_OFF = TMP_ALIASED ? TMP_OFF : TMP_OFF + TMP_FLOATS * 4;
-    // small persistent arrays: kmax[64] kinv[64] b2s[64] dec[D] mref[D] badlist[D] badmask[D/32] nbad, exact
-    static constexpr size_t SMALL_WORDS = 64 * 3 + D * 3 + D / 32 + 4;
+    // Output kernels keep the running state in LDS as fp32 S^T [D][SP] when
+    // everything fits ("resident state"); otherwise the state region holds the
+    // operand-type copy S'^T [D][DP] and the fp32 state lives in registers and
+    // a per-workgroup global slot between chunks.
+    static constexpr size_t S32_BYTES = size_t(D) * SP * 4;
+    // bf16 d = 64 output kernels run two workgroups per compute unit
+    static constexpr size_t BUDGET = (FULL && E == 2 && D == 64) ? 80 * 1024 : 160 * 1024;
+    static constexpr bool SLDS = FULL && (ST_OFF + S32_BYTES + F_BYTES + SMALL_WORDS * 4 <= BUDGET) &&
+                                 (size_t(KB_ELEMS) * E >= TMP_FLOATS * 4);
+    static constexpr size_t ST_BYTES = !FULL ? 0 : SLDS ? S32_BYTES : size_t(D) * DP * E;
+    static constexpr size_t F_OFF = ST_OFF + ST_BYTES;                        // fp32 [64][FP]
+    static constexpr size_t TMP_OFF = F_OFF + F_BYTES;                        // gate-scan scratch
+    // The scan scratch (part sums, raw references) shares a region that is
+    // idle during the gate scan: K~ (resident state: K~ is written after the
+    // scan), S'^T (other output kernels: free until the state phase), else
+    // it has its own.
+    static constexpr int TMP_WHERE = SLDS ? 1 : (FULL && ST_BYTES >= TMP_FLOATS * 4) ? 2 : 0;
+    static constexpr size_t SMALL_OFF = TMP_WHERE ? TMP_OFF : TMP_OFF + TMP_FLOATS * 4;
     static constexpr size_t TOTAL = SMALL_OFF + SMALL_WORDS * 4;
-    static_assert(TOTAL <= 160 * 1024, "LDS budget of a gfx950 workgroup exceeded");
+    static_assert(TOTAL <= BUDGET, "LDS budget of a gfx950 workgroup exceeded");
 };
 
 template <typename T, int D, int GATE, bool FULL>
@@ -111,7 +125,8 @@ struct Smem {
     T* K;      // [NSLOT][64][DP]
     T* Vt;     // [NSLOT][V_ELEMS]: [64][VP] (bf16) or [D][JP] (fp32)
     T* Kb;     // [D][JP] (K~ state, transposed) then [64][DP] (K~ intra)
-    T* St;     // [D][DP]
+    T* St;     // [D][DP] (no resident state)
+    float* S32;   // [D][SP] resident fp32 state, S32[dv][dk] = S[dk][dv]
     float* F;  // [64][FP]
     float* part;  // [kPThreads]
     float* m2raw; // [D]
@@ -122,6 +137,8 @@ struct Smem {
     float* b2s;   // [64] scalar-gate cumulative log2 gate / scalar ell2 before the scan
     float* dec;   // [D] 2^(b_last) per d_k row
     float* mref;  // [D] log2 reference per channel (0 for bad channels)
+    float* emref; // [D] 2^mref
+    float* blast; // [D] log2 decay of the whole chunk per channel
     int* badlist; // [D]
     uint32_t* badmask;  // [D/32]
     int* nbad;
@@ -132,8 +149,10 @@ struct Smem {
         Vt = reinterpret_cast<T*>(base + L::VT_OFF);
         Kb = reinterpret_cast<T*>(base + L::KB_OFF);
         St = reinterpret_cast<T*>(base + L::ST_OFF);
+        S32 = reinterpret_cast<float*>(base + L::ST_OFF);
         F = reinterpret_cast<float*>(base + L::F_OFF);
-        float* tmp = reinterpret_cast<float*>(base + (L::TMP_ALIASED ? L::ST_OFF : L::TMP_OFF));
+        float* tmp = reinterpret_cast<float*>(
+            base + (L::TMP_WHERE == 1 ? L::KB_OFF : L::TMP_WHERE == 2 ? L::ST_OFF : L::TMP_OFF));
         part = tmp;
         m2raw = tmp + kPThreads;
         bl2 = m2raw + D;
@@ -144,7 +163,9 @@ struct Smem {
         b2s = sm + 128;
         dec = sm + 192;
         mref = dec + D;
-        badlist = reinterpret_cast<int*>(mref + D);
+        emref = mref + D;
+        blast = emref + D;
+        badlist = reinterpret_cast<int*>(blast + D);
         badmask = reinterpret_cast<uint32_t*>(badlist + D);
         nbad = reinterpret_cast<int*>(badmask + D / 32);
         exact = nbad + 1;
@@ -398,7 +419,9 @@ struct StateTiles {
 };
 
 // S <- diag(dec) S + Kst^T V over the current chunk (Kst^T = Kb as [D][JP]).
-template <typename T, int D, int GATE, bool FULL>
+// With RES the state is read from and written back to the resident LDS copy
+// (acc returns the new state); otherwise it lives in acc.
+template <typename T, int D, int GATE, bool FULL, bool RES = false>
 __device__ __forceinline__ void state_advance(const Smem<T, D, GATE, FULL>& sm, int slot,
                                               f32x4_t (&acc)[StateTiles<D>::TPW]) {
     typedef Layout<T, D, GATE, FULL> L;
@@ -420,8 +443,30 @@ __device__ __forceinline__ void state_advance(const Smem<T, D, GATE, FULL>& sm, 
             d = M::mma(a, b, d);
         }
         const int r0 = 16 * rt + 4 * g;
+        float* res = sm.S32 + (16 * t + col) * L::SP + r0;
+        if constexpr (RES) {
+            const float4 v = *reinterpret_cast<const float4*>(res);
+            acc[u] = f32x4_t{v.x, v.y, v.z, v.w};
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[u][r] = sm.dec[r0 + r] * acc[u][r] + d[r];
+        if constexpr (RES) *reinterpret_cast<float4*>(res) = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+    }
+}
+
+// Resident state <- acc (tiles in accumulator order).
+template <typename T, int D, int GATE, bool FULL>
+__device__ __forceinline__ void put_resident(const Smem<T, D, GATE, FULL>& sm,
+                                             const f32x4_t (&acc)[StateTiles<D>::TPW]) {
+    typedef Layout<T, D, GATE, FULL> L;
+    typedef StateTiles<D> ST;
+    const int lane = ltid() & 63, wave = ltid() >> 6;
+    const int col = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < ST::TPW; ++u) {
+        const int rt = ST::rt(wave, u), t = ST::ct(wave, u);
+        *reinterpret_cast<float4*>(sm.S32 + (16 * t + col) * L::SP + 16 * rt + 4 * g) =
+            make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
     }
 }
 
@@ -503,49 +548,26 @@ __device__ __forceinline__ void store_slot(float* slot, const f32x4_t (&acc)[Sta
 }
 
 // -------------------------------------------- gate prep shared by P1 and P3
-// After this: dec, mref, badlist/badmask/nbad, F (P3, vector) and the
-// transposed state key operand Kb[c][j] = phik_j[c] 2^(b_last[c] - b_j[c]).
-// Returns (through b2) the per-thread cumulative gates for the intra operand.
+// gate_stats leaves in LDS: key row statistics, the cumulative gates, dec,
+// mref, emref (vector), blast, badlist/badmask/nbad and F (output kernels,
+// vector), and returns (through b2) the per-thread cumulative gates.
 template <typename T, int D, int GATE, bool FULL, int TPT>
-__device__ __forceinline__ void gate_prep(const Smem<T, D, GATE, FULL>& sm, int slot, int nvalid,
-                                          float alpha, float (&b2)[TPT]) {
+__device__ __forceinline__ void gate_stats(const Smem<T, D, GATE, FULL>& sm, int slot, int nvalid,
+                                           float alpha, float (&b2)[TPT]) {
     typedef Layout<T, D, GATE, FULL> L;
-    const T* Ks = sm.K + slot * 64 * L::DP;
     key_row_stats(sm, slot, nvalid);
     __syncthreads();
     if (GATE == 0) {
         scalar_gate_scan(sm);
         __syncthreads();
         const float bl = sm.b2s[nvalid - 1];
-        constexpr int VPL = 16 / sizeof(T);
-        for (int idx = ltid(); idx < 32 * (D / VPL); idx += kPThreads) {
-            const int j0 = 2 * (idx & 31);
-            const int c0 = (idx >> 5) * VPL;
-            const uint4 u0 = *reinterpret_cast<const uint4*>(Ks + j0 * L::DP + c0);
-            const uint4 u1 = *reinterpret_cast<const uint4*>(Ks + (j0 + 1) * L::DP + c0);
-            const T* e0 = reinterpret_cast<const T*>(&u0);
-            const T* e1 = reinterpret_cast<const T*>(&u1);
-            const float m0 = sm.kmax[j0], m1 = sm.kmax[j0 + 1];
-            const float f0 = bl - sm.b2s[j0], f1 = bl - sm.b2s[j0 + 1];
-            const float s0 = sm.kinv[j0], s1 = sm.kinv[j0 + 1];
-            T* dst = sm.Kb + c0 * L::JP + key_pos(j0);
-#pragma unroll
-            for (int e = 0; e < VPL; ++e) {
-                const float a = s0 * fast_exp2((to_f32(e0[e]) - m0) * kLog2e + f0);
-                const float b = s1 * fast_exp2((to_f32(e1[e]) - m1) * kLog2e + f1);
-                if constexpr (sizeof(T) == 2) {
-                    *reinterpret_cast<uint32_t*>(dst + e * L::JP) = pack_bf16x2(a, b);
-                } else {
-                    *reinterpret_cast<float2*>(dst + e * L::JP) = make_float2(a, b);
-                }
-            }
-        }
         // reference for the factorised intra-chunk decay: the middle token
         const float m = sm.b2s[nvalid - 1 < 31 ? nvalid - 1 : 31];
         const bool ex = fmaxf(sm.b2s[0] - m, m - bl) > kEmax2;
         if (ltid() < D) {
             sm.dec[ltid()] = fast_exp2(bl);
             sm.mref[ltid()] = ex ? 0.0f : m;
+            sm.blast[ltid()] = bl;
         }
         if (ltid() == 0) *sm.exact = ex ? 1 : 0;
     } else {
@@ -559,22 +581,78 @@ __device__ __forceinline__ void gate_prep(const Smem<T, D, GATE, FULL>& sm, int 
         const float mref = bad ? 0.0f : m2;
         if (part == 0) {
             sm.mref[c] = mref;
+            sm.emref[c] = fast_exp2(mref);
             sm.dec[c] = fast_exp2(bl);
+            sm.blast[c] = bl;
             if (FULL && bad) {
                 const int idx = atomicAdd(sm.nbad, 1);
                 sm.badlist[idx] = c;
                 atomicOr(&sm.badmask[c >> 5], 1u << (c & 31));
             }
         }
+        if (FULL) {
+#pragma unroll
+            for (int jj = 0; jj < TPT; ++jj) {
+                const int j = part * TPT + jj;
+                sm.F[j * L::FP + c] = bad ? b2[jj] : alpha * fast_exp2(b2[jj] - mref);
+            }
+        }
+    }
+}
+
+// Transposed state key operand Kb[c][key_pos(j)] = phik_j[c] 2^(b_last[c] - b_j[c])
+// (b_last per channel from bl; the scalar gate reads its own scan).
+template <typename T, int D, int GATE, bool FULL, int TPT>
+__device__ __forceinline__ void state_key_operand(const Smem<T, D, GATE, FULL>& sm, int slot, int nvalid,
+                                                  const float* bl, const float (&b2)[TPT]) {
+    typedef Layout<T, D, GATE, FULL> L;
+    const T* Ks = sm.K + slot * 64 * L::DP;
+    if (GATE == 0) {
+        const float blv = sm.b2s[nvalid - 1];
+        constexpr int VPL = 16 / sizeof(T);
+        for (int idx = ltid(); idx < 32 * (D / VPL); idx += kPThreads) {
+            const int j0 = 2 * (idx & 31);
+            const int c0 = (idx >> 5) * VPL;
+            const uint4 u0 = *reinterpret_cast<const uint4*>(Ks + j0 * L::DP + c0);
+            const uint4 u1 = *reinterpret_cast<const uint4*>(Ks + (j0 + 1) * L::DP + c0);
+            const T* e0 = reinterpret_cast<const T*>(&u0);
+            const T* e1 = reinterpret_cast<const T*>(&u1);
+            const float m0 = sm.kmax[j0], m1 = sm.kmax[j0 + 1];
+            const float f0 = blv - sm.b2s[j0], f1 = blv - sm.b2s[j0 + 1];
+            const float s0 = sm.kinv[j0], s1 = sm.kinv[j0 + 1];
+            T* dst = sm.Kb + c0 * L::JP + key_pos(j0);
+#pragma unroll
+            for (int e = 0; e < VPL; ++e) {
+                const float a = s0 * fast_exp2((to_f32(e0[e]) - m0) * kLog2e + f0);
+                const float b = s1 * fast_exp2((to_f32(e1[e]) - m1) * kLog2e + f1);
+                if constexpr (sizeof(T) == 2) {
+                    *reinterpret_cast<uint32_t*>(dst + e * L::JP) = pack_bf16x2(a, b);
+                } else {
+                    *reinterpret_cast<float2*>(dst + e * L::JP) = make_float2(a, b);
+                }
+            }
+        }
+    } else {
+        const int c = ltid() % D;
+        const int part = ltid() / D;
+        const float blc = bl[c];
 #pragma unroll
         for (int jj = 0; jj < TPT; ++jj) {
             const int j = part * TPT + jj;
             const float kv = to_f32(Ks[j * L::DP + c]);
             sm.Kb[c * L::JP + key_pos(j)] =
-                from_f32<T>(sm.kinv[j] * fast_exp2((kv - sm.kmax[j]) * kLog2e + bl - b2[jj]));
-            if (FULL) sm.F[j * L::FP + c] = bad ? b2[jj] : alpha * fast_exp2(b2[jj] - mref);
+                from_f32<T>(sm.kinv[j] * fast_exp2((kv - sm.kmax[j]) * kLog2e + blc - b2[jj]));
         }
     }
+}
+
+// Both steps back to back (segment-state kernel and output kernels without a
+// resident state); the vector gate reads b_last from the scan scratch.
+template <typename T, int D, int GATE, bool FULL, int TPT>
+__device__ __forceinline__ void gate_prep(const Smem<T, D, GATE, FULL>& sm, int slot, int nvalid,
+                                          float alpha, float (&b2)[TPT]) {
+    gate_stats<T, D, GATE, FULL, TPT>(sm, slot, nvalid, alpha, b2);
+    state_key_operand<T, D, GATE, FULL, TPT>(sm, slot, nvalid, sm.bl2, b2);
 }
 
 // Intra operand Kb[j][c] = phik_j[c] 2^(mref[c] - b_j[c]) (vector, good
@@ -743,6 +821,31 @@ __device__ __forceinline__ void load_q_block(QFrags<T, D>& qf, const T* q, int64
             }
         }
     }
+}
+
+// Inter-chunk operand fragment read from the resident fp32 state: row dv,
+// channels k0 .. k0 + KPL - 1, scaled by 2^mref (vector gate), packed to T.
+template <typename T, int D, int GATE>
+__device__ __forceinline__ typename Mfma<T>::frag resident_frag(const Smem<T, D, GATE, true>& sm, int dv, int k0) {
+    typedef Layout<T, D, GATE, true> L;
+    typedef Mfma<T> M;
+    const float* src = sm.S32 + dv * L::SP + k0;
+    float x[M::KPL];
+    if constexpr (M::KPL == 8) {
+        const float4 a = *reinterpret_cast<const float4*>(src);
+        const float4 b = *reinterpret_cast<const float4*>(src + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        if (GATE) {
+            const float4 ea = *reinterpret_cast<const float4*>(sm.emref + k0);
+            const float4 eb = *reinterpret_cast<const float4*>(sm.emref + k0 + 4);
+            x[0] *= ea.x; x[1] *= ea.y; x[2] *= ea.z; x[3] *= ea.w;
+            x[4] *= eb.x; x[5] *= eb.y; x[6] *= eb.z; x[7] *= eb.w;
+        }
+    } else {
+        x[0] = GATE ? src[0] * sm.emref[k0] : src[0];
+    }
+    return M::pack(x);
 }
 
 template <typename T, int D, int GATE, int IB>
@@ -1004,7 +1107,9 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
         f32x4_t acc[2] = {zero4(), zero4()};
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
-            const Frag a = M::load(sm.St + (16 * t + col) * L::DP + M::KSTEP * k + KPL * g);
+            Frag a;
+            if constexpr (L::SLDS) a = resident_frag(sm, 16 * t + col, M::KSTEP * k + KPL * g);
+            else a = M::load(sm.St + (16 * t + col) * L::DP + M::KSTEP * k + KPL * g);
             acc[0] = M::mma(a, qt[0][k], acc[0]);
             acc[1] = M::mma(a, qt[1][k], acc[1]);
         }
@@ -1017,7 +1122,9 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
                 const float bad_q =
                     x.alpha * fast_exp2((qc - qmax[s]) * kLog2e) * qinv[s] * fast_exp2(sm.F[i_loc[s] * L::FP + c]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[s][r] += bad_q * to_f32(sm.St[(16 * t + 4 * g + r) * L::DP + c]);
+                for (int r = 0; r < 4; ++r)
+                    acc[s][r] += bad_q * (L::SLDS ? sm.S32[(16 * t + 4 * g + r) * L::SP + c]
+                                                  : to_f32(sm.St[(16 * t + 4 * g + r) * L::DP + c]));
             }
         }
         if constexpr (BF) {
@@ -1098,6 +1205,72 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
     load_chunk_issue<T, D>(cr, kbase, vbase, row_stride, c_begin * kChunk,
                            p.T - c_begin * kChunk < kChunk ? int(p.T - c_begin * kChunk) : kChunk);
     load_chunk_commit(sm, int(c_begin & 1), cr);
+    const int n_items = p.n_rep * 2;
+    if constexpr (L::SLDS) {
+        // Resident state: per chunk, gate statistics and the intra operand,
+        // then the outputs (inter term from S entering the chunk), then the
+        // state operand and the in-place state update.
+        f32x4_t acc[StateTiles<D>::TPW];
+        load_state<D>(carry_in, acc);
+        put_resident(sm, acc);
+        __syncthreads();
+        for (int64_t c = c_begin; c < c_end; ++c) {
+            const int cur = int(c & 1);
+            const int64_t t0 = c * kChunk;
+            const int nvalid = p.T - t0 < kChunk ? int(p.T - t0) : kChunk;
+            // query fragments of this wave's first output block, loaded now
+            // so their latency overlaps the gate phase
+            __builtin_amdgcn_sched_barrier(0);
+            QFrags<T, D> qpre;
+            if (wave < n_items) {
+                int lane = threadIdx.x & 63;
+                asm volatile("" : "+v"(lane));
+                load_q_block<T, D>(qpre, static_cast<const T*>(p.q), b * p.T + t0, H_q,
+                                   h * p.n_rep + (wave % p.n_rep), 32 * (wave / p.n_rep), nvalid, lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (threadIdx.x == 0) *sm.nbad = 0;
+            if (threadIdx.x < D / 32) sm.badmask[threadIdx.x] = 0u;
+            __syncthreads();
+            float b2[TPT];
+            gate_stats<T, D, GATE, true, TPT>(sm, cur, nvalid, p.alpha, b2);
+            __syncthreads();
+            intra_key_operand<T, D, GATE, true, TPT>(sm, cur, b2);
+            __syncthreads();
+            ItemCtx<T, D, GATE> x;
+            x.q = static_cast<const T*>(p.q);
+            x.o = static_cast<T*>(p.o);
+            x.row0 = b * p.T + t0;
+            x.H_q = H_q;
+            x.nvalid = nvalid;
+            x.window = p.window;
+            x.have_prev = c > 0;
+            x.alpha = p.alpha;
+            x.cur = cur;
+            // next chunk's K/V: in flight during the output phase
+            if (c + 1 < c_end) {
+                const int64_t t1 = t0 + kChunk;
+                load_chunk_issue<T, D>(cr, kbase, vbase, row_stride, t1, p.T - t1 < kChunk ? int(p.T - t1) : kChunk);
+            }
+            for (int it = wave; it < n_items; it += kPWaves) {
+                x.hq = h * p.n_rep + (it % p.n_rep);
+                int lane = threadIdx.x & 63;
+                asm volatile("" : "+v"(lane));  // keep lane-derived addresses inside the loop
+                if (it != wave)
+                    load_q_block<T, D>(qpre, x.q, x.row0, H_q, x.hq, 32 * (it / p.n_rep), nvalid, lane);
+                if (it / p.n_rep == 0) output_block<T, D, GATE, 0>(sm, x, lane, qpre);
+                else output_block<T, D, GATE, 1>(sm, x, lane, qpre);
+            }
+            __syncthreads();
+            if (c + 1 < c_end) load_chunk_commit(sm, cur ^ 1, cr);  // the previous chunk's slot is free now
+            state_key_operand<T, D, GATE, true, TPT>(sm, cur, nvalid, sm.blast, b2);
+            __syncthreads();
+            state_advance<T, D, GATE, true, true>(sm, cur, acc);
+            if (c + 1 == c_end && last_seg) store_state<D>(p.S_T + (size_t(b) * p.H_kv + h) * D * D, acc);
+            // the next chunk's first barrier orders these LDS reads before its gate scan
+        }
+        return;
+    }
     __syncthreads();
     for (int64_t c = c_begin; c < c_end; ++c) {
         const int cur = int(c & 1);
@@ -1110,7 +1283,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
         f32x4_t acc[StateTiles<D>::TPW];
         if (c == c_begin) load_state<D>(carry_in, acc);
         else load_slot<D>(slot, acc);
-        const int n_items = p.n_rep * 2;
         QFrags<T, D> qpre;
         if (wave < n_items) {
             int lane = threadIdx.x & 63;
