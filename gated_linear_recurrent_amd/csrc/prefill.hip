@@ -698,12 +698,48 @@ __device__ __forceinline__ void intra_key_operand(const Smem<T, D, GATE, FULL>& 
 }
 
 // ------------------------------------------------------------------ P1
+// Local end state of a segment (from a zero state) and its total log2 decay:
+//   L = sum_j (phik_j (.) 2^(b_end - b_j))^T v_j ,  lg = b_end
+// over the segment's tokens, in blocks of up to TB tokens held in LDS
+// token-major. Per block: key row statistics; the log2 gates and, per token,
+// the sum of the gates after it (computed as suffix sums, so every factor is
+// at most 1); the key operand phik_j (.) 2^(suffix after j) written over K in
+// place; then one MFMA contraction over the block's tokens added to the
+// running state rescaled by the block's decay.
+template <typename T, int D>
+struct SegLayout {
+    static constexpr int E = sizeof(T);
+    static constexpr int TB = E == 2 ? 256 : 128;      // tokens per block
+    static constexpr int P = D + 16;                   // row pitch (elements) of the K and V tiles
+    static constexpr int VPL = 16 / E;                 // elements per 16-byte piece
+    static constexpr int PPR = D / VPL;                // pieces per row
+    static constexpr int NPT = TB * PPR / kPThreads;   // K (and V) pieces per thread
+    static_assert(NPT * kPThreads == TB * PPR, "pieces per thread");
+    static constexpr int NPART = kPThreads / D;        // vector gate: token ranges per channel
+    static constexpr int TPP = TB / NPART;             // tokens per range
+    static constexpr size_t K_OFF = 0;
+    static constexpr size_t V_OFF = K_OFF + size_t(TB) * P * E;
+    static constexpr size_t F_OFF = V_OFF + size_t(TB) * P * E;
+    // fp32: kmax[TB] kinv[TB] ell[TB] part[kPThreads] tot[D] lg[D]
+    static constexpr size_t TOTAL = F_OFF + (3 * size_t(TB) + kPThreads + 2 * D) * 4;
+    static_assert(TOTAL <= 160 * 1024, "LDS budget of a gfx950 workgroup exceeded");
+};
+
 template <typename T, int D, int GATE>
 __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams p) {
-    typedef Layout<T, D, GATE, false> L;
-    __shared__ __align__(16) char smem[L::TOTAL];
-    const Smem<T, D, GATE, false> sm(smem);
-    constexpr int TPT = 64 / (kPThreads / D);
+    typedef SegLayout<T, D> SL;
+    typedef Mfma<T> M;
+    typedef StateTiles<D> ST;
+    static_assert(ST::NTT % ST::TPW == 0, "a wave's state tiles share one row tile");
+    __shared__ __align__(16) char smem[SL::TOTAL];
+    T* Ks = reinterpret_cast<T*>(smem + SL::K_OFF);
+    T* Vs = reinterpret_cast<T*>(smem + SL::V_OFF);
+    float* kmax = reinterpret_cast<float*>(smem + SL::F_OFF);
+    float* kinv = kmax + SL::TB;
+    float* ell = kinv + SL::TB;     // scalar gate: log2 gate per token, then the sum after it
+    float* part = ell + SL::TB;     // vector gate: gate sums per (token range, channel)
+    float* tot = part + kPThreads;  // log2 decay of the whole block per channel
+    float* lg = tot + D;            // log2 decay of the segment so far per channel
 
     const int s = blockIdx.x;
     const int h = blockIdx.y;
@@ -711,30 +747,201 @@ __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams 
     const int64_t row_stride = int64_t(p.H_kv) * D;
     const T* kbase = static_cast<const T*>(p.k) + (b * p.T * p.H_kv + h) * D;
     const T* vbase = static_cast<const T*>(p.v) + (b * p.T * p.H_kv + h) * D;
+    const int64_t tok0 = int64_t(s) * p.cps * kChunk;  // never the last segment: whole chunks
+    const int ntok = int(p.cps) * kChunk;
 
-    f32x4_t acc[StateTiles<D>::TPW];
-    load_state<D>(nullptr, acc);
-    float lg = 0.f;  // total log2 decay of the segment for channel threadIdx.x (< D)
-    const int64_t c_begin = int64_t(s) * p.cps;
-    const int64_t c_end = c_begin + p.cps;  // never the last segment: always whole chunks
-    ChunkRegs<T, D> cr;
-    load_chunk_issue<T, D>(cr, kbase, vbase, row_stride, c_begin * kChunk, kChunk);
-    for (int64_t c = c_begin; c < c_end; ++c) {
-        load_chunk_commit(sm, 0, cr);
+    uint4 kr[SL::NPT], vr[SL::NPT];
+    auto issue = [&](int blk0, int nb) {
+        const int tid = ltid();
+#pragma unroll
+        for (int n = 0; n < SL::NPT; ++n) {
+            const int idx = tid + n * kPThreads;
+            const int j = idx / SL::PPR;
+            const int64_t off = (tok0 + blk0 + j) * row_stride + (idx % SL::PPR) * SL::VPL;
+            kr[n] = make_uint4(0, 0, 0, 0);
+            vr[n] = make_uint4(0, 0, 0, 0);
+            if (j < nb) {
+                kr[n] = *reinterpret_cast<const uint4*>(kbase + off);
+                vr[n] = *reinterpret_cast<const uint4*>(vbase + off);
+            }
+        }
+    };
+
+    f32x4_t acc[ST::TPW];
+#pragma unroll
+    for (int u = 0; u < ST::TPW; ++u) acc[u] = zero4();
+    if (threadIdx.x < D) lg[threadIdx.x] = 0.0f;
+    issue(0, ntok < SL::TB ? ntok : SL::TB);
+    for (int blk0 = 0; blk0 < ntok; blk0 += SL::TB) {
+        const int nb = ntok - blk0 < SL::TB ? ntok - blk0 : SL::TB;  // a multiple of 64
+        {
+            const int tid = ltid();
+#pragma unroll
+            for (int n = 0; n < SL::NPT; ++n) {
+                const int idx = tid + n * kPThreads;
+                const int o = (idx / SL::PPR) * SL::P + (idx % SL::PPR) * SL::VPL;
+                *reinterpret_cast<uint4*>(Ks + o) = kr[n];
+                *reinterpret_cast<uint4*>(Vs + o) = vr[n];
+            }
+        }
         __syncthreads();
-        // the next chunk's K/V are in flight while this one is processed
-        if (c + 1 < c_end) load_chunk_issue<T, D>(cr, kbase, vbase, row_stride, (c + 1) * kChunk, kChunk);
-        float b2[TPT];
-        gate_prep<T, D, GATE, false, TPT>(sm, 0, kChunk, p.alpha, b2);
+        if (blk0 + SL::TB < ntok) {  // next block in flight while this one is processed
+            const int rest = ntok - blk0 - SL::TB;
+            issue(blk0 + SL::TB, rest < SL::TB ? rest : SL::TB);
+        }
+
+        // key row statistics, eight lanes per row; rows past nb get 1/sum = 0
+        {
+            constexpr int NLD = D / (8 * SL::VPL);
+            const int tid = ltid();
+            const int sub = tid & 7;
+            for (int r0 = 0; r0 < SL::TB; r0 += kPThreads / 8) {
+                const int j = r0 + (tid >> 3);
+                const T* row = Ks + j * SL::P + sub * SL::VPL;
+                float x[NLD * SL::VPL];
+#pragma unroll
+                for (int q = 0; q < NLD; ++q) {
+                    const uint4 u = *reinterpret_cast<const uint4*>(row + q * 8 * SL::VPL);
+                    const T* e = reinterpret_cast<const T*>(&u);
+#pragma unroll
+                    for (int i = 0; i < SL::VPL; ++i) x[q * SL::VPL + i] = to_f32(e[i]);
+                }
+                float mx = -INFINITY, sraw = 0.f;
+#pragma unroll
+                for (int i = 0; i < NLD * SL::VPL; ++i) {
+                    mx = fmaxf(mx, x[i]);
+                    sraw += x[i];
+                }
+                mx = group8_max(mx);
+                float se = 0.f;
+#pragma unroll
+                for (int i = 0; i < NLD * SL::VPL; ++i) se += fast_exp2((x[i] - mx) * kLog2e);
+                se = group8_sum(se);
+                if (GATE == 0) sraw = group8_sum(sraw);
+                if (sub == 0) {
+                    const bool ok = j < nb;
+                    kmax[j] = mx;
+                    kinv[j] = ok ? fast_rcp(se) : 0.0f;
+                    if (GATE == 0) ell[j] = ok ? log2_sigmoid(sraw * (1.0f / D)) : 0.0f;
+                }
+            }
+        }
         __syncthreads();
-        if (threadIdx.x < D) lg += GATE ? sm.bl2[threadIdx.x] : sm.b2s[kChunk - 1];
-        state_advance(sm, 0, acc);
+
+        if (GATE == 0) {
+            // suffix sums over the block (one wave, TPL consecutive tokens per lane)
+            constexpr int TPL = SL::TB / 64;
+            if (ltid() < 64) {
+                const int lane = ltid();
+                float l[TPL];
+                float own = 0.f;
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) {
+                    l[i] = ell[lane * TPL + i];
+                    own += l[i];
+                }
+                float incl = own;  // sum over lanes >= lane
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const float y = __shfl_down(incl, o, 64);
+                    if (lane + o < 64) incl += y;
+                }
+                float run = __shfl_down(incl, 1, 64);
+                if (lane == 63) run = 0.0f;
+#pragma unroll
+                for (int i = TPL - 1; i >= 0; --i) {
+                    ell[lane * TPL + i] = run;
+                    run += l[i];
+                }
+                const float total = __shfl(incl, 0, 64);
+                for (int c = lane; c < D; c += 64) tot[c] = total;
+            }
+            __syncthreads();
+            // key operand in place: phik_j 2^(sum of the gates after j)
+            const int tid = ltid();
+#pragma unroll
+            for (int n = 0; n < SL::NPT; ++n) {
+                const int idx = tid + n * kPThreads;
+                const int j = idx / SL::PPR;
+                T* e = Ks + j * SL::P + (idx % SL::PPR) * SL::VPL;
+                const uint4 u = *reinterpret_cast<const uint4*>(e);
+                const T* x = reinterpret_cast<const T*>(&u);
+                const float m = kmax[j], sc = kinv[j], off = ell[j];
+                float y[SL::VPL];
+#pragma unroll
+                for (int i = 0; i < SL::VPL; ++i) y[i] = sc * fast_exp2((to_f32(x[i]) - m) * kLog2e + off);
+                if constexpr (sizeof(T) == 2) {
+                    *reinterpret_cast<uint4*>(e) = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                                                              pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+                } else {
+                    *reinterpret_cast<float4*>(e) = make_float4(y[0], y[1], y[2], y[3]);
+                }
+            }
+        } else {
+            // thread (c, range): channel c, tokens range*TPP .. +TPP-1; x_j[c] is
+            // the mean of k_j over the in-range channels c-1 .. c+2
+            const int c = ltid() % D;
+            const int rg = ltid() / D;
+            const int lo = c > 0 ? c - 1 : 0;
+            const int hi = c + 3 < D ? c + 3 : D;
+            const float inv_cnt = 1.0f / static_cast<float>(hi - lo);
+            float l[SL::TPP];
+            float own = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < SL::TPP; ++jj) {
+                const int j = rg * SL::TPP + jj;
+                float x = 0.f;
+                for (int m = lo; m < hi; ++m) x += to_f32(Ks[j * SL::P + m]);
+                l[jj] = j < nb ? log2_sigmoid(x * inv_cnt) : 0.0f;
+                own += l[jj];
+            }
+            part[rg * D + c] = own;
+            __syncthreads();  // every pooled read is done before K is overwritten
+            float run = 0.f;
+            for (int r = rg + 1; r < SL::NPART; ++r) run += part[r * D + c];
+#pragma unroll
+            for (int jj = SL::TPP - 1; jj >= 0; --jj) {
+                const int j = rg * SL::TPP + jj;
+                T* e = Ks + j * SL::P + c;
+                *e = from_f32<T>(kinv[j] * fast_exp2((to_f32(*e) - kmax[j]) * kLog2e + run));
+                run += l[jj];
+            }
+            if (rg == 0) tot[c] = run;
+        }
         __syncthreads();
+
+        // running state: acc <- diag(2^tot) acc + Kop^T V over the block
+        {
+            const int lane = ltid() & 63, wave = ltid() >> 6;
+            const int col = lane & 15, g = lane >> 4;
+            const int rt = ST::rt(wave, 0);
+#pragma unroll
+            for (int u = 0; u < ST::TPW; ++u) {
+                const int r0 = 16 * rt + 4 * g;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[u][r] *= fast_exp2(tot[r0 + r]);
+            }
+            for (int ks = 0; ks < nb / M::KSTEP; ++ks) {
+                typename M::frag a;
+                if constexpr (sizeof(T) == 2) a = load_key_frag(Ks, SL::P, M::KSTEP * ks, 16 * rt, lane);
+                else a = Ks[(M::KSTEP * ks + g) * SL::P + 16 * rt + col];
+#pragma unroll
+                for (int u = 0; u < ST::TPW; ++u) {
+                    const int t = ST::ct(wave, u);
+                    typename M::frag bv;
+                    if constexpr (sizeof(T) == 2) bv = load_key_frag(Vs, SL::P, M::KSTEP * ks, 16 * t, lane);
+                    else bv = Vs[(M::KSTEP * ks + g) * SL::P + 16 * t + col];
+                    acc[u] = M::mma(a, bv, acc[u]);
+                }
+            }
+            if (ltid() < D) lg[ltid()] += tot[ltid()];
+        }
+        __syncthreads();  // the next block's commit overwrites K and V
     }
     const size_t rec = size_t(D) * D + D;
     float* dst = p.carry + ((size_t(b) * p.H_kv + h) * size_t(p.n_seg - 1) + s) * rec;
     store_state<D>(dst, acc);
-    if (threadIdx.x < D) dst[size_t(D) * D + threadIdx.x] = lg;
+    if (threadIdx.x < D) dst[size_t(D) * D + threadIdx.x] = lg[threadIdx.x];
 }
 
 // ------------------------------------------------------------------ P2
@@ -1193,25 +1400,24 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
 
     const int64_t c_begin = int64_t(s) * p.cps;
     const int64_t c_end = c_begin + p.cps < p.n_chunks ? c_begin + p.cps : p.n_chunks;
-    if (c_begin > 0) {
-        load_chunk(sm, int((c_begin - 1) & 1), kbase, vbase, row_stride, (c_begin - 1) * kChunk, kChunk);
-    } else {
-        zero_slot(sm, int((c_begin + 1) & 1));
-    }
-    // K/V of the chunk about to be processed: the first one is loaded here;
-    // each following one is issued before the previous chunk's output phase
-    // and stored to LDS right after it
-    ChunkRegs<T, D> cr;
+    // K/V of the chunk about to be processed: the first one is loaded here,
+    // together with the previous chunk (sliding window) and, with a resident
+    // state, the state entering the segment; each following chunk is issued
+    // before the previous chunk's output phase and stored to LDS after it.
+    ChunkRegs<T, D> cr, cp;
     load_chunk_issue<T, D>(cr, kbase, vbase, row_stride, c_begin * kChunk,
                            p.T - c_begin * kChunk < kChunk ? int(p.T - c_begin * kChunk) : kChunk);
+    if (c_begin > 0) load_chunk_issue<T, D>(cp, kbase, vbase, row_stride, (c_begin - 1) * kChunk, kChunk);
+    f32x4_t acc[StateTiles<D>::TPW];
+    if constexpr (L::SLDS) load_state<D>(carry_in, acc);
+    if (c_begin > 0) load_chunk_commit(sm, int((c_begin - 1) & 1), cp);
+    else zero_slot(sm, int((c_begin + 1) & 1));
     load_chunk_commit(sm, int(c_begin & 1), cr);
     const int n_items = p.n_rep * 2;
     if constexpr (L::SLDS) {
         // Resident state: per chunk, gate statistics and the intra operand,
         // then the outputs (inter term from S entering the chunk), then the
         // state operand and the in-place state update.
-        f32x4_t acc[StateTiles<D>::TPW];
-        load_state<D>(carry_in, acc);
         put_resident(sm, acc);
         __syncthreads();
         for (int64_t c = c_begin; c < c_end; ++c) {
@@ -1280,7 +1486,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
         // wave's first output block, loaded now so their latency overlaps the
         // gate and state phases
         __builtin_amdgcn_sched_barrier(0);
-        f32x4_t acc[StateTiles<D>::TPW];
         if (c == c_begin) load_state<D>(carry_in, acc);
         else load_slot<D>(slot, acc);
         QFrags<T, D> qpre;
