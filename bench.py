@@ -3,11 +3,16 @@
 
 A step is one prefill of the Llama-3-8B-shaped workload
 (B=1, T=8192, H_q=32, H_kv=8, d=128, bf16, scalar gate, window 64,
-alpha 0.5) with its inputs already resident in device memory. The JSON
-line reports prefill tokens/s as `value`, the roofline of the dominant kernel
-(the fused output kernel, timed with HIP events on the stream it runs on),
-the float64 CPU oracle on the host as a reported baseline, and the decode
-workload (64 sequences, Llama-3-8B heads, one token per step) as extra keys.
+alpha 0.5) with its inputs already resident in device memory. Each timed
+step is bracketed by HIP events on the stream the kernels run on; before
+each one an untimed 512 MiB write evicts the 256 MB last-level cache, so
+the inputs come from HBM ("cold", the headline `value`, median step). The
+same steps without the eviction are reported as "hot". The JSON line also
+carries the roofline of the dominant kernel (the fused output kernel), the
+float64 CPU oracle on the host as a reported baseline, and the decode
+workload (64 sequences, Llama-3-8B heads, one token per step: eager
+launches, the same launches replayed from a captured HIP graph, and
+cold steps).
 
     python bench.py [--steps K] [--warmup W] [--decode-steps N]
 
@@ -16,7 +21,6 @@ Only one GPU is used; --gpus N with N > 1 exits with a message.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -31,37 +35,28 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PREFILL_WORKLOAD = "prefill_8b_b1_t8192_d128"
 DECODE_WORKLOAD = "decode_8b_n64_d128"
 CHUNK = 64
+SCRUB_BYTES = 512 << 20        # larger than the 256 MB last-level cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = {
-    "prefill_output_kernel": ["gated_linear_recurrent_amd/csrc/prefill.hip",
-                              "gated_linear_recurrent_amd/csrc/device_common.h"],
-    "decode_step_kernel": ["gated_linear_recurrent_amd/csrc/decode.hip",
-                           "gated_linear_recurrent_amd/csrc/device_common.h"],
-}
-
-
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_sha(kernel: str) -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
-
-
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from committed counter runs, if the kernel is unchanged."""
+def counter_record(kernel: str, workload: str) -> dict:
+    """Committed counter readings for this kernel, if its sources are unchanged since."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)[kernel]
     except (OSError, KeyError, ValueError):
-        return None
-    if rec.get("workload") != workload or rec.get("source_sha256") != source_sha(kernel):
-        return None
-    return rec.get("hbm_bytes_per_launch")
+        return {}
+    from gated_linear_recurrent_amd.counters import KERNELS, source_sha
+    if rec.get("workload") != workload or rec.get("source_sha256") != source_sha(KERNELS[kernel][2]):
+        return {}
+    return rec
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE), or None."""
+    return counter_record(kernel, workload).get("hbm_bytes_per_launch")
 
 
 def prefill_algorithmic(cfg: dict) -> tuple[float, float]:
@@ -145,29 +140,42 @@ def main() -> int:
         gla.liger_attn_prefill(q, k, v, gate, cfg["window"], cfg["alpha"], o=o, S_T=S_T, workspace=ws,
                                stage_mask=mask)
 
+    scrub = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def timed_prefill(steps: int, cold: bool):
+        """Per step: (segment states + carry scan, output kernel, total) in ms."""
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i, e in enumerate(ev):
+            if cold:
+                scrub.fill_(float(i))
+            e[0].record()
+            prefill(gla.LIGER_STAGE_SEGMENT_STATES | gla.LIGER_STAGE_CARRY_SCAN)
+            e[1].record()
+            prefill(gla.LIGER_STAGE_OUTPUT)
+            e[2].record()
+        torch.cuda.synchronize()
+        return np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[0].elapsed_time(e[2])] for e in ev])
+
     log(f"[bench] prefill warmup {args.warmup}")
     for _ in range(args.warmup):
         prefill(7)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    log(f"[bench] prefill timed {args.steps}")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e in ev:
-        e[0].record()
-        prefill(gla.LIGER_STAGE_SEGMENT_STATES | gla.LIGER_STAGE_CARRY_SCAN)
-        e[1].record()
-        prefill(gla.LIGER_STAGE_OUTPUT)
-        e[2].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    carry_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    out_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    ms_per_step = wall * 1e3 / args.steps
+    log(f"[bench] prefill timed {args.steps} cold + {args.steps} hot")
+    cold = timed_prefill(args.steps, True)
+    hot = timed_prefill(args.steps, False)
+    ms_per_step = float(np.median(cold[:, 2]))
     tokens_per_s = B * T / (ms_per_step * 1e-3)
     byts, flops = prefill_algorithmic(cfg)
+    # the dominant kernel's average launch duration over every timed launch
+    out_ms = float(np.mean(np.concatenate([cold[:, 1], hot[:, 1]])))
     achieved = byts / (out_ms * 1e-3) / 1e9
-    traffic = measured_traffic("prefill_output_kernel", PREFILL_WORKLOAD)
+    crec = counter_record("prefill_output_kernel", PREFILL_WORKLOAD)
+    traffic = crec.get("hbm_bytes_per_launch")
+
+    def stats(a):
+        return {"median_ms": float(np.median(a)), "min_ms": float(np.min(a)), "mean_ms": float(np.mean(a))}
+
     result = {
         "metric": "Liger Attention prefill tokens/s/GPU at 8B shapes; decode steps/s; % roofline",
         "value": tokens_per_s,
@@ -187,13 +195,18 @@ def main() -> int:
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": "prefill_output_kernel", "kernel_ms": out_ms,
                      "algorithmic_bytes": byts, "algorithmic_flops": flops,
-                     "mfma_frac_algorithmic": flops / (out_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)},
-        "prefill_breakdown_ms": {"segment_states_and_carry_scan": carry_ms, "output": out_ms,
-                                 "events_total": carry_ms + out_ms},
+                     "mfma_frac_algorithmic": flops / (out_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+                     "mfma_busy_frac_counters": crec.get("mfma_busy_frac"),
+                     "tcc_ea_gbs_counters": (traffic / (out_ms * 1e-3) / 1e9) if traffic else None},
+        "prefill_cold": {"total": stats(cold[:, 2]), "segment_states_and_carry_scan": stats(cold[:, 0]),
+                         "output": stats(cold[:, 1])},
+        "prefill_hot": {"total": stats(hot[:, 2]), "segment_states_and_carry_scan": stats(hot[:, 0]),
+                        "output": stats(hot[:, 1]), "tokens_per_s": B * T / (float(np.median(hot[:, 2])) * 1e-3)},
         "prefill_op_roofline_frac": byts / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
-    log(f"[bench] prefill {ms_per_step * 1e3:.1f} us/step; output kernel {out_ms * 1e3:.1f} us "
-        f"({achieved:.0f} GB/s); carries {carry_ms * 1e3:.1f} us")
+    log(f"[bench] prefill cold {ms_per_step * 1e3:.1f} us/step (hot {np.median(hot[:, 2]) * 1e3:.1f}); "
+        f"output kernel {out_ms * 1e3:.1f} us ({achieved:.0f} GB/s); "
+        f"carries cold {np.median(cold[:, 0]) * 1e3:.1f} us")
 
     if not args.no_decode:
         dcfg = CONFIGS[DECODE_WORKLOAD]
@@ -211,33 +224,76 @@ def main() -> int:
             xs = decode_step_inputs(step=s, **dcfg)
             steps_in.append(tuple(torch.from_numpy(xs[n]).to(dev).to(torch.bfloat16) for n in ("q", "k", "v")))
         do = torch.empty((N, Hq, dd), dtype=torch.bfloat16, device=dev)
+
+        def dstep(s):
+            gla.liger_attn_decode_step(*steps_in[s], S, ring, dgate, dcfg["alpha"], o=do)
+
         dwarm = min(16, nsteps)
         for s in range(dwarm):
-            gla.liger_attn_decode_step(*steps_in[s], S, ring, dgate, dcfg["alpha"], o=do)
+            dstep(s)
         torch.cuda.synchronize()
         dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nsteps)]
         t0 = time.perf_counter()
         for s in range(nsteps):
             dev_ev[s][0].record()
-            gla.liger_attn_decode_step(*steps_in[s], S, ring, dgate, dcfg["alpha"], o=do)
+            dstep(s)
             dev_ev[s][1].record()
         torch.cuda.synchronize()
         dwall = time.perf_counter() - t0
-        k_ms = float(np.mean([a.elapsed_time(b) for a, b in dev_ev]))
+        k_all = np.array([a.elapsed_time(b) for a, b in dev_ev])
+        k_ms = float(np.mean(k_all))
+        # the same launches replayed from one captured graph (no host work per step)
+        glen = min(64, nsteps)
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for s in range(glen):
+                    dstep(s)
+        torch.cuda.current_stream().wait_stream(cap)
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, nsteps // glen)
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(reps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_us = g0.elapsed_time(g1) * 1e3 / (reps * glen)
+        # cold steps: the last-level cache is evicted before each one
+        ncold = min(32, nsteps)
+        cold_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ncold)]
+        for s in range(ncold):
+            scrub.fill_(float(s))
+            cold_ev[s][0].record()
+            dstep(s)
+            cold_ev[s][1].record()
+        torch.cuda.synchronize()
+        cold_us = float(np.median([a.elapsed_time(b) for a, b in cold_ev])) * 1e3
         dbytes = decode_algorithmic(dcfg)
         dach = dbytes / (k_ms * 1e-3) / 1e9
+        drec = counter_record("decode_step_kernel", DECODE_WORKLOAD)
+        dtraffic = drec.get("hbm_bytes_per_launch")
         result["decode"] = {
             "workload": DECODE_WORKLOAD, "steps": nsteps, "warmup": dwarm,
             "steps_per_s": nsteps / dwall, "us_per_step_wall": dwall * 1e6 / nsteps,
-            "kernel_us": k_ms * 1e3, "steps_per_s_kernel": 1e3 / k_ms,
-            "tokens_per_s_kernel": N * 1e3 / k_ms,
+            "kernel_us": k_ms * 1e3, "kernel_us_median": float(np.median(k_all)) * 1e3,
+            "kernel_us_min": float(np.min(k_all)) * 1e3,
+            "steps_per_s_kernel": 1e3 / k_ms, "tokens_per_s_kernel": N * 1e3 / k_ms,
+            "graph_us_per_step": graph_us, "graph_steps_per_s": 1e6 / graph_us,
+            "cold_kernel_us_median": cold_us,
             "roofline": {"bound": "hbm", "achieved": dach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": dach / PEAK_HBM_GBS,
-                         "traffic": measured_traffic("decode_step_kernel", DECODE_WORKLOAD),
+                         "frac": dach / PEAK_HBM_GBS, "traffic": dtraffic,
+                         "cold_frac": dbytes / (cold_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
                          "kernel": "decode_step_kernel", "algorithmic_bytes": dbytes,
-                         "note": "state + ring working set (48 MiB) fits the 256 MB last-level cache"},
+                         "tcc_ea_gbs_counters": (dtraffic / (k_ms * 1e-3) / 1e9) if dtraffic else None,
+                         "note": "state + ring working set (48 MiB) fits the 256 MB last-level cache; "
+                                 "cold_frac is measured after evicting it"},
         }
-        log(f"[bench] decode kernel {k_ms * 1e3:.1f} us/step ({dach:.0f} GB/s); wall {dwall * 1e6 / nsteps:.1f} us/step")
+        log(f"[bench] decode kernel {k_ms * 1e3:.1f} us/step ({dach:.0f} GB/s); graph {graph_us:.1f} us/step; "
+            f"cold {cold_us:.1f} us; wall {dwall * 1e6 / nsteps:.1f} us/step")
 
     if args.copy_probe_mib > 0:
         # an elementwise kernel that reads and writes exactly n bytes each
