@@ -79,9 +79,9 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
     const T* rk = ring_k + (static_cast<size_t>(n) * H_kv + h) * window * D;
     const T* rv = ring_v + (static_cast<size_t>(n) * H_kv + h) * window * D;
 
-    // ---- loads, smallest first (memory returns in issue order): the new
-    // token, then the state rows and this thread's ring key and value slices.
-    // None of them depends on pos.
+    // ---- loads (memory returns in issue order): the new token, the ring
+    // keys and values, then the state rows last, so that the whole window
+    // attention runs while the state is still arriving. None depends on pos.
     float kin = 0.f, vin = 0.f;
     if (tid < D) {
         kin = to_f32(kp[tid]);
@@ -93,10 +93,6 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
         const int idx = tid + i * kDecThreads;
         qin[i] = idx < NREP * D ? to_f32(qp[idx]) : 0.f;
     }
-    float4 sv[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i)
-        sv[i] = *reinterpret_cast<const float4*>(Sp + static_cast<size_t>(rg + i * RG) * D + cg * 4);
     const int ks = tid >> 2;    // ring slot of the logit pass
     const int kpart = tid & 3;  // quarter of the head dimension
     uint4 kr[KPT];
@@ -118,6 +114,10 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
             else vraw[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
+    float4 sv[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        sv[i] = *reinterpret_cast<const float4*>(Sp + static_cast<size_t>(rg + i * RG) * D + cg * 4);
 
     const int64_t p = pos[n];
     const int slot = static_cast<int>(p % window);
@@ -134,7 +134,8 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
     }
     __syncthreads();
 
-    // ---- softmax over d of k (row 0) and of each query head; the gate
+    // ---- softmax over d of k (row 0) and of each query head (stored times
+    // alpha, the GRM weight); the gate
     constexpr int EPL = D / 64;
     for (int row = wave; row <= NREP; row += kDecThreads / 64) {
         float x[EPL];
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
         for (int e = 0; e < EPL; ++e) {
             const int c = lane + 64 * e;
             if (row == 0) s_phik[c] = x[e] * inv;
-            else s_phiq[c][row - 1] = x[e] * inv;
+            else s_phiq[c][row - 1] = x[e] * (inv * alpha);
         }
         if (row == 0) {
             if (GATE == 0) {
@@ -178,9 +179,9 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
             }
         }
     }
-    __syncthreads();
 
-    // ---- window logits: q . k_s for this thread's slot and quarter
+    // ---- window logits: q . k_s for this thread's slot and quarter (the
+    // new token's key from LDS)
     {
         float dot[NRP];
 #pragma unroll
@@ -214,37 +215,8 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
             for (int j = 0; j < NREP; ++j) s_p[ks][j] = ks < nvalid ? dot[j] * scale : -INFINITY;
         }
     }
-
-    // ---- state read-modify-write and phi(q) S_t (state rows already loaded)
-    const float4 v4 = *reinterpret_cast<const float4*>(s_v + cg * 4);
-    float acc[NRP][4];
-#pragma unroll
-    for (int j = 0; j < NRP; ++j) acc[j][0] = acc[j][1] = acc[j][2] = acc[j][3] = 0.f;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = rg + i * RG;
-        const float g = s_g[r];
-        const float pk = s_phik[r];
-        float4 st = sv[i];
-        st.x = g * st.x + pk * v4.x;
-        st.y = g * st.y + pk * v4.y;
-        st.z = g * st.z + pk * v4.z;
-        st.w = g * st.w + pk * v4.w;
-        *reinterpret_cast<float4*>(Sp + static_cast<size_t>(r) * D + cg * 4) = st;
-#pragma unroll
-        for (int j4 = 0; j4 < NR4; ++j4) {
-            const float4 pq = *reinterpret_cast<const float4*>(&s_phiq[r][4 * j4]);
-            const float pqs[4] = {pq.x, pq.y, pq.z, pq.w};
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                acc[4 * j4 + jj][0] += pqs[jj] * st.x;
-                acc[4 * j4 + jj][1] += pqs[jj] * st.y;
-                acc[4 * j4 + jj][2] += pqs[jj] * st.z;
-                acc[4 * j4 + jj][3] += pqs[jj] * st.w;
-            }
-        }
-    }
     __syncthreads();
+    // window softmax per head, weights times (1 - alpha)
     for (int j = wave; j < NREP; j += kDecThreads / 64) {
         const float l = s_p[lane][j];
         const float m = dec_wave_max(l);
@@ -254,14 +226,10 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
     }
     __syncthreads();
 
-    // ---- mix: alpha * GRM + sum_s p_s v_s (the new token's value from LDS)
+    // ---- sum_s p_s v_s (the new token's value from LDS)
+    float acc[NRP][4];
 #pragma unroll
-    for (int j = 0; j < NREP; ++j) {
-        acc[j][0] *= alpha;
-        acc[j][1] *= alpha;
-        acc[j][2] *= alpha;
-        acc[j][3] *= alpha;
-    }
+    for (int j = 0; j < NRP; ++j) acc[j][0] = acc[j][1] = acc[j][2] = acc[j][3] = 0.f;
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
         const int s = rg + i * RG;
@@ -289,6 +257,34 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
             for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[4 * j4 + jj][e] += ps[jj] * vr[e];
+        }
+    }
+
+    // ---- state read-modify-write, row by row as the rows arrive, and
+    // alpha phi(q) S_t
+    const float4 v4 = *reinterpret_cast<const float4*>(s_v + cg * 4);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg + i * RG;
+        const float g = s_g[r];
+        const float pk = s_phik[r];
+        float4 st = sv[i];
+        st.x = g * st.x + pk * v4.x;
+        st.y = g * st.y + pk * v4.y;
+        st.z = g * st.z + pk * v4.z;
+        st.w = g * st.w + pk * v4.w;
+        *reinterpret_cast<float4*>(Sp + static_cast<size_t>(r) * D + cg * 4) = st;
+#pragma unroll
+        for (int j4 = 0; j4 < NR4; ++j4) {
+            const float4 pq = *reinterpret_cast<const float4*>(&s_phiq[r][4 * j4]);
+            const float pqs[4] = {pq.x, pq.y, pq.z, pq.w};
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                acc[4 * j4 + jj][0] += pqs[jj] * st.x;
+                acc[4 * j4 + jj][1] += pqs[jj] * st.y;
+                acc[4 * j4 + jj][2] += pqs[jj] * st.z;
+                acc[4 * j4 + jj][3] += pqs[jj] * st.w;
+            }
         }
     }
 #pragma unroll
