@@ -25,6 +25,8 @@
 //   P2 carry_scan_kernel    : S_in[s+1] = 2^(lg_s) (.) S_in[s] + L_s, in place
 //   P3 prefill_output_kernel: per segment, walks its chunks from S_in[s],
 //                             computes o, and (last segment) writes S_T
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -1118,24 +1120,25 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
 
     // ---- window scores over key tiles KT0 .. I0+1; query tile s uses
     // u = s .. s + 4. A key is valid when 0 <= i - j < window. With the full
-    // 64-key window only the diagonal tile (u = s + 4) and the window's first
-    // tile (u = s) are partial.
+    // 64-key window and a previous chunk (the common case, compiled on its
+    // own) only the diagonal tile (u = s + 4) and the window's first tile
+    // (u = s) are partial; otherwise tiles may be dead as a whole.
+    // Maxima are taken on the raw products; the 1/sqrt(d) scale is applied
+    // inside the exponent.
     float sc[2][NKT][4];
-    {
-        const float lscale = kLog2e * rsqrtf(static_cast<float>(D));
+    const float lscale = kLog2e * rsqrtf(static_cast<float>(D));
+    auto window_scores = [&](auto fast_c) {
+        constexpr bool FAST = decltype(fast_c)::value;
         float lmax[2] = {-INFINITY, -INFINITY};
-        const unsigned w = static_cast<unsigned>(x.window);
+        const unsigned w = FAST ? 64u : static_cast<unsigned>(x.window);
 #pragma unroll
         for (int u = 0; u < NKT; ++u) {
             const int kt = KT0 + u;
             bool live[2];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                live[s] = u >= s && u <= s + 4 && (kt >= 0 || x.have_prev) &&
-                          (16 * kt + 15 > 16 * (I0 + s) - x.window);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sc[s][u][r] = -INFINITY;
-            }
+            for (int s = 0; s < 2; ++s)
+                live[s] = u >= s && u <= s + 4 &&
+                          (FAST || ((kt >= 0 || x.have_prev) && (16 * kt + 15 > 16 * (I0 + s) - x.window)));
             if (live[0] || live[1]) {
                 const T* krow = kt >= 0 ? Kcur + (16 * kt + col) * L::DP : Kprv + (16 * kt + 64 + col) * L::DP;
                 f32x4_t d4[2] = {zero4(), zero4()};
@@ -1148,39 +1151,53 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
                 }
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    if (!live[s]) continue;
+                    if (u < s || u > s + 4) continue;
+                    if (!live[s]) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) sc[s][u][r] = -INFINITY;
+                        continue;
+                    }
                     const int dt = 16 * (I0 + s - kt);  // 16 (I - kt), compile-time
-                    const bool partial = (u == s) || (u == s + 4) || !full_window;
+                    const bool partial = (u == s) || (u == s + 4) || !(FAST || full_window);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        float v = d4[s][r] * lscale;
+                        float v = d4[s][r];
                         if (partial) v = static_cast<unsigned>(dt + dl - r) < w ? v : -INFINITY;
                         sc[s][u][r] = v;
                         lmax[s] = fmaxf(lmax[s], v);
                     }
                 }
+            } else if (!FAST) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    if (u >= s && u <= s + 4) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) sc[s][u][r] = -INFINITY;
+                    }
             }
             __builtin_amdgcn_sched_barrier(0);  // bound the number of key fragments in flight
         }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const float m = group4_max(lmax[s]);
+            const float m = group4_max(lmax[s]) * lscale;  // the diagonal key is always valid
             float sum = 0.f;
 #pragma unroll
-            for (int u = 0; u < NKT; ++u)
+            for (int u = s; u <= s + 4; ++u)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float e = fast_exp2(sc[s][u][r] - m);  // exp2(-inf) = 0 for masked keys
+                    const float e = fast_exp2(fmaf(sc[s][u][r], lscale, -m));  // exp2(-inf) = 0 for masked keys
                     sc[s][u][r] = e;
                     sum += e;
                 }
             const float ps = (1.0f - x.alpha) * fast_rcp(group4_sum(sum));
 #pragma unroll
-            for (int u = 0; u < NKT; ++u)
+            for (int u = s; u <= s + 4; ++u)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sc[s][u][r] *= ps;
         }
-    }
+    };
+    if (x.have_prev && full_window) window_scores(std::true_type{});
+    else window_scores(std::false_type{});
 
     // recurrence operand (built after the window scores so qr can retire)
 #pragma unroll
