@@ -994,15 +994,16 @@ struct ItemCtx {
     int cur;
 };
 
-// One wave computes the outputs of 32 query rows (query tiles I0 = 2 IB and
-// I0 + 1) of one query head over all of d_v. Every LDS operand fragment it
+// One wave computes the outputs of 32 query rows (query tiles QA and QB of the
+// chunk) of one query head over all of d_v. The pairs (0, 3) and (1, 2) have
+// the same amount of intra-chunk work. Every LDS operand fragment it
 // reads (key tiles, K~, S'^T, V^T) feeds both query tiles.
 // Scores are kept per (query tile s, key tile kt) in the accumulator layout:
-// lane (col, g) holds keys 16 kt + 4 g + r for query 16 (I0 + s) + col.
+// lane (col, g) holds keys 16 kt + 4 g + r for query 16 I_s + col.
 // The intra-chunk scores (keys of this chunk, j <= i) and the window weights
 // (keys i-w < j <= i) multiply the same V rows, so they are added into one
 // operand per key tile before the product with V.
-// Raw query fragments of a 32-row block: lane (col, g) holds row 16 (I0 + s) + col,
+// Raw query fragments of two query tiles: lane (col, g) holds row 16 I_s + col,
 // elements KSTEP k + KPL g .. + KPL - 1. Rows past the end are zero.
 template <typename T, int D>
 struct QFrags {
@@ -1010,13 +1011,13 @@ struct QFrags {
 };
 
 template <typename T, int D>
-__device__ __forceinline__ void load_q_block(QFrags<T, D>& qf, const T* q, int64_t row0, int H_q, int hq, int i0,
-                                             int nvalid, int lane) {
+__device__ __forceinline__ void load_q_block(QFrags<T, D>& qf, const T* q, int64_t row0, int H_q, int hq, int qa,
+                                             int qb, int nvalid, int lane) {
     typedef Mfma<T> M;
     const int col = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-        const int i = i0 + 16 * s + col;
+        const int i = 16 * (s == 0 ? qa : qb) + col;
         const bool ok = i < nvalid;
         const T* qrow = q + ((row0 + (ok ? i : 0)) * H_q + hq) * D;
 #pragma unroll
@@ -1057,7 +1058,7 @@ __device__ __forceinline__ typename Mfma<T>::frag resident_frag(const Smem<T, D,
     return M::pack(x);
 }
 
-template <typename T, int D, int GATE, int IB>
+template <typename T, int D, int GATE, int QA, int QB>
 __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, const ItemCtx<T, D, GATE>& x,
                                              int lane, const QFrags<T, D>& qin) {
     typedef Layout<T, D, GATE, true> L;
@@ -1067,9 +1068,14 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
     constexpr int KPL = M::KPL;
     constexpr int NT = D / 16;
     constexpr bool BF = sizeof(T) == 2;
-    constexpr int I0 = 2 * IB;          // first query tile of the block
-    constexpr int KT0 = I0 - 4;         // first key tile (relative to the chunk start)
-    constexpr int NKT = 6;              // key tiles KT0 .. I0 + 1
+    constexpr int QTS[2] = {QA, QB};    // query tiles of s = 0, 1 (relative to the chunk start)
+    constexpr int KTMIN = (QA < QB ? QA : QB) - 4;  // key tiles KTMIN .. KTMAX
+    constexpr int KTMAX = QA > QB ? QA : QB;
+    constexpr int NKT = KTMAX - KTMIN + 1;
+    constexpr int GMIN = (KTMIN - (KTMIN & 1)) / 2;  // aligned 32-key groups: key tiles 2G, 2G + 1
+    constexpr int NG = KTMAX / 2 - GMIN + 1;
+    // key tile kt is in query tile s's window range
+    auto inr = [](int s, int kt) { return kt >= QTS[s] - 4 && kt <= QTS[s]; };
     const int col = lane & 15, g = lane >> 4;
     const int dl = col - 4 * g;         // i - j = 16 (I - kt) + dl - r inside a tile pair
     const T* Kcur = sm.K + x.cur * 64 * L::DP;
@@ -1085,7 +1091,7 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
     const T* qrow[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-        i_loc[s] = 16 * (I0 + s) + col;
+        i_loc[s] = 16 * QTS[s] + col;
         row_ok[s] = i_loc[s] < x.nvalid;
         qrow[s] = x.q + ((x.row0 + (row_ok[s] ? i_loc[s] : 0)) * x.H_q + x.hq) * D;
     }
@@ -1118,11 +1124,11 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
         qmax[s] = group4_max(m);
     }
 
-    // ---- window scores over key tiles KT0 .. I0+1; query tile s uses
-    // u = s .. s + 4. A key is valid when 0 <= i - j < window. With the full
+    // ---- window scores over key tiles kt = KTMIN + u; query tile I uses
+    // kt = I - 4 .. I. A key is valid when 0 <= i - j < window. With the full
     // 64-key window and a previous chunk (the common case, compiled on its
-    // own) only the diagonal tile (u = s + 4) and the window's first tile
-    // (u = s) are partial; otherwise tiles may be dead as a whole.
+    // own) only the diagonal tile (kt = I) and the window's first tile
+    // (kt = I - 4) are partial; otherwise tiles may be dead as a whole.
     // Maxima are taken on the raw products; the 1/sqrt(d) scale is applied
     // inside the exponent.
     float sc[2][NKT][4];
@@ -1133,12 +1139,12 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
         const unsigned w = FAST ? 64u : static_cast<unsigned>(x.window);
 #pragma unroll
         for (int u = 0; u < NKT; ++u) {
-            const int kt = KT0 + u;
+            const int kt = KTMIN + u;
             bool live[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                live[s] = u >= s && u <= s + 4 &&
-                          (FAST || ((kt >= 0 || x.have_prev) && (16 * kt + 15 > 16 * (I0 + s) - x.window)));
+                live[s] = inr(s, kt) &&
+                          (FAST || ((kt >= 0 || x.have_prev) && (16 * kt + 15 > 16 * QTS[s] - x.window)));
             if (live[0] || live[1]) {
                 const T* krow = kt >= 0 ? Kcur + (16 * kt + col) * L::DP : Kprv + (16 * kt + 64 + col) * L::DP;
                 f32x4_t d4[2] = {zero4(), zero4()};
@@ -1151,14 +1157,14 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
                 }
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    if (u < s || u > s + 4) continue;
+                    if (!inr(s, kt)) continue;
                     if (!live[s]) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) sc[s][u][r] = -INFINITY;
                         continue;
                     }
-                    const int dt = 16 * (I0 + s - kt);  // 16 (I - kt), compile-time
-                    const bool partial = (u == s) || (u == s + 4) || !(FAST || full_window);
+                    const int dt = 16 * (QTS[s] - kt);  // 16 (I - kt), compile-time
+                    const bool partial = (kt == QTS[s] - 4) || (kt == QTS[s]) || !(FAST || full_window);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         float v = d4[s][r];
@@ -1170,7 +1176,7 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
             } else if (!FAST) {
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
-                    if (u >= s && u <= s + 4) {
+                    if (inr(s, kt)) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) sc[s][u][r] = -INFINITY;
                     }
@@ -1182,7 +1188,7 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
             const float m = group4_max(lmax[s]) * lscale;  // the diagonal key is always valid
             float sum = 0.f;
 #pragma unroll
-            for (int u = s; u <= s + 4; ++u)
+            for (int u = QTS[s] - 4 - KTMIN; u <= QTS[s] - KTMIN; ++u)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float e = fast_exp2(fmaf(sc[s][u][r], lscale, -m));  // exp2(-inf) = 0 for masked keys
@@ -1191,7 +1197,7 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
                 }
             const float ps = (1.0f - x.alpha) * fast_rcp(group4_sum(sum));
 #pragma unroll
-            for (int u = s; u <= s + 4; ++u)
+            for (int u = QTS[s] - 4 - KTMIN; u <= QTS[s] - KTMIN; ++u)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sc[s][u][r] *= ps;
         }
@@ -1237,14 +1243,14 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
         qinv[s] = (GATE ? 1.0f : x.alpha) * fast_rcp(group4_sum(sum));
     }
 
-    // ---- intra-chunk scores on key tiles J = 0 .. I0+s, added into the same
+    // ---- intra-chunk scores on key tiles J = 0 .. I (query tile I), added into the same
     // per-key-tile operand. Tiles below the diagonal are whole; the diagonal
     // tile keeps j <= i. Scalar gate: the decay 2^(b_i - b_j) is split into
     // 2^(b_i - m) (here) and 2^(m - b_j) (in the key operand), or applied per
     // pair when the chunk's decay range is too wide to split.
     float bq[2] = {0.f, 0.f};
     float qsc[2];
-    float4 bk[I0 + 2];
+    float4 bk[KTMAX + 1];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
         if (GATE == 0) bq[s] = sm.b2s[i_loc[s]];
@@ -1252,21 +1258,21 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
     }
     if (GATE == 0 && exact) {
 #pragma unroll
-        for (int J = 0; J <= I0 + 1; ++J) bk[J] = *reinterpret_cast<const float4*>(sm.b2s + 16 * J + 4 * g);
+        for (int J = 0; J <= KTMAX; ++J) bk[J] = *reinterpret_cast<const float4*>(sm.b2s + 16 * J + 4 * g);
     }
 #pragma unroll
-    for (int J = 0; J <= I0 + 1; ++J) {
+    for (int J = 0; J <= KTMAX; ++J) {
         f32x4_t d4[2] = {zero4(), zero4()};
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
             const Frag a = M::load(sm.Kb + (16 * J + col) * L::DP + M::KSTEP * k + KPL * g);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                if (J <= I0 + s) d4[s] = M::mma(a, qt[s][k], d4[s]);
+                if (J <= QTS[s]) d4[s] = M::mma(a, qt[s][k], d4[s]);
         }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            if (J > I0 + s) continue;
+            if (J > QTS[s]) continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r) d4[s][r] *= qsc[s];
             for (int nb = 0; nb < nbad; ++nb) {
@@ -1289,11 +1295,11 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
                     d4[s][r] *= fast_exp2(fminf(bq[s] - bj, 0.0f));
                 }
             }
-            const int u = J - KT0;
+            const int u = J - KTMIN;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float val = d4[s][r];
-                if (J == I0 + s) val = dl >= r ? val : 0.0f;  // diagonal tile: j <= i
+                if (J == QTS[s]) val = dl >= r ? val : 0.0f;  // diagonal tile: j <= i
                 sc[s][u][r] += val;
             }
         }
@@ -1301,19 +1307,24 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
     }
 
     // ---- bf16: pack the combined scores of the aligned key-tile pairs
-    // (u = 2G, 2G + 1); tiles outside query tile s's range u in [s, s+4] are 0.
-    Frag pf[2][3];
+    // (kt = 2G, 2G + 1); tiles outside query tile s's range are 0.
+    auto scv = [&](int s, int kt, int r) -> float {
+        const int u = kt - KTMIN;
+        return inr(s, kt) ? sc[s][u < 0 ? 0 : u][r] : 0.0f;
+    };
+    Frag pf[2][NG];
     if constexpr (BF) {
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int G = 0; G < 3; ++G) {
+            for (int G = 0; G < NG; ++G) {
+                const int kt0 = 2 * (GMIN + G);
+                if (!inr(s, kt0) && !inr(s, kt0 + 1)) continue;
                 float v8[8];
-                const int u0 = 2 * G, u1 = 2 * G + 1;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    v8[r] = (u0 >= s && u0 <= s + 4) ? sc[s][u0][r] : 0.0f;
-                    v8[4 + r] = (u1 >= s && u1 <= s + 4) ? sc[s][u1][r] : 0.0f;
+                    v8[r] = scv(s, kt0, r);
+                    v8[4 + r] = scv(s, kt0 + 1, r);
                 }
                 pf[s][G] = M::pack(v8);
             }
@@ -1352,28 +1363,33 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
             }
         }
         if constexpr (BF) {
-            // key tiles (KT0 + 2G, KT0 + 2G + 1) form one aligned 32-key group
+            // key tiles (2G, 2G + 1) form one aligned 32-key group
 #pragma unroll
-            for (int G = 0; G < 3; ++G) {
-                const int kt = KT0 + 2 * G;
+            for (int G = 0; G < NG; ++G) {
+                const int kt = 2 * (GMIN + G);
+                bool gl[2];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) gl[s] = inr(s, kt) || inr(s, kt + 1);
+                if (!gl[0] && !gl[1]) continue;
                 const Frag a = kt >= 0 ? load_key_frag(Vcur, L::VP, 16 * kt, 16 * t, lane)
                                        : load_key_frag(Vprv, L::VP, 16 * (kt + 4), 16 * t, lane);
-                acc[0] = M::mma(a, pf[0][G], acc[0]);
-                acc[1] = M::mma(a, pf[1][G], acc[1]);
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    if (gl[s]) acc[s] = M::mma(a, pf[s][G], acc[s]);
             }
         } else {
             const T* vrow_c = Vcur + (16 * t + col) * L::JP;
             const T* vrow_p = Vprv + (16 * t + col) * L::JP;
 #pragma unroll
             for (int u = 0; u < NKT; ++u) {
-                const int kt = KT0 + u;
+                const int kt = KTMIN + u;
                 const int kk = kt >= 0 ? kt : kt + 4;
                 const T* base = kt >= 0 ? vrow_c : vrow_p;
                 const float4 pv = *reinterpret_cast<const float4*>(base + 32 * (kk >> 1) + 8 * g + 4 * (kk & 1));
                 const float pr[4] = {pv.x, pv.y, pv.z, pv.w};
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
-                    if (u >= s && u <= s + 4) {
+                    if (inr(s, kt)) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
                             acc[s] = M::mma(__builtin_bit_cast(Frag, pr[r]), __builtin_bit_cast(Frag, sc[s][u][r]), acc[s]);
@@ -1448,8 +1464,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
             if (wave < n_items) {
                 int lane = threadIdx.x & 63;
                 asm volatile("" : "+v"(lane));
+                const int pair = wave / p.n_rep;
                 load_q_block<T, D>(qpre, static_cast<const T*>(p.q), b * p.T + t0, H_q,
-                                   h * p.n_rep + (wave % p.n_rep), 32 * (wave / p.n_rep), nvalid, lane);
+                                   h * p.n_rep + (wave % p.n_rep), pair == 0 ? 0 : 1, pair == 0 ? 3 : 2, nvalid, lane);
             }
             __builtin_amdgcn_sched_barrier(0);
             if (threadIdx.x == 0) *sm.nbad = 0;
@@ -1479,10 +1496,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
                 x.hq = h * p.n_rep + (it % p.n_rep);
                 int lane = threadIdx.x & 63;
                 asm volatile("" : "+v"(lane));  // keep lane-derived addresses inside the loop
+                const int pair = it / p.n_rep;
                 if (it != wave)
-                    load_q_block<T, D>(qpre, x.q, x.row0, H_q, x.hq, 32 * (it / p.n_rep), nvalid, lane);
-                if (it / p.n_rep == 0) output_block<T, D, GATE, 0>(sm, x, lane, qpre);
-                else output_block<T, D, GATE, 1>(sm, x, lane, qpre);
+                    load_q_block<T, D>(qpre, x.q, x.row0, H_q, x.hq, pair == 0 ? 0 : 1, pair == 0 ? 3 : 2, nvalid, lane);
+                if (pair == 0) output_block<T, D, GATE, 0, 3>(sm, x, lane, qpre);
+                else output_block<T, D, GATE, 1, 2>(sm, x, lane, qpre);
             }
             __syncthreads();
             if (c + 1 < c_end) load_chunk_commit(sm, cur ^ 1, cr);  // the previous chunk's slot is free now
@@ -1509,8 +1527,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
         if (wave < n_items) {
             int lane = threadIdx.x & 63;
             asm volatile("" : "+v"(lane));
+            const int pair = wave / p.n_rep;
             load_q_block<T, D>(qpre, static_cast<const T*>(p.q), b * p.T + t0, H_q, h * p.n_rep + (wave % p.n_rep),
-                               32 * (wave / p.n_rep), nvalid, lane);
+                               pair == 0 ? 0 : 1, pair == 0 ? 3 : 2, nvalid, lane);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (threadIdx.x == 0) *sm.nbad = 0;
@@ -1546,10 +1565,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
             x.hq = h * p.n_rep + (it % p.n_rep);
             int lane = threadIdx.x & 63;
             asm volatile("" : "+v"(lane));  // keep lane-derived addresses inside the loop
+            const int pair = it / p.n_rep;
             if (it != wave)
-                load_q_block<T, D>(qpre, x.q, x.row0, H_q, x.hq, 32 * (it / p.n_rep), nvalid, lane);
-            if (it / p.n_rep == 0) output_block<T, D, GATE, 0>(sm, x, lane, qpre);
-            else output_block<T, D, GATE, 1>(sm, x, lane, qpre);
+                load_q_block<T, D>(qpre, x.q, x.row0, H_q, x.hq, pair == 0 ? 0 : 1, pair == 0 ? 3 : 2, nvalid, lane);
+            if (pair == 0) output_block<T, D, GATE, 0, 3>(sm, x, lane, qpre);
+            else output_block<T, D, GATE, 1, 2>(sm, x, lane, qpre);
         }
         __syncthreads();
         if (c + 1 < c_end) {
