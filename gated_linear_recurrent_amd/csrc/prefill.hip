@@ -420,38 +420,51 @@ struct StateTiles {
     __device__ static __forceinline__ int ct(int wave, int u) { return (wave * TPW + u) % NTT; }
 };
 
-// S <- diag(dec) S + Kst^T V over the current chunk (Kst^T = Kb as [D][JP]).
+// S <- diag(dec) S + sfac Kst^T V over the current chunk. The key operand is
+// Kb as [D][JP] (transposed, keys at key_pos) or, with NAT, Kb as the
+// token-major [64][DP] intra operand read with transposing loads.
 // With RES the state is read from and written back to the resident LDS copy
 // (acc returns the new state); otherwise it lives in acc.
-template <typename T, int D, int GATE, bool FULL, bool RES = false>
+template <typename T, int D, int GATE, bool FULL, bool RES = false, bool NAT = false>
 __device__ __forceinline__ void state_advance(const Smem<T, D, GATE, FULL>& sm, int slot,
-                                              f32x4_t (&acc)[StateTiles<D>::TPW]) {
+                                              f32x4_t (&acc)[StateTiles<D>::TPW], float sfac = 1.0f) {
     typedef Layout<T, D, GATE, FULL> L;
     typedef Mfma<T> M;
     typedef StateTiles<D> ST;
+    static_assert(ST::NTT % ST::TPW == 0, "a wave's state tiles share one row tile");
     const int lane = ltid() & 63, wave = ltid() >> 6;
     const int col = lane & 15, g = lane >> 4;
     const T* Vts = sm.Vt + slot * L::V_ELEMS;
+    const int rt = ST::rt(wave, 0);
+    f32x4_t d[ST::TPW];
 #pragma unroll
-    for (int u = 0; u < ST::TPW; ++u) {
-        const int rt = ST::rt(wave, u), t = ST::ct(wave, u);
-        f32x4_t d = zero4();
+    for (int u = 0; u < ST::TPW; ++u) d[u] = zero4();
 #pragma unroll
-        for (int ks = 0; ks < 64 / M::KSTEP; ++ks) {
-            const typename M::frag a = M::load(sm.Kb + (16 * rt + col) * L::JP + M::KSTEP * ks + M::KPL * g);
+    for (int ks = 0; ks < 64 / M::KSTEP; ++ks) {
+        typename M::frag a;
+        if constexpr (NAT && sizeof(T) == 2) a = load_key_frag(sm.Kb, L::DP, M::KSTEP * ks, 16 * rt, lane);
+        else if constexpr (NAT) a = sm.Kb[(M::KSTEP * ks + g) * L::DP + 16 * rt + col];
+        else a = M::load(sm.Kb + (16 * rt + col) * L::JP + M::KSTEP * ks + M::KPL * g);
+#pragma unroll
+        for (int u = 0; u < ST::TPW; ++u) {
+            const int t = ST::ct(wave, u);
             typename M::frag b;
             if constexpr (L::VNAT) b = load_key_frag(Vts, L::VP, M::KSTEP * ks, 16 * t, lane);
             else b = M::load(Vts + (16 * t + col) * L::JP + M::KSTEP * ks + M::KPL * g);
-            d = M::mma(a, b, d);
+            d[u] = M::mma(a, b, d[u]);
         }
-        const int r0 = 16 * rt + 4 * g;
+    }
+    const int r0 = 16 * rt + 4 * g;
+#pragma unroll
+    for (int u = 0; u < ST::TPW; ++u) {
+        const int t = ST::ct(wave, u);
         float* res = sm.S32 + (16 * t + col) * L::SP + r0;
         if constexpr (RES) {
             const float4 v = *reinterpret_cast<const float4*>(res);
             acc[u] = f32x4_t{v.x, v.y, v.z, v.w};
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[u][r] = sm.dec[r0 + r] * acc[u][r] + d[r];
+        for (int r = 0; r < 4; ++r) acc[u][r] = sm.dec[r0 + r] * acc[u][r] + (NAT ? sfac * d[u][r] : d[u][r]);
         if constexpr (RES) *reinterpret_cast<float4*>(res) = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
     }
 }
@@ -1504,9 +1517,21 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
             }
             __syncthreads();
             if (c + 1 < c_end) load_chunk_commit(sm, cur ^ 1, cr);  // the previous chunk's slot is free now
-            state_key_operand<T, D, GATE, true, TPT>(sm, cur, nvalid, sm.blast, b2);
+            // Scalar gate (bf16): the state key operand phik_j 2^(b_last - b_j)
+            // is the intra operand phik_j 2^(m - b_j) times the chunk constant
+            // 2^(b_last - m), so the intra operand (token-major, read with
+            // transposing loads in the same key order as V) is reused unless
+            // this chunk takes the exact per-pair path.
+            constexpr bool CAN_REUSE = GATE == 0 && L::VNAT;
+            const bool reuse = CAN_REUSE && *sm.exact == 0;
+            if (!reuse) state_key_operand<T, D, GATE, true, TPT>(sm, cur, nvalid, sm.blast, b2);
             __syncthreads();
-            state_advance<T, D, GATE, true, true>(sm, cur, acc);
+            if constexpr (CAN_REUSE) {
+                if (reuse) state_advance<T, D, GATE, true, true, true>(sm, cur, acc, fast_exp2(sm.blast[0] - sm.mref[0]));
+                else state_advance<T, D, GATE, true, true>(sm, cur, acc);
+            } else {
+                state_advance<T, D, GATE, true, true>(sm, cur, acc);
+            }
             if (c + 1 == c_end && last_seg) store_state<D>(p.S_T + (size_t(b) * p.H_kv + h) * D * D, acc);
             // the next chunk's first barrier orders these LDS reads before its gate scan
         }
