@@ -745,7 +745,9 @@ __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams 
     typedef SegLayout<T, D> SL;
     typedef Mfma<T> M;
     typedef StateTiles<D> ST;
-    static_assert(ST::NTT % ST::TPW == 0, "a wave's state tiles share one row tile");
+    constexpr int RTW = ST::NTT >= 8 ? 2 : 1;  // state row tiles per wave
+    constexpr int CTW = ST::TPW / RTW;          // state column tiles per wave
+    static_assert(RTW * CTW == ST::TPW && (ST::NTT / RTW) * (ST::NTT / CTW) == kPWaves, "state tiling");
     __shared__ __align__(16) char smem[SL::TOTAL];
     T* Ks = reinterpret_cast<T*>(smem + SL::K_OFF);
     T* Vs = reinterpret_cast<T*>(smem + SL::V_OFF);
@@ -805,45 +807,51 @@ __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams 
             issue(blk0 + SL::TB, rest < SL::TB ? rest : SL::TB);
         }
 
-        // key row statistics, eight lanes per row; rows past nb get 1/sum = 0
-        {
-            constexpr int NLD = D / (8 * SL::VPL);
+        if constexpr (GATE == 0) {
+            // Piece mapping of the loads: PPR consecutive lanes share a key
+            // row. Row statistics reduce over those lanes; the exponentials
+            // stay in registers until the gate suffix sums are known.
+            static_assert(SL::PPR == 8 || SL::PPR == 16, "a key row spans 8 or 16 lanes");
+            auto red_max = [](float v) {
+                v = group8_max(v);
+                if (SL::PPR == 16) v = fmaxf(v, dpp<kDppMirror>(v));
+                return v;
+            };
+            auto red_sum = [](float v) {
+                v = group8_sum(v);
+                if (SL::PPR == 16) v += dpp<kDppMirror>(v);
+                return v;
+            };
             const int tid = ltid();
-            const int sub = tid & 7;
-            for (int r0 = 0; r0 < SL::TB; r0 += kPThreads / 8) {
-                const int j = r0 + (tid >> 3);
-                const T* row = Ks + j * SL::P + sub * SL::VPL;
-                float x[NLD * SL::VPL];
+            float ex[SL::NPT][SL::VPL];
+            float kiv[SL::NPT];
 #pragma unroll
-                for (int q = 0; q < NLD; ++q) {
-                    const uint4 u = *reinterpret_cast<const uint4*>(row + q * 8 * SL::VPL);
-                    const T* e = reinterpret_cast<const T*>(&u);
-#pragma unroll
-                    for (int i = 0; i < SL::VPL; ++i) x[q * SL::VPL + i] = to_f32(e[i]);
-                }
+            for (int n = 0; n < SL::NPT; ++n) {
+                const int idx = tid + n * kPThreads;
+                const int j = idx / SL::PPR;
+                const uint4 u = *reinterpret_cast<const uint4*>(Ks + j * SL::P + (idx % SL::PPR) * SL::VPL);
+                const T* e = reinterpret_cast<const T*>(&u);
                 float mx = -INFINITY, sraw = 0.f;
 #pragma unroll
-                for (int i = 0; i < NLD * SL::VPL; ++i) {
-                    mx = fmaxf(mx, x[i]);
-                    sraw += x[i];
+                for (int i = 0; i < SL::VPL; ++i) {
+                    ex[n][i] = to_f32(e[i]);
+                    mx = fmaxf(mx, ex[n][i]);
+                    sraw += ex[n][i];
                 }
-                mx = group8_max(mx);
+                mx = red_max(mx) * kLog2e;
                 float se = 0.f;
 #pragma unroll
-                for (int i = 0; i < NLD * SL::VPL; ++i) se += fast_exp2((x[i] - mx) * kLog2e);
-                se = group8_sum(se);
-                if (GATE == 0) sraw = group8_sum(sraw);
-                if (sub == 0) {
-                    const bool ok = j < nb;
-                    kmax[j] = mx;
-                    kinv[j] = ok ? fast_rcp(se) : 0.0f;
-                    if (GATE == 0) ell[j] = ok ? log2_sigmoid(sraw * (1.0f / D)) : 0.0f;
+                for (int i = 0; i < SL::VPL; ++i) {
+                    ex[n][i] = fast_exp2(fmaf(ex[n][i], kLog2e, -mx));
+                    se += ex[n][i];
                 }
+                se = red_sum(se);
+                sraw = red_sum(sraw);
+                const bool ok = j < nb;
+                kiv[n] = ok ? fast_rcp(se) : 0.0f;
+                if (idx % SL::PPR == 0) ell[j] = ok ? log2_sigmoid(sraw * (1.0f / D)) : 0.0f;
             }
-        }
-        __syncthreads();
-
-        if (GATE == 0) {
+            __syncthreads();
             // suffix sums over the block (one wave, TPL consecutive tokens per lane)
             constexpr int TPL = SL::TB / 64;
             if (ltid() < 64) {
@@ -873,18 +881,15 @@ __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams 
             }
             __syncthreads();
             // key operand in place: phik_j 2^(sum of the gates after j)
-            const int tid = ltid();
 #pragma unroll
             for (int n = 0; n < SL::NPT; ++n) {
                 const int idx = tid + n * kPThreads;
                 const int j = idx / SL::PPR;
                 T* e = Ks + j * SL::P + (idx % SL::PPR) * SL::VPL;
-                const uint4 u = *reinterpret_cast<const uint4*>(e);
-                const T* x = reinterpret_cast<const T*>(&u);
-                const float m = kmax[j], sc = kinv[j], off = ell[j];
+                const float f = kiv[n] * fast_exp2(ell[j]);
                 float y[SL::VPL];
 #pragma unroll
-                for (int i = 0; i < SL::VPL; ++i) y[i] = sc * fast_exp2((to_f32(x[i]) - m) * kLog2e + off);
+                for (int i = 0; i < SL::VPL; ++i) y[i] = f * ex[n][i];
                 if constexpr (sizeof(T) == 2) {
                     *reinterpret_cast<uint4*>(e) = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
                                                               pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
@@ -892,7 +897,39 @@ __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams 
                     *reinterpret_cast<float4*>(e) = make_float4(y[0], y[1], y[2], y[3]);
                 }
             }
+            __syncthreads();
         } else {
+            // key row statistics, eight lanes per row; rows past nb get 1/sum = 0
+            {
+                constexpr int NLD = D / (8 * SL::VPL);
+                const int tid = ltid();
+                const int sub = tid & 7;
+                for (int r0 = 0; r0 < SL::TB; r0 += kPThreads / 8) {
+                    const int j = r0 + (tid >> 3);
+                    const T* row = Ks + j * SL::P + sub * SL::VPL;
+                    float x[NLD * SL::VPL];
+#pragma unroll
+                    for (int q = 0; q < NLD; ++q) {
+                        const uint4 u = *reinterpret_cast<const uint4*>(row + q * 8 * SL::VPL);
+                        const T* e = reinterpret_cast<const T*>(&u);
+#pragma unroll
+                        for (int i = 0; i < SL::VPL; ++i) x[q * SL::VPL + i] = to_f32(e[i]);
+                    }
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int i = 0; i < NLD * SL::VPL; ++i) mx = fmaxf(mx, x[i]);
+                    mx = group8_max(mx);
+                    float se = 0.f;
+#pragma unroll
+                    for (int i = 0; i < NLD * SL::VPL; ++i) se += fast_exp2((x[i] - mx) * kLog2e);
+                    se = group8_sum(se);
+                    if (sub == 0) {
+                        kmax[j] = mx;
+                        kinv[j] = j < nb ? fast_rcp(se) : 0.0f;
+                    }
+                }
+            }
+            __syncthreads();
             // thread (c, range): channel c, tokens range*TPP .. +TPP-1; x_j[c] is
             // the mean of k_j over the in-range channels c-1 .. c+2
             const int c = ltid() % D;
@@ -922,31 +959,39 @@ __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams 
                 run += l[jj];
             }
             if (rg == 0) tot[c] = run;
+            __syncthreads();
         }
-        __syncthreads();
 
-        // running state: acc <- diag(2^tot) acc + Kop^T V over the block
+        // running state: acc <- diag(2^tot) acc + Kop^T V over the block;
+        // wave w owns row tiles rt0 .. rt0+RTW-1 and column tiles ct0 .. ct0+CTW-1
         {
             const int lane = ltid() & 63, wave = ltid() >> 6;
             const int col = lane & 15, g = lane >> 4;
-            const int rt = ST::rt(wave, 0);
+            const int rt0 = (wave % (ST::NTT / RTW)) * RTW;
+            const int ct0 = (wave / (ST::NTT / RTW)) * CTW;
 #pragma unroll
-            for (int u = 0; u < ST::TPW; ++u) {
-                const int r0 = 16 * rt + 4 * g;
+            for (int a = 0; a < RTW; ++a)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[u][r] *= fast_exp2(tot[r0 + r]);
-            }
+                for (int r = 0; r < 4; ++r) {
+                    const float f = fast_exp2(tot[16 * (rt0 + a) + 4 * g + r]);
+#pragma unroll
+                    for (int tt = 0; tt < CTW; ++tt) acc[a * CTW + tt][r] *= f;
+                }
             for (int ks = 0; ks < nb / M::KSTEP; ++ks) {
-                typename M::frag a;
-                if constexpr (sizeof(T) == 2) a = load_key_frag(Ks, SL::P, M::KSTEP * ks, 16 * rt, lane);
-                else a = Ks[(M::KSTEP * ks + g) * SL::P + 16 * rt + col];
+                typename M::frag af[RTW];
 #pragma unroll
-                for (int u = 0; u < ST::TPW; ++u) {
-                    const int t = ST::ct(wave, u);
+                for (int a = 0; a < RTW; ++a) {
+                    if constexpr (sizeof(T) == 2) af[a] = load_key_frag(Ks, SL::P, M::KSTEP * ks, 16 * (rt0 + a), lane);
+                    else af[a] = Ks[(M::KSTEP * ks + g) * SL::P + 16 * (rt0 + a) + col];
+                }
+#pragma unroll
+                for (int tt = 0; tt < CTW; ++tt) {
+                    const int t = ct0 + tt;
                     typename M::frag bv;
                     if constexpr (sizeof(T) == 2) bv = load_key_frag(Vs, SL::P, M::KSTEP * ks, 16 * t, lane);
                     else bv = Vs[(M::KSTEP * ks + g) * SL::P + 16 * t + col];
-                    acc[u] = M::mma(a, bv, acc[u]);
+#pragma unroll
+                    for (int a = 0; a < RTW; ++a) acc[a * CTW + tt] = M::mma(af[a], bv, acc[a * CTW + tt]);
                 }
             }
             if (ltid() < D) lg[ltid()] += tot[ltid()];
@@ -955,7 +1000,19 @@ __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams 
     }
     const size_t rec = size_t(D) * D + D;
     float* dst = p.carry + ((size_t(b) * p.H_kv + h) * size_t(p.n_seg - 1) + s) * rec;
-    store_state<D>(dst, acc);
+    {
+        const int lane = ltid() & 63, wave = ltid() >> 6;
+        const int col = lane & 15, g = lane >> 4;
+        const int rt0 = (wave % (ST::NTT / RTW)) * RTW;
+        const int ct0 = (wave / (ST::NTT / RTW)) * CTW;
+#pragma unroll
+        for (int a = 0; a < RTW; ++a)
+#pragma unroll
+            for (int tt = 0; tt < CTW; ++tt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dst[(16 * (rt0 + a) + 4 * g + r) * D + 16 * (ct0 + tt) + col] = acc[a * CTW + tt][r];
+    }
     if (threadIdx.x < D) dst[size_t(D) * D + threadIdx.x] = lg[threadIdx.x];
 }
 
