@@ -82,25 +82,25 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
     // ---- loads (memory returns in issue order): the new token, the ring
     // keys and values, then the state rows last, so that the whole window
     // attention runs while the state is still arriving. None depends on pos.
-    float kin = 0.f, vin = 0.f;
-    if (tid < D) {
-        kin = to_f32(kp[tid]);
-        vin = to_f32(vp[tid]);
-    }
-    float qin[(NREP * D + kDecThreads - 1) / kDecThreads];
+    // raw element pairs, converted only after every load has been issued:
+    // threads 0 .. D/2-1 read k, D/2 .. D-1 read v, all threads read q
+    typedef typename std::conditional<sizeof(T) == 2, uint32_t, float2>::type Pair;
+    constexpr int QPT = (NREP * D / 2 + kDecThreads - 1) / kDecThreads;
+    Pair kvin;
+    if (tid < D) kvin = *reinterpret_cast<const Pair*>((tid < D / 2 ? kp : vp) + 2 * (tid % (D / 2)));
+    Pair qin[QPT];
 #pragma unroll
-    for (int i = 0; i < (NREP * D + kDecThreads - 1) / kDecThreads; ++i) {
-        const int idx = tid + i * kDecThreads;
-        qin[i] = idx < NREP * D ? to_f32(qp[idx]) : 0.f;
+    for (int i = 0; i < QPT; ++i) {
+        const int pidx = tid + i * kDecThreads;
+        if (pidx < NREP * D / 2) qin[i] = *reinterpret_cast<const Pair*>(qp + 2 * pidx);
     }
     const int ks = tid >> 2;    // ring slot of the logit pass
     const int kpart = tid & 3;  // quarter of the head dimension
     uint4 kr[KPT];
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
-        kr[i] = ks < window
-                    ? *reinterpret_cast<const uint4*>(rk + static_cast<size_t>(ks) * D + kpart * (D / 4) + i * VPL)
-                    : make_uint4(0, 0, 0, 0);
+        kr[i] = ks < window ? *reinterpret_cast<const uint4*>(rk + (ks * D + kpart * (D / 4) + i * VPL))
+                            : make_uint4(0, 0, 0, 0);
     // ring values stay packed in registers until they are used
     typedef typename std::conditional<sizeof(T) == 2, uint2, float4>::type VRaw;
     VRaw vraw[SPT];
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
     for (int i = 0; i < SPT; ++i) {
         const int s = rg + i * RG;
         if (s < window) {
-            vraw[i] = *reinterpret_cast<const VRaw*>(rv + static_cast<size_t>(s) * D + cg * 4);
+            vraw[i] = *reinterpret_cast<const VRaw*>(rv + (s * D + cg * 4));
         } else {
             if constexpr (sizeof(T) == 2) vraw[i] = make_uint2(0, 0);
             else vraw[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -117,20 +117,41 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
     float4 sv[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-        sv[i] = *reinterpret_cast<const float4*>(Sp + static_cast<size_t>(rg + i * RG) * D + cg * 4);
+        sv[i] = *reinterpret_cast<const float4*>(Sp + ((rg + i * RG) * D + cg * 4));
+    // every load is in flight before the first use waits on one
+    __builtin_amdgcn_sched_barrier(0);
 
     const int64_t p = pos[n];
     const int slot = static_cast<int>(p % window);
     const int nvalid = static_cast<int>(p + 1 < window ? p + 1 : window);
 
+    auto unpair = [](const Pair& p2, float& lo, float& hi) {
+        if constexpr (sizeof(T) == 2) {
+            lo = __uint_as_float(p2 << 16);
+            hi = __uint_as_float(p2 & 0xffff0000u);
+        } else {
+            lo = p2.x;
+            hi = p2.y;
+        }
+    };
     if (tid < D) {
-        s_k[tid] = kin;
-        s_v[tid] = vin;
+        float lo, hi;
+        unpair(kvin, lo, hi);
+        float* dst = tid < D / 2 ? s_k : s_v;
+        const int c = 2 * (tid % (D / 2));
+        dst[c] = lo;
+        dst[c + 1] = hi;
     }
 #pragma unroll
-    for (int i = 0; i < (NREP * D + kDecThreads - 1) / kDecThreads; ++i) {
-        const int idx = tid + i * kDecThreads;
-        if (idx < NREP * D) s_q[idx % D][idx / D] = qin[i];
+    for (int i = 0; i < QPT; ++i) {
+        const int pidx = tid + i * kDecThreads;
+        if (pidx < NREP * D / 2) {
+            float lo, hi;
+            unpair(qin[i], lo, hi);
+            const int idx = 2 * pidx;  // element of the NREP x D query block; D is even
+            s_q[idx % D][idx / D] = lo;
+            s_q[(idx + 1) % D][idx / D] = hi;
+        }
     }
     __syncthreads();
 
@@ -154,7 +175,7 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
             x[e] = fast_exp2((x[e] - mx) * kLog2e);
             se += x[e];
         }
-        const float inv = 1.0f / dec_wave_sum(se);
+        const float inv = fast_rcp(dec_wave_sum(se));
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             const int c = lane + 64 * e;
@@ -174,7 +195,7 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
                     const int hi = c + 3 < D ? c + 3 : D;
                     float sm = 0.f;
                     for (int m = lo; m < hi; ++m) sm += s_k[m];
-                    s_g[c] = sigmoidf_stable(sm / static_cast<float>(hi - lo));
+                    s_g[c] = sigmoidf_stable(sm * (c == 0 || c == D - 2 ? (1.0f / 3.0f) : c == D - 1 ? 0.5f : 0.25f));
                 }
             }
         }
@@ -221,7 +242,7 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
         const float l = s_p[lane][j];
         const float m = dec_wave_max(l);
         const float e = lane < nvalid ? fast_exp2(l - m) : 0.f;
-        const float inv = 1.0f / dec_wave_sum(e);
+        const float inv = fast_rcp(dec_wave_sum(e));
         s_p[lane][j] = e * inv * (1.0f - alpha);
     }
     __syncthreads();
@@ -273,7 +294,7 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
         st.y = g * st.y + pk * v4.y;
         st.z = g * st.z + pk * v4.z;
         st.w = g * st.w + pk * v4.w;
-        *reinterpret_cast<float4*>(Sp + static_cast<size_t>(r) * D + cg * 4) = st;
+        *reinterpret_cast<float4*>(Sp + (r * D + cg * 4)) = st;
 #pragma unroll
         for (int j4 = 0; j4 < NR4; ++j4) {
             const float4 pq = *reinterpret_cast<const float4*>(&s_phiq[r][4 * j4]);

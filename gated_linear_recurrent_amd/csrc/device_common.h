@@ -55,8 +55,8 @@ __device__ __forceinline__ float log2_sigmoid(float x) {
 }
 
 __device__ __forceinline__ float sigmoidf_stable(float x) {
-    float e = __expf(-fabsf(x));
-    float s = 1.0f / (1.0f + e);
+    const float e = fast_exp2(-fabsf(x) * kLog2e);
+    const float s = fast_rcp(1.0f + e);
     return x >= 0.0f ? s : e * s;
 }
 
