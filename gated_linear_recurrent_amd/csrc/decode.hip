@@ -156,35 +156,46 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
     __syncthreads();
 
     // ---- softmax over d of k (row 0) and of each query head (stored times
-    // alpha, the GRM weight); the gate
-    constexpr int EPL = D / 64;
-    for (int row = wave; row <= NREP; row += kDecThreads / 64) {
-        float x[EPL];
-        float mx = -INFINITY, sum_raw = 0.f;
+    // alpha, the GRM weight), one row per half wave; the gate on the last wave
+    {
+        constexpr int EPH = D / 32;  // elements per lane of a half-wave row
+        const int hl = lane & 31;
+        for (int row = 2 * wave + (lane >> 5); row <= NREP; row += kDecThreads / 32) {
+            float x[EPH];
+            float mx = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const int c = lane + 64 * e;
-            x[e] = row == 0 ? s_k[c] : s_q[c][row - 1];
-            mx = fmaxf(mx, x[e]);
-            sum_raw += x[e];
-        }
-        mx = dec_wave_max(mx);
-        float se = 0.f;
+            for (int e = 0; e < EPH; ++e) {
+                const int c = hl + 32 * e;
+                x[e] = row == 0 ? s_k[c] : s_q[c][row - 1];
+                mx = fmaxf(mx, x[e]);
+            }
+            mx = group8_max(mx);
+            mx = fmaxf(mx, dpp<kDppMirror>(mx));
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            float se = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            x[e] = fast_exp2((x[e] - mx) * kLog2e);
-            se += x[e];
-        }
-        const float inv = fast_rcp(dec_wave_sum(se));
+            for (int e = 0; e < EPH; ++e) {
+                x[e] = fast_exp2((x[e] - mx) * kLog2e);
+                se += x[e];
+            }
+            se = group8_sum(se);
+            se += dpp<kDppMirror>(se);
+            se += __shfl_xor(se, 16, 64);
+            const float inv = fast_rcp(se) * (row == 0 ? 1.0f : alpha);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const int c = lane + 64 * e;
-            if (row == 0) s_phik[c] = x[e] * inv;
-            else s_phiq[c][row - 1] = x[e] * (inv * alpha);
+            for (int e = 0; e < EPH; ++e) {
+                const int c = hl + 32 * e;
+                if (row == 0) s_phik[c] = x[e] * inv;
+                else s_phiq[c][row - 1] = x[e] * inv;
+            }
         }
-        if (row == 0) {
+        if (wave == kDecThreads / 64 - 1) {
+            constexpr int EPL = D / 64;
             if (GATE == 0) {
-                const float g = sigmoidf_stable(dec_wave_sum(sum_raw) * (1.0f / D));
+                float sm = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) sm += s_k[lane + 64 * e];
+                const float g = sigmoidf_stable(dec_wave_sum(sm) * (1.0f / D));
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) s_g[lane + 64 * e] = g;
             } else {
@@ -324,10 +335,7 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
     // ---- ring slot <- (k, v), bit copy of the inputs
     T* rkw = ring_k + ((static_cast<size_t>(n) * H_kv + h) * window + slot) * D;
     T* rvw = ring_v + ((static_cast<size_t>(n) * H_kv + h) * window + slot) * D;
-    for (int i = tid; i < D; i += kDecThreads) {
-        rkw[i] = kp[i];
-        rvw[i] = vp[i];
-    }
+    if (tid < D) *reinterpret_cast<Pair*>((tid < D / 2 ? rkw : rvw) + 2 * (tid % (D / 2))) = kvin;
 
     // ---- the last of the H_kv workgroups of sequence n advances pos[n].
     // Every wave of every workgroup consumed pos before its first barrier, so
