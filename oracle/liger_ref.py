@@ -220,3 +220,25 @@ def decode_step(q, k, v, S, ring_k, ring_v, pos, gate_mode, alpha, *,
     if return_parts:
         return out + (o_grm, o_swa)
     return out
+
+
+def prefill_continue(q, k, v, S0, ring_k, ring_v, pos, gate_mode, alpha, *, gate_override=None):
+    """T more tokens per sequence after `pos` already consumed ones.
+
+    The plain definition: T successive decode steps from the fixed-size state
+    (S0, ring of the last `window` keys/values, pos), the same state decoding
+    carries ([News] 実験分析). q: [B, T, H_q, d]; k, v: [B, T, H_kv, d];
+    S0: [B, H_kv, d, d]; ring_k, ring_v: [B, H_kv, window, d]; pos: [B].
+    Returns (o [B, T, H_q, d], S_T, ring_k', ring_v', pos + T).
+    """
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
+    B, T, H_q, d = q.shape
+    S = _f64(S0)
+    rk, rv = np.array(ring_k, copy=True), np.array(ring_v, copy=True)
+    p = np.asarray(pos, dtype=np.int64).copy()
+    o = np.empty((B, T, H_q, d))
+    for t in range(T):
+        o[:, t], S, rk, rv, p = decode_step(q[:, t], k[:, t], v[:, t], S, rk, rv, p, gate_mode, alpha,
+                                            gate_override=gate_override)
+    return o, S, rk, rv, p
+

@@ -219,6 +219,28 @@ def test_decode_continues_prefill(mode, T0, n, window):
 
 
 @pytest.mark.parametrize("mode", [oracle.SCALAR_MEAN, oracle.VECTOR_AVGPOOL4])
+@pytest.mark.parametrize("T1,T2,window", [(0, 9, 4), (5, 7, 4), (1, 12, 64), (70, 3, 64), (3, 5, 1), (40, 30, 17)])
+def test_prefill_continue_is_concatenation(mode, T1, T2, window):
+    """Pin 5 for the continuation: prefill(T1), ring after it, then T2 tokens
+    in one continuation call == prefill(T1 + T2): outputs of the last T2
+    tokens, the final state, the ring (the last `window` tokens) and pos.
+    T1 = 0 starts from a zero state and an empty ring."""
+    x = prefill_inputs(B=2, T=T1 + T2, H_q=4, H_kv=2, d=8, dtype="f32", seed=23)
+    q, k, v = x["q"], x["k"], x["v"]
+    o_full, S_full = oracle.prefill(q, k, v, mode, window, 0.35)
+    if T1 > 0:
+        _, S0 = oracle.prefill(q[:, :T1], k[:, :T1], v[:, :T1], mode, window, 0.35)
+    else:
+        S0 = np.zeros((2, 2, 8, 8))
+    rk, rv, pos = oracle.ring_fill(k[:, :T1], v[:, :T1], window)
+    o, S, rk, rv, pos = oracle.prefill_continue(q[:, T1:], k[:, T1:], v[:, T1:], S0, rk, rv, pos, mode, 0.35)
+    assert _close(o, o_full[:, T1:])
+    assert _close(S, S_full)
+    rk_ref, rv_ref, pos_ref = oracle.ring_fill(k, v, window)
+    assert np.array_equal(rk, rk_ref) and np.array_equal(rv, rv_ref) and np.array_equal(pos, pos_ref)
+
+
+@pytest.mark.parametrize("mode", [oracle.SCALAR_MEAN, oracle.VECTOR_AVGPOOL4])
 @pytest.mark.parametrize("c", [0.0, -1.5, 2.0])
 def test_closed_form_constant_key(mode, c):
     """Pin 6: k_t = c*1, v_t = v: a geometric series, derived by hand.
