@@ -41,6 +41,7 @@ EXPORTED = (
     "liger_attn_prefill",
     "liger_attn_prefill_ex",
     "liger_attn_prefill_stages",
+    "liger_attn_prefill_continue",
     "liger_attn_decode_step",
     "liger_kv_ring_fill",
     "liger_last_error",
@@ -87,6 +88,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.liger_attn_prefill_ex.restype = i32
     lib.liger_attn_prefill_stages.argtypes = [vp, vp, vp, i32, i32, f32, shp, vp, vp, vp, sz, i32, i32, vp]
     lib.liger_attn_prefill_stages.restype = i32
+    lib.liger_attn_prefill_continue.argtypes = [vp, vp, vp, vp, ring, i32, f32, shp, vp, vp, vp, sz, vp]
+    lib.liger_attn_prefill_continue.restype = i32
     lib.liger_attn_decode_step.argtypes = [vp, vp, vp, vp, ring, i32, f32, shp, vp, vp]
     lib.liger_attn_decode_step.restype = i32
     lib.liger_kv_ring_fill.argtypes = [vp, vp, shp, ring, vp]
@@ -199,6 +202,30 @@ def liger_kv_ring_fill(k, v, ring: KVRing, stream=None) -> KVRing:
     cring = ring.as_c()
     _check(lib.liger_kv_ring_fill(_ptr(k), _ptr(v), ctypes.byref(shp), ctypes.byref(cring), _stream(stream)))
     return ring
+
+
+def liger_attn_prefill_continue(q, k, v, S0, ring: KVRing, gate_mode: int, alpha: float, *, o=None, S_T=None,
+                                workspace=None, stream=None):
+    """T more tokens after ring.pos[b] consumed ones, from state S0 (not modified) and the ring
+    (updated in place: last tokens written, pos += T). Window = ring.window. -> (o, S_T)."""
+    torch = _torch()
+    lib = load_library()
+    B, T, H_q, d = q.shape
+    H_kv = k.shape[2]
+    shp = make_shape(B, T, H_q, H_kv, d, _dtype_code(q))
+    if o is None:
+        o = torch.empty_like(q)
+    if S_T is None:
+        S_T = torch.empty((B, H_kv, d, d), dtype=torch.float32, device=q.device)
+    need = int(lib.liger_attn_prefill_workspace_size_ex(ctypes.byref(shp), 0))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    cring = ring.as_c()
+    _check(lib.liger_attn_prefill_continue(_ptr(q), _ptr(k), _ptr(v), _ptr(S0), ctypes.byref(cring), gate_mode,
+                                           alpha, ctypes.byref(shp), _ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes,
+                                           _stream(stream)))
+    return o, S_T
 
 
 def liger_attn_decode_step(q, k, v, S, ring: KVRing, gate_mode: int, alpha: float, *, o=None, stream=None):

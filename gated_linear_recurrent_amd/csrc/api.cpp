@@ -145,6 +145,82 @@ liger_status liger_attn_prefill(const void* q, const void* k, const void* v, int
                                  stream);
 }
 
+liger_status liger_attn_prefill_continue(const void* q, const void* k, const void* v, const float* S0,
+                                        const liger_kv_ring* kv_ring, int32_t gate_mode, float alpha,
+                                        const liger_shape* shape, void* o, float* S_T, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+    LIGER_TRY(check_shape(shape, true));
+    LIGER_TRY(check_common(gate_mode, alpha));
+    if (!kv_ring) return fail(LIGER_E_INVALID_ARG, "kv_ring is NULL");
+    const int32_t window = kv_ring->window;
+    if (window < 1 || window > 64) return fail(LIGER_E_INVALID_ARG, "ring window must be in 1..64");
+    if (shape->dtype == LIGER_F32 && shape->d != 64)
+        return fail(LIGER_E_UNSUPPORTED, "fp32 prefill is built for d = 64 only");
+    LIGER_TRY(check_ptr(q, "q"));
+    LIGER_TRY(check_ptr(k, "k"));
+    LIGER_TRY(check_ptr(v, "v"));
+    LIGER_TRY(check_ptr(S0, "S0"));
+    LIGER_TRY(check_ptr(o, "o"));
+    LIGER_TRY(check_ptr(S_T, "S_T"));
+    LIGER_TRY(check_ptr(kv_ring->k, "kv_ring->k"));
+    LIGER_TRY(check_ptr(kv_ring->v, "kv_ring->v"));
+    if (!kv_ring->pos) return fail(LIGER_E_INVALID_ARG, "kv_ring->pos is NULL");
+    if (!kv_ring->sync) return fail(LIGER_E_INVALID_ARG, "kv_ring->sync is NULL");
+    if (o == q || o == k || o == v) return fail(LIGER_E_INVALID_ARG, "o must not alias q, k or v");
+    const size_t sbytes = size_t(shape->B) * shape->H_kv * shape->d * shape->d * sizeof(float);
+    const char* s0c = reinterpret_cast<const char*>(S0);
+    const char* stc = reinterpret_cast<const char*>(S_T);
+    if (s0c < stc + sbytes && stc < s0c + sbytes) return fail(LIGER_E_INVALID_ARG, "S_T must not overlap S0");
+    const liger::PrefillPlan pl = liger::make_prefill_plan(shape->B, shape->T, shape->H_kv, shape->d,
+                                                           shape->dtype == LIGER_BF16, 0);
+    if (pl.workspace_bytes > 0) {
+        if (!workspace) return fail(LIGER_E_WORKSPACE, "workspace is NULL but " + std::to_string(pl.workspace_bytes) + " bytes are needed");
+        if (!aligned16(workspace)) return fail(LIGER_E_INVALID_ARG, "workspace is not 16-byte aligned");
+        if (workspace_bytes < pl.workspace_bytes)
+            return fail(LIGER_E_WORKSPACE, "workspace too small: " + std::to_string(workspace_bytes) + " < " +
+                                               std::to_string(pl.workspace_bytes) + " bytes");
+    }
+    liger::PrefillArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.S_T = S_T;
+    a.workspace = static_cast<float*>(workspace);
+    a.B = shape->B;
+    a.T = shape->T;
+    a.H_kv = shape->H_kv;
+    a.n_rep = shape->H_q / shape->H_kv;
+    a.d = shape->d;
+    a.window = window;
+    a.gate = gate_mode;
+    a.bf16 = shape->dtype == LIGER_BF16;
+    a.alpha = alpha;
+    a.plan = pl;
+    a.stage_mask = 7;
+    a.stream = stream;
+    a.S0 = S0;
+    a.ring_k = kv_ring->k;
+    a.ring_v = kv_ring->v;
+    a.pos = kv_ring->pos;
+    LIGER_TRY(map_hip(liger::launch_prefill(a), "prefill continuation launch"));
+    liger::RingFillArgs r;
+    r.k = k;
+    r.v = v;
+    r.ring_k = kv_ring->k;
+    r.ring_v = kv_ring->v;
+    r.pos = kv_ring->pos;
+    r.sync = kv_ring->sync;
+    r.B = shape->B;
+    r.T = shape->T;
+    r.H_kv = shape->H_kv;
+    r.d = shape->d;
+    r.window = window;
+    r.bf16 = shape->dtype == LIGER_BF16;
+    r.stream = stream;
+    return map_hip(liger::launch_ring_append(r), "ring append launch");
+}
+
 liger_status liger_attn_decode_step(const void* q, const void* k, const void* v, float* S,
                                     const liger_kv_ring* kv_ring, int32_t gate_mode, float alpha,
                                     const liger_shape* shape, void* o, void* stream) {

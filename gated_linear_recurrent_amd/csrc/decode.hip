@@ -373,6 +373,37 @@ __global__ __launch_bounds__(64) void ring_fill_kernel(
     }
 }
 
+// Continuation: the ring after T more tokens. Slot s receives the new token at
+// absolute position P = s (mod window) among the last `window` positions when
+// P >= pos (a new token); otherwise it keeps the older token it holds.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void ring_append_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ ring_k,
+    T* __restrict__ ring_v, const int64_t* __restrict__ pos, int64_t Tlen, int H_kv, int window) {
+    const int slot = blockIdx.x;
+    const int h = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int64_t pos0 = pos[b];
+    const int64_t first = pos0 + Tlen - window;  // oldest position the ring keeps
+    const int64_t P = first + (((slot - first) % window) + window) % window;
+    if (P < pos0) return;
+    const size_t src = ((static_cast<size_t>(b) * Tlen + (P - pos0)) * H_kv + h) * D;
+    const size_t dst = ((static_cast<size_t>(b) * H_kv + h) * window + slot) * D;
+    for (int i = threadIdx.x; i < D; i += 64) {
+        ring_k[dst + i] = k[src + i];
+        ring_v[dst + i] = v[src + i];
+    }
+}
+
+// pos[b] += T and the arrival counters cleared, after the ring append has read pos.
+__global__ void ring_advance_kernel(int64_t* __restrict__ pos, uint32_t* __restrict__ sync, int64_t B, int64_t Tlen) {
+    const int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (b < B) {
+        pos[b] += Tlen;
+        sync[b] = 0u;
+    }
+}
+
 // ------------------------------------------------------------------ launchers
 template <typename T, int D, int GATE, int NREP>
 static hipError_t launch_dec_t(const DecodeArgs& a) {
@@ -413,6 +444,25 @@ static hipError_t launch_fill_t(const RingFillArgs& a) {
                        static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<T*>(a.ring_k),
                        static_cast<T*>(a.ring_v), a.pos, a.sync, a.T, a.H_kv, a.window);
     return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_append_t(const RingFillArgs& a) {
+    hipStream_t st = static_cast<hipStream_t>(a.stream);
+    dim3 grid(a.window, a.H_kv, static_cast<unsigned>(a.B));
+    hipLaunchKernelGGL((ring_append_kernel<T, D>), grid, dim3(64), 0, st, static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), static_cast<T*>(a.ring_k), static_cast<T*>(a.ring_v), a.pos, a.T,
+                       a.H_kv, a.window);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ring_advance_kernel, dim3(static_cast<unsigned>((a.B + 255) / 256)), dim3(256), 0, st, a.pos,
+                       a.sync, a.B, a.T);
+    return hipGetLastError();
+}
+
+hipError_t launch_ring_append(const RingFillArgs& a) {
+    if (a.bf16) return a.d == 64 ? launch_append_t<bf16_t, 64>(a) : launch_append_t<bf16_t, 128>(a);
+    return a.d == 64 ? launch_append_t<float, 64>(a) : launch_append_t<float, 128>(a);
 }
 
 hipError_t launch_ring_fill(const RingFillArgs& a) {

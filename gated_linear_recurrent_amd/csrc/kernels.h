@@ -79,6 +79,12 @@ struct PrefillArgs {
     PrefillPlan plan;
     int stage_mask;  // 1 segment states, 2 carry scan, 4 outputs
     void* stream;
+    // continuation (all null for a prefill from a zero state): the state and
+    // KV ring (window = `window`) after pos[b] tokens
+    const float* S0 = nullptr;
+    const void* ring_k = nullptr;
+    const void* ring_v = nullptr;
+    const int64_t* pos = nullptr;
 };
 
 constexpr int kChunk = 64;
@@ -87,6 +93,9 @@ PrefillPlan make_prefill_plan(int64_t B, int64_t T, int H_kv, int d, bool bf16, 
 
 hipError_t launch_decode_step(const DecodeArgs& a);
 hipError_t launch_ring_fill(const RingFillArgs& a);
+// Continuation: the last min(T, window) new tokens go to slots (pos + t) mod
+// window, older slots keep their tokens, then pos += T.
+hipError_t launch_ring_append(const RingFillArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 
 }  // namespace liger

@@ -190,6 +190,12 @@ struct PrefillParams {
     int n_rep;
     int window;
     float alpha;
+    // continuation: entering state [B, H_kv, d, d] and the KV ring
+    // [B, H_kv, window, d] after pos[b] tokens (null for a zero state)
+    const float* S0;
+    const void* ring_k;
+    const void* ring_v;
+    const int64_t* pos;
 };
 
 // ------------------------------------------------------------ chunk loading
@@ -246,6 +252,49 @@ __device__ __forceinline__ void load_chunk_issue(ChunkRegs<T, D>& cr, const T* k
         if (idx < 32 * CR::PPR) {
             if (j0 < nvalid) cr.v0[n] = *reinterpret_cast<const uint4*>(vbase + (t0 + j0) * row_stride + c0);
             if (j0 + 1 < nvalid) cr.v1[n] = *reinterpret_cast<const uint4*>(vbase + (t0 + j0 + 1) * row_stride + c0);
+        }
+    }
+}
+
+// The 64 tokens before a continuation as a chunk: row j is token pos - 64 + j,
+// read from ring slot (pos - 64 + j) mod window when it is among the npv
+// (= min(pos, window)) tokens the ring holds, zero otherwise. Same register
+// mapping as load_chunk_issue.
+template <typename T, int D>
+__device__ __forceinline__ void load_ring_issue(ChunkRegs<T, D>& cr, const T* rk, const T* rv, int64_t pos,
+                                                int window, int npv) {
+    typedef ChunkRegs<T, D> CR;
+    const int tid = ltid();
+    auto row_of = [&](int j) -> int64_t {  // ring row of chunk row j, or -1
+        if (j < 64 - npv) return -1;
+        return (pos - 64 + j) % window;  // pos - 64 + j >= pos - npv >= 0
+    };
+#pragma unroll
+    for (int n = 0; n < CR::NK; ++n) {
+        const int idx = tid + n * kPThreads;
+        const int j = idx / CR::PPR;
+        const int c0 = (idx % CR::PPR) * CR::VPL;
+        cr.k[n] = make_uint4(0, 0, 0, 0);
+        const int64_t rr = idx < 64 * CR::PPR ? row_of(j) : -1;
+        if (rr >= 0) cr.k[n] = *reinterpret_cast<const uint4*>(rk + rr * D + c0);
+        if constexpr (CR::VNAT) {
+            cr.v[n] = make_uint4(0, 0, 0, 0);
+            if (rr >= 0) cr.v[n] = *reinterpret_cast<const uint4*>(rv + rr * D + c0);
+        }
+    }
+    if constexpr (!CR::VNAT) {
+#pragma unroll
+        for (int n = 0; n < CR::NV; ++n) {
+            const int idx = tid + n * kPThreads;
+            const int j0 = 2 * (idx & 31);
+            const int c0 = (idx >> 5) * CR::VPL;
+            cr.v0[n] = make_uint4(0, 0, 0, 0);
+            cr.v1[n] = make_uint4(0, 0, 0, 0);
+            if (idx < 32 * CR::PPR) {
+                const int64_t r0 = row_of(j0), r1 = row_of(j0 + 1);
+                if (r0 >= 0) cr.v0[n] = *reinterpret_cast<const uint4*>(rv + r0 * D + c0);
+                if (r1 >= 0) cr.v1[n] = *reinterpret_cast<const uint4*>(rv + r1 * D + c0);
+            }
         }
     }
 }
@@ -1020,7 +1069,8 @@ __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams 
 // One thread per state element; the carries of up to BATCH segments are
 // loaded before the first multiply-add so their latencies overlap.
 template <int D>
-__global__ __launch_bounds__(256) void carry_scan_kernel(float* __restrict__ carry, int64_t n_seg, int H_kv) {
+__global__ __launch_bounds__(256) void carry_scan_kernel(float* __restrict__ carry, const float* __restrict__ S0,
+                                                          int64_t n_seg, int H_kv) {
     constexpr int BATCH = 32;
     const int e = blockIdx.x * 256 + threadIdx.x;  // D*D is a multiple of 256
     const int h = blockIdx.y;
@@ -1028,7 +1078,7 @@ __global__ __launch_bounds__(256) void carry_scan_kernel(float* __restrict__ car
     const size_t rec = size_t(D) * D + D;
     float* base = carry + (size_t(b) * H_kv + h) * size_t(n_seg - 1) * rec;
     const int r = e / D;
-    float acc = 0.f;
+    float acc = S0 ? S0[(size_t(b) * H_kv + h) * D * D + e] : 0.f;
     for (int64_t s0 = 0; s0 < n_seg - 1; s0 += BATCH) {
         float Ls[BATCH], lg[BATCH];
 #pragma unroll
@@ -1059,7 +1109,7 @@ struct ItemCtx {
     int hq;
     int nvalid;
     int window;
-    bool have_prev;    // a previous chunk exists (chunk index > 0)
+    int npv;           // keys of the previous-chunk slot that exist (64, or fewer at the sequence start)
     float alpha;
     int cur;
 };
@@ -1214,7 +1264,7 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
 #pragma unroll
             for (int s = 0; s < 2; ++s)
                 live[s] = inr(s, kt) &&
-                          (FAST || ((kt >= 0 || x.have_prev) && (16 * kt + 15 > 16 * QTS[s] - x.window)));
+                          (FAST || ((kt >= 0 || x.npv > 0) && (16 * kt + 15 > 16 * QTS[s] - x.window)));
             if (live[0] || live[1]) {
                 const T* krow = kt >= 0 ? Kcur + (16 * kt + col) * L::DP : Kprv + (16 * kt + 64 + col) * L::DP;
                 f32x4_t d4[2] = {zero4(), zero4()};
@@ -1234,11 +1284,14 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
                         continue;
                     }
                     const int dt = 16 * (QTS[s] - kt);  // 16 (I - kt), compile-time
-                    const bool partial = (kt == QTS[s] - 4) || (kt == QTS[s]) || !(FAST || full_window);
+                    const bool before = !FAST && kt < 0 && x.npv < 64;  // keys before the sequence start
+                    const bool partial = (kt == QTS[s] - 4) || (kt == QTS[s]) || !(FAST || full_window) || before;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         float v = d4[s][r];
-                        if (partial) v = static_cast<unsigned>(dt + dl - r) < w ? v : -INFINITY;
+                        if (partial)
+                            v = (static_cast<unsigned>(dt + dl - r) < w && (!before || 16 * kt + 4 * g + r >= -x.npv))
+                                    ? v : -INFINITY;
                         sc[s][u][r] = v;
                         lmax[s] = fmaxf(lmax[s], v);
                     }
@@ -1272,7 +1325,7 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
                 for (int r = 0; r < 4; ++r) sc[s][u][r] *= ps;
         }
     };
-    if (x.have_prev && full_window) window_scores(std::true_type{});
+    if (x.npv == 64 && full_window) window_scores(std::true_type{});
     else window_scores(std::false_type{});
 
     // recurrence operand (built after the window scores so qr can retire)
@@ -1498,7 +1551,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
     const size_t rec = size_t(D) * D + D;
 
     float* slot = p.state_slots + ((size_t(b) * p.H_kv + h) * size_t(p.n_seg) + s) * size_t(D) * D;
-    const float* carry_in = s == 0 ? nullptr : p.carry + ((size_t(b) * p.H_kv + h) * size_t(p.n_seg - 1) + (s - 1)) * rec;
+    const float* carry_in = s > 0 ? p.carry + ((size_t(b) * p.H_kv + h) * size_t(p.n_seg - 1) + (s - 1)) * rec
+                            : p.S0 ? p.S0 + (size_t(b) * p.H_kv + h) * D * D : nullptr;
+    // continuation: tokens already consumed, and how many of the 64 before the
+    // first chunk exist (the ring holds the last min(pos, window))
+    const int64_t pos_b = p.pos ? p.pos[b] : 0;
+    const int npv0 = int(pos_b < p.window ? pos_b : p.window);
     const bool last_seg = s == p.n_seg - 1;
 
     const int64_t c_begin = int64_t(s) * p.cps;
@@ -1511,9 +1569,13 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
     load_chunk_issue<T, D>(cr, kbase, vbase, row_stride, c_begin * kChunk,
                            p.T - c_begin * kChunk < kChunk ? int(p.T - c_begin * kChunk) : kChunk);
     if (c_begin > 0) load_chunk_issue<T, D>(cp, kbase, vbase, row_stride, (c_begin - 1) * kChunk, kChunk);
+    else if (npv0 > 0)
+        load_ring_issue<T, D>(cp, static_cast<const T*>(p.ring_k) + (size_t(b) * p.H_kv + h) * p.window * D,
+                              static_cast<const T*>(p.ring_v) + (size_t(b) * p.H_kv + h) * p.window * D, pos_b,
+                              p.window, npv0);
     f32x4_t acc[StateTiles<D>::TPW];
     if constexpr (L::SLDS) load_state<D>(carry_in, acc);
-    if (c_begin > 0) load_chunk_commit(sm, int((c_begin - 1) & 1), cp);
+    if (c_begin > 0 || npv0 > 0) load_chunk_commit(sm, int((c_begin + 1) & 1), cp);
     else zero_slot(sm, int((c_begin + 1) & 1));
     load_chunk_commit(sm, int(c_begin & 1), cr);
     const int n_items = p.n_rep * 2;
@@ -1554,7 +1616,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
             x.H_q = H_q;
             x.nvalid = nvalid;
             x.window = p.window;
-            x.have_prev = c > 0;
+            x.npv = c > 0 ? 64 : npv0;
             x.alpha = p.alpha;
             x.cur = cur;
             // next chunk's K/V: in flight during the output phase
@@ -1635,7 +1697,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
         x.H_q = H_q;
         x.nvalid = nvalid;
         x.window = p.window;
-        x.have_prev = c > 0;
+        x.npv = c > 0 ? 64 : npv0;
         x.alpha = p.alpha;
         x.cur = cur;
         // next chunk's K/V: in flight during the output phase, stored after it
@@ -1703,6 +1765,10 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     p.n_rep = a.n_rep;
     p.window = a.window;
     p.alpha = a.alpha;
+    p.S0 = a.S0;
+    p.ring_k = a.ring_k;
+    p.ring_v = a.ring_v;
+    p.pos = a.pos;
     hipStream_t st = static_cast<hipStream_t>(a.stream);
     if (p.n_seg > 1 && (a.stage_mask & 1)) {
         hipLaunchKernelGGL((segment_state_kernel<T, D, GATE>), dim3(unsigned(p.n_seg - 1), a.H_kv, unsigned(a.B)),
@@ -1712,7 +1778,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     }
     if (p.n_seg > 1 && (a.stage_mask & 2)) {
         hipLaunchKernelGGL((carry_scan_kernel<D>), dim3(D * D / 256, a.H_kv, unsigned(a.B)), dim3(256), 0, st,
-                           p.carry, p.n_seg, p.H_kv);
+                           p.carry, p.S0, p.n_seg, p.H_kv);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

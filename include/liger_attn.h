@@ -151,6 +151,34 @@ liger_status liger_attn_prefill_stages(const void* q, const void* k, const void*
                                        void* stream);
 
 /*
+ * Prefill continuation: T = shape->T more tokens for each of B sequences
+ * after the kv_ring->pos[b] tokens already consumed, from the state S0 and
+ * the KV ring those tokens left (after liger_attn_prefill + liger_kv_ring_fill,
+ * decode steps or an earlier continuation). The result equals one prefill of
+ * the concatenated sequence restricted to the new tokens, and T decode steps
+ * (the fixed-size decoding state of the recurrence; paper-notes page "Liger:
+ * Linearizing Large Language Models to Gated Recurrent Structures", unified
+ * gated linear recurrence; news article on Liger, 実験分析: constant-memory
+ * decoding).
+ *   q [B, T, H_q, d], k, v [B, T, H_kv, d] (dtype of the shape); o as q.
+ *   S0 [B, H_kv, d, d] float32, read only; S_T [B, H_kv, d, d] float32,
+ *   written; they must not overlap.
+ *   kv_ring: window = kv_ring->window (1..64) is the attention window; the
+ *   ring is read, then the last min(T, window) new tokens are written to
+ *   slots (pos + t) mod window, older slots keep their tokens, pos[b] += T
+ *   and sync[b] = 0. Entries of pos may differ between sequences.
+ *   workspace as for liger_attn_prefill (liger_attn_prefill_workspace_size).
+ * gate_mode and alpha must be those that produced S0. Errors as for
+ * liger_attn_prefill; a NULL ring, pos or sync is LIGER_E_INVALID_ARG.
+ */
+liger_status liger_attn_prefill_continue(const void* q, const void* k, const void* v,
+                                        const float* S0, const liger_kv_ring* kv_ring,
+                                        int32_t gate_mode, float alpha,
+                                        const liger_shape* shape, void* o, float* S_T,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/*
  * Decode step: one new token for each of N = shape->B sequences.
  * q [N, H_q, d], k, v [N, H_kv, d] (dtype of the shape); o [N, H_q, d].
  * S [N, H_kv, d, d] float32 is updated in place to G (.) S + phi(k)^T v.

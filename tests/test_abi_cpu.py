@@ -143,6 +143,36 @@ def test_decode_rejects_null_ring_and_alias(lib):
     assert _decode(lib, _shape(), _ring(), gate=-1) == gla.LIGER_E_INVALID_ARG
 
 
+def _continue(lib, shape, ring, S0=FAKE + 131072, S_T=FAKE + 196608, o=FAKE + 4096, gate=1, alpha=0.5,
+              ws=FAKE << 8, ws_bytes=1 << 40):
+    return lib.liger_attn_prefill_continue(FAKE, FAKE + 65536, FAKE + 98304, S0,
+                                           ctypes.byref(ring) if ring is not None else None, gate, alpha,
+                                           ctypes.byref(shape), o, S_T, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,rkw,ckw,code", [
+    (dict(), dict(), dict(S0=None), gla.LIGER_E_INVALID_ARG),
+    (dict(), dict(window=0), dict(), gla.LIGER_E_INVALID_ARG),
+    (dict(), dict(window=65), dict(), gla.LIGER_E_INVALID_ARG),
+    (dict(), dict(pos=None), dict(), gla.LIGER_E_INVALID_ARG),
+    (dict(), dict(sync=None), dict(), gla.LIGER_E_INVALID_ARG),
+    (dict(), dict(), dict(S_T=FAKE + 131072 + 16), gla.LIGER_E_INVALID_ARG),   # S_T overlaps S0
+    (dict(), dict(), dict(o=FAKE), gla.LIGER_E_INVALID_ARG),                   # o aliases q
+    (dict(), dict(), dict(ws=None), gla.LIGER_E_WORKSPACE),
+    (dict(dtype=gla.LIGER_F32, d=128), dict(), dict(), gla.LIGER_E_UNSUPPORTED),
+    (dict(T=0), dict(), dict(), gla.LIGER_E_INVALID_ARG),
+    (dict(), dict(), dict(gate=5), gla.LIGER_E_INVALID_ARG),
+])
+def test_continue_rejects_bad_arguments(lib, kw, rkw, ckw, code):
+    shp = _shape(**{**dict(T=256, H_q=4, H_kv=1), **kw})
+    assert _continue(lib, shp, _ring(**rkw), **ckw) == code
+    assert gla.liger_last_error() != ""
+
+
+def test_continue_rejects_null_ring(lib):
+    assert _continue(lib, _shape(T=256), None) == gla.LIGER_E_INVALID_ARG
+
+
 def test_ring_fill_rejects_bad_arguments(lib):
     shp = _shape()
     assert lib.liger_kv_ring_fill(FAKE, FAKE, ctypes.byref(shp), None, None) == gla.LIGER_E_INVALID_ARG
