@@ -51,12 +51,16 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
     constexpr int RPT = D / RG;           // state rows per thread
     constexpr int SPT = 64 / RG;          // ring slots per thread in the value pass
     constexpr int VPL = 16 / sizeof(T);   // elements per 16-byte load
-    constexpr int KPT = (D / 4) / VPL;    // 16-byte key loads per thread in the logit pass
+    constexpr int LPR = D / VPL;          // lanes per key row in the logit pass (16-byte pieces)
+    constexpr int SPI = kDecThreads / LPR;  // ring slots per key load instruction
+    constexpr int KPT = 64 / SPI;         // key loads (slots) per thread in the logit pass
     constexpr int NR4 = (NREP + 3) / 4;   // float4 groups of the per-head values
     constexpr int NRP = 4 * NR4;          // per-head values padded to a float4 multiple
-    static_assert(kDecThreads == 256, "four lanes per ring slot");
+    static_assert(kDecThreads == 256 && LPR >= 8 && LPR <= 32, "key rows of 8 to 32 pieces");
 
     __shared__ float s_k[D], s_v[D], s_phik[D], s_g[D];
+    __shared__ __align__(16) uint32_t s_kraw[D * sizeof(T) / 4];  // the new key, input bits
+    __shared__ int64_t s_pos;
     __shared__ __align__(16) float s_q[D][NRP];      // raw q, head-minor
     __shared__ __align__(16) float s_phiq[D][NRP];   // phi(q), head-minor
     __shared__ __align__(16) float s_p[64][NRP];     // window weights, head-minor
@@ -94,13 +98,15 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
         const int pidx = tid + i * kDecThreads;
         if (pidx < NREP * D / 2) qin[i] = *reinterpret_cast<const Pair*>(qp + 2 * pidx);
     }
-    const int ks = tid >> 2;    // ring slot of the logit pass
-    const int kpart = tid & 3;  // quarter of the head dimension
+    // ring keys: consecutive lanes read consecutive 16-byte pieces; thread
+    // tid holds piece kl of the rows of slots ks0 + i * SPI
+    const int ks0 = tid / LPR;
+    const int kl = tid % LPR;
     uint4 kr[KPT];
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
-        kr[i] = ks < window ? *reinterpret_cast<const uint4*>(rk + (ks * D + kpart * (D / 4) + i * VPL))
-                            : make_uint4(0, 0, 0, 0);
+        kr[i] = ks0 + i * SPI < window ? *reinterpret_cast<const uint4*>(rk + ((ks0 + i * SPI) * D + kl * VPL))
+                                       : make_uint4(0, 0, 0, 0);
     // ring values stay packed in registers until they are used
     typedef typename std::conditional<sizeof(T) == 2, uint2, float4>::type VRaw;
     VRaw vraw[SPT];
@@ -121,9 +127,17 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
     // every load is in flight before the first use waits on one
     __builtin_amdgcn_sched_barrier(0);
 
-    const int64_t p = pos[n];
-    const int slot = static_cast<int>(p % window);
-    const int nvalid = static_cast<int>(p + 1 < window ? p + 1 : window);
+    // pos[n] is read by thread 0 alone and handed to the other waves through
+    // LDS. Its arrival on sync[n] depends on the value read, so it is counted
+    // only after that read; the last of the H_kv workgroups of sequence n to
+    // arrive advances pos[n] at its end, when every workgroup has read it.
+    uint32_t prev = 0;
+    if (tid == 0) {
+        const int64_t p0 = pos[n];
+        s_pos = p0;
+        prev = __hip_atomic_fetch_add(&sync[n], 1u + static_cast<uint32_t>(p0 >> 62), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     auto unpair = [](const Pair& p2, float& lo, float& hi) {
         if constexpr (sizeof(T) == 2) {
@@ -134,6 +148,10 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
             hi = p2.y;
         }
     };
+    if (tid < D / 2) s_kraw[tid * sizeof(T) / 2] = *reinterpret_cast<const uint32_t*>(&kvin);
+    if constexpr (sizeof(T) == 4) {
+        if (tid < D / 2) s_kraw[tid * 2 + 1] = *(reinterpret_cast<const uint32_t*>(&kvin) + 1);
+    }
     if (tid < D) {
         float lo, hi;
         unpair(kvin, lo, hi);
@@ -154,6 +172,9 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
         }
     }
     __syncthreads();
+    const int64_t p = s_pos;
+    const int slot = static_cast<int>(p % window);
+    const int nvalid = static_cast<int>(p + 1 < window ? p + 1 : window);
 
     // ---- softmax over d of k (row 0) and of each query head (stored times
     // alpha, the GRM weight), one row per half wave; the gate on the last wave
@@ -212,39 +233,51 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
         }
     }
 
-    // ---- window logits: q . k_s for this thread's slot and quarter (the
-    // new token's key from LDS)
+    // ---- window logits q . k_s: this thread's piece of KPT slots, summed over
+    // the LPR lanes of each row (the new token's key from LDS)
     {
-        float dot[NRP];
+        float qv[VPL][NRP];
 #pragma unroll
-        for (int j = 0; j < NRP; ++j) dot[j] = 0.f;
-        const int c0 = kpart * (D / 4);
+        for (int t = 0; t < VPL; ++t)
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const T* e = reinterpret_cast<const T*>(&kr[i]);
-#pragma unroll
-            for (int t = 0; t < VPL; ++t) {
-                const int c = c0 + i * VPL + t;
-                const float kv = ks == slot ? s_k[c] : to_f32(e[t]);
-#pragma unroll
-                for (int j4 = 0; j4 < NR4; ++j4) {
-                    const float4 q4 = *reinterpret_cast<const float4*>(&s_q[c][4 * j4]);
-                    dot[4 * j4 + 0] += q4.x * kv;
-                    dot[4 * j4 + 1] += q4.y * kv;
-                    dot[4 * j4 + 2] += q4.z * kv;
-                    dot[4 * j4 + 3] += q4.w * kv;
-                }
+            for (int j4 = 0; j4 < NR4; ++j4) {
+                const float4 q4 = *reinterpret_cast<const float4*>(&s_q[kl * VPL + t][4 * j4]);
+                qv[t][4 * j4 + 0] = q4.x;
+                qv[t][4 * j4 + 1] = q4.y;
+                qv[t][4 * j4 + 2] = q4.z;
+                qv[t][4 * j4 + 3] = q4.w;
             }
-        }
+        const uint4 knew = reinterpret_cast<const uint4*>(s_kraw)[kl];
         const float scale = kLog2e * rsqrtf(static_cast<float>(D));
 #pragma unroll
-        for (int j = 0; j < NREP; ++j) {
-            dot[j] += dpp<kDppXor1>(dot[j]);
-            dot[j] += dpp<kDppXor2>(dot[j]);
-        }
-        if (kpart == 0) {
+        for (int i = 0; i < KPT; ++i) {
+            const int s_i = ks0 + i * SPI;
+            const uint4 kk = s_i == slot ? knew : kr[i];
+            const T* e = reinterpret_cast<const T*>(&kk);
+            float dot[NRP];
 #pragma unroll
-            for (int j = 0; j < NREP; ++j) s_p[ks][j] = ks < nvalid ? dot[j] * scale : -INFINITY;
+            for (int j = 0; j < NRP; ++j) dot[j] = 0.f;
+#pragma unroll
+            for (int t = 0; t < VPL; ++t) {
+                const float kv = to_f32(e[t]);
+#pragma unroll
+                for (int j = 0; j < NREP; ++j) dot[j] += qv[t][j] * kv;
+            }
+#pragma unroll
+            for (int j = 0; j < NREP; ++j) {
+                dot[j] += dpp<kDppXor1>(dot[j]);
+                dot[j] += dpp<kDppXor2>(dot[j]);
+                dot[j] += dpp<kDppHalfMirror>(dot[j]);
+                if constexpr (LPR >= 16) dot[j] += dpp<kDppMirror>(dot[j]);
+                if constexpr (LPR >= 32) dot[j] += __shfl_xor(dot[j], 16, 64);
+                dot[j] = s_i < nvalid ? dot[j] * scale : -INFINITY;
+            }
+            if (kl == 0) {
+#pragma unroll
+                for (int j4 = 0; j4 < NR4; ++j4)
+                    *reinterpret_cast<float4*>(&s_p[s_i][4 * j4]) =
+                        make_float4(dot[4 * j4], dot[4 * j4 + 1], dot[4 * j4 + 2], dot[4 * j4 + 3]);
+            }
         }
     }
     __syncthreads();
@@ -324,12 +357,20 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
         *reinterpret_cast<float4*>(&s_red[rg][j][cg * 4]) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
     __syncthreads();
     T* op = o + (static_cast<size_t>(n) * H_q + static_cast<size_t>(h) * NREP) * D;
-    for (int idx = tid; idx < NREP * D; idx += kDecThreads) {
-        const int j = idx / D, c = idx % D;
-        float sum = 0.f;
+    for (int idx = 2 * tid; idx < NREP * D; idx += 2 * kDecThreads) {
+        const int j = idx / D, c = idx % D;  // c is even: the pair stays in one head
+        float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-        for (int r = 0; r < RG; ++r) sum += s_red[r][j][c];
-        op[idx] = from_f32<T>(sum);
+        for (int r = 0; r < RG; ++r) {
+            const float2 x = *reinterpret_cast<const float2*>(&s_red[r][j][c]);
+            s0 += x.x;
+            s1 += x.y;
+        }
+        if constexpr (sizeof(T) == 2)
+            *reinterpret_cast<uint32_t*>(op + idx) =
+                static_cast<uint32_t>(from_f32<T>(s0)) | (static_cast<uint32_t>(from_f32<T>(s1)) << 16);
+        else
+            *reinterpret_cast<float2*>(op + idx) = make_float2(s0, s1);
     }
 
     // ---- ring slot <- (k, v), bit copy of the inputs
@@ -337,16 +378,10 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
     T* rvw = ring_v + ((static_cast<size_t>(n) * H_kv + h) * window + slot) * D;
     if (tid < D) *reinterpret_cast<Pair*>((tid < D / 2 ? rkw : rvw) + 2 * (tid % (D / 2))) = kvin;
 
-    // ---- the last of the H_kv workgroups of sequence n advances pos[n].
-    // Every wave of every workgroup consumed pos before its first barrier, so
-    // the counter needs atomicity only: a relaxed atomic does not wait for
-    // this workgroup's state stores to complete.
-    if (tid == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(&sync[n], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == static_cast<uint32_t>(H_kv - 1)) {
-            sync[n] = 0u;
-            pos[n] = p + 1;
-        }
+    // ---- the last of the H_kv workgroups of sequence n to arrive advances pos[n]
+    if (tid == 0 && prev == static_cast<uint32_t>(H_kv - 1)) {
+        sync[n] = 0u;
+        pos[n] = p + 1;
     }
 }
 
