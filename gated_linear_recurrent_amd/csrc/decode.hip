@@ -40,6 +40,14 @@ __device__ __forceinline__ float dec_wave_sum(float v) {
     return v + __shfl_xor(v, 32, 64);
 }
 
+// Per 4-lane block of a wave (lanes 4b .. 4b+3), register i of lane 4b+j
+// accumulates a[lane 4b+i] * b[lane 4b+j]: sixteen independent 4 x 4 outer
+// products in one fp32 matrix instruction.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 outer4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
+}
+
 template <typename T, int D, int GATE, int NREP>
 __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2) void decode_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -291,10 +299,18 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
     }
     __syncthreads();
 
-    // ---- sum_s p_s v_s (the new token's value from LDS)
-    float acc[NRP][4];
+    // ---- sum_s p_s v_s (the new token's value from LDS). Both this and
+    // phi(q) S below are head x column outer products summed over a slot or a
+    // state row, on the matrix cores: in 4-lane block b (four consecutive
+    // column groups of one row group) lane 4b+i brings the weight of head
+    // 4 hg + i, lane 4b+j the value of its own column, so register i of acc[hg][e]
+    // collects head 4 hg + i at this thread's column 4 cg + e.
+    const int hq = tid & 3;
+    f32x4 acc[NR4][4];
 #pragma unroll
-    for (int j = 0; j < NRP; ++j) acc[j][0] = acc[j][1] = acc[j][2] = acc[j][3] = 0.f;
+    for (int hg = 0; hg < NR4; ++hg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[hg][e] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
         const int s = rg + i * RG;
@@ -315,13 +331,10 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
             for (int e = 0; e < 4; ++e) vr[e] = s_v[cg * 4 + e];
         }
 #pragma unroll
-        for (int j4 = 0; j4 < NR4; ++j4) {
-            const float4 p4 = *reinterpret_cast<const float4*>(&s_p[s][4 * j4]);  // 0 outside the window
-            const float ps[4] = {p4.x, p4.y, p4.z, p4.w};
+        for (int hg = 0; hg < NR4; ++hg) {
+            const float a = s_p[s][4 * hg + hq];  // 0 outside the window
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[4 * j4 + jj][e] += ps[jj] * vr[e];
+            for (int e = 0; e < 4; ++e) acc[hg][e] = outer4(a, vr[e], acc[hg][e]);
         }
     }
 
@@ -340,21 +353,18 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
         st.w = g * st.w + pk * v4.w;
         *reinterpret_cast<float4*>(Sp + (r * D + cg * 4)) = st;
 #pragma unroll
-        for (int j4 = 0; j4 < NR4; ++j4) {
-            const float4 pq = *reinterpret_cast<const float4*>(&s_phiq[r][4 * j4]);
-            const float pqs[4] = {pq.x, pq.y, pq.z, pq.w};
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                acc[4 * j4 + jj][0] += pqs[jj] * st.x;
-                acc[4 * j4 + jj][1] += pqs[jj] * st.y;
-                acc[4 * j4 + jj][2] += pqs[jj] * st.z;
-                acc[4 * j4 + jj][3] += pqs[jj] * st.w;
-            }
+        for (int hg = 0; hg < NR4; ++hg) {
+            const float a = s_phiq[r][4 * hg + hq];
+            acc[hg][0] = outer4(a, st.x, acc[hg][0]);
+            acc[hg][1] = outer4(a, st.y, acc[hg][1]);
+            acc[hg][2] = outer4(a, st.z, acc[hg][2]);
+            acc[hg][3] = outer4(a, st.w, acc[hg][3]);
         }
     }
 #pragma unroll
     for (int j = 0; j < NREP; ++j)
-        *reinterpret_cast<float4*>(&s_red[rg][j][cg * 4]) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+        *reinterpret_cast<float4*>(&s_red[rg][j][cg * 4]) =
+            make_float4(acc[j / 4][0][j % 4], acc[j / 4][1][j % 4], acc[j / 4][2][j % 4], acc[j / 4][3][j % 4]);
     __syncthreads();
     T* op = o + (static_cast<size_t>(n) * H_q + static_cast<size_t>(h) * NREP) * D;
     for (int idx = 2 * tid; idx < NREP * D; idx += 2 * kDecThreads) {
