@@ -7,6 +7,7 @@ from .liger_ref import (  # noqa: F401
     SCALAR_MEAN,
     VECTOR_AVGPOOL4,
     decode_step,
+    full_attention,
     gate,
     pool_scalar_mean,
     pool_vector_avg4,

@@ -42,6 +42,11 @@ Sources (the page titles and sections are cited, nothing else):
   GQA      query head h reads key/value head h // (H_q // H_kv); the state is
            kept per key/value head (the pages are silent; the plainest reading).
 
+full     the hybrid's standard softmax attention layer (one after every few
+attention Liger blocks: [Notes] section "Liger 整体架构", inter-layer hybrid):
+           causal softmax attention of raw q over every earlier key, the
+           current one included, scale 1/sqrt(d), the same GQA head map.
+
 Decode keeps (S, ring of the last `window` keys/values, pos) per sequence: the
 fixed-size state that linear decoding carries instead of a growing KV cache
 ([News] 実験分析: constant memory at long context). Token t of a sequence
@@ -242,3 +247,28 @@ def prefill_continue(q, k, v, S0, ring_k, ring_v, pos, gate_mode, alpha, *, gate
                                             gate_override=gate_override)
     return o, S, rk, rv, p
 
+
+
+def full_attention(q, k, v):
+    """Causal softmax attention over all earlier keys (the hybrid's softmax layer).
+
+    o_t = sum_{j <= t} softmax_j(q_t . k_j / sqrt(d)) v_j for every query head,
+    query head h reading key/value head h // (H_q // H_kv) ([Notes] section
+    "Liger 整体架构": a standard softmax attention block between Liger blocks).
+    q: [B, T, H_q, d]; k, v: [B, T, H_kv, d]. Returns o [B, T, H_q, d].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, H_q, d = q.shape
+    H_kv = k.shape[2]
+    if H_q % H_kv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    n_rep = H_q // H_kv
+    scale = 1.0 / np.sqrt(d)
+    qg = q.reshape(B, T, H_kv, n_rep, d)
+    o = np.empty((B, T, H_kv, n_rep, d))
+    for t in range(T):
+        kw = k[:, :t + 1].transpose(0, 2, 3, 1)            # [B, H_kv, d, t+1]
+        vw = v[:, :t + 1].transpose(0, 2, 1, 3)            # [B, H_kv, t+1, d]
+        p = softmax(np.matmul(qg[:, t], kw) * scale)       # [B, H_kv, n_rep, t+1]
+        o[:, t] = np.matmul(p, vw)
+    return o.reshape(B, T, H_q, d)

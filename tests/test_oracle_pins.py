@@ -184,6 +184,56 @@ def test_full_window_equals_library_causal_attention(n_rep):
     assert _close(o_swa, ref, rtol=1e-12)
 
 
+@pytest.mark.parametrize("n_rep", [1, 4])
+def test_full_attention_equals_library_causal_attention(n_rep):
+    """The hybrid's softmax layer against torch's scaled_dot_product_attention.
+
+    float64, CPU, is_causal, scale 1/sqrt(d), the key/value head repeated for
+    its n_rep query heads. Catches a wrong scale, mask or head map.
+    """
+    rng = np.random.default_rng(11 + n_rep)
+    B, T, H_kv, d = 2, 37, 2, 16
+    q = rng.standard_normal((B, T, H_kv * n_rep, d)) * 2.0
+    k = rng.standard_normal((B, T, H_kv, d))
+    v = rng.standard_normal((B, T, H_kv, d))
+    o = oracle.full_attention(q, k, v)
+    tq = torch.from_numpy(q).transpose(1, 2)
+    tk = torch.from_numpy(k).transpose(1, 2).repeat_interleave(n_rep, dim=1)
+    tv = torch.from_numpy(v).transpose(1, 2).repeat_interleave(n_rep, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, is_causal=True, scale=1.0 / math.sqrt(d)).transpose(1, 2).numpy()
+    assert _close(o, ref, rtol=1e-12)
+
+
+def test_full_attention_equals_unbounded_window():
+    """The softmax layer is the Liger SWA with a window longer than the sequence."""
+    rng = np.random.default_rng(5)
+    B, T, H_kv, n_rep, d = 1, 29, 2, 2, 8
+    q = rng.standard_normal((B, T, H_kv * n_rep, d))
+    k = rng.standard_normal((B, T, H_kv, d))
+    v = rng.standard_normal((B, T, H_kv, d))
+    _, _, _, o_swa = oracle.prefill(q, k, v, oracle.SCALAR_MEAN, T, 0.0, return_parts=True)
+    assert _close(oracle.full_attention(q, k, v), o_swa, rtol=1e-12)
+
+
+def test_full_attention_closed_forms():
+    """Equal keys give uniform weights: o_t is the running mean of v_0..v_t.
+    The first token attends to itself alone: o_0 = v_0. Catches an off-by-one
+    in the causal range (the mean would include one value too many or few)."""
+    rng = np.random.default_rng(3)
+    B, T, H_kv, n_rep, d = 2, 17, 1, 3, 8
+    q = rng.standard_normal((B, T, H_kv * n_rep, d))
+    k = np.broadcast_to(rng.standard_normal((B, 1, H_kv, d)), (B, T, H_kv, d))
+    v = rng.standard_normal((B, T, H_kv, d))
+    o = oracle.full_attention(q, k, v)
+    run_mean = np.cumsum(v, axis=1) / np.arange(1, T + 1)[None, :, None, None]
+    for h in range(H_kv * n_rep):
+        assert _close(o[:, :, h], run_mean[:, :, h // n_rep], rtol=1e-12)
+    o2 = oracle.full_attention(rng.standard_normal((B, T, H_kv * n_rep, d)), rng.standard_normal((B, T, H_kv, d)), v)
+    for h in range(H_kv * n_rep):
+        assert _close(o2[:, 0, h], v[:, 0, h // n_rep], rtol=1e-12)
+
+
 def test_alpha_is_affine_and_endpoints():
     """Pin 4: o(alpha) = alpha o(1) + (1-alpha) o(0); alpha=1 pure GRM, 0 pure SWA."""
     x = prefill_inputs(B=1, T=40, H_q=4, H_kv=2, d=8, dtype="f32", seed=3)
