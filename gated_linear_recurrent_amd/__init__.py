@@ -44,6 +44,7 @@ EXPORTED = (
     "liger_attn_prefill_continue",
     "liger_attn_decode_step",
     "liger_kv_ring_fill",
+    "liger_attn_full_causal",
     "liger_last_error",
 )
 
@@ -94,6 +95,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.liger_attn_decode_step.restype = i32
     lib.liger_kv_ring_fill.argtypes = [vp, vp, shp, ring, vp]
     lib.liger_kv_ring_fill.restype = i32
+    lib.liger_attn_full_causal.argtypes = [vp, vp, vp, shp, vp, vp]
+    lib.liger_attn_full_causal.restype = i32
     lib.liger_last_error.argtypes = []
     lib.liger_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -226,6 +229,19 @@ def liger_attn_prefill_continue(q, k, v, S0, ring: KVRing, gate_mode: int, alpha
                                            alpha, ctypes.byref(shp), _ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes,
                                            _stream(stream)))
     return o, S_T
+
+
+def liger_attn_full_causal(q, k, v, *, o=None, stream=None):
+    """The hybrid's softmax layer: q [B,T,H_q,d], k/v [B,T,H_kv,d] (bf16); returns o."""
+    torch = _torch()
+    lib = load_library()
+    B, T, H_q, d = q.shape
+    H_kv = k.shape[2]
+    shp = make_shape(B, T, H_q, H_kv, d, _dtype_code(q))
+    if o is None:
+        o = torch.empty_like(q)
+    _check(lib.liger_attn_full_causal(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(shp), _ptr(o), _stream(stream)))
+    return o
 
 
 def liger_attn_decode_step(q, k, v, S, ring: KVRing, gate_mode: int, alpha: float, *, o=None, stream=None):

@@ -263,6 +263,34 @@ liger_status liger_attn_decode_step(const void* q, const void* k, const void* v,
     return map_hip(liger::launch_decode_step(a), "decode launch");
 }
 
+liger_status liger_attn_full_causal(const void* q, const void* k, const void* v, const liger_shape* shape,
+                                    void* o, void* stream) {
+    LIGER_TRY(check_shape(shape, true));
+    if (shape->dtype != LIGER_BF16) return fail(LIGER_E_UNSUPPORTED, "full causal attention is built for bf16 only");
+    const int n_rep = shape->H_q / shape->H_kv;
+    if (n_rep != 1 && n_rep != 2 && n_rep != 4 && n_rep != 8)
+        return fail(LIGER_E_UNSUPPORTED, "full causal attention is built for H_q / H_kv in {1, 2, 4, 8}");
+    if ((shape->T + 63) / 64 > 2147483647LL) return fail(LIGER_E_INVALID_ARG, "T too large");
+    LIGER_TRY(check_ptr(q, "q"));
+    LIGER_TRY(check_ptr(k, "k"));
+    LIGER_TRY(check_ptr(v, "v"));
+    LIGER_TRY(check_ptr(o, "o"));
+    if (o == q || o == k || o == v) return fail(LIGER_E_INVALID_ARG, "o must not alias q, k or v");
+    liger::FullAttnArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.B = shape->B;
+    a.T = shape->T;
+    a.H_q = shape->H_q;
+    a.H_kv = shape->H_kv;
+    a.n_rep = n_rep;
+    a.d = shape->d;
+    a.stream = stream;
+    return map_hip(liger::launch_full_attn(a), "full attention launch");
+}
+
 liger_status liger_kv_ring_fill(const void* k, const void* v, const liger_shape* shape,
                                 const liger_kv_ring* kv_ring, void* stream) {
     LIGER_TRY(check_shape(shape, true));

@@ -1,0 +1,214 @@
+// Full causal softmax attention for gfx950: the standard softmax attention
+// layer that the inter-layer hybrid places between Liger blocks (paper-notes
+// page "Liger: Linearizing Large Language Models to Gated Recurrent
+// Structures", section "Liger 整体架构"):
+//   o_i = sum_{j <= i} softmax_j(q_i . k_j / sqrt(d)) v_j ,
+// query head h reading key/value head h / n_rep. bf16 in and out, fp32
+// accumulation.
+//
+// One workgroup per (64-query block, group of up to four query heads that
+// share a key/value head): two waves per head, 32 queries each, so every
+// 64-key K/V tile staged in LDS serves all the heads of the group. Key
+// blocks 0 .. the diagonal are walked with an online softmax (running row
+// maximum in log2 units, running sum kept per lane and reduced once at the
+// end). Scores are formed as S^T = K Q^T, so a lane holds four keys of one
+// query and the probabilities pack straight into the key-indexed operand of
+// O^T += V^T P (V^T read from the token-major tile with transposing loads).
+// Query blocks are launched heaviest (last) first.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace liger {
+
+template <int D, int HPW>
+__global__ __launch_bounds__(128 * HPW) void full_attn_kernel(FullAttnArgs p) {
+    typedef Mfma<bf16_t> M;
+    typedef M::frag Frag;
+    constexpr int NW = 2 * HPW;         // waves
+    constexpr int NTH = 64 * NW;        // threads
+    constexpr int KS = D / M::KSTEP;    // k-steps over the head dimension
+    constexpr int NT = D / 16;          // 16-wide output column tiles
+    constexpr int DP = D + 8;           // pitch of the K tile (rows 4 banks apart)
+    constexpr int VP = D + 16;          // pitch of the V tile (transposing reads)
+    constexpr int PPR = D / 8;          // 16-byte pieces per row
+    constexpr int NPC = 64 * PPR / NTH;  // pieces of each tile per thread
+    static_assert(NPC * NTH == 64 * PPR, "tile pieces must divide over the threads");
+
+    __shared__ __align__(16) bf16_t sK[2][64 * DP];
+    __shared__ __align__(16) bf16_t sV[2][64 * VP];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, g = lane >> 4;
+    const int64_t T = p.T;
+    const int nqb = static_cast<int>((T + 63) / 64);
+    const int qb = nqb - 1 - static_cast<int>(blockIdx.x);
+    const int hq = static_cast<int>(blockIdx.y) * HPW + wave / 2;
+    const int hk = static_cast<int>(blockIdx.y) * HPW / p.n_rep;
+    const int64_t b = blockIdx.z;
+    const int qoff = 32 * (wave & 1);   // this wave's queries within the block
+    const bf16_t* q = static_cast<const bf16_t*>(p.q);
+    const bf16_t* kg = static_cast<const bf16_t*>(p.k) + (b * T * p.H_kv + hk) * D;
+    const bf16_t* vg = static_cast<const bf16_t*>(p.v) + (b * T * p.H_kv + hk) * D;
+    const int64_t kv_stride = static_cast<int64_t>(p.H_kv) * D;
+
+    // query fragments: query 64 qb + qoff + 16 s + col, channels 32 k + 8 g ..
+    Frag qf[2][KS];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int64_t row = 64 * static_cast<int64_t>(qb) + qoff + 16 * s + col;
+        const bf16_t* qr = q + ((b * T + (row < T ? row : 0)) * p.H_q + hq) * D + 8 * g;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) qf[s][k] = row < T ? M::load(qr + M::KSTEP * k) : M::zero();
+    }
+
+    uint4 kr[NPC], vr[NPC];
+    auto issue = [&](int kb) {
+#pragma unroll
+        for (int n = 0; n < NPC; ++n) {
+            const int idx = tid + n * NTH;
+            const int64_t row = 64 * static_cast<int64_t>(kb) + idx / PPR;
+            const int c0 = (idx % PPR) * 8;
+            kr[n] = make_uint4(0, 0, 0, 0);
+            vr[n] = make_uint4(0, 0, 0, 0);
+            if (row < T) {
+                kr[n] = *reinterpret_cast<const uint4*>(kg + row * kv_stride + c0);
+                vr[n] = *reinterpret_cast<const uint4*>(vg + row * kv_stride + c0);
+            }
+        }
+    };
+    auto commit = [&](int buf) {
+#pragma unroll
+        for (int n = 0; n < NPC; ++n) {
+            const int idx = tid + n * NTH;
+            *reinterpret_cast<uint4*>(&sK[buf][(idx / PPR) * DP + (idx % PPR) * 8]) = kr[n];
+            *reinterpret_cast<uint4*>(&sV[buf][(idx / PPR) * VP + (idx % PPR) * 8]) = vr[n];
+        }
+    };
+
+    f32x4_t acc[2][NT];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[s][t] = zero4();
+    float m[2] = {-INFINITY, -INFINITY};  // running maximum, log2 units
+    float l[2] = {0.f, 0.f};              // running sum of this lane's keys
+    const float c = kLog2e * rsqrtf(static_cast<float>(D));
+
+    issue(0);
+    commit(0);
+    __syncthreads();
+    for (int kb = 0; kb <= qb; ++kb) {
+        const int cur = kb & 1;
+        if (kb < qb) issue(kb + 1);
+        const bool diag = kb == qb;
+        // ---- S^T = K Q^T: lane (col, g) holds keys 16 kt + 4 g + r of query col
+        f32x4_t sc[2][4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            sc[0][kt] = zero4();
+            sc[1][kt] = zero4();
+            // on the diagonal block a key tile past a query tile is masked whole
+            const bool live0 = !diag || kt <= 2 * (wave & 1);
+            const bool live1 = !diag || kt <= 2 * (wave & 1) + 1;
+            if (!live1) continue;
+            const bf16_t* krow = &sK[cur][(16 * kt + col) * DP + 8 * g];
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                const Frag a = M::load(krow + M::KSTEP * k);
+                if (live0) sc[0][kt] = M::mma(a, qf[0][k], sc[0][kt]);
+                sc[1][kt] = M::mma(a, qf[1][k], sc[1][kt]);
+            }
+        }
+        // ---- online softmax
+        Frag pf[2][2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float x = sc[s][kt][r];
+                    if (diag && 16 * kt + 4 * g + r > qoff + 16 * s + col) x = -INFINITY;
+                    sc[s][kt][r] = x;
+                    mx = fmaxf(mx, x);
+                }
+            // every query keeps at least one key (itself) on the diagonal block
+            const float mnew = fmaxf(m[s], group4_max(mx) * c);
+            const float alpha = fast_exp2(m[s] - mnew);
+            m[s] = mnew;
+            float ls = 0.f;
+            float pv[4][4];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float e = fast_exp2(fmaf(sc[s][kt][r], c, -mnew));  // exp2(-inf) = 0 when masked
+                    pv[kt][r] = e;
+                    ls += e;
+                }
+            l[s] = fmaf(l[s], alpha, ls);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[s][t] *= alpha;
+#pragma unroll
+            for (int G = 0; G < 2; ++G) {
+                const float v8[8] = {pv[2 * G][0], pv[2 * G][1], pv[2 * G][2], pv[2 * G][3],
+                                     pv[2 * G + 1][0], pv[2 * G + 1][1], pv[2 * G + 1][2], pv[2 * G + 1][3]};
+                pf[s][G] = M::pack(v8);
+            }
+        }
+        // ---- O^T += V^T P over the two 32-key groups
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int G = 0; G < 2; ++G) {
+                const Frag a = load_key_frag(sV[cur], VP, 32 * G, 16 * t, lane);
+                acc[0][t] = M::mma(a, pf[0][G], acc[0][t]);
+                acc[1][t] = M::mma(a, pf[1][G], acc[1][t]);
+            }
+        // the next tile goes to the other buffer, last read one iteration ago
+        if (kb < qb) commit(cur ^ 1);
+        __syncthreads();
+    }
+
+    // ---- normalise and store: lane (col, g) holds channels 16 t + 4 g + r of query col
+    bf16_t* o = static_cast<bf16_t*>(p.o);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int64_t row = 64 * static_cast<int64_t>(qb) + qoff + 16 * s + col;
+        const float inv = fast_rcp(group4_sum(l[s]));
+        if (row >= T) continue;
+        bf16_t* orow = o + ((b * T + row) * p.H_q + hq) * D + 4 * g;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            *reinterpret_cast<uint2*>(orow + 16 * t) =
+                make_uint2(pack_bf16x2(acc[s][t][0] * inv, acc[s][t][1] * inv),
+                           pack_bf16x2(acc[s][t][2] * inv, acc[s][t][3] * inv));
+    }
+}
+
+template <int D, int HPW>
+static hipError_t launch_full_t(const FullAttnArgs& a) {
+    const unsigned nqb = static_cast<unsigned>((a.T + 63) / 64);
+    dim3 grid(nqb, static_cast<unsigned>(a.H_q / HPW), static_cast<unsigned>(a.B));
+    hipLaunchKernelGGL((full_attn_kernel<D, HPW>), grid, dim3(128 * HPW), 0, static_cast<hipStream_t>(a.stream), a);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_full_d(const FullAttnArgs& a) {
+    switch (a.n_rep) {
+        case 1: return launch_full_t<D, 1>(a);
+        case 2: return launch_full_t<D, 2>(a);
+        case 4:
+        case 8: return launch_full_t<D, 4>(a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_full_attn(const FullAttnArgs& a) {
+    if (a.T == 0) return hipSuccess;
+    return a.d == 64 ? launch_full_d<64>(a) : launch_full_d<128>(a);
+}
+
+}  // namespace liger

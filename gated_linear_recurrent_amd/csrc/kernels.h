@@ -46,6 +46,21 @@ struct RingFillArgs {
     void* stream;
 };
 
+// Full causal softmax attention (bf16). q, o: [B, T, H_q, d]; k, v: [B, T, H_kv, d].
+struct FullAttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    int64_t B;
+    int64_t T;
+    int H_q;
+    int H_kv;
+    int n_rep;
+    int d;
+    void* stream;
+};
+
 // Segment plan of the chunked prefill: chunks of 64 tokens grouped into
 // n_seg segments of cps chunks (the last segment may be shorter).
 // Workspace: carry records (state entering each segment but the first, plus
@@ -97,5 +112,6 @@ hipError_t launch_ring_fill(const RingFillArgs& a);
 // window, older slots keep their tokens, then pos += T.
 hipError_t launch_ring_append(const RingFillArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
+hipError_t launch_full_attn(const FullAttnArgs& a);
 
 }  // namespace liger

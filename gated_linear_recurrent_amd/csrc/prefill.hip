@@ -45,33 +45,6 @@ __device__ __forceinline__ int ltid() {
     return t;
 }
 
-// Channel-major tiles ([c][64 keys]: V^T and the transposed state key operand)
-// store key j at position key_pos(j): inside each 32-key group the two
-// 16-key halves are interleaved in units of 4, so positions 8g .. 8g+7 of a
-// group hold keys 4g..4g+3 and 16+4g..16+4g+3. One 16-byte read then yields
-// the operand of a key-tile pair in the MFMA order used for the score
-// matrices, and two consecutive keys (2m, 2m+1) stay adjacent.
-__device__ __forceinline__ int key_pos(int j) {
-    return (j & 32) | (((j & 15) >> 2) << 3) | (((j >> 4) & 1) << 2) | (j & 3);
-}
-
-// bf16 operand fragment over keys (the contraction index) from a token-major
-// [key][channel] tile, read with two transposing LDS loads (ds_read_b64_tr_b16:
-// in each 16-lane group, lane i supplies 4 consecutive elements of a row and
-// lane 4a+b receives element b of the rows supplied by lanes a, a+4, a+8, a+12).
-// Lane (n, g) gets channel c0 + n of keys kb + 4g + 0..3 and kb + 16 + 4g + 0..3,
-// the key_pos order of a 32-key group used by the score operands.
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) short4_t lds_short4_t;
-__device__ __forceinline__ bf16x8_t load_key_frag(const bf16_t* tile, int pitch, int kb, int c0, int lane) {
-    const int i = lane & 15, g = lane >> 4;
-    const bf16_t* p0 = tile + (kb + 4 * g + (i >> 2)) * pitch + c0 + 4 * (i & 3);
-    const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p0));
-    const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p0 + 16 * pitch));
-    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
-    return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
-}
-
 // ------------------------------------------------------------- LDS layout
 template <typename T, int D, int GATE, bool FULL>
 struct Layout {

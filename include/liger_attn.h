@@ -203,6 +203,20 @@ liger_status liger_kv_ring_fill(const void* k, const void* v,
                                 const liger_shape* shape,
                                 const liger_kv_ring* kv_ring, void* stream);
 
+/*
+ * The hybrid's standard softmax attention layer (paper-notes page "Liger:
+ * Linearizing Large Language Models to Gated Recurrent Structures", section
+ * "Liger 整体架构": a softmax attention block after every few Liger blocks):
+ *   o_t = sum_{j <= t} softmax_j(q_t . k_j / sqrt(d)) v_j
+ * for every query head h, which reads key/value head h / (H_q / H_kv).
+ * q, o [B, T, H_q, d]; k, v [B, T, H_kv, d]; contiguous, device memory,
+ * 16-byte aligned, bf16 only (fp32 is LIGER_E_UNSUPPORTED), d in {64, 128},
+ * H_q / H_kv in {1, 2, 4, 8}. o must not alias the inputs. No workspace;
+ * enqueued on `stream` (NULL: the default stream), nothing is synchronised.
+ */
+liger_status liger_attn_full_causal(const void* q, const void* k, const void* v,
+                                    const liger_shape* shape, void* o, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* liger_last_error(void);
 

@@ -201,3 +201,20 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(gla.LigerError):
         gla.liger_attn_prefill(q, k, k, 1, 64, 0.5, o=q.clone(), S_T=torch.zeros(1, 1, 128, 128),
                                workspace=None)
+
+
+@pytest.mark.parametrize("kw,ptrs,code", [
+    (dict(dtype=gla.LIGER_F32), {}, gla.LIGER_E_UNSUPPORTED),
+    (dict(H_q=3, H_kv=1), {}, gla.LIGER_E_UNSUPPORTED),
+    (dict(H_q=6, H_kv=4), {}, gla.LIGER_E_INVALID_ARG),
+    (dict(d=96), {}, gla.LIGER_E_UNSUPPORTED),
+    (dict(T=0), {}, gla.LIGER_E_INVALID_ARG),
+    ({}, dict(q=None), gla.LIGER_E_INVALID_ARG),
+    ({}, dict(v=FAKE + 2), gla.LIGER_E_INVALID_ARG),
+    ({}, dict(o=FAKE), gla.LIGER_E_INVALID_ARG),
+])
+def test_full_causal_rejects_bad_arguments(lib, kw, ptrs, code):
+    p = dict(q=FAKE, k=FAKE + 4096, v=FAKE + 8192, o=FAKE + 12288)
+    p.update(ptrs)
+    st = lib.liger_attn_full_causal(p["q"], p["k"], p["v"], ctypes.byref(_shape(**kw)), p["o"], None)
+    assert st == code, gla.liger_last_error()
