@@ -41,10 +41,25 @@ __global__ __launch_bounds__(128 * HPW) void full_attn_kernel(FullAttnArgs p) {
     const int col = lane & 15, g = lane >> 4;
     const int64_t T = p.T;
     const int nqb = static_cast<int>((T + 63) / 64);
-    const int qb = nqb - 1 - static_cast<int>(blockIdx.x);
-    const int hq = static_cast<int>(blockIdx.y) * HPW + wave / 2;
-    const int hk = static_cast<int>(blockIdx.y) * HPW / p.n_rep;
-    const int64_t b = blockIdx.z;
+    // Workgroup L runs on XCD L mod 8 (round-robin dispatch). When the
+    // (sequence, head group) count is a multiple of 8, each group stays on one
+    // XCD, so its K/V (T x d per tensor) is shared in that XCD's L2; query
+    // blocks go heaviest (last) first.
+    const int L = static_cast<int>(blockIdx.x);
+    int grp, qi;
+    if (p.ngroups % 8 == 0) {
+        const int per = p.ngroups / 8, j = L / 8;
+        grp = (L % 8) + 8 * (j % per);
+        qi = j / per;
+    } else {
+        grp = L % p.ngroups;
+        qi = L / p.ngroups;
+    }
+    const int qb = nqb - 1 - qi;
+    const int hgrp = grp % (p.H_q / HPW);
+    const int64_t b = grp / (p.H_q / HPW);
+    const int hq = hgrp * HPW + wave / 2;
+    const int hk = hgrp * HPW / p.n_rep;
     const int qoff = 32 * (wave & 1);   // this wave's queries within the block
     const bf16_t* q = static_cast<const bf16_t*>(p.q);
     const bf16_t* kg = static_cast<const bf16_t*>(p.k) + (b * T * p.H_kv + hk) * D;
@@ -133,8 +148,14 @@ __global__ __launch_bounds__(128 * HPW) void full_attn_kernel(FullAttnArgs p) {
                     sc[s][kt][r] = x;
                     mx = fmaxf(mx, x);
                 }
-            // every query keeps at least one key (itself) on the diagonal block
-            const float mnew = fmaxf(m[s], group4_max(mx) * c);
+            // Every query keeps at least one key (itself) on the diagonal
+            // block. The running maximum moves only when the block's exceeds
+            // it by more than 8 (log2 units): probabilities up to 2^8 are
+            // exact enough in fp32 sums and bf16 operands, and the O rescale
+            // is skipped whenever no query of the wave moved.
+            const float mblk = group4_max(mx) * c;
+            const bool grow = mblk > m[s] + 8.0f;
+            const float mnew = grow ? mblk : m[s];
             const float alpha = fast_exp2(m[s] - mnew);
             m[s] = mnew;
             float ls = 0.f;
@@ -148,8 +169,10 @@ __global__ __launch_bounds__(128 * HPW) void full_attn_kernel(FullAttnArgs p) {
                     ls += e;
                 }
             l[s] = fmaf(l[s], alpha, ls);
+            if (__any(grow)) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t) acc[s][t] *= alpha;
+                for (int t = 0; t < NT; ++t) acc[s][t] *= alpha;
+            }
 #pragma unroll
             for (int G = 0; G < 2; ++G) {
                 const float v8[8] = {pv[2 * G][0], pv[2 * G][1], pv[2 * G][2], pv[2 * G][3],
@@ -189,9 +212,12 @@ __global__ __launch_bounds__(128 * HPW) void full_attn_kernel(FullAttnArgs p) {
 
 template <int D, int HPW>
 static hipError_t launch_full_t(const FullAttnArgs& a) {
-    const unsigned nqb = static_cast<unsigned>((a.T + 63) / 64);
-    dim3 grid(nqb, static_cast<unsigned>(a.H_q / HPW), static_cast<unsigned>(a.B));
-    hipLaunchKernelGGL((full_attn_kernel<D, HPW>), grid, dim3(128 * HPW), 0, static_cast<hipStream_t>(a.stream), a);
+    FullAttnArgs p = a;
+    p.ngroups = static_cast<int>(a.B * (a.H_q / HPW));
+    const int64_t nwg = ((a.T + 63) / 64) * p.ngroups;
+    if (nwg > 2147483647LL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((full_attn_kernel<D, HPW>), dim3(static_cast<unsigned>(nwg)), dim3(128 * HPW), 0,
+                       static_cast<hipStream_t>(a.stream), p);
     return hipGetLastError();
 }
 

@@ -58,6 +58,7 @@ struct FullAttnArgs {
     int H_kv;
     int n_rep;
     int d;
+    int ngroups;  // B x (query-head groups); set by the launcher
     void* stream;
 };
 
