@@ -9,10 +9,11 @@ each one an untimed 512 MiB write evicts the 256 MB last-level cache, so
 the inputs come from HBM ("cold", the headline `value`, median step). The
 same steps without the eviction are reported as "hot". The JSON line also
 carries the roofline of the dominant kernel (the fused output kernel), the
-float64 CPU oracle on the host as a reported baseline, and the decode
-workload (64 sequences, Llama-3-8B heads, one token per step: eager
-launches, the same launches replayed from a captured HIP graph, and
-cold steps).
+float64 CPU oracle on the host as a reported baseline, the hybrid's full
+causal softmax attention layer on the same inputs (cold and hot, against
+the dense bf16 MFMA peak), and the decode workload (64 sequences,
+Llama-3-8B heads, one token per step: launched back to back, each between
+its own events, replayed from a captured HIP graph, and cold steps).
 
     python bench.py [--steps K] [--warmup W] [--decode-steps N]
 
@@ -34,6 +35,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PREFILL_WORKLOAD = "prefill_8b_b1_t8192_d128"
 DECODE_WORKLOAD = "decode_8b_n64_d128"
+FULL_WORKLOAD = "full_attn_8b_b1_t8192_d128"  # the softmax layer on the prefill workload's inputs
 CHUNK = 64
 SCRUB_BYTES = 512 << 20        # larger than the 256 MB last-level cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
@@ -105,6 +107,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-full", action="store_true", help="skip the full causal attention layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-tokens", type=int, default=8192)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -207,6 +210,40 @@ def main() -> int:
     log(f"[bench] prefill cold {ms_per_step * 1e3:.1f} us/step (hot {np.median(hot[:, 2]) * 1e3:.1f}); "
         f"output kernel {out_ms * 1e3:.1f} us ({achieved:.0f} GB/s); "
         f"carries cold {np.median(cold[:, 0]) * 1e3:.1f} us")
+
+    if not args.no_full:
+        # the hybrid's softmax layer on the same 8B inputs (q, k, v in HBM)
+        fo = torch.empty_like(q)
+        for _ in range(max(1, args.warmup // 2)):
+            gla.liger_attn_full_causal(q, k, v, o=fo)
+        torch.cuda.synchronize()
+        nfull = max(5, args.steps // 2)
+
+        def timed_full(cold_steps: bool):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nfull)]
+            for i, (e0, e1) in enumerate(ev):
+                if cold_steps:
+                    scrub.fill_(float(i))
+                e0.record()
+                gla.liger_attn_full_causal(q, k, v, o=fo)
+                e1.record()
+            torch.cuda.synchronize()
+            return np.array([a.elapsed_time(b) for a, b in ev])
+
+        fcold, fhot = timed_full(True), timed_full(False)
+        fflops = 4.0 * d * (T * (T + 1) / 2) * H_q * B  # q.k and p.v over the causal pairs
+        fms = float(np.mean(np.concatenate([fcold, fhot])))
+        fach = fflops / (fms * 1e-3) / 1e12
+        result["full_attention"] = {
+            "workload": FULL_WORKLOAD, "steps": nfull,
+            "cold": stats(fcold), "hot": stats(fhot),
+            "tokens_per_s": B * T / (float(np.median(fcold)) * 1e-3),
+            "roofline": {"bound": "mfma", "achieved": fach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": fach / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "full_attn_kernel",
+                         "kernel_ms": fms, "algorithmic_flops": fflops},
+        }
+        log(f"[bench] full attention {fms * 1e3:.1f} us ({fach:.0f} TFLOP/s, "
+            f"{100 * fach / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
 
     if not args.no_decode:
         dcfg = CONFIGS[DECODE_WORKLOAD]
