@@ -15,6 +15,8 @@
 // query and the probabilities pack straight into the key-indexed operand of
 // O^T += V^T P (V^T read from the token-major tile with transposing loads).
 // Query blocks are launched heaviest (last) first.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -112,10 +114,11 @@ __global__ __launch_bounds__(128 * HPW) void full_attn_kernel(FullAttnArgs p) {
     issue(0);
     commit(0);
     __syncthreads();
-    for (int kb = 0; kb <= qb; ++kb) {
+    // one key block; the diagonal block (the last) is compiled on its own
+    auto block = [&](int kb, auto diag_c) {
+        constexpr bool diag = decltype(diag_c)::value;
         const int cur = kb & 1;
-        if (kb < qb) issue(kb + 1);
-        const bool diag = kb == qb;
+        if (!diag) issue(kb + 1);
         // ---- S^T = K Q^T: lane (col, g) holds keys 16 kt + 4 g + r of query col
         f32x4_t sc[2][4];
 #pragma unroll
@@ -190,9 +193,11 @@ __global__ __launch_bounds__(128 * HPW) void full_attn_kernel(FullAttnArgs p) {
                 acc[1][t] = M::mma(a, pf[1][G], acc[1][t]);
             }
         // the next tile goes to the other buffer, last read one iteration ago
-        if (kb < qb) commit(cur ^ 1);
+        if (!diag) commit(cur ^ 1);
         __syncthreads();
-    }
+    };
+    for (int kb = 0; kb < qb; ++kb) block(kb, std::false_type{});
+    block(qb, std::true_type{});
 
     // ---- normalise and store: lane (col, g) holds channels 16 t + 4 g + r of query col
     bf16_t* o = static_cast<bf16_t*>(p.o);
