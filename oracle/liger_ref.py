@@ -42,6 +42,13 @@ Sources (the page titles and sections are cited, nothing else):
   GQA      query head h reads key/value head h // (H_q // H_kv); the state is
            kept per key/value head (the pages are silent; the plainest reading).
 
+sinks    meta-memory tokens (Japanese summary page of Lizard, section
+           "アンカーウィンドウアテンション"): n extra key/value pairs per key/value
+           head that every window's softmax also sees; they act as attention
+           sinks. The page gives no formula; the reading fixed here: the n
+           pairs are prepended to the window of every query, with the same
+           1/sqrt(d) scale and no causal or window mask, and they do not enter
+           the recurrence. Their values are synthetic inputs.
 full     the hybrid's standard softmax attention layer (one after every few
 attention Liger blocks: [Notes] section "Liger 整体架构", inter-layer hybrid):
            causal softmax attention of raw q over every earlier key, the
@@ -119,14 +126,26 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
+def _with_sinks(kw, vw, sink_k, sink_v, lead):
+    """Prepend the sink keys/values ([H_kv, n, d]) to a window's keys [..., d, L]
+    and values [..., L, d]; `lead` leading batch axes are broadcast."""
+    if sink_k is None:
+        return kw, vw
+    sk, sv = _f64(sink_k), _f64(sink_v)
+    skT = np.broadcast_to(sk.transpose(0, 2, 1), kw.shape[:lead] + sk.transpose(0, 2, 1).shape)
+    svb = np.broadcast_to(sv, vw.shape[:lead] + sv.shape)
+    return np.concatenate([skT, kw], axis=-1), np.concatenate([svb, vw], axis=-2)
+
+
 def prefill(q, k, v, gate_mode, window, alpha, *, gate_override=None,
-            S0=None, return_parts=False):
+            S0=None, return_parts=False, sink_k=None, sink_v=None):
     """Token-by-token Liger Attention over whole sequences.
 
     q: [B, T, H_q, d]; k, v: [B, T, H_kv, d]. Returns (o [B, T, H_q, d],
     S_T [B, H_kv, d, d]); with return_parts, also (o_grm, o_swa).
     `gate_override(k_t) -> g_t` replaces the pooled gate (test hook).
-    `S0` is the initial state (zero when None).
+    `S0` is the initial state (zero when None). `sink_k`, `sink_v`
+    ([H_kv, n, d]) are meta-memory tokens prepended to every window.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, T, H_q, d = q.shape
@@ -155,7 +174,8 @@ def prefill(q, k, v, gate_mode, window, alpha, *, gate_override=None,
         lo = max(0, t - window + 1)
         kw = k[:, lo:t + 1].transpose(0, 2, 3, 1)          # [B, H_kv, d, L]
         vw = v[:, lo:t + 1].transpose(0, 2, 1, 3)          # [B, H_kv, L, d]
-        p = softmax(np.matmul(qg[:, t], kw) * scale)       # [B, H_kv, n_rep, L]
+        kw, vw = _with_sinks(kw, vw, sink_k, sink_v, 1)    # sinks first: [.., n + L]
+        p = softmax(np.matmul(qg[:, t], kw) * scale)       # [B, H_kv, n_rep, n + L]
         o_swa[:, t] = np.matmul(p, vw)
     o_grm = o_grm.reshape(B, T, H_q, d)
     o_swa = o_swa.reshape(B, T, H_q, d)
@@ -182,14 +202,15 @@ def ring_fill(k, v, window):
 
 
 def decode_step(q, k, v, S, ring_k, ring_v, pos, gate_mode, alpha, *,
-                gate_override=None, return_parts=False):
+                gate_override=None, return_parts=False, sink_k=None, sink_v=None):
     """One token per sequence from the fixed-size decode state.
 
     q: [N, H_q, d]; k, v: [N, H_kv, d]; S: [N, H_kv, d, d];
     ring_k, ring_v: [N, H_kv, window, d]; pos: [N] tokens already consumed.
     Returns (o [N, H_q, d], S', ring_k', ring_v', pos + 1). The new token is
     token number pos[n]; it is written to slot pos[n] mod window and the
-    window covers tokens max(0, pos-window+1) .. pos (the new one included).
+    window covers tokens max(0, pos-window+1) .. pos (the new one included),
+    after the meta-memory tokens `sink_k`, `sink_v` ([H_kv, n, d]) if given.
     """
     q, kf, vf = _f64(q), _f64(k), _f64(v)
     N, H_q, d = q.shape
@@ -214,9 +235,10 @@ def decode_step(q, k, v, S, ring_k, ring_v, pos, gate_mode, alpha, *,
         ring_v_new[n, :, p_n % window] = v[n]
         toks = range(max(0, p_n - window + 1), p_n + 1)
         slots = [t % window for t in toks]
-        kw = _f64(ring_k_new[n][:, slots])                 # [H_kv, L, d]
-        vw = _f64(ring_v_new[n][:, slots])
-        p = softmax(np.matmul(qg[n], kw.transpose(0, 2, 1)) * scale)
+        kw = _f64(ring_k_new[n][:, slots]).transpose(0, 2, 1)   # [H_kv, d, L]
+        vw = _f64(ring_v_new[n][:, slots])                      # [H_kv, L, d]
+        kw, vw = _with_sinks(kw, vw, sink_k, sink_v, 0)
+        p = softmax(np.matmul(qg[n], kw) * scale)
         o_swa[n] = np.matmul(p, vw)
     o_grm = o_grm.reshape(N, H_q, d)
     o_swa = o_swa.reshape(N, H_q, d)
@@ -227,7 +249,8 @@ def decode_step(q, k, v, S, ring_k, ring_v, pos, gate_mode, alpha, *,
     return out
 
 
-def prefill_continue(q, k, v, S0, ring_k, ring_v, pos, gate_mode, alpha, *, gate_override=None):
+def prefill_continue(q, k, v, S0, ring_k, ring_v, pos, gate_mode, alpha, *, gate_override=None,
+                     sink_k=None, sink_v=None):
     """T more tokens per sequence after `pos` already consumed ones.
 
     The plain definition: T successive decode steps from the fixed-size state
@@ -244,7 +267,7 @@ def prefill_continue(q, k, v, S0, ring_k, ring_v, pos, gate_mode, alpha, *, gate
     o = np.empty((B, T, H_q, d))
     for t in range(T):
         o[:, t], S, rk, rv, p = decode_step(q[:, t], k[:, t], v[:, t], S, rk, rv, p, gate_mode, alpha,
-                                            gate_override=gate_override)
+                                            gate_override=gate_override, sink_k=sink_k, sink_v=sink_v)
     return o, S, rk, rv, p
 
 

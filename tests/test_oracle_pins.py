@@ -234,6 +234,75 @@ def test_full_attention_closed_forms():
         assert _close(o2[:, 0, h], v[:, 0, h // n_rep], rtol=1e-12)
 
 
+def _sink_inputs(rng, B, T, H_kv, n_rep, d, n):
+    q = rng.standard_normal((B, T, H_kv * n_rep, d))
+    k = rng.standard_normal((B, T, H_kv, d))
+    v = rng.standard_normal((B, T, H_kv, d))
+    sk = rng.standard_normal((H_kv, n, d))
+    sv = rng.standard_normal((H_kv, n, d))
+    return q, k, v, sk, sv
+
+
+@pytest.mark.parametrize("window,n", [(4, 1), (64, 3), (7, 16)])
+def test_sinks_are_prepended_tokens_bruteforce(window, n):
+    """Meta-memory tokens as n extra tokens placed before the sequence that
+    every query may see: an explicit [T, n + T] visibility mask and a plain
+    exp / sum over it, against the oracle's SWA with sinks. Catches sinks
+    that are windowed, causally masked, scaled differently or left out of
+    the normaliser."""
+    rng = np.random.default_rng(100 + window + n)
+    B, T, H_kv, n_rep, d = 2, 19, 2, 2, 8
+    q, k, v, sk, sv = _sink_inputs(rng, B, T, H_kv, n_rep, d, n)
+    _, _, _, o_swa = oracle.prefill(q, k, v, oracle.VECTOR_AVGPOOL4, window, 0.0, return_parts=True,
+                                    sink_k=sk, sink_v=sv)
+    ref = np.zeros_like(o_swa)
+    for b in range(B):
+        for h in range(H_kv * n_rep):
+            hk = h // n_rep
+            kk = np.concatenate([sk[hk], k[b, :, hk]])        # [n + T, d]
+            vv = np.concatenate([sv[hk], v[b, :, hk]])
+            for t in range(T):
+                vis = np.array([j < n or (t - window < j - n <= t) for j in range(n + T)])
+                w = np.exp(kk @ q[b, t, h] / math.sqrt(d)) * vis
+                ref[b, t, h] = (w / w.sum()) @ vv
+    assert _close(o_swa, ref, rtol=1e-12)
+
+
+def test_sinks_zero_keys_and_values_closed_form():
+    """n sinks with zero keys and values add e^0 = 1 each to the softmax
+    normaliser and nothing to the numerator: o_sink = o_plain * Z / (Z + n),
+    Z = sum over the window of e^{q.k/sqrt(d)}."""
+    rng = np.random.default_rng(9)
+    B, T, H_kv, n_rep, d, n, window = 1, 15, 1, 2, 8, 5, 6
+    q, k, v, _, _ = _sink_inputs(rng, B, T, H_kv, n_rep, d, n)
+    zk, zv = np.zeros((H_kv, n, d)), np.zeros((H_kv, n, d))
+    _, _, _, o_plain = oracle.prefill(q, k, v, oracle.SCALAR_MEAN, window, 0.0, return_parts=True)
+    _, _, _, o_sink = oracle.prefill(q, k, v, oracle.SCALAR_MEAN, window, 0.0, return_parts=True,
+                                     sink_k=zk, sink_v=zv)
+    for t in range(T):
+        lo = max(0, t - window + 1)
+        for h in range(H_kv * n_rep):
+            Z = np.exp(k[0, lo:t + 1, h // n_rep] @ q[0, t, h] / math.sqrt(d)).sum()
+            assert _close(o_sink[0, t, h], o_plain[0, t, h] * Z / (Z + n), rtol=1e-12)
+
+
+@pytest.mark.parametrize("mode", [oracle.SCALAR_MEAN, oracle.VECTOR_AVGPOOL4])
+def test_sinks_decode_continues_prefill(mode):
+    """Prefill(T0) then decode steps with the same sinks equals prefill(T0 + n)."""
+    rng = np.random.default_rng(21)
+    B, T, H_kv, n_rep, d, n, window = 2, 13, 2, 2, 8, 4, 5
+    q, k, v, sk, sv = _sink_inputs(rng, B, T, H_kv, n_rep, d, n)
+    T0 = 8
+    o_full, S_full = oracle.prefill(q, k, v, mode, window, 0.5, sink_k=sk, sink_v=sv)
+    _, S = oracle.prefill(q[:, :T0], k[:, :T0], v[:, :T0], mode, window, 0.5, sink_k=sk, sink_v=sv)
+    rk, rv, pos = oracle.ring_fill(k[:, :T0], v[:, :T0], window)
+    for t in range(T0, T):
+        o, S, rk, rv, pos = oracle.decode_step(q[:, t], k[:, t], v[:, t], S, rk, rv, pos, mode, 0.5,
+                                               sink_k=sk, sink_v=sv)
+        assert _close(o, o_full[:, t], rtol=1e-11)
+    assert _close(S, S_full, rtol=1e-11)
+
+
 def test_alpha_is_affine_and_endpoints():
     """Pin 4: o(alpha) = alpha o(1) + (1-alpha) o(0); alpha=1 pure GRM, 0 pure SWA."""
     x = prefill_inputs(B=1, T=40, H_q=4, H_kv=2, d=8, dtype="f32", seed=3)
