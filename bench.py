@@ -35,7 +35,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PREFILL_WORKLOAD = "prefill_8b_b1_t8192_d128"
 DECODE_WORKLOAD = "decode_8b_n64_d128"
-FULL_WORKLOAD = "full_attn_8b_b1_t8192_d128"  # the softmax layer on the prefill workload's inputs
+FULL_WORKLOAD = "full_attn_8b_b1_t8192_d128"
+N_SINKS = 16      # meta-memory tokens per key/value head in the sink measurements (synthetic, N(0, 1))
+SINK_SEED = 17  # the softmax layer on the prefill workload's inputs
 CHUNK = 64
 SCRUB_BYTES = 512 << 20        # larger than the 256 MB last-level cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
@@ -245,6 +247,34 @@ def main() -> int:
         log(f"[bench] full attention {fms * 1e3:.1f} us ({fach:.0f} TFLOP/s, "
             f"{100 * fach / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
 
+    # the same prefill with meta-memory sink tokens prepended to every window
+    rng = np.random.default_rng(SINK_SEED)
+    sink_np = [rng.standard_normal((H_kv, N_SINKS, d)).astype(np.float32) for _ in range(2)]
+    psinks = tuple(torch.from_numpy(a).to(dev).to(torch.bfloat16) for a in sink_np)
+
+    def prefill_sinks():
+        gla.liger_attn_prefill(q, k, v, gate, cfg["window"], cfg["alpha"], o=o, S_T=S_T, workspace=ws, sinks=psinks)
+
+    for _ in range(max(1, args.warmup // 2)):
+        prefill_sinks()
+    torch.cuda.synchronize()
+
+    def timed_sinks(cold_steps: bool):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i, (e0, e1) in enumerate(ev):
+            if cold_steps:
+                scrub.fill_(float(i))
+            e0.record()
+            prefill_sinks()
+            e1.record()
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev])
+
+    scold, shot = timed_sinks(True), timed_sinks(False)
+    result["prefill_sinks"] = {"workload": PREFILL_WORKLOAD, "n_sinks": N_SINKS, "cold": stats(scold), "hot": stats(shot),
+                               "tokens_per_s": B * T / (float(np.median(scold)) * 1e-3)}
+    log(f"[bench] prefill with {N_SINKS} sinks: cold {np.median(scold) * 1e3:.1f} us, hot {np.median(shot) * 1e3:.1f} us")
+
     if not args.no_decode:
         dcfg = CONFIGS[DECODE_WORKLOAD]
         dgate = gla.LIGER_GATE_SCALAR_MEAN if dcfg["gate"] == "scalar" else gla.LIGER_GATE_VECTOR_AVGPOOL4
@@ -320,6 +350,18 @@ def main() -> int:
             cold_ev[s][1].record()
         torch.cuda.synchronize()
         cold_us = float(np.median([a.elapsed_time(b) for a, b in cold_ev])) * 1e3
+        # the same steps with meta-memory sink tokens, back to back
+        rng = np.random.default_rng(SINK_SEED + 1)
+        dsinks = tuple(torch.from_numpy(rng.standard_normal((Hkv, N_SINKS, dd)).astype(np.float32)).to(dev)
+                       .to(torch.bfloat16) for _ in range(2))
+        for s in range(dwarm):
+            gla.liger_attn_decode_step(*steps_in[s], S, ring, dgate, dcfg["alpha"], o=do, sinks=dsinks)
+        e0.record()
+        for s in range(nsteps):
+            gla.liger_attn_decode_step(*steps_in[s], S, ring, dgate, dcfg["alpha"], o=do, sinks=dsinks)
+        e1.record()
+        torch.cuda.synchronize()
+        sink_us = e0.elapsed_time(e1) * 1e3 / nsteps
         dbytes = decode_algorithmic(dcfg)
         dach = dbytes / (k_ms * 1e-3) / 1e9
         drec = counter_record("decode_step_kernel", DECODE_WORKLOAD)
@@ -332,6 +374,7 @@ def main() -> int:
             "steps_per_s_kernel": 1e3 / k_ms, "tokens_per_s_kernel": N * 1e3 / k_ms,
             "graph_us_per_step": graph_us, "graph_steps_per_s": 1e6 / graph_us,
             "cold_kernel_us_median": cold_us,
+            "with_sinks": {"n_sinks": N_SINKS, "kernel_us": sink_us},
             "roofline": {"bound": "hbm", "achieved": dach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": dach / PEAK_HBM_GBS, "traffic": dtraffic,
                          "cold_frac": dbytes / (cold_us * 1e-6) / 1e9 / PEAK_HBM_GBS,

@@ -45,6 +45,9 @@ EXPORTED = (
     "liger_attn_decode_step",
     "liger_kv_ring_fill",
     "liger_attn_full_causal",
+    "liger_attn_prefill_sinks",
+    "liger_attn_prefill_continue_sinks",
+    "liger_attn_decode_step_sinks",
     "liger_last_error",
 )
 
@@ -63,6 +66,10 @@ class liger_shape(ctypes.Structure):
 class liger_kv_ring(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p),
                 ("sync", ctypes.c_void_p), ("window", ctypes.c_int32)]
+
+
+class liger_sinks(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("n", ctypes.c_int32)]
 
 
 _lib = None
@@ -97,6 +104,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.liger_kv_ring_fill.restype = i32
     lib.liger_attn_full_causal.argtypes = [vp, vp, vp, shp, vp, vp]
     lib.liger_attn_full_causal.restype = i32
+    snk = ctypes.POINTER(liger_sinks)
+    lib.liger_attn_prefill_sinks.argtypes = [vp, vp, vp, snk, i32, i32, f32, shp, vp, vp, vp, sz, vp]
+    lib.liger_attn_prefill_sinks.restype = i32
+    lib.liger_attn_prefill_continue_sinks.argtypes = [vp, vp, vp, vp, ring, snk, i32, f32, shp, vp, vp, vp, sz, vp]
+    lib.liger_attn_prefill_continue_sinks.restype = i32
+    lib.liger_attn_decode_step_sinks.argtypes = [vp, vp, vp, vp, ring, snk, i32, f32, shp, vp, vp]
+    lib.liger_attn_decode_step_sinks.restype = i32
     lib.liger_last_error.argtypes = []
     lib.liger_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -152,11 +166,20 @@ def liger_attn_prefill_workspace_size(B: int, T: int, H_q: int, H_kv: int, d: in
     return int(load_library().liger_attn_prefill_workspace_size_ex(ctypes.byref(shp), chunks_per_segment))
 
 
+def _sinks_c(sinks):
+    """(sink_k, sink_v) device tensors [H_kv, n, d] -> liger_sinks."""
+    sk, sv = sinks
+    return liger_sinks(_ptr(sk), _ptr(sv), int(sk.shape[1]))
+
+
 def liger_attn_prefill(q, k, v, gate_mode: int, window: int, alpha: float, *, o=None, S_T=None,
-                       workspace=None, chunks_per_segment: int = 0, stage_mask: int = 7, stream=None):
+                       workspace=None, chunks_per_segment: int = 0, stage_mask: int = 7, stream=None,
+                       sinks=None):
     """Prefill from a zero state. q [B,T,H_q,d], k/v [B,T,H_kv,d] -> (o, S_T fp32 [B,H_kv,d,d]).
 
-    stage_mask < 7 enqueues only some kernels (liger_attn_prefill_stages)."""
+    stage_mask < 7 enqueues only some kernels (liger_attn_prefill_stages).
+    sinks = (sink_k, sink_v) [H_kv, n, d] prepends meta-memory tokens to every
+    window (liger_attn_prefill_sinks)."""
     torch = _torch()
     lib = load_library()
     B, T, H_q, d = q.shape
@@ -170,6 +193,14 @@ def liger_attn_prefill(q, k, v, gate_mode: int, window: int, alpha: float, *, o=
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if sinks is not None:
+        if stage_mask != 7 or chunks_per_segment != 0:
+            raise LigerError(LIGER_E_INVALID_ARG, "sinks take the default stages and segment plan")
+        cs = _sinks_c(sinks)
+        _check(lib.liger_attn_prefill_sinks(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs), gate_mode, window, alpha,
+                                            ctypes.byref(shp), _ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes,
+                                            _stream(stream)))
+        return o, S_T
     _check(lib.liger_attn_prefill_stages(_ptr(q), _ptr(k), _ptr(v), gate_mode, window, alpha,
                                          ctypes.byref(shp), _ptr(o), _ptr(S_T), _ptr(workspace),
                                          ws_bytes, chunks_per_segment, stage_mask, _stream(stream)))
@@ -208,7 +239,7 @@ def liger_kv_ring_fill(k, v, ring: KVRing, stream=None) -> KVRing:
 
 
 def liger_attn_prefill_continue(q, k, v, S0, ring: KVRing, gate_mode: int, alpha: float, *, o=None, S_T=None,
-                                workspace=None, stream=None):
+                                workspace=None, stream=None, sinks=None):
     """T more tokens after ring.pos[b] consumed ones, from state S0 (not modified) and the ring
     (updated in place: last tokens written, pos += T). Window = ring.window. -> (o, S_T)."""
     torch = _torch()
@@ -225,6 +256,12 @@ def liger_attn_prefill_continue(q, k, v, S0, ring: KVRing, gate_mode: int, alpha
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     cring = ring.as_c()
+    if sinks is not None:
+        cs = _sinks_c(sinks)
+        _check(lib.liger_attn_prefill_continue_sinks(_ptr(q), _ptr(k), _ptr(v), _ptr(S0), ctypes.byref(cring),
+                                                     ctypes.byref(cs), gate_mode, alpha, ctypes.byref(shp), _ptr(o),
+                                                     _ptr(S_T), _ptr(workspace), ws_bytes, _stream(stream)))
+        return o, S_T
     _check(lib.liger_attn_prefill_continue(_ptr(q), _ptr(k), _ptr(v), _ptr(S0), ctypes.byref(cring), gate_mode,
                                            alpha, ctypes.byref(shp), _ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes,
                                            _stream(stream)))
@@ -244,7 +281,8 @@ def liger_attn_full_causal(q, k, v, *, o=None, stream=None):
     return o
 
 
-def liger_attn_decode_step(q, k, v, S, ring: KVRing, gate_mode: int, alpha: float, *, o=None, stream=None):
+def liger_attn_decode_step(q, k, v, S, ring: KVRing, gate_mode: int, alpha: float, *, o=None, stream=None,
+                           sinks=None):
     """One token per sequence: q [N,H_q,d], k/v [N,H_kv,d]; S and ring updated in place; returns o."""
     torch = _torch()
     lib = load_library()
@@ -254,6 +292,12 @@ def liger_attn_decode_step(q, k, v, S, ring: KVRing, gate_mode: int, alpha: floa
     if o is None:
         o = torch.empty_like(q)
     cring = ring.as_c()
+    if sinks is not None:
+        cs = _sinks_c(sinks)
+        _check(lib.liger_attn_decode_step_sinks(_ptr(q), _ptr(k), _ptr(v), _ptr(S), ctypes.byref(cring),
+                                                ctypes.byref(cs), gate_mode, alpha, ctypes.byref(shp), _ptr(o),
+                                                _stream(stream)))
+        return o
     _check(lib.liger_attn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(S), ctypes.byref(cring), gate_mode,
                                       alpha, ctypes.byref(shp), _ptr(o), _stream(stream)))
     return o

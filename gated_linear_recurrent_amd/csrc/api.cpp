@@ -65,6 +65,15 @@ liger_status map_hip(hipError_t e, const char* what) {
         if (st_ != LIGER_OK) return st_;   \
     } while (0)
 
+// Sink tokens: NULL means none; otherwise 1..16 tokens with aligned k and v.
+liger_status check_sinks(const liger_sinks* sk) {
+    if (!sk) return ok();
+    if (sk->n < 1 || sk->n > 16) return fail(LIGER_E_INVALID_ARG, "sinks->n must be in 1..16");
+    LIGER_TRY(check_ptr(sk->k, "sinks->k"));
+    LIGER_TRY(check_ptr(sk->v, "sinks->v"));
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -82,11 +91,16 @@ size_t liger_attn_prefill_workspace_size(const liger_shape* shape) {
     return liger_attn_prefill_workspace_size_ex(shape, 0);
 }
 
-liger_status liger_attn_prefill_stages(const void* q, const void* k, const void* v, int32_t gate_mode,
-                                       int32_t window, float alpha, const liger_shape* shape, void* o,
-                                       float* S_T, void* workspace, size_t workspace_bytes,
-                                       int32_t chunks_per_segment, int32_t stage_mask, void* stream) {
+}  // extern "C"
+
+namespace {
+
+liger_status prefill_impl(const void* q, const void* k, const void* v, const liger_sinks* sinks, int32_t gate_mode,
+                          int32_t window, float alpha, const liger_shape* shape, void* o, float* S_T,
+                          void* workspace, size_t workspace_bytes, int32_t chunks_per_segment, int32_t stage_mask,
+                          void* stream) {
     if (stage_mask < 1 || stage_mask > 7) return fail(LIGER_E_INVALID_ARG, "stage_mask must be in 1..7");
+    LIGER_TRY(check_sinks(sinks));
     LIGER_TRY(check_shape(shape, true));
     LIGER_TRY(check_common(gate_mode, alpha));
     if (window < 1 || window > 64) return fail(LIGER_E_INVALID_ARG, "window must be in 1..64");
@@ -127,7 +141,32 @@ liger_status liger_attn_prefill_stages(const void* q, const void* k, const void*
     a.plan = pl;
     a.stage_mask = stage_mask;
     a.stream = stream;
+    if (sinks) {
+        a.sink_k = sinks->k;
+        a.sink_v = sinks->v;
+        a.n_sink = sinks->n;
+    }
     return map_hip(liger::launch_prefill(a), "prefill launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+liger_status liger_attn_prefill_stages(const void* q, const void* k, const void* v, int32_t gate_mode,
+                                       int32_t window, float alpha, const liger_shape* shape, void* o,
+                                       float* S_T, void* workspace, size_t workspace_bytes,
+                                       int32_t chunks_per_segment, int32_t stage_mask, void* stream) {
+    return prefill_impl(q, k, v, nullptr, gate_mode, window, alpha, shape, o, S_T, workspace, workspace_bytes,
+                        chunks_per_segment, stage_mask, stream);
+}
+
+liger_status liger_attn_prefill_sinks(const void* q, const void* k, const void* v, const liger_sinks* sinks,
+                                      int32_t gate_mode, int32_t window, float alpha, const liger_shape* shape,
+                                      void* o, float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!sinks) return fail(LIGER_E_INVALID_ARG, "sinks is NULL");
+    return prefill_impl(q, k, v, sinks, gate_mode, window, alpha, shape, o, S_T, workspace, workspace_bytes, 0, 7,
+                        stream);
 }
 
 liger_status liger_attn_prefill_ex(const void* q, const void* k, const void* v, int32_t gate_mode,
@@ -145,11 +184,16 @@ liger_status liger_attn_prefill(const void* q, const void* k, const void* v, int
                                  stream);
 }
 
-liger_status liger_attn_prefill_continue(const void* q, const void* k, const void* v, const float* S0,
-                                        const liger_kv_ring* kv_ring, int32_t gate_mode, float alpha,
-                                        const liger_shape* shape, void* o, float* S_T, void* workspace,
-                                        size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+liger_status continue_impl(const void* q, const void* k, const void* v, const float* S0,
+                           const liger_kv_ring* kv_ring, const liger_sinks* sinks, int32_t gate_mode, float alpha,
+                           const liger_shape* shape, void* o, float* S_T, void* workspace, size_t workspace_bytes,
+                           void* stream) {
     LIGER_TRY(check_shape(shape, true));
+    LIGER_TRY(check_sinks(sinks));
     LIGER_TRY(check_common(gate_mode, alpha));
     if (!kv_ring) return fail(LIGER_E_INVALID_ARG, "kv_ring is NULL");
     const int32_t window = kv_ring->window;
@@ -203,6 +247,11 @@ liger_status liger_attn_prefill_continue(const void* q, const void* k, const voi
     a.ring_k = kv_ring->k;
     a.ring_v = kv_ring->v;
     a.pos = kv_ring->pos;
+    if (sinks) {
+        a.sink_k = sinks->k;
+        a.sink_v = sinks->v;
+        a.n_sink = sinks->n;
+    }
     LIGER_TRY(map_hip(liger::launch_prefill(a), "prefill continuation launch"));
     liger::RingFillArgs r;
     r.k = k;
@@ -221,10 +270,36 @@ liger_status liger_attn_prefill_continue(const void* q, const void* k, const voi
     return map_hip(liger::launch_ring_append(r), "ring append launch");
 }
 
-liger_status liger_attn_decode_step(const void* q, const void* k, const void* v, float* S,
-                                    const liger_kv_ring* kv_ring, int32_t gate_mode, float alpha,
-                                    const liger_shape* shape, void* o, void* stream) {
+}  // namespace
+
+extern "C" {
+
+liger_status liger_attn_prefill_continue(const void* q, const void* k, const void* v, const float* S0,
+                                        const liger_kv_ring* kv_ring, int32_t gate_mode, float alpha,
+                                        const liger_shape* shape, void* o, float* S_T, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+    return continue_impl(q, k, v, S0, kv_ring, nullptr, gate_mode, alpha, shape, o, S_T, workspace, workspace_bytes,
+                         stream);
+}
+
+liger_status liger_attn_prefill_continue_sinks(const void* q, const void* k, const void* v, const float* S0,
+                                              const liger_kv_ring* kv_ring, const liger_sinks* sinks,
+                                              int32_t gate_mode, float alpha, const liger_shape* shape, void* o,
+                                              float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!sinks) return fail(LIGER_E_INVALID_ARG, "sinks is NULL");
+    return continue_impl(q, k, v, S0, kv_ring, sinks, gate_mode, alpha, shape, o, S_T, workspace, workspace_bytes,
+                         stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+liger_status decode_impl(const void* q, const void* k, const void* v, float* S, const liger_kv_ring* kv_ring,
+                         const liger_sinks* sinks, int32_t gate_mode, float alpha, const liger_shape* shape, void* o,
+                         void* stream) {
     LIGER_TRY(check_shape(shape, false));
+    LIGER_TRY(check_sinks(sinks));
     LIGER_TRY(check_common(gate_mode, alpha));
     if (!kv_ring) return fail(LIGER_E_INVALID_ARG, "kv_ring is NULL");
     if (kv_ring->window < 1 || kv_ring->window > 64) return fail(LIGER_E_INVALID_ARG, "ring window must be in 1..64");
@@ -260,7 +335,29 @@ liger_status liger_attn_decode_step(const void* q, const void* k, const void* v,
     a.bf16 = shape->dtype == LIGER_BF16;
     a.alpha = alpha;
     a.stream = stream;
+    if (sinks) {
+        a.sink_k = sinks->k;
+        a.sink_v = sinks->v;
+        a.n_sink = sinks->n;
+    }
     return map_hip(liger::launch_decode_step(a), "decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+liger_status liger_attn_decode_step(const void* q, const void* k, const void* v, float* S,
+                                    const liger_kv_ring* kv_ring, int32_t gate_mode, float alpha,
+                                    const liger_shape* shape, void* o, void* stream) {
+    return decode_impl(q, k, v, S, kv_ring, nullptr, gate_mode, alpha, shape, o, stream);
+}
+
+liger_status liger_attn_decode_step_sinks(const void* q, const void* k, const void* v, float* S,
+                                          const liger_kv_ring* kv_ring, const liger_sinks* sinks, int32_t gate_mode,
+                                          float alpha, const liger_shape* shape, void* o, void* stream) {
+    if (!sinks) return fail(LIGER_E_INVALID_ARG, "sinks is NULL");
+    return decode_impl(q, k, v, S, kv_ring, sinks, gate_mode, alpha, shape, o, stream);
 }
 
 liger_status liger_attn_full_causal(const void* q, const void* k, const void* v, const liger_shape* shape,

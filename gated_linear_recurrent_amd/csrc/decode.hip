@@ -21,6 +21,7 @@
 namespace liger {
 
 constexpr int kDecThreads = 256;
+constexpr int kMaxSinks = 16;  // meta-memory tokens per key/value head
 
 // 64-lane reductions: DPP inside rows of 16, then two cross-row exchanges.
 __device__ __forceinline__ float dec_wave_max(float v) {
@@ -48,12 +49,12 @@ __device__ __forceinline__ f32x4 outer4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
 }
 
-template <typename T, int D, int GATE, int NREP>
+template <typename T, int D, int GATE, int NREP, bool SINK>
 __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2) void decode_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     float* __restrict__ S, T* __restrict__ ring_k, T* __restrict__ ring_v,
     int64_t* __restrict__ pos, uint32_t* __restrict__ sync, T* __restrict__ o,
-    int H_kv, int window, float alpha) {
+    int H_kv, int window, float alpha, const T* __restrict__ sink_k, const T* __restrict__ sink_v, int n_sink) {
     constexpr int CG = D / 4;             // float4 column groups of a state row
     constexpr int RG = kDecThreads / CG;  // row groups
     constexpr int RPT = D / RG;           // state rows per thread
@@ -71,7 +72,8 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
     __shared__ int64_t s_pos;
     __shared__ __align__(16) float s_q[D][NRP];      // raw q, head-minor
     __shared__ __align__(16) float s_phiq[D][NRP];   // phi(q), head-minor
-    __shared__ __align__(16) float s_p[64][NRP];     // window weights, head-minor
+    constexpr int NS = SINK ? kMaxSinks : 0;         // sink rows (meta-memory tokens)
+    __shared__ __align__(16) float s_p[64 + NS][NRP];  // window weights (then sinks), head-minor
     __shared__ __align__(16) float s_red[RG][NREP][D];
 
     const int h = blockIdx.x;
@@ -127,6 +129,21 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
             if constexpr (sizeof(T) == 2) vraw[i] = make_uint2(0, 0);
             else vraw[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
+    }
+    // sink tokens (rows past n_sink repeat the last one; their weight is 0)
+    constexpr int SKI = SINK ? (kMaxSinks + SPI - 1) / SPI : 0;   // sink key loads per thread
+    constexpr int SVI = SINK ? (kMaxSinks + RG - 1) / RG : 0;     // sink value loads per thread
+    uint4 skr[SKI > 0 ? SKI : 1];
+    VRaw svr[SVI > 0 ? SVI : 1];
+    if constexpr (SINK) {
+        const T* skp = sink_k + static_cast<size_t>(h) * n_sink * D;
+        const T* svp = sink_v + static_cast<size_t>(h) * n_sink * D;
+#pragma unroll
+        for (int i = 0; i < SKI; ++i)
+            skr[i] = *reinterpret_cast<const uint4*>(skp + (min(ks0 + i * SPI, n_sink - 1) * D + kl * VPL));
+#pragma unroll
+        for (int i = 0; i < SVI; ++i)
+            svr[i] = *reinterpret_cast<const VRaw*>(svp + (min(rg + i * RG, n_sink - 1) * D + cg * 4));
     }
     float4 sv[RPT];
 #pragma unroll
@@ -257,10 +274,9 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
             }
         const uint4 knew = reinterpret_cast<const uint4*>(s_kraw)[kl];
         const float scale = kLog2e * rsqrtf(static_cast<float>(D));
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int s_i = ks0 + i * SPI;
-            const uint4 kk = s_i == slot ? knew : kr[i];
+        // logit of one key row (all LPR lanes of the row take part); row
+        // `prow` of s_p, -inf where the key is not valid
+        auto logit_row = [&](const uint4& kk, int prow, bool valid) {
             const T* e = reinterpret_cast<const T*>(&kk);
             float dot[NRP];
 #pragma unroll
@@ -278,13 +294,25 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
                 dot[j] += dpp<kDppHalfMirror>(dot[j]);
                 if constexpr (LPR >= 16) dot[j] += dpp<kDppMirror>(dot[j]);
                 if constexpr (LPR >= 32) dot[j] += __shfl_xor(dot[j], 16, 64);
-                dot[j] = s_i < nvalid ? dot[j] * scale : -INFINITY;
+                dot[j] = valid ? dot[j] * scale : -INFINITY;
             }
             if (kl == 0) {
 #pragma unroll
                 for (int j4 = 0; j4 < NR4; ++j4)
-                    *reinterpret_cast<float4*>(&s_p[s_i][4 * j4]) =
+                    *reinterpret_cast<float4*>(&s_p[prow][4 * j4]) =
                         make_float4(dot[4 * j4], dot[4 * j4 + 1], dot[4 * j4 + 2], dot[4 * j4 + 3]);
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int s_i = ks0 + i * SPI;
+            logit_row(s_i == slot ? knew : kr[i], s_i, s_i < nvalid);
+        }
+        if constexpr (SINK) {
+#pragma unroll
+            for (int i = 0; i < SKI; ++i) {
+                const int r = ks0 + i * SPI;
+                if (r < kMaxSinks) logit_row(skr[i], 64 + r, r < n_sink);
             }
         }
     }
@@ -292,10 +320,14 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
     // window softmax per head, weights times (1 - alpha)
     for (int j = wave; j < NREP; j += kDecThreads / 64) {
         const float l = s_p[lane][j];
-        const float m = dec_wave_max(l);
+        // lane < kMaxSinks also takes sink `lane` (logit -inf past n_sink)
+        const float ls = (SINK && lane < kMaxSinks) ? s_p[64 + (lane & (kMaxSinks - 1))][j] : -INFINITY;
+        const float m = dec_wave_max(fmaxf(l, ls));
         const float e = lane < nvalid ? fast_exp2(l - m) : 0.f;
-        const float inv = fast_rcp(dec_wave_sum(e));
+        const float es = fast_exp2(ls - m);  // exp2(-inf) = 0
+        const float inv = fast_rcp(dec_wave_sum(e + es));
         s_p[lane][j] = e * inv * (1.0f - alpha);
+        if (SINK && lane < kMaxSinks) s_p[64 + (lane & (kMaxSinks - 1))][j] = es * inv * (1.0f - alpha);
     }
     __syncthreads();
 
@@ -335,6 +367,31 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
             const float a = s_p[s][4 * hg + hq];  // 0 outside the window
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[hg][e] = outer4(a, vr[e], acc[hg][e]);
+        }
+    }
+    if constexpr (SINK) {
+#pragma unroll
+        for (int i = 0; i < SVI; ++i) {
+            const int r = rg + i * RG;
+            if (r >= kMaxSinks) continue;
+            float vr[4];
+            if constexpr (sizeof(T) == 2) {
+                vr[0] = __uint_as_float(svr[i].x << 16);
+                vr[1] = __uint_as_float(svr[i].x & 0xffff0000u);
+                vr[2] = __uint_as_float(svr[i].y << 16);
+                vr[3] = __uint_as_float(svr[i].y & 0xffff0000u);
+            } else {
+                vr[0] = svr[i].x;
+                vr[1] = svr[i].y;
+                vr[2] = svr[i].z;
+                vr[3] = svr[i].w;
+            }
+#pragma unroll
+            for (int hg = 0; hg < NR4; ++hg) {
+                const float a = s_p[64 + r][4 * hg + hq];  // 0 past n_sink
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[hg][e] = outer4(a, vr[e], acc[hg][e]);
+            }
         }
     }
 
@@ -453,11 +510,19 @@ __global__ void ring_advance_kernel(int64_t* __restrict__ pos, uint32_t* __restr
 template <typename T, int D, int GATE, int NREP>
 static hipError_t launch_dec_t(const DecodeArgs& a) {
     dim3 grid(a.H_kv, static_cast<unsigned>(a.N));
-    hipLaunchKernelGGL((decode_step_kernel<T, D, GATE, NREP>), grid, dim3(kDecThreads), 0,
-                       static_cast<hipStream_t>(a.stream),
-                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                       a.S, static_cast<T*>(a.ring_k), static_cast<T*>(a.ring_v), a.pos, a.sync,
-                       static_cast<T*>(a.o), a.H_kv, a.window, a.alpha);
+    if (a.n_sink > 0)
+        hipLaunchKernelGGL((decode_step_kernel<T, D, GATE, NREP, true>), grid, dim3(kDecThreads), 0,
+                           static_cast<hipStream_t>(a.stream),
+                           static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                           a.S, static_cast<T*>(a.ring_k), static_cast<T*>(a.ring_v), a.pos, a.sync,
+                           static_cast<T*>(a.o), a.H_kv, a.window, a.alpha, static_cast<const T*>(a.sink_k),
+                           static_cast<const T*>(a.sink_v), a.n_sink);
+    else
+        hipLaunchKernelGGL((decode_step_kernel<T, D, GATE, NREP, false>), grid, dim3(kDecThreads), 0,
+                           static_cast<hipStream_t>(a.stream),
+                           static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                           a.S, static_cast<T*>(a.ring_k), static_cast<T*>(a.ring_v), a.pos, a.sync,
+                           static_cast<T*>(a.o), a.H_kv, a.window, a.alpha, nullptr, nullptr, 0);
     return hipGetLastError();
 }
 

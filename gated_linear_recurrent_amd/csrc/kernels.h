@@ -28,6 +28,10 @@ struct DecodeArgs {
     bool bf16;
     float alpha;
     void* stream;
+    // meta-memory sink tokens [H_kv, n_sink, d] (none when n_sink == 0)
+    const void* sink_k = nullptr;
+    const void* sink_v = nullptr;
+    int n_sink = 0;
 };
 
 struct RingFillArgs {
@@ -101,6 +105,11 @@ struct PrefillArgs {
     const void* ring_k = nullptr;
     const void* ring_v = nullptr;
     const int64_t* pos = nullptr;
+    // meta-memory sink tokens [H_kv, n_sink, d] prepended to every window
+    // (none when n_sink == 0)
+    const void* sink_k = nullptr;
+    const void* sink_v = nullptr;
+    int n_sink = 0;
 };
 
 constexpr int kChunk = 64;

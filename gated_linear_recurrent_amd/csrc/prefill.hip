@@ -169,6 +169,10 @@ struct PrefillParams {
     const void* ring_k;
     const void* ring_v;
     const int64_t* pos;
+    // meta-memory sink tokens [H_kv, n_sink, d] (output kernel, SINK = true)
+    const void* sink_k;
+    const void* sink_v;
+    int n_sink;
 };
 
 // ------------------------------------------------------------ chunk loading
@@ -1085,6 +1089,9 @@ struct ItemCtx {
     int npv;           // keys of the previous-chunk slot that exist (64, or fewer at the sequence start)
     float alpha;
     int cur;
+    const T* sink_k;  // this key/value head's sink tokens [n_sink][D]
+    const T* sink_v;
+    int n_sink;
 };
 
 // One wave computes the outputs of 32 query rows (query tiles QA and QB of the
@@ -1151,7 +1158,7 @@ __device__ __forceinline__ typename Mfma<T>::frag resident_frag(const Smem<T, D,
     return M::pack(x);
 }
 
-template <typename T, int D, int GATE, int QA, int QB>
+template <typename T, int D, int GATE, int QA, int QB, bool SINK>
 __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, const ItemCtx<T, D, GATE>& x,
                                              int lane, const QFrags<T, D>& qin) {
     typedef Layout<T, D, GATE, true> L;
@@ -1225,6 +1232,7 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
     // Maxima are taken on the raw products; the 1/sqrt(d) scale is applied
     // inside the exponent.
     float sc[2][NKT][4];
+    float ss[2][4];  // sink tokens: lane (col, g) holds sinks 4 g + r of query col
     const float lscale = kLog2e * rsqrtf(static_cast<float>(D));
     auto window_scores = [&](auto fast_c) {
         constexpr bool FAST = decltype(fast_c)::value;
@@ -1279,6 +1287,26 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
             }
             __builtin_amdgcn_sched_barrier(0);  // bound the number of key fragments in flight
         }
+        if constexpr (SINK) {
+            // sink scores: the sink keys (rows past n_sink repeat the last one
+            // and are masked) against both query tiles
+            const T* srow = x.sink_k + (col < x.n_sink ? col : x.n_sink - 1) * D + KPL * g;
+            f32x4_t d4[2] = {zero4(), zero4()};
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                const Frag a = M::load(srow + M::KSTEP * k);
+                d4[0] = M::mma(a, qr[0][k], d4[0]);
+                d4[1] = M::mma(a, qr[1][k], d4[1]);
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float v = 4 * g + r < x.n_sink ? d4[s][r] : -INFINITY;
+                    ss[s][r] = v;
+                    lmax[s] = fmaxf(lmax[s], v);
+                }
+        }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const float m = group4_max(lmax[s]) * lscale;  // the diagonal key is always valid
@@ -1291,11 +1319,23 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
                     sc[s][u][r] = e;
                     sum += e;
                 }
+            if constexpr (SINK) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float e = fast_exp2(fmaf(ss[s][r], lscale, -m));
+                    ss[s][r] = e;
+                    sum += e;
+                }
+            }
             const float ps = (1.0f - x.alpha) * fast_rcp(group4_sum(sum));
 #pragma unroll
             for (int u = QTS[s] - 4 - KTMIN; u <= QTS[s] - KTMIN; ++u)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sc[s][u][r] *= ps;
+            if constexpr (SINK) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ss[s][r] *= ps;
+            }
         }
     };
     if (x.npv == 64 && full_window) window_scores(std::true_type{});
@@ -1425,6 +1465,15 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
                 pf[s][G] = M::pack(v8);
             }
     }
+    // sink probabilities as the operand of a 32-key group whose upper 16 keys are zero
+    Frag pfs[2];
+    if constexpr (SINK && BF) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const float v8[8] = {ss[s][0], ss[s][1], ss[s][2], ss[s][3], 0.f, 0.f, 0.f, 0.f};
+            pfs[s] = M::pack(v8);
+        }
+    }
     float inter_scale[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) inter_scale[s] = GATE == 0 ? qinv[s] * fast_exp2(bq[s]) : qinv[s];
@@ -1492,6 +1541,24 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
                     }
             }
         }
+        if constexpr (SINK) {
+            // sink values: lane (col, g) takes channel 16 t + col of sinks 4 g + r
+            const T* sv = x.sink_v + 16 * t + col;
+            float vs[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) vs[r] = to_f32(sv[(4 * g + r < x.n_sink ? 4 * g + r : x.n_sink - 1) * D]);
+            if constexpr (BF) {
+                const Frag a = __builtin_bit_cast(Frag, make_uint4(pack_bf16x2(vs[0], vs[1]), pack_bf16x2(vs[2], vs[3]), 0u, 0u));
+                acc[0] = M::mma(a, pfs[0], acc[0]);
+                acc[1] = M::mma(a, pfs[1], acc[1]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    acc[0] = M::mma(__builtin_bit_cast(Frag, vs[r]), __builtin_bit_cast(Frag, ss[0][r]), acc[0]);
+                    acc[1] = M::mma(__builtin_bit_cast(Frag, vs[r]), __builtin_bit_cast(Frag, ss[1][r]), acc[1]);
+                }
+            }
+        }
 #pragma unroll
         for (int s = 0; s < 2; ++s)
             if (row_ok[s]) {
@@ -1506,7 +1573,7 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
     }
 }
 
-template <typename T, int D, int GATE>
+template <typename T, int D, int GATE, bool SINK>
 __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams p) {
     typedef Layout<T, D, GATE, true> L;
     __shared__ __align__(16) char smem[L::TOTAL];
@@ -1591,6 +1658,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
             x.window = p.window;
             x.npv = c > 0 ? 64 : npv0;
             x.alpha = p.alpha;
+            x.sink_k = SINK ? static_cast<const T*>(p.sink_k) + size_t(h) * p.n_sink * D : nullptr;
+            x.sink_v = SINK ? static_cast<const T*>(p.sink_v) + size_t(h) * p.n_sink * D : nullptr;
+            x.n_sink = SINK ? p.n_sink : 0;
             x.cur = cur;
             // next chunk's K/V: in flight during the output phase
             if (c + 1 < c_end) {
@@ -1604,8 +1674,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
                 const int pair = it / p.n_rep;
                 if (it != wave)
                     load_q_block<T, D>(qpre, x.q, x.row0, H_q, x.hq, pair == 0 ? 0 : 1, pair == 0 ? 3 : 2, nvalid, lane);
-                if (pair == 0) output_block<T, D, GATE, 0, 3>(sm, x, lane, qpre);
-                else output_block<T, D, GATE, 1, 2>(sm, x, lane, qpre);
+                if (pair == 0) output_block<T, D, GATE, 0, 3, SINK>(sm, x, lane, qpre);
+                else output_block<T, D, GATE, 1, 2, SINK>(sm, x, lane, qpre);
             }
             __syncthreads();
             if (c + 1 < c_end) load_chunk_commit(sm, cur ^ 1, cr);  // the previous chunk's slot is free now
@@ -1672,6 +1742,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
         x.window = p.window;
         x.npv = c > 0 ? 64 : npv0;
         x.alpha = p.alpha;
+        x.sink_k = SINK ? static_cast<const T*>(p.sink_k) + size_t(h) * p.n_sink * D : nullptr;
+        x.sink_v = SINK ? static_cast<const T*>(p.sink_v) + size_t(h) * p.n_sink * D : nullptr;
+        x.n_sink = SINK ? p.n_sink : 0;
         x.cur = cur;
         // next chunk's K/V: in flight during the output phase, stored after it
         if (c + 1 < c_end) {
@@ -1685,8 +1758,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
             const int pair = it / p.n_rep;
             if (it != wave)
                 load_q_block<T, D>(qpre, x.q, x.row0, H_q, x.hq, pair == 0 ? 0 : 1, pair == 0 ? 3 : 2, nvalid, lane);
-            if (pair == 0) output_block<T, D, GATE, 0, 3>(sm, x, lane, qpre);
-            else output_block<T, D, GATE, 1, 2>(sm, x, lane, qpre);
+            if (pair == 0) output_block<T, D, GATE, 0, 3, SINK>(sm, x, lane, qpre);
+            else output_block<T, D, GATE, 1, 2, SINK>(sm, x, lane, qpre);
         }
         __syncthreads();
         if (c + 1 < c_end) {
@@ -1742,6 +1815,9 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     p.ring_k = a.ring_k;
     p.ring_v = a.ring_v;
     p.pos = a.pos;
+    p.sink_k = a.sink_k;
+    p.sink_v = a.sink_v;
+    p.n_sink = a.n_sink;
     hipStream_t st = static_cast<hipStream_t>(a.stream);
     if (p.n_seg > 1 && (a.stage_mask & 1)) {
         hipLaunchKernelGGL((segment_state_kernel<T, D, GATE>), dim3(unsigned(p.n_seg - 1), a.H_kv, unsigned(a.B)),
@@ -1756,8 +1832,12 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
         if (e != hipSuccess) return e;
     }
     if (a.stage_mask & 4) {
-        hipLaunchKernelGGL((prefill_output_kernel<T, D, GATE>), dim3(unsigned(p.n_seg), a.H_kv, unsigned(a.B)),
-                           dim3(kPThreads), 0, st, p);
+        if (a.n_sink > 0)
+            hipLaunchKernelGGL((prefill_output_kernel<T, D, GATE, true>), dim3(unsigned(p.n_seg), a.H_kv, unsigned(a.B)),
+                               dim3(kPThreads), 0, st, p);
+        else
+            hipLaunchKernelGGL((prefill_output_kernel<T, D, GATE, false>), dim3(unsigned(p.n_seg), a.H_kv, unsigned(a.B)),
+                               dim3(kPThreads), 0, st, p);
         return hipGetLastError();
     }
     return hipSuccess;

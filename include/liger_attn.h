@@ -97,6 +97,19 @@ typedef struct liger_kv_ring {
 } liger_kv_ring;
 
 /*
+ * Meta-memory tokens ("attention sinks", Japanese summary page of Lizard,
+ * section "アンカーウィンドウアテンション"): n extra key/value pairs per key/value
+ * head that the sliding-window softmax of every query also sees, with the
+ * same 1/sqrt(d) scale and no causal or window mask; they do not enter the
+ * recurrence. Device pointers, dtype of the shape, 16-byte aligned, read only.
+ */
+typedef struct liger_sinks {
+    const void* k;  /* [H_kv, n, d] */
+    const void* v;  /* [H_kv, n, d] */
+    int32_t n;      /* 1 .. 16      */
+} liger_sinks;
+
+/*
  * Bytes of device workspace liger_attn_prefill needs for `shape`: the state
  * carried into each segment of the chunked scan and a running-state slot per
  * segment. Returns 0 when the shape is invalid. `chunks_per_segment` selects the segment length
@@ -216,6 +229,33 @@ liger_status liger_kv_ring_fill(const void* k, const void* v,
  */
 liger_status liger_attn_full_causal(const void* q, const void* k, const void* v,
                                     const liger_shape* shape, void* o, void* stream);
+
+/*
+ * The three calls above with meta-memory tokens (liger_sinks) prepended to
+ * every sliding window: o's window part becomes softmax over
+ * [sink keys; window keys] applied to [sink values; window values]. The
+ * same arguments as liger_attn_prefill, liger_attn_prefill_continue and
+ * liger_attn_decode_step; `sinks` must not be NULL and sinks->n must be in
+ * 1..16 (else LIGER_E_INVALID_ARG). A decode or a continuation must be given
+ * the sinks its prefill used.
+ */
+liger_status liger_attn_prefill_sinks(const void* q, const void* k, const void* v,
+                                      const liger_sinks* sinks, int32_t gate_mode,
+                                      int32_t window, float alpha,
+                                      const liger_shape* shape, void* o, float* S_T,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream);
+liger_status liger_attn_prefill_continue_sinks(const void* q, const void* k, const void* v,
+                                              const float* S0, const liger_kv_ring* kv_ring,
+                                              const liger_sinks* sinks, int32_t gate_mode,
+                                              float alpha, const liger_shape* shape,
+                                              void* o, float* S_T, void* workspace,
+                                              size_t workspace_bytes, void* stream);
+liger_status liger_attn_decode_step_sinks(const void* q, const void* k, const void* v,
+                                          float* S, const liger_kv_ring* kv_ring,
+                                          const liger_sinks* sinks, int32_t gate_mode,
+                                          float alpha, const liger_shape* shape, void* o,
+                                          void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* liger_last_error(void);

@@ -218,3 +218,32 @@ def test_full_causal_rejects_bad_arguments(lib, kw, ptrs, code):
     p.update(ptrs)
     st = lib.liger_attn_full_causal(p["q"], p["k"], p["v"], ctypes.byref(_shape(**kw)), p["o"], None)
     assert st == code, gla.liger_last_error()
+
+
+@pytest.mark.parametrize("n,k,v,code", [
+    (0, FAKE, FAKE, gla.LIGER_E_INVALID_ARG),
+    (17, FAKE, FAKE, gla.LIGER_E_INVALID_ARG),
+    (4, None, FAKE, gla.LIGER_E_INVALID_ARG),
+    (4, FAKE, FAKE + 8, gla.LIGER_E_INVALID_ARG),
+])
+def test_sinks_rejected(lib, n, k, v, code):
+    sk = gla.liger_sinks(k, v, n)
+    shp = _shape()
+    st = lib.liger_attn_prefill_sinks(FAKE, FAKE, FAKE, ctypes.byref(sk), 1, 64, 0.5, ctypes.byref(shp),
+                                      FAKE + 4096, FAKE + 8192, FAKE << 8, 1 << 30, None)
+    assert st == code, gla.liger_last_error()
+    ring = gla.liger_kv_ring(FAKE, FAKE, FAKE, FAKE, 64)
+    st = lib.liger_attn_decode_step_sinks(FAKE, FAKE, FAKE, FAKE, ctypes.byref(ring), ctypes.byref(sk), 1, 0.5,
+                                          ctypes.byref(shp), FAKE + 4096, None)
+    assert st == code, gla.liger_last_error()
+    st = lib.liger_attn_prefill_continue_sinks(FAKE, FAKE, FAKE, FAKE, ctypes.byref(ring), ctypes.byref(sk), 1, 0.5,
+                                               ctypes.byref(shp), FAKE + 4096, FAKE + 8192, FAKE << 8, 1 << 30, None)
+    assert st == code, gla.liger_last_error()
+
+
+def test_sinks_null_struct_rejected(lib):
+    shp = _shape()
+    st = lib.liger_attn_prefill_sinks(FAKE, FAKE, FAKE, None, 1, 64, 0.5, ctypes.byref(shp),
+                                      FAKE + 4096, FAKE + 8192, FAKE << 8, 1 << 30, None)
+    assert st == gla.LIGER_E_INVALID_ARG
+    assert "sinks" in gla.liger_last_error()

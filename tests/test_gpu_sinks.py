@@ -1,0 +1,114 @@
+"""GPU parity of the sliding window with meta-memory sink tokens against the
+float64 oracle: prefill, decode steps, the prefill continuation, and a GPU
+prefill handing over to GPU decode steps, all with the same sinks. Bars as
+for the plain path (fp32 relative 1e-4; bf16 2e-2 absolute on o, state
+1e-2 relative); ring contents bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_linear_recurrent_amd as gla
+import oracle
+from liger_testutil import DEV, TORCH_DT, abs_inf, check_prefill, rel_inf, say, to_dev, to_np
+from synth import prefill_inputs, round_to_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _sinks(H_kv, n, d, dtype, seed):
+    rng = np.random.default_rng(seed)
+    sk = rng.standard_normal((H_kv, n, d)).astype(np.float32)
+    sv = rng.standard_normal((H_kv, n, d)).astype(np.float32)
+    if dtype == "bf16":
+        sk, sv = round_to_bf16(sk), round_to_bf16(sv)
+    return sk, sv
+
+
+def _o_bar(dtype, o_gpu, o_ref, tag):
+    if dtype == "f32":
+        assert rel_inf(o_gpu, o_ref) <= 1e-4, (tag, rel_inf(o_gpu, o_ref))
+    else:
+        assert abs_inf(o_gpu, o_ref) <= 2e-2, (tag, abs_inf(o_gpu, o_ref))
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("n_rep,window,T,n", [(1, 64, 100, 1), (4, 64, 300, 16), (4, 7, 130, 5), (2, 1, 70, 3)])
+def test_prefill_with_sinks(dtype, d, gate, n_rep, window, T, n):
+    H_kv = 2
+    tag = f"sinks prefill {dtype} d={d} gate={gate} n_rep={n_rep} w={window} T={T} n={n}"
+    say(f"[sinks] {tag}")
+    x = prefill_inputs(B=2, T=T, H_q=H_kv * n_rep, H_kv=H_kv, d=d, dtype=dtype, seed=T + n + 3 * n_rep)
+    sk, sv = _sinks(H_kv, n, d, dtype, seed=n + d)
+    o_ref, S_ref = oracle.prefill(x["q"], x["k"], x["v"], gate, window, 0.5, sink_k=sk, sink_v=sv)
+    q, k, v = (to_dev(x[m], dtype) for m in ("q", "k", "v"))
+    o = torch.full_like(q, float("nan"))
+    o, S_T = gla.liger_attn_prefill(q, k, v, gate, window, 0.5, o=o, sinks=(to_dev(sk, dtype), to_dev(sv, dtype)))
+    torch.cuda.synchronize()
+    check_prefill(dtype, to_np(o), o_ref, to_np(S_T), S_ref, tag=tag)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("n_rep,window,T0,n", [(4, 64, 70, 16), (1, 17, 3, 2), (8, 64, 1, 7)])
+def test_decode_with_sinks(dtype, d, gate, n_rep, window, T0, n):
+    steps, N, H_kv = 8, 3, 2
+    tag = f"sinks decode {dtype} d={d} gate={gate} n_rep={n_rep} w={window} T0={T0} n={n}"
+    say(f"[sinks] {tag}")
+    x = prefill_inputs(B=N, T=T0 + steps, H_q=H_kv * n_rep, H_kv=H_kv, d=d, dtype=dtype, seed=5 * T0 + n)
+    sk, sv = _sinks(H_kv, n, d, dtype, seed=100 + n)
+    o_full, S_full = oracle.prefill(x["q"], x["k"], x["v"], gate, window, 0.5, sink_k=sk, sink_v=sv)
+    _, S0 = oracle.prefill(x["q"][:, :T0], x["k"][:, :T0], x["v"][:, :T0], gate, window, 0.5, sink_k=sk, sink_v=sv)
+    S = torch.from_numpy(S0.astype(np.float32)).to(DEV)
+    ring = gla.KVRing.empty(N, H_kv, window, d, TORCH_DT[dtype], DEV)
+    gla.liger_kv_ring_fill(to_dev(x["k"][:, :T0], dtype), to_dev(x["v"][:, :T0], dtype), ring)
+    sinks = (to_dev(sk, dtype), to_dev(sv, dtype))
+    for i in range(steps):
+        t = T0 + i
+        o = gla.liger_attn_decode_step(to_dev(x["q"][:, t], dtype), to_dev(x["k"][:, t], dtype),
+                                       to_dev(x["v"][:, t], dtype), S, ring, gate, 0.5, sinks=sinks)
+        torch.cuda.synchronize()
+        _o_bar(dtype, to_np(o), o_full[:, t], f"{tag} step {i}")
+    assert rel_inf(to_np(S), S_full) <= 1e-5, (tag, rel_inf(to_np(S), S_full))
+
+
+@pytest.mark.parametrize("gate", [0, 1])
+def test_continuation_with_sinks(gate):
+    dtype, d, n_rep, window, T1, T2, n, H_kv = "bf16", 128, 4, 64, 150, 200, 9, 2
+    say(f"[sinks] continuation gate={gate}")
+    x = prefill_inputs(B=2, T=T1 + T2, H_q=H_kv * n_rep, H_kv=H_kv, d=d, dtype=dtype, seed=61 + gate)
+    sk, sv = _sinks(H_kv, n, d, dtype, seed=7)
+    q, k, v = x["q"], x["k"], x["v"]
+    o_full, S_full = oracle.prefill(q, k, v, gate, window, 0.5, sink_k=sk, sink_v=sv)
+    _, S0 = oracle.prefill(q[:, :T1], k[:, :T1], v[:, :T1], gate, window, 0.5, sink_k=sk, sink_v=sv)
+    rk, rv, pos = oracle.ring_fill(k[:, :T1], v[:, :T1], window)
+    ring = gla.KVRing(to_dev(rk, dtype), to_dev(rv, dtype), torch.from_numpy(np.asarray(pos, np.int64)).to(DEV),
+                      torch.zeros(2, dtype=torch.int32, device=DEV), window)
+    o, S_T = gla.liger_attn_prefill_continue(*(to_dev(a[:, T1:], dtype) for a in (q, k, v)),
+                                             torch.from_numpy(S0.astype(np.float32)).to(DEV), ring, gate, 0.5,
+                                             sinks=(to_dev(sk, dtype), to_dev(sv, dtype)))
+    torch.cuda.synchronize()
+    check_prefill(dtype, to_np(o), o_full[:, T1:], to_np(S_T), S_full, tag="sinks continuation")
+
+
+def test_gpu_prefill_hands_over_to_decode_with_sinks():
+    dtype, d, n_rep, T0, steps, n, H_kv, N = "bf16", 128, 4, 260, 12, 16, 2, 2
+    say("[sinks] hand-over")
+    x = prefill_inputs(B=N, T=T0 + steps, H_q=H_kv * n_rep, H_kv=H_kv, d=d, dtype=dtype, seed=91)
+    sk, sv = _sinks(H_kv, n, d, dtype, seed=13)
+    o_full, S_full = oracle.prefill(x["q"], x["k"], x["v"], 1, 64, 0.5, sink_k=sk, sink_v=sv)
+    sinks = (to_dev(sk, dtype), to_dev(sv, dtype))
+    q0, k0, v0 = (to_dev(x[m][:, :T0], dtype) for m in ("q", "k", "v"))
+    o0, S = gla.liger_attn_prefill(q0, k0, v0, 1, 64, 0.5, sinks=sinks)
+    ring = gla.KVRing.empty(N, H_kv, 64, d, torch.bfloat16, DEV)
+    gla.liger_kv_ring_fill(k0, v0, ring)
+    torch.cuda.synchronize()
+    assert abs_inf(to_np(o0), o_full[:, :T0]) <= 2e-2
+    for i in range(steps):
+        t = T0 + i
+        o = gla.liger_attn_decode_step(to_dev(x["q"][:, t], dtype), to_dev(x["k"][:, t], dtype),
+                                       to_dev(x["v"][:, t], dtype), S, ring, 1, 0.5, sinks=sinks)
+        torch.cuda.synchronize()
+        assert abs_inf(to_np(o), o_full[:, t]) <= 2e-2, i
+    assert rel_inf(to_np(S), S_full) <= 1e-2
