@@ -236,13 +236,15 @@ def main() -> int:
         fflops = 4.0 * d * (T * (T + 1) / 2) * H_q * B  # q.k and p.v over the causal pairs
         fms = float(np.mean(np.concatenate([fcold, fhot])))
         fach = fflops / (fms * 1e-3) / 1e12
+        frec = counter_record("full_attn_kernel", FULL_WORKLOAD)
         result["full_attention"] = {
             "workload": FULL_WORKLOAD, "steps": nfull,
             "cold": stats(fcold), "hot": stats(fhot),
             "tokens_per_s": B * T / (float(np.median(fcold)) * 1e-3),
             "roofline": {"bound": "mfma", "achieved": fach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": fach / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "full_attn_kernel",
-                         "kernel_ms": fms, "algorithmic_flops": fflops},
+                         "frac": fach / PEAK_BF16_TFLOPS, "traffic": frec.get("hbm_bytes_per_launch"),
+                         "kernel": "full_attn_kernel", "kernel_ms": fms, "algorithmic_flops": fflops,
+                         "mfma_busy_frac_counters": frec.get("mfma_busy_frac")},
         }
         log(f"[bench] full attention {fms * 1e3:.1f} us ({fach:.0f} TFLOP/s, "
             f"{100 * fach / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")

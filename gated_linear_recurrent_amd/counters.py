@@ -34,12 +34,15 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # kernel -> (name prefix in the trace, workload it was measured on, sources hashed)
 KERNELS = {
-    "prefill_output_kernel": ("liger::prefill_output_kernel<unsigned short, 128, 0>", "prefill_8b_b1_t8192_d128",
+    "prefill_output_kernel": ("liger::prefill_output_kernel<unsigned short, 128, 0, false>", "prefill_8b_b1_t8192_d128",
                               ["gated_linear_recurrent_amd/csrc/prefill.hip",
                                "gated_linear_recurrent_amd/csrc/device_common.h"]),
-    "decode_step_kernel": ("liger::decode_step_kernel<unsigned short, 128, 1, 4>", "decode_8b_n64_d128",
+    "decode_step_kernel": ("liger::decode_step_kernel<unsigned short, 128, 1, 4, false>", "decode_8b_n64_d128",
                            ["gated_linear_recurrent_amd/csrc/decode.hip",
                             "gated_linear_recurrent_amd/csrc/device_common.h"]),
+    "full_attn_kernel": ("liger::full_attn_kernel<128, 4>", "full_attn_8b_b1_t8192_d128",
+                         ["gated_linear_recurrent_amd/csrc/full_attn.hip",
+                          "gated_linear_recurrent_amd/csrc/device_common.h"]),
 }
 N_SIMD = 1024
 N_XCD = 8
