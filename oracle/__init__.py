@@ -12,6 +12,7 @@ from .liger_ref import (  # noqa: F401
     pool_scalar_mean,
     pool_vector_avg4,
     prefill,
+    prefill_backward,
     prefill_continue,
     ring_fill,
     sigmoid,

@@ -295,3 +295,86 @@ def full_attention(q, k, v):
         p = softmax(np.matmul(qg[:, t], kw) * scale)       # [B, H_kv, n_rep, t+1]
         o[:, t] = np.matmul(p, vw)
     return o.reshape(B, T, H_q, d)
+
+
+def prefill_backward(q, k, v, dO, gate_mode, window, alpha):
+    """Gradients (dq, dk, dv) of sum(o * dO) for o = prefill(q, k, v, ...) from a zero state.
+
+    The chain rule through each step of the definition, in reverse token
+    order ([Notes] unified recurrence and Liger Attention sections):
+      GRM  o_t = phi(q_t) S_t, S_t = G_t (.) S_{t-1} + phi(k_t)^T v_t, adjoint
+           dS_t = sum_h phi(q_t^h)^T (alpha dO_t^h) + G_{t+1} (.) dS_{t+1};
+           dphi(q_t^h) = S_t (alpha dO_t^h), dphi(k_t) = dS_t v_t,
+           dv_t += phi(k_t) dS_t, dG_t = dS_t (.) S_{t-1} (summed over the
+           entries G_t scales: all of S for the scalar gate, row c for g[c]).
+      gate g = sigmoid(pool(k)): ds = dg g (1 - g), then the pool's transpose.
+      phi  softmax: dx = phi (.) (dphi - <dphi, phi>).
+      SWA  p = softmax(q k^T / sqrt(d)) over the window, o = p v:
+           dp = (1 - alpha) dO v^T, dz = p (.) (dp - <dp, p>),
+           dq += dz k / sqrt(d), dk += dz^T q / sqrt(d), dv += p^T (1 - alpha) dO.
+    q, dO: [B, T, H_q, d]; k, v: [B, T, H_kv, d]. Returns float64 arrays.
+    """
+    q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
+    B, T, H_q, d = q.shape
+    H_kv = k.shape[2]
+    n_rep = H_q // H_kv
+    scale = 1.0 / np.sqrt(d)
+    phi_q = softmax(q).reshape(B, T, H_kv, n_rep, d)
+    phi_k = softmax(k)
+    dOg = dO.reshape(B, T, H_kv, n_rep, d)
+    qg = q.reshape(B, T, H_kv, n_rep, d)
+    # forward: gates and every state (the adjoint needs S_{t-1})
+    if gate_mode == SCALAR_MEAN:
+        s_pre = pool_scalar_mean(k)                       # [B, T, H_kv, 1]
+    else:
+        s_pre = pool_vector_avg4(k)                       # [B, T, H_kv, d]
+    g = sigmoid(s_pre)
+    gS = np.broadcast_to(g, (B, T, H_kv, d))
+    S_all = np.zeros((T + 1, B, H_kv, d, d))              # S_all[t + 1] = S_t
+    for t in range(T):
+        S_all[t + 1] = gS[:, t, :, :, None] * S_all[t] + phi_k[:, t, :, :, None] * v[:, t, :, None, :]
+    d_phi_q = np.zeros((B, T, H_kv, n_rep, d))
+    d_phi_k = np.zeros((B, T, H_kv, d))
+    dv = np.zeros((B, T, H_kv, d))
+    dg = np.zeros_like(g)
+    dS = np.zeros((B, H_kv, d, d))
+    for t in range(T - 1, -1, -1):
+        if t + 1 < T:
+            dS = gS[:, t + 1, :, :, None] * dS
+        dS = dS + np.einsum("bhrc,bhre->bhce", phi_q[:, t], alpha * dOg[:, t])
+        S_t = S_all[t + 1]
+        d_phi_q[:, t] = np.einsum("bhce,bhre->bhrc", S_t, alpha * dOg[:, t])
+        d_phi_k[:, t] = np.einsum("bhce,bhe->bhc", dS, v[:, t])
+        dv[:, t] += np.einsum("bhc,bhce->bhe", phi_k[:, t], dS)
+        prod = dS * S_all[t]                              # dS_t (.) S_{t-1}
+        if gate_mode == SCALAR_MEAN:
+            dg[:, t] = prod.sum(axis=(-1, -2))[..., None]
+        else:
+            dg[:, t] = prod.sum(axis=-1)
+    # gate: sigmoid, then the pool's transpose
+    ds = dg * g * (1.0 - g)
+    dk = np.zeros((B, T, H_kv, d))
+    if gate_mode == SCALAR_MEAN:
+        dk += ds / d
+    else:
+        for c in range(d):
+            lo, hi = max(0, c - 1), min(d, c + 3)
+            dk[..., lo:hi] += ds[..., c:c + 1] / (hi - lo)
+    # softmax feature maps
+    dq = (phi_q * (d_phi_q - np.sum(d_phi_q * phi_q, axis=-1, keepdims=True))).reshape(B, T, H_q, d)
+    dk += phi_k * (d_phi_k - np.sum(d_phi_k * phi_k, axis=-1, keepdims=True))
+    dq = dq.reshape(B, T, H_kv, n_rep, d)
+    # sliding-window softmax attention
+    for t in range(T):
+        lo = max(0, t - window + 1)
+        kw = k[:, lo:t + 1]                                # [B, L, H_kv, d]
+        vw = v[:, lo:t + 1]
+        z = np.einsum("bhrc,blhc->bhrl", qg[:, t], kw) * scale
+        p = softmax(z)                                     # [B, H_kv, n_rep, L]
+        do = (1.0 - alpha) * dOg[:, t]                     # [B, H_kv, n_rep, d]
+        dp = np.einsum("bhre,blhe->bhrl", do, vw)
+        dz = p * (dp - np.sum(dp * p, axis=-1, keepdims=True))
+        dq[:, t] += np.einsum("bhrl,blhc->bhrc", dz, kw) * scale
+        dk[:, lo:t + 1] += np.einsum("bhrl,bhrc->blhc", dz, qg[:, t]) * scale
+        dv[:, lo:t + 1] += np.einsum("bhrl,bhre->blhe", p, do)
+    return dq.reshape(B, T, H_q, d), dk, dv

@@ -303,6 +303,62 @@ def test_sinks_decode_continues_prefill(mode):
     assert _close(S, S_full, rtol=1e-11)
 
 
+@pytest.mark.parametrize("mode", [oracle.SCALAR_MEAN, oracle.VECTOR_AVGPOOL4])
+@pytest.mark.parametrize("n_rep,window,alpha", [(1, 1, 0.5), (2, 3, 0.3), (2, 64, 0.8)])
+def test_backward_matches_central_differences(mode, n_rep, window, alpha):
+    """Every entry of dq, dk, dv against central differences of sum(o * W)
+    on the float64 forward (h = 1e-6). Catches any dropped term of the
+    chain rule (adjoint decay, gate, pool transpose, softmax Jacobians,
+    window range)."""
+    rng = np.random.default_rng(50 + 7 * n_rep + window + mode)
+    B, T, H_kv, d = 1, 6, 1, 4
+    q = rng.standard_normal((B, T, H_kv * n_rep, d))
+    k = rng.standard_normal((B, T, H_kv, d))
+    v = rng.standard_normal((B, T, H_kv, d))
+    W = rng.standard_normal((B, T, H_kv * n_rep, d))
+    dq, dk, dv = oracle.prefill_backward(q, k, v, W, mode, window, alpha)
+
+    def loss(qq, kk, vv):
+        return float(np.sum(oracle.prefill(qq, kk, vv, mode, window, alpha)[0] * W))
+
+    h = 1e-6
+    for name, X, G in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in np.ndindex(X.shape):
+            args = {"qq": q, "kk": k, "vv": v}
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += h
+            Xm[idx] -= h
+            args[name * 2] = Xp
+            lp = loss(**args)
+            args[name * 2] = Xm
+            lm = loss(**args)
+            assert abs((lp - lm) / (2 * h) - G[idx]) <= 1e-6, (name, idx)
+
+
+@pytest.mark.parametrize("n_rep", [1, 2])
+def test_backward_full_window_is_library_attention_gradient(n_rep):
+    """alpha = 0 and a window longer than the sequence: the gradients of plain
+    causal softmax attention, from torch autograd of scaled_dot_product_attention
+    in float64."""
+    rng = np.random.default_rng(70 + n_rep)
+    B, T, H_kv, d = 2, 11, 2, 8
+    q = rng.standard_normal((B, T, H_kv * n_rep, d))
+    k = rng.standard_normal((B, T, H_kv, d))
+    v = rng.standard_normal((B, T, H_kv, d))
+    W = rng.standard_normal((B, T, H_kv * n_rep, d))
+    dq, dk, dv = oracle.prefill_backward(q, k, v, W, oracle.SCALAR_MEAN, T + 3, 0.0)
+    tq = torch.from_numpy(q).transpose(1, 2).requires_grad_()
+    tk = torch.from_numpy(k).transpose(1, 2).requires_grad_()
+    tv = torch.from_numpy(v).transpose(1, 2).requires_grad_()
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(n_rep, dim=1), tv.repeat_interleave(n_rep, dim=1), is_causal=True,
+        scale=1.0 / math.sqrt(d))
+    (o * torch.from_numpy(W).transpose(1, 2)).sum().backward()
+    assert _close(dq, tq.grad.transpose(1, 2).numpy(), rtol=1e-12)
+    assert _close(dk, tk.grad.transpose(1, 2).numpy(), rtol=1e-12)
+    assert _close(dv, tv.grad.transpose(1, 2).numpy(), rtol=1e-12)
+
+
 def test_alpha_is_affine_and_endpoints():
     """Pin 4: o(alpha) = alpha o(1) + (1-alpha) o(0); alpha=1 pure GRM, 0 pure SWA."""
     x = prefill_inputs(B=1, T=40, H_q=4, H_kv=2, d=8, dtype="f32", seed=3)
