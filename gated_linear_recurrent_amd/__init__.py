@@ -48,6 +48,8 @@ EXPORTED = (
     "liger_attn_prefill_sinks",
     "liger_attn_prefill_continue_sinks",
     "liger_attn_decode_step_sinks",
+    "liger_attn_prefill_backward_workspace_size",
+    "liger_attn_prefill_backward",
     "liger_last_error",
 )
 
@@ -111,6 +113,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.liger_attn_prefill_continue_sinks.restype = i32
     lib.liger_attn_decode_step_sinks.argtypes = [vp, vp, vp, vp, ring, snk, i32, f32, shp, vp, vp]
     lib.liger_attn_decode_step_sinks.restype = i32
+    lib.liger_attn_prefill_backward_workspace_size.argtypes = [shp]
+    lib.liger_attn_prefill_backward_workspace_size.restype = sz
+    lib.liger_attn_prefill_backward.argtypes = [vp, vp, vp, vp, i32, i32, f32, shp, vp, vp, vp, vp, sz, vp]
+    lib.liger_attn_prefill_backward.restype = i32
     lib.liger_last_error.argtypes = []
     lib.liger_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -279,6 +285,31 @@ def liger_attn_full_causal(q, k, v, *, o=None, stream=None):
         o = torch.empty_like(q)
     _check(lib.liger_attn_full_causal(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(shp), _ptr(o), _stream(stream)))
     return o
+
+
+def liger_attn_prefill_backward(q, k, v, dO, gate_mode: int, window: int, alpha: float, *, dq=None, dk=None,
+                                dv=None, workspace=None, stream=None):
+    """Gradients of sum(o * dO) for o = liger_attn_prefill(q, k, v, ...): q, dO [B,T,H_q,d], k/v [B,T,H_kv,d]
+    (bf16); returns float32 (dq, dk, dv)."""
+    torch = _torch()
+    lib = load_library()
+    B, T, H_q, d = q.shape
+    H_kv = k.shape[2]
+    shp = make_shape(B, T, H_q, H_kv, d, _dtype_code(q))
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    need = lib.liger_attn_prefill_backward_workspace_size(ctypes.byref(shp))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.liger_attn_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), gate_mode, window, alpha,
+                                           ctypes.byref(shp), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                           ws_bytes, _stream(stream)))
+    return dq, dk, dv
 
 
 def liger_attn_decode_step(q, k, v, S, ring: KVRing, gate_mode: int, alpha: float, *, o=None, stream=None,

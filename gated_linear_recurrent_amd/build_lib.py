@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libliger_attn.so")
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "full_attn.hip"]
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "full_attn.hip", "backward.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -388,6 +388,56 @@ liger_status liger_attn_full_causal(const void* q, const void* k, const void* v,
     return map_hip(liger::launch_full_attn(a), "full attention launch");
 }
 
+size_t liger_attn_prefill_backward_workspace_size(const liger_shape* shape) {
+    if (check_shape(shape, true) != LIGER_OK) return 0;
+    return liger::backward_workspace_bytes(shape->B, shape->T, shape->H_kv, shape->H_q, shape->d);
+}
+
+liger_status liger_attn_prefill_backward(const void* q, const void* k, const void* v, const void* dO,
+                                         int32_t gate_mode, int32_t window, float alpha,
+                                         const liger_shape* shape, float* dq, float* dk, float* dv,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+    LIGER_TRY(check_shape(shape, true));
+    LIGER_TRY(check_common(gate_mode, alpha));
+    if (shape->dtype != LIGER_BF16) return fail(LIGER_E_UNSUPPORTED, "the backward is built for bf16 inputs only");
+    if (window < 1 || window > 64) return fail(LIGER_E_INVALID_ARG, "window must be in 1..64");
+    LIGER_TRY(check_ptr(q, "q"));
+    LIGER_TRY(check_ptr(k, "k"));
+    LIGER_TRY(check_ptr(v, "v"));
+    LIGER_TRY(check_ptr(dO, "dO"));
+    LIGER_TRY(check_ptr(dq, "dq"));
+    LIGER_TRY(check_ptr(dk, "dk"));
+    LIGER_TRY(check_ptr(dv, "dv"));
+    const void* outs[3] = {dq, dk, dv};
+    const void* ins[4] = {q, k, v, dO};
+    for (const void* o : outs)
+        for (const void* i : ins)
+            if (o == i) return fail(LIGER_E_INVALID_ARG, "dq, dk and dv must not alias the inputs");
+    if (dq == dk || dq == dv || dk == dv) return fail(LIGER_E_INVALID_ARG, "dq, dk and dv must be distinct");
+    const size_t need = liger::backward_workspace_bytes(shape->B, shape->T, shape->H_kv, shape->H_q, shape->d);
+    if (workspace_bytes < need) return fail(LIGER_E_WORKSPACE, "workspace smaller than liger_attn_prefill_backward_workspace_size");
+    if (need > 0) LIGER_TRY(check_ptr(workspace, "workspace"));
+    liger::BackwardArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dO = dO;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.B = shape->B;
+    a.T = shape->T;
+    a.H_kv = shape->H_kv;
+    a.n_rep = shape->H_q / shape->H_kv;
+    a.d = shape->d;
+    a.window = window;
+    a.gate = gate_mode;
+    a.alpha = alpha;
+    a.workspace = static_cast<float*>(workspace);
+    a.stream = stream;
+    return map_hip(liger::launch_backward(a), "backward launch");
+}
+
 liger_status liger_kv_ring_fill(const void* k, const void* v, const liger_shape* shape,
                                 const liger_kv_ring* kv_ring, void* stream) {
     LIGER_TRY(check_shape(shape, true));

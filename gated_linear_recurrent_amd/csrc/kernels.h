@@ -123,5 +123,31 @@ hipError_t launch_ring_fill(const RingFillArgs& a);
 hipError_t launch_ring_append(const RingFillArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 hipError_t launch_full_attn(const FullAttnArgs& a);
+// Carry records [B, H_kv, n_seg - 1, d*d + d] (state, log2 row decay) are
+// replaced in place by the running states R_s = 2^(lg_s) (.) R_{s-1} + L_s, R_{-1} = 0.
+hipError_t launch_carry_scan(float* carry, int64_t n_seg, int H_kv, int64_t B, int d, void* stream);
+
+// Backward of the prefill (bf16 inputs, float32 gradients).
+struct BackwardArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dO;
+    float* dq;
+    float* dk;
+    float* dv;
+    int64_t B;
+    int64_t T;
+    int H_kv;
+    int n_rep;
+    int d;
+    int window;
+    int gate;
+    float alpha;
+    float* workspace;
+    void* stream;
+};
+size_t backward_workspace_bytes(int64_t B, int64_t T, int H_kv, int H_q, int d);
+hipError_t launch_backward(const BackwardArgs& a);
 
 }  // namespace liger

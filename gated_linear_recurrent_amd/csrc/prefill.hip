@@ -1843,6 +1843,18 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     return hipSuccess;
 }
 
+hipError_t launch_carry_scan(float* carry, int64_t n_seg, int H_kv, int64_t B, int d, void* stream) {
+    if (n_seg <= 1) return hipSuccess;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (d == 64)
+        hipLaunchKernelGGL((carry_scan_kernel<64>), dim3(64 * 64 / 256, H_kv, unsigned(B)), dim3(256), 0, st, carry,
+                           nullptr, n_seg, H_kv);
+    else
+        hipLaunchKernelGGL((carry_scan_kernel<128>), dim3(128 * 128 / 256, H_kv, unsigned(B)), dim3(256), 0, st,
+                           carry, nullptr, n_seg, H_kv);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill(const PrefillArgs& a) {
     if (a.bf16) {
         if (a.d == 64) return a.gate ? launch_prefill_t<bf16_t, 64, 1>(a) : launch_prefill_t<bf16_t, 64, 0>(a);

@@ -257,6 +257,33 @@ liger_status liger_attn_decode_step_sinks(const void* q, const void* k, const vo
                                           float alpha, const liger_shape* shape, void* o,
                                           void* stream);
 
+/*
+ * Backward of liger_attn_prefill (training): the gradients of
+ * L = sum(o * dO) with respect to q, k and v, for o the prefill output of
+ * q, k, v from a zero state (paper-notes page "Liger: Linearizing Large
+ * Language Models to Gated Recurrent Structures": unified gated linear
+ * recurrence, Liger Attention, and the gate built from the key projection;
+ * the gradient flows through phi, the pooled sigmoid gate and both token
+ * mixers).
+ *   q, dO [B, T, H_q, d]; k, v [B, T, H_kv, d]: bf16 only (fp32 is
+ *   LIGER_E_UNSUPPORTED), d in {64, 128}, any H_q / H_kv.
+ *   dq [B, T, H_q, d], dk, dv [B, T, H_kv, d]: float32, written (not
+ *   accumulated); distinct and not aliasing any input.
+ *   gate_mode, window (1..64) and alpha as given to the prefill.
+ *   workspace: at least liger_attn_prefill_backward_workspace_size bytes of
+ *   device memory (chunk-start states, chunk adjoints, per-row gate
+ *   gradients and window statistics); contents on entry ignored, on return
+ *   unspecified.
+ * Meta-memory sink tokens are not part of this call.
+ */
+size_t liger_attn_prefill_backward_workspace_size(const liger_shape* shape);
+liger_status liger_attn_prefill_backward(const void* q, const void* k, const void* v,
+                                         const void* dO, int32_t gate_mode, int32_t window,
+                                         float alpha, const liger_shape* shape,
+                                         float* dq, float* dk, float* dv,
+                                         void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* liger_last_error(void);
 

@@ -13,4 +13,5 @@ from .inputs import (  # noqa: F401
     prefill_inputs,
     decode_initial,
     decode_step_inputs,
+    grad_output,
 )

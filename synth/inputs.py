@@ -99,6 +99,13 @@ def prefill_inputs(B: int, T: int, H_q: int, H_kv: int, d: int, dtype: str,
                 outlier_rows=np.sort(rows))
 
 
+def grad_output(shape, dtype: str, seed: int, scale: float = 1.0) -> np.ndarray:
+    """Upstream gradient dO ~ scale * N(0, 1) of the given shape, from
+    PCG64(SeedSequence([seed, 7])), as canonical stored values."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7])))
+    return _store(np.float32(scale) * rng.standard_normal(tuple(shape), dtype=np.float32), dtype)
+
+
 def config_prefill_inputs(name: str, T: int | None = None) -> dict:
     """Inputs of a named prefill workload (optionally only its first T tokens).
 

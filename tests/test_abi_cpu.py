@@ -247,3 +247,39 @@ def test_sinks_null_struct_rejected(lib):
                                       FAKE + 4096, FAKE + 8192, FAKE << 8, 1 << 30, None)
     assert st == gla.LIGER_E_INVALID_ARG
     assert "sinks" in gla.liger_last_error()
+
+
+@pytest.mark.parametrize("kw,ptrs,extra,code", [
+    (dict(dtype=gla.LIGER_F32, d=64), {}, {}, gla.LIGER_E_UNSUPPORTED),
+    (dict(d=96), {}, {}, gla.LIGER_E_UNSUPPORTED),
+    ({}, {}, dict(window=0), gla.LIGER_E_INVALID_ARG),
+    ({}, {}, dict(window=65), gla.LIGER_E_INVALID_ARG),
+    ({}, {}, dict(alpha=1.5), gla.LIGER_E_INVALID_ARG),
+    ({}, {}, dict(gate=2), gla.LIGER_E_INVALID_ARG),
+    ({}, dict(dO=None), {}, gla.LIGER_E_INVALID_ARG),
+    ({}, dict(dq=FAKE), {}, gla.LIGER_E_INVALID_ARG),
+    ({}, dict(dv=FAKE + 0x4000), {}, gla.LIGER_E_INVALID_ARG),
+    ({}, dict(dk=FAKE + 0x5008), {}, gla.LIGER_E_INVALID_ARG),
+    ({}, {}, dict(ws_bytes=16), gla.LIGER_E_WORKSPACE),
+])
+def test_backward_rejects_bad_arguments(lib, kw, ptrs, extra, code):
+    p = dict(q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, dO=FAKE + 0x3000, dq=FAKE + 0x4000, dk=FAKE + 0x5000,
+             dv=FAKE + 0x6000)
+    p.update(ptrs)
+    e = dict(gate=1, window=64, alpha=0.5, ws_bytes=1 << 40)
+    e.update(extra)
+    shp = _shape(**kw)
+    st = lib.liger_attn_prefill_backward(p["q"], p["k"], p["v"], p["dO"], e["gate"], e["window"], e["alpha"],
+                                         ctypes.byref(shp), p["dq"], p["dk"], p["dv"], FAKE << 8, e["ws_bytes"],
+                                         None)
+    assert st == code, gla.liger_last_error()
+
+
+def test_backward_workspace_size(lib):
+    """Two record sets of d*d + d floats per chunk boundary, per-row gate
+    gradients, chunk sums and two window statistics per query row."""
+    shp = _shape(B=2, T=130, H_q=8, H_kv=2, d=64)
+    n = 3
+    want = 4 * (2 * 2 * 2 * (n - 1) * (64 * 64 + 64) + 2 * 2 * 130 * 64 + 2 * 2 * n * 64 + 2 * 130 * 8 * 2)
+    assert lib.liger_attn_prefill_backward_workspace_size(ctypes.byref(shp)) == want
+    assert lib.liger_attn_prefill_backward_workspace_size(ctypes.byref(_shape(T=0))) == 0

@@ -1,0 +1,94 @@
+"""GPU parity of the prefill backward (dq, dk, dv of sum(o * dO)) against the
+float64 oracle's reverse pass, on bf16 inputs (the gradients are float32).
+
+Bar: for each of dq, dk, dv, max |gpu - ref| <= 2e-3 * max |ref|. Every
+product of the recurrent part is taken in fp32 (raw bf16 operands exactly,
+computed operands unrounded), so the errors come from fp32 rounding and the
+hardware exp2; 2e-3 leaves room for the cancellation in the gate gradient
+(the difference of the q-side and k-side terms, summed over the suffix).
+
+Cases span one and many 64-token chunks, ragged tails, T = 1, windows
+1 .. 64, H_q / H_kv from 1 to 8, alpha = 0 and 1, both gates, and keys
+scaled x40 so that gate channels become extreme (cumulative decay beyond
+2^96 inside a chunk: the pair-by-pair path).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_linear_recurrent_amd as gla
+import oracle
+from liger_testutil import DEV, say, to_dev, to_np
+from synth import grad_output, prefill_inputs, round_to_bf16
+
+pytestmark = pytest.mark.gpu
+
+BAR = 2e-3
+
+
+def _run(x, dO, gate, window, alpha):
+    q, k, v = (to_dev(x[n], "bf16") for n in ("q", "k", "v"))
+    g = to_dev(dO, "bf16")
+    dq = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    dk = torch.full(k.shape, float("nan"), dtype=torch.float32, device=DEV)
+    dv = torch.full(v.shape, float("nan"), dtype=torch.float32, device=DEV)
+    gla.liger_attn_prefill_backward(q, k, v, g, gate, window, alpha, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return to_np(dq), to_np(dk), to_np(dv)
+
+
+def _check(got, ref, tag):
+    errs = []
+    for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+        assert np.all(np.isfinite(a)), f"{tag}: {name} has non-finite entries"
+        scale = max(float(np.max(np.abs(r))), 1e-30)
+        errs.append(float(np.max(np.abs(a - r))) / scale)
+    say(f"  {tag}: rel err dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}")
+    assert max(errs) <= BAR, (tag, errs)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("B,T,n_rep,window", [(2, 100, 1, 64), (1, 300, 4, 64), (2, 130, 2, 7),
+                                              (1, 70, 8, 1), (1, 64, 4, 33), (1, 1, 2, 64)])
+def test_backward_matches_oracle(d, gate, B, T, n_rep, window):
+    H_kv = 2
+    tag = f"bwd d={d} gate={gate} B={B} T={T} n_rep={n_rep} w={window}"
+    say(f"[bwd] {tag}")
+    x = prefill_inputs(B=B, T=T, H_q=H_kv * n_rep, H_kv=H_kv, d=d, dtype="bf16", seed=T + 3 * n_rep + d + gate)
+    dO = grad_output(x["q"].shape, "bf16", seed=T + window)
+    ref = oracle.prefill_backward(x["q"], x["k"], x["v"], dO, gate, window, 0.5)
+    _check(_run(x, dO, gate, window, 0.5), ref, tag)
+
+
+@pytest.mark.parametrize("alpha", [0.0, 1.0])
+@pytest.mark.parametrize("gate", [0, 1])
+def test_backward_alpha_ends(alpha, gate):
+    tag = f"bwd alpha={alpha} gate={gate}"
+    say(f"[bwd] {tag}")
+    x = prefill_inputs(B=1, T=200, H_q=8, H_kv=2, d=128, dtype="bf16", seed=17 + gate)
+    dO = grad_output(x["q"].shape, "bf16", seed=23)
+    ref = oracle.prefill_backward(x["q"], x["k"], x["v"], dO, gate, 64, alpha)
+    _check(_run(x, dO, gate, 64, alpha), ref, tag)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_extreme_gate_channels(d):
+    """Keys x40: per-channel decays beyond 2^96 within a chunk (vector gate)."""
+    tag = f"bwd extreme d={d}"
+    say(f"[bwd] {tag}")
+    x = prefill_inputs(B=1, T=150, H_q=4, H_kv=2, d=d, dtype="bf16", seed=77)
+    x["k"] = round_to_bf16(x["k"] * 40.0)
+    dO = grad_output(x["q"].shape, "bf16", seed=5)
+    ref = oracle.prefill_backward(x["q"], x["k"], x["v"], dO, 1, 64, 0.5)
+    _check(_run(x, dO, 1, 64, 0.5), ref, tag)
+
+
+def test_backward_long_sequence():
+    """32 chunks through both scans: T = 2048, H_q = 8, H_kv = 2, d = 128."""
+    tag = "bwd long"
+    say(f"[bwd] {tag}")
+    x = prefill_inputs(B=1, T=2048, H_q=8, H_kv=2, d=128, dtype="bf16", seed=2048)
+    dO = grad_output(x["q"].shape, "bf16", seed=9)
+    ref = oracle.prefill_backward(x["q"], x["k"], x["v"], dO, 1, 64, 0.5)
+    _check(_run(x, dO, 1, 64, 0.5), ref, tag)
