@@ -231,7 +231,8 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
     const int nv = static_cast<int>(T - t0 < 64 ? T - t0 : 64);
     const int H_q = p.H_kv * p.n_rep;
     const int64_t kvs = static_cast<int64_t>(p.H_kv) * D, qs = static_cast<int64_t>(H_q) * D;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, g = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
     const int cb = w % NCB, eb0 = (w / NCB) * NE;
 
     stage_f32<D, kBT>(sK, FP, p.k + ((b * T + t0) * p.H_kv + hk) * D, kvs, nv);
@@ -355,8 +356,10 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
     const int nv = static_cast<int>(T - t0 < 64 ? T - t0 : 64);
     const int H_q = p.H_kv * p.n_rep;
     const int64_t kvs = static_cast<int64_t>(p.H_kv) * D, qs = static_cast<int64_t>(H_q) * D;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, g = lane >> 4;
-    const int jb = w % NCB, i0 = (w / NCB) * NTI;
+    const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+    // with one wave per column block every wave starts at row tile 0 (known at compile time)
+    const int jb = w % NCB, i0 = WPC == 1 ? 0 : (w / NCB) * NTI;
     const int cc = 16 * jb + col;  // this lane's output column
     const float alpha = p.alpha;
     const size_t rec = size_t(D) * D + D;
@@ -409,20 +412,26 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
         // Q^ = phi(q) 2^(b-m) (extreme channels: phi(q))
         row_softmax<D, true>(sQ, FP, nv, sBeta, sM, sExt);
         // A^h = alpha dO V^T, zero above the diagonal
+        {
+            // tiles w and w + 8 of the 4 x 4 grid (row tile s-block, column tile t-block)
+            const int is0 = w >> 2, it0 = w & 3, is1 = (w + 8) >> 2, it1 = w & 3;
+            f32x4_t a0 = zero4(), a1 = zero4();
+            const bool live0 = it0 <= is0, live1 = it1 <= is1;
 #pragma unroll
-        for (int rep = 0; rep < 2; ++rep) {
-            const int tile = w + 8 * rep, is = tile >> 2, it = tile & 3;
-            f32x4_t a = zero4();
-            if (it <= is) {
-#pragma unroll
-                for (int k = 0; k < KS; ++k)
-                    a = M::mma(M::load(sO + (16 * is + col) * HP + 8 * g + M::KSTEP * k),
-                               M::load(sV + (16 * it + col) * HP + 8 * g + M::KSTEP * k), a);
+            for (int k = 0; k < KS; ++k) {
+                if (live0)
+                    a0 = M::mma(M::load(sO + (16 * is0 + col) * HP + 8 * g + M::KSTEP * k),
+                                M::load(sV + (16 * it0 + col) * HP + 8 * g + M::KSTEP * k), a0);
+                if (live1)
+                    a1 = M::mma(M::load(sO + (16 * is1 + col) * HP + 8 * g + M::KSTEP * k),
+                                M::load(sV + (16 * it1 + col) * HP + 8 * g + M::KSTEP * k), a1);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int s = 16 * is + 4 * g + r, t = 16 * it + col;
-                sA[s * AP + t] = t <= s ? alpha * a[r] : 0.f;
+                const int s0 = 16 * is0 + 4 * g + r, t0c = 16 * it0 + col;
+                const int s1 = 16 * is1 + 4 * g + r, t1c = 16 * it1 + col;
+                sA[s0 * AP + t0c] = t0c <= s0 ? alpha * a0[r] : 0.f;
+                sA[s1 * AP + t1c] = t1c <= s1 ? alpha * a1[r] : 0.f;
             }
         }
         __syncthreads();
@@ -514,27 +523,33 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
         }
         __syncthreads();
 
-        // alpha B^h[t][s] (s >= t), stored transposed over A^h
+        // alpha B^h[t][s] (s >= t), stored transposed over A^h; tiles w and w + 8 of
+        // the 4 x 4 grid (row tile t-block, column tile s-block), computed together
+        {
+            const int it0 = w >> 2, is0 = w & 3, it1 = (w + 8) >> 2, is1 = w & 3;
+            const bool live0 = is0 >= it0, live1 = is1 >= it1;
+            f32x4_t a0 = zero4(), a1 = zero4();
 #pragma unroll
-        for (int rep = 0; rep < 2; ++rep) {
-            const int tile = w + 8 * rep, it = tile >> 2, is = tile & 3;
-            f32x4_t a = zero4();
-            if (is >= it) {
+            for (int k4 = 0; k4 < KQ / 4; ++k4) {
+                const float4 y4 = *reinterpret_cast<const float4*>(sQ + (16 * is0 + col) * FP + g * KQ + 4 * k4);
+                const float4 x40 = *reinterpret_cast<const float4*>(sKh + (16 * it0 + col) * FP + g * KQ + 4 * k4);
+                const float4 x41 = *reinterpret_cast<const float4*>(sKh + (16 * it1 + col) * FP + g * KQ + 4 * k4);
+                const float ys[4] = {y4.x, y4.y, y4.z, y4.w};
+                const float xs0[4] = {x40.x, x40.y, x40.z, x40.w}, xs1[4] = {x41.x, x41.y, x41.z, x41.w};
 #pragma unroll
-                for (int k4 = 0; k4 < KQ / 4; ++k4) {
-                    const float4 x4 = *reinterpret_cast<const float4*>(sKh + (16 * it + col) * FP + g * KQ + 4 * k4);
-                    const float4 y4 = *reinterpret_cast<const float4*>(sQ + (16 * is + col) * FP + g * KQ + 4 * k4);
-                    const float xs[4] = {x4.x, x4.y, x4.z, x4.w}, ys[4] = {y4.x, y4.y, y4.z, y4.w};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const bool ext = (kbits >> (4 * k4 + j)) & 1u;
-                        a = mma4(ext ? 0.f : xs[j], ys[j], a);
-                    }
+                for (int j = 0; j < 4; ++j) {
+                    const bool ext = (kbits >> (4 * k4 + j)) & 1u;
+                    if (live0) a0 = mma4(ext ? 0.f : xs0[j], ys[j], a0);
+                    if (live1) a1 = mma4(ext ? 0.f : xs1[j], ys[j], a1);
                 }
-                if (any_ext) {
+            }
+            if (any_ext) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int t = 16 * it + 4 * g + r, s = 16 * is + col;
+                for (int r = 0; r < 4; ++r) {
+                    const int s = 16 * is0 + col;
+#pragma unroll
+                    for (int tl = 0; tl < 2; ++tl) {
+                        const int t = 16 * (tl ? it1 : it0) + 4 * g + r;
                         if (s < t) continue;
                         float sum = 0.f;
                         for (int wd = 0; wd < D / 32; ++wd) {
@@ -546,14 +561,17 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
                                        fast_exp2(sBeta[s * D + ch] - sBeta[t * D + ch]);
                             }
                         }
-                        a[r] += sum;
+                        if (tl) a1[r] += sum;
+                        else a0[r] += sum;
                     }
                 }
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 16 * it + 4 * g + r, s = 16 * is + col;
-                sA[s * AP + t] = s >= t ? alpha * a[r] : 0.f;
+                const int s = 16 * is0 + col;
+                const int t0r = 16 * it0 + 4 * g + r, t1r = 16 * it1 + 4 * g + r;
+                sA[s * AP + t0r] = s >= t0r ? alpha * a0[r] : 0.f;
+                sA[s * AP + t1r] = s >= t1r ? alpha * a1[r] : 0.f;
             }
         }
         // dq^h = phi(q) (.) (dphi(q) - <dphi(q), phi(q)>)
@@ -687,7 +705,8 @@ __global__ __launch_bounds__(kST) void bwd_swa_q_kernel(BwdParams p) {
     const int64_t b = blockIdx.z, T = p.T, t0 = 64 * static_cast<int64_t>(c);
     const int H_q = p.H_kv * p.n_rep;
     const int64_t kvs = static_cast<int64_t>(p.H_kv) * D, qs = static_cast<int64_t>(H_q) * D;
-    const int tid = threadIdx.x, lane = tid & 63, wi = tid >> 6, col = lane & 15, g = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g = lane >> 4;
+    const int wi = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
     // key row kk of the tiles is token t0 - 64 + kk
     {
         const int64_t first = t0 - 64;
@@ -820,7 +839,8 @@ __global__ __launch_bounds__(kST) void bwd_swa_k_kernel(BwdParams p) {
     const int64_t b = blockIdx.z, T = p.T, t0 = 64 * static_cast<int64_t>(c);
     const int H_q = p.H_kv * p.n_rep;
     const int64_t kvs = static_cast<int64_t>(p.H_kv) * D, qs = static_cast<int64_t>(H_q) * D;
-    const int tid = threadIdx.x, lane = tid & 63, wi = tid >> 6, col = lane & 15, g = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g = lane >> 4;
+    const int wi = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
     const int w = p.window;
     const float sc = kLog2e * rsqrtf(static_cast<float>(D));
     const float beta = 1.0f - p.alpha;
@@ -926,6 +946,7 @@ __global__ __launch_bounds__(kST) void bwd_gate_kernel(BwdParams p) {
     constexpr int FP = D + 4;
     __shared__ __align__(16) float sK[64 * FP];
     __shared__ __align__(16) float sS[64 * FP];
+    __shared__ float sSuf[kST];
 
     const int c = blockIdx.x, hk = blockIdx.y;
     const int64_t b = blockIdx.z, n = p.n, T = p.T, t0 = 64 * static_cast<int64_t>(c);
@@ -941,10 +962,31 @@ __global__ __launch_bounds__(kST) void bwd_gate_kernel(BwdParams p) {
         }
     }
     __syncthreads();
+    {
+        // sum of the chunk sums after this chunk: thread (channel, part) takes
+        // every P-th later chunk, 16 loads in flight at a time
+        constexpr int P = kST / D, U = 16;
+        const int ch = tid % D, part = tid / D;
+        const float* tot = p.tot + (b * p.H_kv + hk) * n * D + ch;
+        float a[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) a[u] = 0.f;
+        for (int64_t j0 = c + 1 + part; j0 < n; j0 += U * P) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t j = j0 + u * P;
+                if (j < n) a[u] += tot[j * D];
+            }
+        }
+#pragma unroll
+        for (int u = 1; u < U; ++u) a[0] += a[u];
+        sSuf[part * D + ch] = a[0];
+    }
+    __syncthreads();
     if (tid < D) {
         float run = 0.f;
-        const float* tot = p.tot + (b * p.H_kv + hk) * n * D + tid;
-        for (int64_t j = c + 1; j < n; ++j) run += tot[j * D];
+#pragma unroll
+        for (int j = 0; j < kST / D; ++j) run += sSuf[j * D + tid];
         for (int t = nv - 1; t >= 0; --t) {
             run += sS[t * FP + tid];
             sS[t * FP + tid] = run;

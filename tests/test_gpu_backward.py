@@ -1,11 +1,11 @@
 """GPU parity of the prefill backward (dq, dk, dv of sum(o * dO)) against the
 float64 oracle's reverse pass, on bf16 inputs (the gradients are float32).
 
-Bar: for each of dq, dk, dv, max |gpu - ref| <= 2e-3 * max |ref|. Every
-product of the recurrent part is taken in fp32 (raw bf16 operands exactly,
-computed operands unrounded), so the errors come from fp32 rounding and the
-hardware exp2; 2e-3 leaves room for the cancellation in the gate gradient
-(the difference of the q-side and k-side terms, summed over the suffix).
+Bar: for each of dq, dk, dv, max |gpu - ref| <= 1e-4 * max |ref| (the
+fp32 bar of the forward). Every product is taken in fp32 (raw bf16 operands
+exactly, computed operands unrounded), so the errors come from fp32
+rounding and the hardware exp2 (measured: below 1e-6, and below 1e-5 with
+extreme gate channels).
 
 Cases span one and many 64-token chunks, ragged tails, T = 1, windows
 1 .. 64, H_q / H_kv from 1 to 8, alpha = 0 and 1, both gates, and keys
@@ -23,7 +23,7 @@ from synth import grad_output, prefill_inputs, round_to_bf16
 
 pytestmark = pytest.mark.gpu
 
-BAR = 2e-3
+BAR = 1e-4
 
 
 def _run(x, dO, gate, window, alpha):
