@@ -11,7 +11,8 @@ same steps without the eviction are reported as "hot". The JSON line also
 carries the roofline of the dominant kernel (the fused output kernel), the
 float64 CPU oracle on the host as a reported baseline, the hybrid's full
 causal softmax attention layer on the same inputs (cold and hot, against
-the dense bf16 MFMA peak), and the decode workload (64 sequences,
+the dense bf16 MFMA peak), the prefill's backward on the same inputs (cold
+and hot), and the decode workload (64 sequences,
 Llama-3-8B heads, one token per step: launched back to back, each between
 its own events, replayed from a captured HIP graph, and cold steps).
 
@@ -38,6 +39,7 @@ DECODE_WORKLOAD = "decode_8b_n64_d128"
 FULL_WORKLOAD = "full_attn_8b_b1_t8192_d128"
 N_SINKS = 16      # meta-memory tokens per key/value head in the sink measurements (synthetic, N(0, 1))
 SINK_SEED = 17  # the softmax layer on the prefill workload's inputs
+BWD_SEED = 23   # upstream gradient of the backward measurement
 CHUNK = 64
 SCRUB_BYTES = 512 << 20        # larger than the 256 MB last-level cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
@@ -110,6 +112,7 @@ def main() -> int:
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-full", action="store_true", help="skip the full causal attention layer")
+    ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-tokens", type=int, default=8192)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -276,6 +279,43 @@ def main() -> int:
     result["prefill_sinks"] = {"workload": PREFILL_WORKLOAD, "n_sinks": N_SINKS, "cold": stats(scold), "hot": stats(shot),
                                "tokens_per_s": B * T / (float(np.median(scold)) * 1e-3)}
     log(f"[bench] prefill with {N_SINKS} sinks: cold {np.median(scold) * 1e3:.1f} us, hot {np.median(shot) * 1e3:.1f} us")
+
+    if not args.no_backward:
+        # the prefill's backward on the same inputs, upstream gradient dO ~ N(0, 1) (bf16)
+        from synth import grad_output
+        dO = torch.from_numpy(grad_output(x["q"].shape, "bf16", seed=BWD_SEED)).to(dev).to(torch.bfloat16)
+        bdq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        bdk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+        bdv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+        bws = torch.empty(max(gla.liger_attn_prefill_backward_workspace_size(B, T, H_q, H_kv, d), 16),
+                          dtype=torch.uint8, device=dev)
+
+        def backward():
+            gla.liger_attn_prefill_backward(q, k, v, dO, gate, cfg["window"], cfg["alpha"], dq=bdq, dk=bdk, dv=bdv,
+                                            workspace=bws)
+
+        for _ in range(max(1, args.warmup // 2)):
+            backward()
+        torch.cuda.synchronize()
+        nb = max(5, args.steps // 2)
+
+        def timed_backward(cold_steps: bool):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nb)]
+            for i, (e0, e1) in enumerate(ev):
+                if cold_steps:
+                    scrub.fill_(float(i))
+                e0.record()
+                backward()
+                e1.record()
+            torch.cuda.synchronize()
+            return np.array([a.elapsed_time(b) for a, b in ev])
+
+        bcold, bhot = timed_backward(True), timed_backward(False)
+        result["backward"] = {"workload": PREFILL_WORKLOAD, "steps": nb, "cold": stats(bcold), "hot": stats(bhot),
+                              "tokens_per_s": B * T / (float(np.median(bcold)) * 1e-3),
+                              "vs_forward_cold": float(np.median(bcold)) / ms_per_step,
+                              "workspace_bytes": int(bws.numel())}
+        log(f"[bench] backward cold {np.median(bcold) * 1e3:.1f} us, hot {np.median(bhot) * 1e3:.1f} us")
 
     if not args.no_decode:
         dcfg = CONFIGS[DECODE_WORKLOAD]

@@ -172,6 +172,11 @@ def liger_attn_prefill_workspace_size(B: int, T: int, H_q: int, H_kv: int, d: in
     return int(load_library().liger_attn_prefill_workspace_size_ex(ctypes.byref(shp), chunks_per_segment))
 
 
+def liger_attn_prefill_backward_workspace_size(B: int, T: int, H_q: int, H_kv: int, d: int) -> int:
+    shp = make_shape(B, T, H_q, H_kv, d, LIGER_BF16)
+    return int(load_library().liger_attn_prefill_backward_workspace_size(ctypes.byref(shp)))
+
+
 def _sinks_c(sinks):
     """(sink_k, sink_v) device tensors [H_kv, n, d] -> liger_sinks."""
     sk, sv = sinks

@@ -57,7 +57,7 @@ def source_sha(files) -> str:
 
 
 def _short(name: str) -> str:
-    return re.sub(r"\(.*", "", name).replace("void ", "")
+    return re.sub(r"\(.*", "", name.replace("(anonymous namespace)::", "")).replace("void ", "")
 
 
 def trace(db: str, title: str, command: str) -> str:

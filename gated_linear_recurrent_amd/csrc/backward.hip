@@ -93,6 +93,19 @@ __device__ __forceinline__ float group16_sum(float v) {
     return v;
 }
 
+// x = hi + lo + e with hi, lo bf16 (round to nearest even) and |e| <= 2^-17 |x|:
+// two bf16 MFMAs against an exact bf16 operand give the fp32-accurate product.
+__device__ __forceinline__ void split_bf16x8(const float* x, bf16x8_t& hi, bf16x8_t& lo) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+        l[i] = pack_bf16x2(x[2 * i] - __uint_as_float(h[i] << 16), x[2 * i + 1] - __uint_as_float(h[i] & 0xffff0000u));
+    }
+    hi = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+    lo = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
+}
+
 // Rows 0..63 of a bf16 matrix (row stride `stride` elements) into LDS as
 // float32 (pitch in floats); rows >= nv are zero.
 template <int D, int NTH>
@@ -210,19 +223,27 @@ __device__ __forceinline__ void chunk_gate(float* sK, int FP, float* sBeta, floa
 // Forward record of chunk c (c < n-1): L = sum_t (phik_t (.) 2^(Delta-b_t))^T v_t, lg = Delta.
 // Adjoint record of chunk c (c > 0), stored at index n-1-c:
 // X = alpha sum_{s,h} (phiq_s^h (.) 2^(b_s))^T dO_s^h, lg = Delta.
+// Both are contractions over the chunk's tokens: the scaled feature operand
+// is split into bf16 hi + lo tiles, and both operands are read token-major
+// with transposing loads (32 tokens per MFMA).
 template <int D, int GATE>
 __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
-    constexpr int FP = D + 4, HP = D + 8;
+    typedef Mfma<bf16_t> M;
+    constexpr int FPK = D + 16, FP = D + 4, HP = D + 16;
     constexpr int NCB = D / 16;
     constexpr int WPC = 8 / NCB;   // waves per channel block
     constexpr int NE = NCB / WPC;  // column tiles per wave
-    __shared__ __align__(16) float sK[64 * FP];
+    // raw k -> phi(k) (fp32, pitch FPK); later the hi and lo bf16 tiles [64][HP] in the same bytes
+    __shared__ __align__(16) float sK[64 * FPK];
     __shared__ __align__(16) float sQ[64 * FP];
     __shared__ __align__(16) float sBeta[64 * D];
     __shared__ __align__(16) bf16_t sV[64 * HP];
     __shared__ __align__(16) bf16_t sO[64 * HP];
     __shared__ float sScr[kBT];
     __shared__ float sDelta[D];
+    static_assert(64 * FPK * 4 == 2 * 64 * HP * 2, "hi and lo tiles fill the phi(k) tile");
+    bf16_t* sXh = reinterpret_cast<bf16_t*>(sK);
+    bf16_t* sXl = sXh + 64 * HP;
 
     const int c = blockIdx.x, hk = blockIdx.y;
     const int64_t b = blockIdx.z, n = p.n, T = p.T, t0 = 64 * static_cast<int64_t>(c);
@@ -235,33 +256,55 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
     const int cb = w % NCB, eb0 = (w / NCB) * NE;
 
-    stage_f32<D, kBT>(sK, FP, p.k + ((b * T + t0) * p.H_kv + hk) * D, kvs, nv);
+    stage_f32<D, kBT>(sK, FPK, p.k + ((b * T + t0) * p.H_kv + hk) * D, kvs, nv);
     stage_bf16<D, 64, kBT>(sV, HP, p.v + ((b * T + t0) * p.H_kv + hk) * D, kvs, nv);
     __syncthreads();
-    chunk_gate<D, GATE>(sK, FP, sBeta, sScr, nv);
+    chunk_gate<D, GATE>(sK, FPK, sBeta, sScr, nv);
     if (tid < D) sDelta[tid] = sBeta[63 * D + tid];
     __syncthreads();
     const size_t rec = size_t(D) * D + D;
 
+    // acc[u] += X Y over the 64 tokens, X = hi + lo tiles (channel-indexed rows), Y token-major bf16
+    auto contract = [&](const bf16_t* Y, f32x4_t* acc) {
+#pragma unroll
+        for (int G = 0; G < 2; ++G) {
+            const M::frag xh = load_key_frag(sXh, HP, 32 * G, 16 * cb, lane);
+            const M::frag xl = load_key_frag(sXl, HP, 32 * G, 16 * cb, lane);
+#pragma unroll
+            for (int u = 0; u < NE; ++u) {
+                const M::frag y = load_key_frag(Y, HP, 32 * G, 16 * (eb0 + u), lane);
+                acc[u] = M::mma(xh, y, acc[u]);
+                acc[u] = M::mma(xl, y, acc[u]);
+            }
+        }
+    };
+    // element (t, ch) of the split operand lives at [t][ch] of the hi and lo tiles
+    auto put_split = [&](int t, int ch, float x) {
+        const uint32_t h = pack_bf16x2(x, 0.f) & 0xffffu;
+        sXh[t * HP + ch] = static_cast<bf16_t>(h);
+        sXl[t * HP + ch] = f32_to_bf16(x - __uint_as_float(h << 16));
+    };
+
     f32x4_t acc[NE];
     if (need_fwd) {
-        for (int idx = tid; idx < 64 * D; idx += kBT) {
-            const int t = idx / D, cc = idx % D;
-            sK[t * FP + cc] *= fast_exp2(sDelta[cc] - sBeta[t * D + cc]);
+        // K~ = phi(k) (.) 2^(Delta - b), read out before its bytes are reused
+        constexpr int PER = 64 * D / kBT;
+        float kt[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int idx = tid + e * kBT, t = idx / D, ch = idx % D;
+            kt[e] = sK[t * FPK + ch] * fast_exp2(sDelta[ch] - sBeta[t * D + ch]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int idx = tid + e * kBT;
+            put_split(idx / D, idx % D, kt[e]);
         }
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < NE; ++u) acc[u] = zero4();
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int tok = 16 * tb + 4 * g + kk;
-                const float x = sK[tok * FP + 16 * cb + col];
-#pragma unroll
-                for (int u = 0; u < NE; ++u)
-                    acc[u] = mma4(x, bf16_to_f32(sV[tok * HP + 16 * (eb0 + u) + col]), acc[u]);
-            }
+        contract(sV, acc);
         float* dst = p.fwd + ((b * p.H_kv + hk) * (n - 1) + c) * rec;
 #pragma unroll
         for (int u = 0; u < NE; ++u)
@@ -278,10 +321,10 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
             stage_f32<D, kBT>(sQ, FP, p.q + ((b * T + t0) * H_q + hq) * D, qs, nv);
             stage_bf16<D, 64, kBT>(sO, HP, p.dO + ((b * T + t0) * H_q + hq) * D, qs, nv);
             __syncthreads();
-            // Q~ = phi(q) (.) 2^(b): softmax, then the decay from the chunk start
+            // Q~ = phi(q) (.) 2^(b), written as the split operand
             {
                 const int row = tid >> 3, part = tid & 7;
-                float* xr = sQ + row * FP;
+                const float* xr = sQ + row * FP;
                 float v[D / 8];
                 float mx = -INFINITY;
 #pragma unroll
@@ -301,20 +344,11 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
 #pragma unroll
                 for (int i = 0; i < D / 8; ++i) {
                     const int cc = part + 8 * i;
-                    xr[cc] = v[i] * inv * fast_exp2(sBeta[row * D + cc]);
+                    put_split(row, cc, v[i] * inv * fast_exp2(sBeta[row * D + cc]));
                 }
             }
             __syncthreads();
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int tok = 16 * tb + 4 * g + kk;
-                    const float x = sQ[tok * FP + 16 * cb + col];
-#pragma unroll
-                    for (int u = 0; u < NE; ++u)
-                        acc[u] = mma4(x, bf16_to_f32(sO[tok * HP + 16 * (eb0 + u) + col]), acc[u]);
-                }
+            contract(sO, acc);
         }
         float* dst = p.adj + ((b * p.H_kv + hk) * (n - 1) + (n - 1 - c)) * rec;
 #pragma unroll
@@ -693,18 +727,20 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
 // ---------------------------------------------------------------- window: queries
 // One workgroup per (chunk, key/value head, sequence); wave i holds query
 // tile i of the chunk, all query heads of the group in turn. Keys of the
-// previous and the current chunk are staged once.
+// previous and the current chunk are staged once (token-major, rows 8 banks
+// apart for the transposing reads). Key tiles are taken in aligned pairs
+// (2G, 2G + 1), the 32-key groups of the dq product.
 template <int D>
 __global__ __launch_bounds__(kST) void bwd_swa_q_kernel(BwdParams p) {
     typedef Mfma<bf16_t> M;
-    constexpr int HP = D + 8, KS = D / M::KSTEP, NCB = D / 16;
+    constexpr int HP = D + 16, KS = D / M::KSTEP, NCB = D / 16;
     __shared__ __align__(16) bf16_t sK[128 * HP];
     __shared__ __align__(16) bf16_t sV[128 * HP];
 
     const int c = blockIdx.x, hk = blockIdx.y;
     const int64_t b = blockIdx.z, T = p.T, t0 = 64 * static_cast<int64_t>(c);
     const int H_q = p.H_kv * p.n_rep;
-    const int64_t kvs = static_cast<int64_t>(p.H_kv) * D, qs = static_cast<int64_t>(H_q) * D;
+    const int64_t qs = static_cast<int64_t>(H_q) * D;
     const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g = lane >> 4;
     const int wi = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
     // key row kk of the tiles is token t0 - 64 + kk
@@ -731,7 +767,8 @@ __global__ __launch_bounds__(kST) void bwd_swa_q_kernel(BwdParams p) {
     const float beta = 1.0f - p.alpha;
     const int qq = 64 + 16 * wi + col;  // this lane's query in key-row coordinates
     const int64_t qtok = t0 + 16 * wi + col;
-    const int ktlo = (64 + 16 * wi - w + 1) >> 4;  // first key tile touching the wave's windows
+    const int kt0 = 2 * (wi >> 1);                   // first key tile of the aligned pairs
+    const int ktlo = max(wi, (64 + 16 * wi - w + 1) >> 4);  // live key tiles: ktlo .. wi + 4
     const int64_t qrow = qtok < T ? qtok : T - 1;
 
     for (int h = 0; h < p.n_rep; ++h) {
@@ -744,15 +781,15 @@ __global__ __launch_bounds__(kST) void bwd_swa_q_kernel(BwdParams p) {
             qf[k] = M::load(qr + M::KSTEP * k);
             of[k] = M::load(orow + M::KSTEP * k);
         }
-        // scores and value products for key tiles kt = ktlo .. 4 + wi
-        f32x4_t z[5], dp[5];
+        // scores and value products on key tiles kt0 .. kt0 + 5: lane (query col, g) holds keys 16 kt + 4 g + r
+        f32x4_t z[6], dp[6];
         float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 5; ++j) {
-            const int kt = wi + j;
-            z[j] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // p = 0 for tiles outside every window
+        for (int j = 0; j < 6; ++j) {
+            const int kt = kt0 + j;
+            z[j] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // p = 0 outside every window
             dp[j] = zero4();
-            if (kt < ktlo) continue;
+            if (kt < ktlo || kt > wi + 4) continue;
             z[j] = zero4();
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
@@ -770,7 +807,7 @@ __global__ __launch_bounds__(kST) void bwd_swa_q_kernel(BwdParams p) {
         mx = group4_max(mx);
         float l = 0.f;
 #pragma unroll
-        for (int j = 0; j < 5; ++j)
+        for (int j = 0; j < 6; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 z[j][r] = fast_exp2(z[j][r] - mx);
@@ -780,7 +817,7 @@ __global__ __launch_bounds__(kST) void bwd_swa_q_kernel(BwdParams p) {
         const float inv = 1.0f / l;
         float ds = 0.f;
 #pragma unroll
-        for (int j = 0; j < 5; ++j)
+        for (int j = 0; j < 6; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 z[j][r] *= inv;
@@ -793,22 +830,30 @@ __global__ __launch_bounds__(kST) void bwd_swa_q_kernel(BwdParams p) {
             st[0] = mx + fast_log2(l);
             st[1] = ds;
         }
+        // dz = p (dp - sum p dp), split into bf16 hi + lo per aligned key pair
+        M::frag zh[3], zl[3];
 #pragma unroll
-        for (int j = 0; j < 5; ++j)
+        for (int G = 0; G < 3; ++G) {
+            float v8[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dp[j][r] = z[j][r] * (dp[j][r] - ds);  // dz
+            for (int r = 0; r < 4; ++r) {
+                v8[r] = z[2 * G][r] * (dp[2 * G][r] - ds);
+                v8[4 + r] = z[2 * G + 1][r] * (dp[2 * G + 1][r] - ds);
+            }
+            split_bf16x8(v8, zh[G], zl[G]);
+        }
         // dq^T[c][q] = sum_key k[key][c] dz[key][q] / sqrt(d)
         const float rs = rsqrtf(static_cast<float>(D));
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
             f32x4_t a = zero4();
 #pragma unroll
-            for (int j = 0; j < 5; ++j) {
-                const int kt = wi + j;
-                if (kt < ktlo) continue;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    a = mma4(bf16_to_f32(sK[(16 * kt + 4 * g + r) * HP + 16 * cb + col]), dp[j][r], a);
+            for (int G = 0; G < 3; ++G) {
+                const int kt = kt0 + 2 * G;
+                if (kt + 1 < ktlo || kt > wi + 4) continue;
+                const M::frag kx = load_key_frag(sK, HP, 16 * kt, 16 * cb, lane);
+                a = M::mma(kx, zh[G], a);
+                a = M::mma(kx, zl[G], a);
             }
             if (qtok < T) {
                 float4* dst = reinterpret_cast<float4*>(p.dq + (b * T + qtok) * qs + hq * D + 16 * cb + 4 * g);
@@ -826,11 +871,12 @@ __global__ __launch_bounds__(kST) void bwd_swa_q_kernel(BwdParams p) {
 // ---------------------------------------------------------------- window: keys
 // One workgroup per (chunk, key/value head, sequence); wave i holds key tile
 // i of the chunk. The queries that can see those keys are in this chunk and
-// the next; dk and dv are summed over the query heads of the group.
+// the next, taken in aligned query-tile pairs (2G, 2G + 1); dk and dv are
+// summed over the query heads of the group.
 template <int D>
-__global__ __launch_bounds__(kST) void bwd_swa_k_kernel(BwdParams p) {
+__global__ __launch_bounds__(kST) __attribute__((amdgpu_waves_per_eu(2))) void bwd_swa_k_kernel(BwdParams p) {
     typedef Mfma<bf16_t> M;
-    constexpr int HP = D + 8, KS = D / M::KSTEP, NCB = D / 16;
+    constexpr int HP = D + 16, KS = D / M::KSTEP, NCB = D / 16;
     __shared__ __align__(16) bf16_t sQ[128 * HP];
     __shared__ __align__(16) bf16_t sO[128 * HP];
     __shared__ float sL[128], sDs[128];
@@ -848,7 +894,8 @@ __global__ __launch_bounds__(kST) void bwd_swa_k_kernel(BwdParams p) {
     const int kj = 16 * wi + col;                                   // this lane's key (chunk-local)
     const int64_t ktok = t0 + kj;
     const int64_t krow = ktok < T ? ktok : T - 1;
-    const int qthi = (16 * wi + 15 + w - 1) >> 4;  // last query tile that sees the wave's keys
+    const int qt0 = 2 * (wi >> 1);                     // first query tile of the aligned pairs
+    const int qthi = min(7, (16 * wi + 15 + w - 1) >> 4);  // live query tiles: wi .. qthi
 
     M::frag kf[KS], vf[KS];
     {
@@ -878,42 +925,48 @@ __global__ __launch_bounds__(kST) void bwd_swa_k_kernel(BwdParams p) {
             sDs[tid] = ok ? st[1] : 0.f;
         }
         __syncthreads();
-        // query tiles qt = wi .. qthi (at most 5): S[q][key], lane (key col, g) holds queries 16 qt + 4 g + r
-        f32x4_t pz[5], dz[5];
+        // S[q][key] on query tiles qt0 .. qt0 + 5: lane (key col, g) holds queries 16 qt + 4 g + r
+        M::frag ph[3], pl[3], dh[3], dl[3];
 #pragma unroll
-        for (int j = 0; j < 5; ++j) {
-            const int qt = wi + j;
-            pz[j] = zero4();
-            dz[j] = zero4();
-            if (qt > qthi || qt >= 8) continue;
-            f32x4_t z = zero4(), dp = zero4();
+        for (int G = 0; G < 3; ++G) {
+            float pv[8], dv8[8];
 #pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                z = M::mma(M::load(sQ + (16 * qt + col) * HP + 8 * g + M::KSTEP * k), kf[k], z);
-                dp = M::mma(M::load(sO + (16 * qt + col) * HP + 8 * g + M::KSTEP * k), vf[k], dp);
+            for (int half = 0; half < 2; ++half) {
+                const int qt = qt0 + 2 * G + half;
+                f32x4_t z = zero4(), dp = zero4();
+                const bool live_tile = qt >= wi && qt <= qthi;
+                if (live_tile) {
+#pragma unroll
+                    for (int k = 0; k < KS; ++k) {
+                        z = M::mma(M::load(sQ + (16 * qt + col) * HP + 8 * g + M::KSTEP * k), kf[k], z);
+                        dp = M::mma(M::load(sO + (16 * qt + col) * HP + 8 * g + M::KSTEP * k), vf[k], dp);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int qi = 16 * qt + 4 * g + r;
+                    const bool live = live_tile && qi >= kj && qi < kj + w && qi < nq;
+                    const float pr = live ? fast_exp2(z[r] * sc - sL[qi]) : 0.f;
+                    pv[4 * half + r] = beta * pr;
+                    dv8[4 * half + r] = live ? pr * (beta * dp[r] - sDs[qi]) : 0.f;
+                }
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int qi = 16 * qt + 4 * g + r;
-                const bool live = qi >= kj && qi < kj + w && qi < nq;
-                const float pr = live ? fast_exp2(z[r] * sc - sL[qi]) : 0.f;
-                pz[j][r] = pr;
-                dz[j][r] = pr * (beta * dp[r] - sDs[qi]);
-            }
+            split_bf16x8(dv8, dh[G], dl[G]);
+            split_bf16x8(pv, ph[G], pl[G]);
         }
         // dk^T[c][key] += sum_q q[q][c] dz[q][key]; dv^T[e][key] += sum_q dO[q][e] beta p[q][key]
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-            for (int j = 0; j < 5; ++j) {
-                const int qt = wi + j;
-                if (qt > qthi || qt >= 8) continue;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int qi = 16 * qt + 4 * g + r;
-                    adk[cb] = mma4(bf16_to_f32(sQ[qi * HP + 16 * cb + col]), dz[j][r], adk[cb]);
-                    adv[cb] = mma4(bf16_to_f32(sO[qi * HP + 16 * cb + col]), beta * pz[j][r], adv[cb]);
-                }
+            for (int G = 0; G < 3; ++G) {
+                const int qt = qt0 + 2 * G;
+                if (qt + 1 < wi || qt > qthi) continue;
+                const M::frag qx = load_key_frag(sQ, HP, 16 * qt, 16 * cb, lane);
+                const M::frag ox = load_key_frag(sO, HP, 16 * qt, 16 * cb, lane);
+                adk[cb] = M::mma(qx, dh[G], adk[cb]);
+                adk[cb] = M::mma(qx, dl[G], adk[cb]);
+                adv[cb] = M::mma(ox, ph[G], adv[cb]);
+                adv[cb] = M::mma(ox, pl[G], adv[cb]);
             }
         }
     }
@@ -984,18 +1037,23 @@ __global__ __launch_bounds__(kST) void bwd_gate_kernel(BwdParams p) {
     }
     __syncthreads();
     if (tid < D) {
+        // reverse inclusive scan down the chunk's rows, in registers
         float run = 0.f;
 #pragma unroll
         for (int j = 0; j < kST / D; ++j) run += sSuf[j * D + tid];
-        for (int t = nv - 1; t >= 0; --t) {
-            run += sS[t * FP + tid];
+        float r[64];
+#pragma unroll
+        for (int t = 0; t < 64; ++t) r[t] = sS[t * FP + tid];  // rows >= nv hold 0
+#pragma unroll
+        for (int t = 63; t >= 0; --t) {
+            run += r[t];
             sS[t * FP + tid] = run;
         }
     }
     __syncthreads();
-    float* dk = p.dk + ((b * T + t0) * p.H_kv + hk) * D;
+    // sS[t][c] becomes the dk contribution of row t, channel c
     if (GATE == 0) {
-        // four lanes per row
+        // four lanes per row: ds_t = (sum_c d ln g_t[c]) (1 - g_t) / d on every channel
         const int row = tid >> 2, part = tid & 3;
         float sk = 0.f, ss = 0.f;
         for (int i = part; i < D; i += 4) {
@@ -1007,8 +1065,8 @@ __global__ __launch_bounds__(kST) void bwd_gate_kernel(BwdParams p) {
         ss += dpp<kDppXor1>(ss);
         ss += dpp<kDppXor2>(ss);
         const float ds = ss * sigmoidf_stable(-sk * (1.0f / D)) * (1.0f / D);
-        if (row < nv)
-            for (int i = part; i < D; i += 4) dk[row * kvs + i] += ds;
+        __syncthreads();
+        for (int i = part; i < D; i += 4) sS[row * FP + i] = ds;
     } else {
         for (int idx = tid; idx < 64 * D; idx += kST) {
             const int t = idx / D, ch = idx % D;
@@ -1019,13 +1077,30 @@ __global__ __launch_bounds__(kST) void bwd_gate_kernel(BwdParams p) {
             sS[t * FP + ch] *= sigmoidf_stable(-x) / static_cast<float>(hi - lo);
         }
         __syncthreads();
-        for (int idx = tid; idx < nv * D; idx += kST) {
+        // pool transpose: channel c'' collects channels c'' - 2 .. c'' + 1
+        for (int idx = tid; idx < 64 * D; idx += kST) {
             const int t = idx / D, ch = idx % D;
             float add = 0.f;
+#pragma unroll
             for (int j = ch - 2; j <= ch + 1; ++j)
                 if (j >= 0 && j < D) add += sS[t * FP + j];
-            dk[t * kvs + ch] += add;
+            sK[t * FP + ch] = add;  // raw k no longer needed
         }
+    }
+    __syncthreads();
+    const float* add = GATE == 0 ? sS : sK;
+    float* dk = p.dk + ((b * T + t0) * p.H_kv + hk) * D;
+    constexpr int PPR = D / 4;
+    for (int idx = tid; idx < nv * PPR; idx += kST) {
+        const int t = idx / PPR, c4 = (idx % PPR) * 4;
+        float4* dst = reinterpret_cast<float4*>(dk + t * kvs + c4);
+        const float4 a = *reinterpret_cast<const float4*>(add + t * FP + c4);
+        float4 o = *dst;
+        o.x += a.x;
+        o.y += a.y;
+        o.z += a.z;
+        o.w += a.w;
+        *dst = o;
     }
 }
 
