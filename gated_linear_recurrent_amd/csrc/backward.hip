@@ -38,8 +38,9 @@
 //   bwd_swa_q_kernel   : window softmax per query; dq += ..; row statistics
 //   bwd_swa_k_kernel   : per key tile: dk += .., dv += ..
 //   bwd_gate_kernel    : suffix sums of dL/dB, sigmoid and pool transpose: dk += ..
-// Contractions with raw bf16 operands use the bf16 MFMA (products exact in
-// fp32); those with computed operands use the fp32 MFMA.
+// Computed operands enter the bf16 MFMA as hi + lo bf16 pairs (fp32-accurate
+// products), raw bf16 inputs as they are. Barriers order LDS only: no kernel
+// here reads back a global value it wrote.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -86,11 +87,19 @@ __device__ __forceinline__ void bf8_to_f32(uint4 u, float* f) {
     f[7] = __uint_as_float(u.w & 0xffff0000u);
 }
 
-// Sum over the 16 lanes of a fragment row group (lanes with the same L >> 4).
+// Maximum over the 16 lanes of a fragment row group, on DPP.
+__device__ __forceinline__ float group16_max(float v) {
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    return fmaxf(v, dpp<kDppMirror>(v));
+}
+// Sum over the 16 lanes of a fragment row group (lanes with the same L >> 4), on DPP.
 __device__ __forceinline__ float group16_sum(float v) {
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    return v + dpp<kDppMirror>(v);
 }
 
 // x = hi + lo + e with hi, lo bf16 (round to nearest even) and |e| <= 2^-17 |x|:
@@ -175,7 +184,7 @@ __device__ __forceinline__ void row_softmax(float* x, int pitch, int nv, const f
 // Chunk set-up shared by the records and gradient kernels: raw k staged in
 // sK (fp32) becomes phi(k); sBeta gets the inclusive cumulative log2 gate;
 // scratch needs kBT floats. Ends synchronised.
-template <int D, int GATE>
+template <int D, int GATE, int BP = D>
 __device__ __forceinline__ void chunk_gate(float* sK, int FP, float* sBeta, float* scratch, int nv) {
     const int row = threadIdx.x >> 3, part = threadIdx.x & 7;
     const float* kr = sK + row * FP;
@@ -187,7 +196,7 @@ __device__ __forceinline__ void chunk_gate(float* sK, int FP, float* sBeta, floa
         s = group8_sum(s);
         const float l2 = row < nv ? log2_sigmoid(s * (1.0f / D)) : 0.f;
 #pragma unroll
-        for (int i = 0; i < D / 8; ++i) sBeta[row * D + part + 8 * i] = l2;
+        for (int i = 0; i < D / 8; ++i) sBeta[row * BP + part + 8 * i] = l2;
     } else {
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) {
@@ -195,10 +204,10 @@ __device__ __forceinline__ void chunk_gate(float* sK, int FP, float* sBeta, floa
             const int lo = c > 0 ? c - 1 : 0, hi = c + 3 < D ? c + 3 : D;
             float s = 0.f;
             for (int j = lo; j < hi; ++j) s += kr[j];
-            sBeta[row * D + c] = row < nv ? log2_sigmoid(s / static_cast<float>(hi - lo)) : 0.f;
+            sBeta[row * BP + c] = row < nv ? log2_sigmoid(s / static_cast<float>(hi - lo)) : 0.f;
         }
     }
-    __syncthreads();
+    lds_barrier();
     row_softmax<D, false>(sK, FP, nv, nullptr, nullptr, nullptr);
     // inclusive scan of the log2 gates over the 64 rows, per channel
     constexpr int P = kBT / D, TPP = 64 / P;
@@ -206,17 +215,17 @@ __device__ __forceinline__ void chunk_gate(float* sK, int FP, float* sBeta, floa
     float run = 0.f;
 #pragma unroll
     for (int u = 0; u < TPP; ++u) {
-        float* e = &sBeta[(pp * TPP + u) * D + c];
+        float* e = &sBeta[(pp * TPP + u) * BP + c];
         run += *e;
         *e = run;
     }
     scratch[pp * D + c] = run;
-    __syncthreads();
+    lds_barrier();
     float off = 0.f;
     for (int j = 0; j < pp; ++j) off += scratch[j * D + c];
 #pragma unroll
-    for (int u = 0; u < TPP; ++u) sBeta[(pp * TPP + u) * D + c] += off;
-    __syncthreads();
+    for (int u = 0; u < TPP; ++u) sBeta[(pp * TPP + u) * BP + c] += off;
+    lds_barrier();
 }
 
 // ---------------------------------------------------------------- records
@@ -258,10 +267,10 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
 
     stage_f32<D, kBT>(sK, FPK, p.k + ((b * T + t0) * p.H_kv + hk) * D, kvs, nv);
     stage_bf16<D, 64, kBT>(sV, HP, p.v + ((b * T + t0) * p.H_kv + hk) * D, kvs, nv);
-    __syncthreads();
+    lds_barrier();
     chunk_gate<D, GATE>(sK, FPK, sBeta, sScr, nv);
     if (tid < D) sDelta[tid] = sBeta[63 * D + tid];
-    __syncthreads();
+    lds_barrier();
     const size_t rec = size_t(D) * D + D;
 
     // acc[u] += X Y over the 64 tokens, X = hi + lo tiles (channel-indexed rows), Y token-major bf16
@@ -295,13 +304,13 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
             const int idx = tid + e * kBT, t = idx / D, ch = idx % D;
             kt[e] = sK[t * FPK + ch] * fast_exp2(sDelta[ch] - sBeta[t * D + ch]);
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
             const int idx = tid + e * kBT;
             put_split(idx / D, idx % D, kt[e]);
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int u = 0; u < NE; ++u) acc[u] = zero4();
         contract(sV, acc);
@@ -317,10 +326,10 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
         for (int u = 0; u < NE; ++u) acc[u] = zero4();
         for (int h = 0; h < p.n_rep; ++h) {
             const int hq = hk * p.n_rep + h;
-            __syncthreads();
+            lds_barrier();
             stage_f32<D, kBT>(sQ, FP, p.q + ((b * T + t0) * H_q + hq) * D, qs, nv);
             stage_bf16<D, 64, kBT>(sO, HP, p.dO + ((b * T + t0) * H_q + hq) * D, qs, nv);
-            __syncthreads();
+            lds_barrier();
             // Q~ = phi(q) (.) 2^(b), written as the split operand
             {
                 const int row = tid >> 3, part = tid & 7;
@@ -347,7 +356,7 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
                     put_split(row, cc, v[i] * inv * fast_exp2(sBeta[row * D + cc]));
                 }
             }
-            __syncthreads();
+            lds_barrier();
             contract(sO, acc);
         }
         float* dst = p.adj + ((b * p.H_kv + hk) * (n - 1) + (n - 1 - c)) * rec;
@@ -361,29 +370,99 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- GRM gradients
+// x -> (hi, lo) bf16 at [idx] of two tiles; get_split returns hi + lo.
+__device__ __forceinline__ void put_split(bf16_t* hi, bf16_t* lo, int idx, float x) {
+    const bf16_t h = f32_to_bf16(x);
+    hi[idx] = h;
+    lo[idx] = f32_to_bf16(x - bf16_to_f32(h));
+}
+// Two adjacent elements (idx even) as one 32-bit store per tile.
+__device__ __forceinline__ void put_split2(bf16_t* hi, bf16_t* lo, int idx, float x0, float x1) {
+    const uint32_t h = pack_bf16x2(x0, x1);
+    *reinterpret_cast<uint32_t*>(hi + idx) = h;
+    *reinterpret_cast<uint32_t*>(lo + idx) =
+        pack_bf16x2(x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xffff0000u));
+}
+// Sum of N (4 or 8) partials stored contiguously (16-byte aligned).
+template <int N>
+__device__ __forceinline__ float row_total(const float* p) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    float s = (a.x + a.y) + (a.z + a.w);
+    if constexpr (N == 8) {
+        const float4 b = *reinterpret_cast<const float4*>(p + 4);
+        s += (b.x + b.y) + (b.z + b.w);
+    }
+    return s;
+}
+__device__ __forceinline__ float get_split(const bf16_t* hi, const bf16_t* lo, int idx) {
+    return bf16_to_f32(hi[idx]) + bf16_to_f32(lo[idx]);
+}
+// Eight elements of a row in the key_pos order of load_key_frag: [kb + 4g, +4) then [kb + 16 + 4g, +4).
+__device__ __forceinline__ bf16x8_t row_keypos(const bf16_t* row, int kb, int g) {
+    const uint2 a = *reinterpret_cast<const uint2*>(row + kb + 4 * g);
+    const uint2 b = *reinterpret_cast<const uint2*>(row + kb + 16 + 4 * g);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
+}
+// Element j of a fragment cleared where bit j of `bits` is set.
+__device__ __forceinline__ bf16x8_t clear_elems(bf16x8_t f, uint32_t bits) {
+    uint4 u = __builtin_bit_cast(uint4, f);
+    uint32_t* w = reinterpret_cast<uint32_t*>(&u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t m = (((bits >> (2 * i)) & 1u) ? 0xffffu : 0u) | (((bits >> (2 * i + 1)) & 1u) ? 0xffff0000u : 0u);
+        w[i] &= ~m;
+    }
+    return __builtin_bit_cast(bf16x8_t, u);
+}
+// acc += X Y for X = xh + xl, Y = yh + yl (the xl yl term is below 2^-16 relative)
+__device__ __forceinline__ f32x4_t mma3(bf16x8_t xh, bf16x8_t xl, bf16x8_t yh, bf16x8_t yl, f32x4_t acc) {
+    acc = Mfma<bf16_t>::mma(xh, yh, acc);
+    acc = Mfma<bf16_t>::mma(xh, yl, acc);
+    return Mfma<bf16_t>::mma(xl, yh, acc);
+}
+
 // One workgroup per (chunk, key/value head, sequence); the query heads of the
 // group are taken one after another. Every [64 x d] result (dphi(q^h),
-// dphi(k), dv, dL/dB) uses the same tiles: wave w owns column block
-// w mod (d/16) and NTI consecutive 16-row tiles.
+// dphi(k), dv, dL/dB) is computed transposed, as [d x 64] tiles: wave w owns
+// channel block jb = w mod (d/16) and NTI consecutive 16-row tiles, and lane
+// (col, g) holds channels 16 jb + 4 g + r of row 16 i + col, so results leave
+// as float4 per lane. Computed operands (K^, Q^, A^h, alpha B^h, K~ and the
+// states) enter the bf16 MFMA as hi + lo pairs, raw bf16 inputs as they are;
+// products whose contraction index is the token run on transposing loads.
 template <int D, int GATE>
 __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
     typedef Mfma<bf16_t> M;
-    constexpr int FP = D + 4, HP = D + 8, AP = 68;
+    typedef M::frag Frag;
+    constexpr int FP = D + 4;   // raw k staging pitch (fp32)
+    constexpr int XP = D + 8;   // split operand tiles [64][XP]
+    constexpr int BP = D + 4;   // cumulative gate pitch
+    constexpr int VP = D + 8;   // raw v and dO tiles
+    constexpr int AP = 64 + 8;  // A / B tiles [64][AP]
     constexpr int NCB = D / 16;
     constexpr int WPC = 8 / NCB;
     constexpr int NTI = 4 / WPC;
-    constexpr int KQ = D / 4;  // contraction elements per lane group in the permuted products
     constexpr int KS = D / M::KSTEP;
-    __shared__ __align__(16) float sKh[64 * FP];  // K^: phik 2^(m-b) (extreme channels: phik)
-    __shared__ __align__(16) float sQ[64 * FP];   // Q^ of the current head; afterwards K~
-    __shared__ __align__(16) float sBeta[64 * D];
-    __shared__ __align__(16) bf16_t sV[64 * HP];
-    __shared__ __align__(16) bf16_t sO[64 * HP];
-    __shared__ __align__(16) float sA[64 * AP];   // A^h[s][t]; then alpha B^h stored as [s][t]
-    __shared__ float sRow[64 * NCB];
-    __shared__ float sCol[WPC * D];
-    __shared__ float sM[D], sDelta[D];
+    __shared__ __align__(16) bf16_t sQx[2 * 64 * XP];  // Q^ hi, lo; raw k (fp32) during set-up; K~ hi, lo at the end
+    __shared__ __align__(16) bf16_t sKx[2 * 64 * XP];  // K^ hi, lo: phik 2^(m-b) (extreme channels: phik)
+    __shared__ __align__(16) float sBeta[64 * BP];
+    __shared__ __align__(16) bf16_t sV[64 * VP];
+    __shared__ __align__(16) bf16_t sO[64 * VP];
+    __shared__ __align__(16) bf16_t sAx[2 * 64 * AP];  // A^h[s][t] hi, lo; then alpha B^h[t][s] stored at [s][t]
+    __shared__ __align__(16) float sRow[64 * NCB];
+    __shared__ __align__(16) float sM[D];
+    __shared__ __align__(16) float sDelta[D];
     __shared__ uint32_t sExt[D / 32];
+    static_assert(64 * FP * 4 <= 2 * 64 * XP * 2, "raw k staging fits the Q^ tiles");
+    static_assert(2 * 64 * AP * 2 >= kBT * 4, "scan scratch fits the A tiles");
+    static_assert(2 * 64 * AP * 2 >= WPC * D * 4, "column sums fit the A tiles");
+    float* sCol = reinterpret_cast<float*>(sAx);  // [WPC][D], used after the last A / B tile
+    float* sKraw = reinterpret_cast<float*>(sQx);
+    bf16_t* sQh = sQx;
+    bf16_t* sQl = sQx + 64 * XP;
+    bf16_t* sKh = sKx;
+    bf16_t* sKl = sKx + 64 * XP;
+    bf16_t* sAh = sAx;
+    bf16_t* sAl = sAx + 64 * AP;
 
     const int c = blockIdx.x, hk = blockIdx.y;
     const int64_t b = blockIdx.z, n = p.n, T = p.T, t0 = 64 * static_cast<int64_t>(c);
@@ -392,18 +471,19 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
     const int64_t kvs = static_cast<int64_t>(p.H_kv) * D, qs = static_cast<int64_t>(H_q) * D;
     const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-    // with one wave per column block every wave starts at row tile 0 (known at compile time)
+    // with one wave per channel block every wave starts at row tile 0 (known at compile time)
     const int jb = w % NCB, i0 = WPC == 1 ? 0 : (w / NCB) * NTI;
-    const int cc = 16 * jb + col;  // this lane's output column
+    const int cf = 16 * jb + col;     // the channel of this lane's operand fragments
+    const int ch0 = 16 * jb + 4 * g;  // the channels ch0 .. ch0 + 3 of this lane's results
     const float alpha = p.alpha;
     const size_t rec = size_t(D) * D + D;
 
-    stage_f32<D, kBT>(sKh, FP, p.k + ((b * T + t0) * p.H_kv + hk) * D, kvs, nv);
-    stage_bf16<D, 64, kBT>(sV, HP, p.v + ((b * T + t0) * p.H_kv + hk) * D, kvs, nv);
-    __syncthreads();
-    chunk_gate<D, GATE>(sKh, FP, sBeta, sA, nv);
+    stage_f32<D, kBT>(sKraw, FP, p.k + ((b * T + t0) * p.H_kv + hk) * D, kvs, nv);
+    stage_bf16<D, 64, kBT>(sV, VP, p.v + ((b * T + t0) * p.H_kv + hk) * D, kvs, nv);
+    lds_barrier();
+    chunk_gate<D, GATE, BP>(sKraw, FP, sBeta, reinterpret_cast<float*>(sAx), nv);
     if (tid < D) {
-        const float m = sBeta[31 * D + tid], dl = sBeta[63 * D + tid];
+        const float m = sBeta[31 * BP + tid], dl = sBeta[63 * BP + tid];
         sM[tid] = m;
         sDelta[tid] = dl;
         const bool ext = fmaxf(sBeta[tid] - m, m - dl) > kExtreme;
@@ -413,22 +493,26 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
             sExt[2 * w + 1] = static_cast<uint32_t>(bal >> 32);
         }
     }
-    __syncthreads();
+    lds_barrier();
     uint32_t any_ext = 0;
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) any_ext |= sExt[j];
-    for (int idx = tid; idx < 64 * D; idx += kBT) {
-        const int t = idx / D, ch = idx % D;
-        if (!((sExt[ch >> 5] >> (ch & 31)) & 1u)) sKh[t * FP + ch] *= fast_exp2(sM[ch] - sBeta[t * D + ch]);
+    auto is_ext = [&](int ch) -> bool { return (sExt[ch >> 5] >> (ch & 31)) & 1u; };
+    for (int idx = tid; idx < 32 * D; idx += kBT) {  // two adjacent channels per item
+        const int t = idx / (D / 2), ch = 2 * (idx % (D / 2));
+        float x0 = sKraw[t * FP + ch], x1 = sKraw[t * FP + ch + 1];
+        if (!is_ext(ch)) x0 *= fast_exp2(sM[ch] - sBeta[t * BP + ch]);
+        if (!is_ext(ch + 1)) x1 *= fast_exp2(sM[ch + 1] - sBeta[t * BP + ch + 1]);
+        put_split2(sKh, sKl, t * XP + ch, x0, x1);
     }
-    const bool colx = (sExt[cc >> 5] >> (cc & 31)) & 1u;
-    // extreme flags of the contraction channels g*KQ + ks of this lane group
-    const uint32_t kbits = KQ == 32 ? sExt[g] : ((sExt[g >> 1] >> (16 * (g & 1))) & 0xffffu);
-
-    // state entering the chunk (Y operands S0[cc][g*KQ + ks]; none for the first chunk)
-    const float* S0row = c > 0 ? p.fwd + ((b * p.H_kv + hk) * (n - 1) + (c - 1)) * rec + size_t(cc) * D + g * KQ
-                               : nullptr;
-    __syncthreads();
+    const bool colx = is_ext(cf);                             // this lane's fragment channel
+    const uint32_t extr = (sExt[ch0 >> 5] >> (ch0 & 31)) & 0xfu;  // result channels ch0 + r
+    const Frag fzero = M::zero();
+    const float4 m4 = *reinterpret_cast<const float4*>(sM + ch0);
+    const float mr[4] = {m4.x, m4.y, m4.z, m4.w};
+    // state entering the chunk (fragments S0[cf][e]; none for the first chunk)
+    const float* S0row = c > 0 ? p.fwd + ((b * p.H_kv + hk) * (n - 1) + (c - 1)) * rec + size_t(cf) * D : nullptr;
+    lds_barrier();
 
     f32x4_t accK[NTI], accV[NTI], accDB[NTI];
 #pragma unroll
@@ -437,40 +521,92 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
         accV[u] = zero4();
         accDB[u] = zero4();
     }
+    // four cumulative gates b[row][ch0 .. ch0 + 3]
+    auto beta4 = [&](int row) -> float4 { return *reinterpret_cast<const float4*>(sBeta + row * BP + ch0); };
+    // four split values [row][ch0 .. ch0 + 3] of a pair of tiles
+    auto split4 = [&](const bf16_t* hi, const bf16_t* lo, int idx, float* out) {
+        const uint2 h = *reinterpret_cast<const uint2*>(hi + idx), l = *reinterpret_cast<const uint2*>(lo + idx);
+        out[0] = __uint_as_float(h.x << 16) + __uint_as_float(l.x << 16);
+        out[1] = __uint_as_float(h.x & 0xffff0000u) + __uint_as_float(l.x & 0xffff0000u);
+        out[2] = __uint_as_float(h.y << 16) + __uint_as_float(l.y << 16);
+        out[3] = __uint_as_float(h.y & 0xffff0000u) + __uint_as_float(l.y & 0xffff0000u);
+    };
 
     for (int h = 0; h < p.n_rep; ++h) {
         const int hq = hk * p.n_rep + h;
-        stage_f32<D, kBT>(sQ, FP, p.q + ((b * T + t0) * H_q + hq) * D, qs, nv);
-        stage_bf16<D, 64, kBT>(sO, HP, p.dO + ((b * T + t0) * H_q + hq) * D, qs, nv);
-        __syncthreads();
-        // Q^ = phi(q) 2^(b-m) (extreme channels: phi(q))
-        row_softmax<D, true>(sQ, FP, nv, sBeta, sM, sExt);
-        // A^h = alpha dO V^T, zero above the diagonal
+        // Q^ = phi(q) 2^(b-m) (extreme channels: phi(q)) straight from the raw rows:
+        // 16 lanes per row, channel pairs 2 l + 32 i; a wave's four rows per
+        // instruction are 4 apart, so their LDS rows fall on disjoint banks
         {
-            // tiles w and w + 8 of the 4 x 4 grid (row tile s-block, column tile t-block)
-            const int is0 = w >> 2, it0 = w & 3, is1 = (w + 8) >> 2, it1 = w & 3;
-            f32x4_t a0 = zero4(), a1 = zero4();
-            const bool live0 = it0 <= is0, live1 = it1 <= is1;
+            const int l16 = lane & 15, sub = lane >> 4;
 #pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                if (live0)
-                    a0 = M::mma(M::load(sO + (16 * is0 + col) * HP + 8 * g + M::KSTEP * k),
-                                M::load(sV + (16 * it0 + col) * HP + 8 * g + M::KSTEP * k), a0);
-                if (live1)
-                    a1 = M::mma(M::load(sO + (16 * is1 + col) * HP + 8 * g + M::KSTEP * k),
-                                M::load(sV + (16 * it1 + col) * HP + 8 * g + M::KSTEP * k), a1);
-            }
+            for (int pass = 0; pass < 2; ++pass) {
+                const int row = (w & 3) + 16 * ((w >> 2) + 2 * pass) + 4 * sub;
+                float v[D / 16];
+                if (row < nv) {
+                    const bf16_t* qr = p.q + ((b * T + t0 + row) * H_q + hq) * D + 2 * l16;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int s0 = 16 * is0 + 4 * g + r, t0c = 16 * it0 + col;
-                const int s1 = 16 * is1 + 4 * g + r, t1c = 16 * it1 + col;
-                sA[s0 * AP + t0c] = t0c <= s0 ? alpha * a0[r] : 0.f;
-                sA[s1 * AP + t1c] = t1c <= s1 ? alpha * a1[r] : 0.f;
+                    for (int i = 0; i < D / 32; ++i) {
+                        const uint32_t u = *reinterpret_cast<const uint32_t*>(qr + 32 * i);
+                        v[2 * i] = __uint_as_float(u << 16);
+                        v[2 * i + 1] = __uint_as_float(u & 0xffff0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < D / 16; ++i) v[i] = 0.f;
+                }
+                float mx = v[0];
+#pragma unroll
+                for (int i = 1; i < D / 16; ++i) mx = fmaxf(mx, v[i]);
+                mx = group16_max(mx);
+                float sum = 0.f;
+#pragma unroll
+                for (int i = 0; i < D / 16; ++i) {
+                    v[i] = fast_exp2((v[i] - mx) * kLog2e);
+                    sum += v[i];
+                }
+                sum = group16_sum(sum);
+                const float inv = row < nv ? 1.0f / sum : 0.0f;
+#pragma unroll
+                for (int i = 0; i < D / 32; ++i) {
+                    const int ch = 2 * l16 + 32 * i;
+                    float y0 = v[2 * i] * inv, y1 = v[2 * i + 1] * inv;
+                    const float2 bb = *reinterpret_cast<const float2*>(sBeta + row * BP + ch);
+                    if (!is_ext(ch)) y0 *= fast_exp2(bb.x - sM[ch]);
+                    if (!is_ext(ch + 1)) y1 *= fast_exp2(bb.y - sM[ch + 1]);
+                    put_split2(sQh, sQl, row * XP + ch, y0, y1);
+                }
             }
         }
-        __syncthreads();
+        stage_bf16<D, 64, kBT>(sO, VP, p.dO + ((b * T + t0) * H_q + hq) * D, qs, nv);
+        lds_barrier();
+        // A^h = alpha dO V^T, zero above the diagonal, as A^T tiles (rows t, columns s):
+        // tiles w and w + 8 of the 4 x 4 grid; lane (s col, g) holds t = 16 it + 4 g + r
+        {
+            const int is0 = w >> 2, it0 = w & 3, is1 = is0 + 2;
+            f32x4_t a0 = zero4(), a1 = zero4();
+            const bool live0 = it0 <= is0, live1 = it0 <= is1;
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                const Frag x = M::load(sV + (16 * it0 + col) * VP + 8 * g + M::KSTEP * k);
+                if (live0) a0 = M::mma(x, M::load(sO + (16 * is0 + col) * VP + 8 * g + M::KSTEP * k), a0);
+                if (live1) a1 = M::mma(x, M::load(sO + (16 * is1 + col) * VP + 8 * g + M::KSTEP * k), a1);
+            }
+            const int s0 = 16 * is0 + col, s1 = 16 * is1 + col, tb = 16 * it0 + 4 * g;
+            float y0[4], y1[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                y0[r] = tb + r <= s0 ? alpha * a0[r] : 0.f;
+                y1[r] = tb + r <= s1 ? alpha * a1[r] : 0.f;
+            }
+            put_split2(sAh, sAl, s0 * AP + tb, y0[0], y0[1]);
+            put_split2(sAh, sAl, s0 * AP + tb + 2, y0[2], y0[3]);
+            put_split2(sAh, sAl, s1 * AP + tb, y1[0], y1[1]);
+            put_split2(sAh, sAl, s1 * AP + tb + 2, y1[2], y1[3]);
+        }
+        lds_barrier();
 
-        // dphi(q^h): state term and intra-chunk term
+        // dphi(q^h)^T: state term (accS) and intra-chunk term (accI)
         f32x4_t accS[NTI], accI[NTI];
 #pragma unroll
         for (int u = 0; u < NTI; ++u) {
@@ -478,112 +614,153 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
             accI[u] = zero4();
         }
         if (S0row) {
-#pragma unroll 2
-            for (int k8 = 0; k8 < KQ / 8; ++k8) {
-                const float4 y0 = reinterpret_cast<const float4*>(S0row)[2 * k8];
-                const float4 y1 = reinterpret_cast<const float4*>(S0row)[2 * k8 + 1];
-                const float ys[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                const float4 y0 = *reinterpret_cast<const float4*>(S0row + M::KSTEP * k + 8 * g);
+                const float4 y1 = *reinterpret_cast<const float4*>(S0row + M::KSTEP * k + 8 * g + 4);
+                const float xs[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+                Frag xh, xl;
+                split_bf16x8(xs, xh, xl);
 #pragma unroll
                 for (int u = 0; u < NTI; ++u) {
-                    float xf[8];
-                    bf8_to_f32(*reinterpret_cast<const uint4*>(sO + (16 * (i0 + u) + col) * HP + g * KQ + 8 * k8), xf);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) accS[u] = mma4(xf[j], ys[j], accS[u]);
+                    const Frag y = M::load(sO + (16 * (i0 + u) + col) * VP + 8 * g + M::KSTEP * k);
+                    accS[u] = M::mma(xh, y, accS[u]);
+                    accS[u] = M::mma(xl, y, accS[u]);
                 }
             }
         }
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int tok = 16 * tb + 4 * g + kk;
-                const float y = colx ? 0.f : sKh[tok * FP + cc];
-#pragma unroll
-                for (int u = 0; u < NTI; ++u)
-                    if (tb <= i0 + u) accI[u] = mma4(sA[(16 * (i0 + u) + col) * AP + tok], y, accI[u]);
+        for (int G = 0; G < 2; ++G) {
+            Frag xh = load_key_frag(sKh, XP, 32 * G, 16 * jb, lane);
+            Frag xl = load_key_frag(sKl, XP, 32 * G, 16 * jb, lane);
+            if (colx) {
+                xh = fzero;
+                xl = fzero;
             }
-        if (any_ext && colx) {
+#pragma unroll
+            for (int u = 0; u < NTI; ++u) {
+                const int i = i0 + u;
+                if (32 * G > 16 * i + 15) continue;  // keys after every query of the tile
+                const bf16_t* ar = sAh + (16 * i + col) * AP;
+                const bf16_t* al = sAl + (16 * i + col) * AP;
+                accI[u] = mma3(xh, xl, row_keypos(ar, 32 * G, g), row_keypos(al, 32 * G, g), accI[u]);
+            }
+        }
+        if (any_ext && extr) {
 #pragma unroll
             for (int u = 0; u < NTI; ++u)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int s = 16 * (i0 + u) + 4 * g + r;
-                    const float bs = sBeta[s * D + cc];
+                    if (!((extr >> r) & 1u)) continue;
+                    const int s = 16 * (i0 + u) + col, ch = ch0 + r;
+                    const float bs = sBeta[s * BP + ch];
                     float sum = 0.f;
                     for (int t = 0; t <= s; ++t)
-                        sum += sA[s * AP + t] * sKh[t * FP + cc] * fast_exp2(bs - sBeta[t * D + cc]);
+                        sum += get_split(sAh, sAl, s * AP + t) * get_split(sKh, sKl, t * XP + ch) *
+                               fast_exp2(bs - sBeta[t * BP + ch]);
                     accI[u][r] = sum;
                 }
         }
         float dpq[NTI][4], pq[NTI][4];
 #pragma unroll
-        for (int u = 0; u < NTI; ++u)
+        for (int u = 0; u < NTI; ++u) {
+            const int s = 16 * (i0 + u) + col;
+            const float4 b4 = beta4(s);
+            const float bs[4] = {b4.x, b4.y, b4.z, b4.w};
+            float qh[4];
+            split4(sQh, sQl, s * XP + ch0, qh);
+            float rsum = 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int s = 16 * (i0 + u) + 4 * g + r;
-                const float bs = sBeta[s * D + cc], m = sM[cc];
-                const float intra = colx ? accI[u][r] : accI[u][r] * fast_exp2(bs - m);
-                dpq[u][r] = intra + alpha * accS[u][r] * fast_exp2(bs);
-                const float qh = sQ[s * FP + cc];
-                pq[u][r] = colx ? qh : qh * fast_exp2(m - bs);
+                const bool ex = (extr >> r) & 1u;
+                const float intra = ex ? accI[u][r] : accI[u][r] * fast_exp2(bs[r] - mr[r]);
+                dpq[u][r] = intra + alpha * accS[u][r] * fast_exp2(bs[r]);
+                pq[u][r] = ex ? qh[r] : qh[r] * fast_exp2(mr[r] - bs[r]);
                 const float pd = pq[u][r] * dpq[u][r];
                 accDB[u][r] += pd;
-                const float rs = group16_sum(pd);
-                if (col == 0) sRow[s * NCB + jb] = rs;
+                rsum += pd;
             }
-        // dphi(k) intra-chunk term, summed over the heads
+            rsum = group4_sum(rsum);
+            if (g == 0) sRow[s * NCB + jb] = rsum;
+        }
+        lds_barrier();
+        // dq^h = phi(q) (.) (dphi(q) - <dphi(q), phi(q)>)
+        {
+            float* dq = p.dq + ((b * T + t0) * H_q + hq) * D + ch0;
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int s = 16 * sb + 4 * g + kk;
-                const float y = colx ? 0.f : sQ[s * FP + cc];
-#pragma unroll
-                for (int u = 0; u < NTI; ++u)
-                    if (sb >= i0 + u) accK[u] = mma4(sA[s * AP + 16 * (i0 + u) + col], y, accK[u]);
+            for (int u = 0; u < NTI; ++u) {
+                const int s = 16 * (i0 + u) + col;
+                const float rs = row_total<NCB>(sRow + s * NCB);
+                if (s < nv)
+                    *reinterpret_cast<float4*>(dq + s * qs) =
+                        make_float4(pq[u][0] * (dpq[u][0] - rs), pq[u][1] * (dpq[u][1] - rs),
+                                    pq[u][2] * (dpq[u][2] - rs), pq[u][3] * (dpq[u][3] - rs));
             }
-        if (any_ext && colx) {
+        }
+        // dphi(k)^T intra-chunk term, summed over the heads
+#pragma unroll
+        for (int G = 0; G < 2; ++G) {
+            Frag xh = load_key_frag(sQh, XP, 32 * G, 16 * jb, lane);
+            Frag xl = load_key_frag(sQl, XP, 32 * G, 16 * jb, lane);
+            if (colx) {
+                xh = fzero;
+                xl = fzero;
+            }
+#pragma unroll
+            for (int u = 0; u < NTI; ++u) {
+                const int i = i0 + u;
+                if (32 * G + 31 < 16 * i) continue;  // queries before every key of the tile
+                accK[u] = mma3(xh, xl, load_key_frag(sAh, AP, 32 * G, 16 * i, lane),
+                               load_key_frag(sAl, AP, 32 * G, 16 * i, lane), accK[u]);
+            }
+        }
+        if (any_ext && extr) {
 #pragma unroll
             for (int u = 0; u < NTI; ++u)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * (i0 + u) + 4 * g + r;
-                    const float bt = sBeta[t * D + cc];
+                    if (!((extr >> r) & 1u)) continue;
+                    const int t = 16 * (i0 + u) + col, ch = ch0 + r;
+                    const float bt = sBeta[t * BP + ch];
                     float sum = 0.f;
                     for (int s = t; s < 64; ++s)
-                        sum += sA[s * AP + t] * sQ[s * FP + cc] * fast_exp2(sBeta[s * D + cc] - bt);
+                        sum += get_split(sAh, sAl, s * AP + t) * get_split(sQh, sQl, s * XP + ch) *
+                               fast_exp2(sBeta[s * BP + ch] - bt);
                     accK[u][r] += sum;
                 }
         }
-        __syncthreads();
+        lds_barrier();
 
-        // alpha B^h[t][s] (s >= t), stored transposed over A^h; tiles w and w + 8 of
+        // alpha B^h[t][s] (s >= t), stored at [s][t] over A^h; tiles w and w + 8 of
         // the 4 x 4 grid (row tile t-block, column tile s-block), computed together
         {
-            const int it0 = w >> 2, is0 = w & 3, it1 = (w + 8) >> 2, is1 = w & 3;
-            const bool live0 = is0 >= it0, live1 = is1 >= it1;
+            const int it0 = w >> 2, is0 = w & 3, it1 = it0 + 2;
+            const bool live0 = is0 >= it0, live1 = is0 >= it1;
             f32x4_t a0 = zero4(), a1 = zero4();
 #pragma unroll
-            for (int k4 = 0; k4 < KQ / 4; ++k4) {
-                const float4 y4 = *reinterpret_cast<const float4*>(sQ + (16 * is0 + col) * FP + g * KQ + 4 * k4);
-                const float4 x40 = *reinterpret_cast<const float4*>(sKh + (16 * it0 + col) * FP + g * KQ + 4 * k4);
-                const float4 x41 = *reinterpret_cast<const float4*>(sKh + (16 * it1 + col) * FP + g * KQ + 4 * k4);
-                const float ys[4] = {y4.x, y4.y, y4.z, y4.w};
-                const float xs0[4] = {x40.x, x40.y, x40.z, x40.w}, xs1[4] = {x41.x, x41.y, x41.z, x41.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bool ext = (kbits >> (4 * k4 + j)) & 1u;
-                    if (live0) a0 = mma4(ext ? 0.f : xs0[j], ys[j], a0);
-                    if (live1) a1 = mma4(ext ? 0.f : xs1[j], ys[j], a1);
+            for (int k = 0; k < KS; ++k) {
+                const int cb = M::KSTEP * k + 8 * g;  // this lane group's 8 channels
+                const Frag yh = M::load(sQh + (16 * is0 + col) * XP + cb);
+                const Frag yl = M::load(sQl + (16 * is0 + col) * XP + cb);
+                Frag xh0 = M::load(sKh + (16 * it0 + col) * XP + cb), xl0 = M::load(sKl + (16 * it0 + col) * XP + cb);
+                Frag xh1 = M::load(sKh + (16 * it1 + col) * XP + cb), xl1 = M::load(sKl + (16 * it1 + col) * XP + cb);
+                if (any_ext) {
+                    const uint32_t bits = (sExt[cb >> 5] >> (cb & 31)) & 0xffu;
+                    xh0 = clear_elems(xh0, bits);
+                    xl0 = clear_elems(xl0, bits);
+                    xh1 = clear_elems(xh1, bits);
+                    xl1 = clear_elems(xl1, bits);
                 }
+                if (live0) a0 = mma3(xh0, xl0, yh, yl, a0);
+                if (live1) a1 = mma3(xh1, xl1, yh, yl, a1);
             }
+            const int s = 16 * is0 + col, tb0 = 16 * it0 + 4 * g, tb1 = 16 * it1 + 4 * g;
             if (any_ext) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int s = 16 * is0 + col;
 #pragma unroll
                     for (int tl = 0; tl < 2; ++tl) {
-                        const int t = 16 * (tl ? it1 : it0) + 4 * g + r;
+                        const int t = (tl ? tb1 : tb0) + r;
                         if (s < t) continue;
                         float sum = 0.f;
                         for (int wd = 0; wd < D / 32; ++wd) {
@@ -591,8 +768,8 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
                             while (bits) {
                                 const int ch = 32 * wd + __builtin_ctz(bits);
                                 bits &= bits - 1;
-                                sum += sKh[t * FP + ch] * sQ[s * FP + ch] *
-                                       fast_exp2(sBeta[s * D + ch] - sBeta[t * D + ch]);
+                                sum += get_split(sKh, sKl, t * XP + ch) * get_split(sQh, sQl, s * XP + ch) *
+                                       fast_exp2(sBeta[s * BP + ch] - sBeta[t * BP + ch]);
                             }
                         }
                         if (tl) a1[r] += sum;
@@ -600,122 +777,126 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
                     }
                 }
             }
+            float y0[4], y1[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int s = 16 * is0 + col;
-                const int t0r = 16 * it0 + 4 * g + r, t1r = 16 * it1 + 4 * g + r;
-                sA[s * AP + t0r] = s >= t0r ? alpha * a0[r] : 0.f;
-                sA[s * AP + t1r] = s >= t1r ? alpha * a1[r] : 0.f;
+                y0[r] = s >= tb0 + r ? alpha * a0[r] : 0.f;
+                y1[r] = s >= tb1 + r ? alpha * a1[r] : 0.f;
+            }
+            put_split2(sAh, sAl, s * AP + tb0, y0[0], y0[1]);
+            put_split2(sAh, sAl, s * AP + tb0 + 2, y0[2], y0[3]);
+            put_split2(sAh, sAl, s * AP + tb1, y1[0], y1[1]);
+            put_split2(sAh, sAl, s * AP + tb1 + 2, y1[2], y1[3]);
+        }
+        lds_barrier();
+        // dv^T intra-chunk term: sum_s dO_s[e] alpha B^h[t][s]
+#pragma unroll
+        for (int G = 0; G < 2; ++G) {
+            const Frag x = load_key_frag(sO, VP, 32 * G, 16 * jb, lane);
+#pragma unroll
+            for (int u = 0; u < NTI; ++u) {
+                const int i = i0 + u;
+                if (32 * G + 31 < 16 * i) continue;
+                accV[u] = M::mma(x, load_key_frag(sAh, AP, 32 * G, 16 * i, lane), accV[u]);
+                accV[u] = M::mma(x, load_key_frag(sAl, AP, 32 * G, 16 * i, lane), accV[u]);
             }
         }
-        // dq^h = phi(q) (.) (dphi(q) - <dphi(q), phi(q)>)
-        {
-            float* dq = p.dq + ((b * T + t0) * H_q + hq) * D + cc;
-#pragma unroll
-            for (int u = 0; u < NTI; ++u)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int s = 16 * (i0 + u) + 4 * g + r;
-                    float rs = 0.f;
-#pragma unroll
-                    for (int j = 0; j < NCB; ++j) rs += sRow[s * NCB + j];
-                    if (s < nv) dq[s * qs] = pq[u][r] * (dpq[u][r] - rs);
-                }
-        }
-        __syncthreads();
-        // dv intra-chunk term: sum_s alpha B^h[t][s] dO_s
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int s = 16 * sb + 4 * g + kk;
-                const float y = bf16_to_f32(sO[s * HP + cc]);
-#pragma unroll
-                for (int u = 0; u < NTI; ++u)
-                    if (sb >= i0 + u) accV[u] = mma4(sA[s * AP + 16 * (i0 + u) + col], y, accV[u]);
-            }
-        __syncthreads();
+        lds_barrier();
     }
 
-    // adjoint entering the chunk's last state (Y operands U[cc][g*KQ + ks]; none for the last chunk)
-    const float* Urow = c < n - 1 ? p.adj + ((b * p.H_kv + hk) * (n - 1) + (n - 2 - c)) * rec + size_t(cc) * D + g * KQ
-                                  : nullptr;
-    // dphi(k) = intra + 2^(Delta-b) (.) (U v)
+    // adjoint entering the chunk's last state (none for the last chunk)
+    const float* Ubase = c < n - 1 ? p.adj + ((b * p.H_kv + hk) * (n - 1) + (n - 2 - c)) * rec : nullptr;
+    // dphi(k)^T = intra + 2^(Delta-b) (.) (U v), U v from fragments U[cf][e]
+    f32x4_t us[NTI];
+#pragma unroll
+    for (int u = 0; u < NTI; ++u) us[u] = zero4();
+    if (Ubase) {
+        const float* Urow = Ubase + size_t(cf) * D;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            const float4 y0 = *reinterpret_cast<const float4*>(Urow + M::KSTEP * k + 8 * g);
+            const float4 y1 = *reinterpret_cast<const float4*>(Urow + M::KSTEP * k + 8 * g + 4);
+            const float xs[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+            Frag xh, xl;
+            split_bf16x8(xs, xh, xl);
+#pragma unroll
+            for (int u = 0; u < NTI; ++u) {
+                const Frag y = M::load(sV + (16 * (i0 + u) + col) * VP + 8 * g + M::KSTEP * k);
+                us[u] = M::mma(xh, y, us[u]);
+                us[u] = M::mma(xl, y, us[u]);
+            }
+        }
+    }
+    const float4 d4 = *reinterpret_cast<const float4*>(sDelta + ch0);
+    const float dlr[4] = {d4.x, d4.y, d4.z, d4.w};
     float dpk[NTI][4], pk[NTI][4];
 #pragma unroll
     for (int u = 0; u < NTI; ++u) {
-        const int i = i0 + u;
-        f32x4_t us = zero4();
-        if (Urow) {
-#pragma unroll 2
-            for (int k8 = 0; k8 < KQ / 8; ++k8) {
-                const float4 y0 = reinterpret_cast<const float4*>(Urow)[2 * k8];
-                const float4 y1 = reinterpret_cast<const float4*>(Urow)[2 * k8 + 1];
-                const float ys[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-                float xf[8];
-                bf8_to_f32(*reinterpret_cast<const uint4*>(sV + (16 * i + col) * HP + g * KQ + 8 * k8), xf);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) us = mma4(xf[j], ys[j], us);
-            }
-        }
+        const int t = 16 * (i0 + u) + col;
+        const float4 b4 = beta4(t);
+        const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
+        float kh[4], kt[4];
+        split4(sKh, sKl, t * XP + ch0, kh);
+        float rsum = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = 16 * i + 4 * g + r;
-            const float bt = sBeta[t * D + cc], m = sM[cc], dl = sDelta[cc];
-            const float intra = colx ? accK[u][r] : accK[u][r] * fast_exp2(m - bt);
-            dpk[u][r] = intra + us[r] * fast_exp2(dl - bt);
-            const float kh = sKh[t * FP + cc];
-            pk[u][r] = colx ? kh : kh * fast_exp2(bt - m);
-            sQ[t * FP + cc] = pk[u][r] * fast_exp2(dl - bt);  // K~
+            const bool ex = (extr >> r) & 1u;
+            const float intra = ex ? accK[u][r] : accK[u][r] * fast_exp2(mr[r] - bt[r]);
+            dpk[u][r] = intra + us[u][r] * fast_exp2(dlr[r] - bt[r]);
+            pk[u][r] = ex ? kh[r] : kh[r] * fast_exp2(bt[r] - mr[r]);
+            kt[r] = pk[u][r] * fast_exp2(dlr[r] - bt[r]);  // K~
             const float pd = pk[u][r] * dpk[u][r];
             accDB[u][r] -= pd;
-            const float rs = group16_sum(pd);
-            if (col == 0) sRow[t * NCB + jb] = rs;
+            rsum += pd;
         }
+        put_split2(sQh, sQl, t * XP + ch0, kt[0], kt[1]);
+        put_split2(sQh, sQl, t * XP + ch0 + 2, kt[2], kt[3]);
+        rsum = group4_sum(rsum);
+        if (g == 0) sRow[t * NCB + jb] = rsum;
     }
-    __syncthreads();
-    // dv += K~ U: Y = U[g*KQ + ks][cc]
-    {
-        const bool has_u = c < n - 1;
-        const float* Ub = p.adj + ((b * p.H_kv + hk) * (n - 1) + (has_u ? n - 2 - c : 0)) * rec + cc;
+    lds_barrier();
+    // dv^T += U^T K~^T: X = U[32 k + 8 g ..][cf], Y = K~ rows
+    if (Ubase) {
+        const float* Ucol = Ubase + cf;
 #pragma unroll
-        for (int k4 = 0; k4 < KQ / 4; ++k4) {
-            float ys[4];
+        for (int k = 0; k < KS; ++k) {
+            float xs[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ys[j] = has_u ? Ub[size_t(g * KQ + 4 * k4 + j) * D] : 0.f;
+            for (int j = 0; j < 8; ++j) xs[j] = Ucol[size_t(M::KSTEP * k + 8 * g + j) * D];
+            Frag xh, xl;
+            split_bf16x8(xs, xh, xl);
 #pragma unroll
             for (int u = 0; u < NTI; ++u) {
-                const float4 x4 = *reinterpret_cast<const float4*>(sQ + (16 * (i0 + u) + col) * FP + g * KQ + 4 * k4);
-                accV[u] = mma4(x4.x, ys[0], accV[u]);
-                accV[u] = mma4(x4.y, ys[1], accV[u]);
-                accV[u] = mma4(x4.z, ys[2], accV[u]);
-                accV[u] = mma4(x4.w, ys[3], accV[u]);
+                const int row = 16 * (i0 + u) + col;
+                accV[u] = mma3(xh, xl, M::load(sQh + row * XP + M::KSTEP * k + 8 * g),
+                               M::load(sQl + row * XP + M::KSTEP * k + 8 * g), accV[u]);
             }
         }
     }
-    // outputs
-    float* dk = p.dk + ((b * T + t0) * p.H_kv + hk) * D + cc;
-    float* dv = p.dv + ((b * T + t0) * p.H_kv + hk) * D + cc;
-    float* db = p.db + ((b * p.H_kv + hk) * T + t0) * D + cc;
-    float csum = 0.f;
+    // outputs (float4 per lane: channels ch0 .. ch0 + 3 of row t)
+    float* dk = p.dk + ((b * T + t0) * p.H_kv + hk) * D + ch0;
+    float* dv = p.dv + ((b * T + t0) * p.H_kv + hk) * D + ch0;
+    float* db = p.db + ((b * p.H_kv + hk) * T + t0) * D + ch0;
+    float csum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < NTI; ++u)
+    for (int u = 0; u < NTI; ++u) {
+        const int t = 16 * (i0 + u) + col;
+        const float rs = row_total<NCB>(sRow + t * NCB);
+        if (t < nv) {
+            *reinterpret_cast<float4*>(dk + t * kvs) =
+                make_float4(pk[u][0] * (dpk[u][0] - rs), pk[u][1] * (dpk[u][1] - rs), pk[u][2] * (dpk[u][2] - rs),
+                            pk[u][3] * (dpk[u][3] - rs));
+            *reinterpret_cast<float4*>(dv + t * kvs) = make_float4(accV[u][0], accV[u][1], accV[u][2], accV[u][3]);
+            *reinterpret_cast<float4*>(db + t * D) = make_float4(accDB[u][0], accDB[u][1], accDB[u][2], accDB[u][3]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * (i0 + u) + 4 * g + r;
-            float rs = 0.f;
-#pragma unroll
-            for (int j = 0; j < NCB; ++j) rs += sRow[t * NCB + j];
-            if (t < nv) {
-                dk[t * kvs] = pk[u][r] * (dpk[u][r] - rs);
-                dv[t * kvs] = accV[u][r];
-                db[t * D] = accDB[u][r];
-                csum += accDB[u][r];
-            }
+            for (int r = 0; r < 4; ++r) csum[r] += accDB[u][r];
         }
-    csum = group4_sum(csum);
-    if (g == 0) sCol[(w / NCB) * D + cc] = csum;
-    __syncthreads();
+    }
+    // chunk sums of dL/dB per channel: over this lane's rows, then the 16 row lanes
+#pragma unroll
+    for (int r = 0; r < 4; ++r) csum[r] = group16_sum(csum[r]);
+    if (col == 0) *reinterpret_cast<float4*>(sCol + (w / NCB) * D + ch0) = make_float4(csum[0], csum[1], csum[2], csum[3]);
+    lds_barrier();
     if (tid < D) {
         float s = 0.f;
 #pragma unroll
@@ -761,7 +942,7 @@ __global__ __launch_bounds__(kST) void bwd_swa_q_kernel(BwdParams p) {
             *reinterpret_cast<uint4*>(sV + r * HP + cpos) = vu;
         }
     }
-    __syncthreads();
+    lds_barrier();
     const int w = p.window;
     const float sc = kLog2e * rsqrtf(static_cast<float>(D));
     const float beta = 1.0f - p.alpha;
@@ -915,7 +1096,7 @@ __global__ __launch_bounds__(kST) __attribute__((amdgpu_waves_per_eu(2))) void b
     }
     for (int h = 0; h < p.n_rep; ++h) {
         const int hq = hk * p.n_rep + h;
-        __syncthreads();
+        lds_barrier();
         stage_bf16<D, 128, kST>(sQ, HP, p.q + ((b * T + t0) * H_q + hq) * D, qs, nq);
         stage_bf16<D, 128, kST>(sO, HP, p.dO + ((b * T + t0) * H_q + hq) * D, qs, nq);
         if (tid < 128) {
@@ -924,7 +1105,7 @@ __global__ __launch_bounds__(kST) __attribute__((amdgpu_waves_per_eu(2))) void b
             sL[tid] = ok ? st[0] : 0.f;
             sDs[tid] = ok ? st[1] : 0.f;
         }
-        __syncthreads();
+        lds_barrier();
         // S[q][key] on query tiles qt0 .. qt0 + 5: lane (key col, g) holds queries 16 qt + 4 g + r
         M::frag ph[3], pl[3], dh[3], dl[3];
 #pragma unroll
@@ -1014,7 +1195,7 @@ __global__ __launch_bounds__(kST) void bwd_gate_kernel(BwdParams p) {
             sS[t * FP + ch] = t < nv ? src[t * D + ch] : 0.f;
         }
     }
-    __syncthreads();
+    lds_barrier();
     {
         // sum of the chunk sums after this chunk: thread (channel, part) takes
         // every P-th later chunk, 16 loads in flight at a time
@@ -1035,7 +1216,7 @@ __global__ __launch_bounds__(kST) void bwd_gate_kernel(BwdParams p) {
         for (int u = 1; u < U; ++u) a[0] += a[u];
         sSuf[part * D + ch] = a[0];
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < D) {
         // reverse inclusive scan down the chunk's rows, in registers
         float run = 0.f;
@@ -1050,7 +1231,7 @@ __global__ __launch_bounds__(kST) void bwd_gate_kernel(BwdParams p) {
             sS[t * FP + tid] = run;
         }
     }
-    __syncthreads();
+    lds_barrier();
     // sS[t][c] becomes the dk contribution of row t, channel c
     if (GATE == 0) {
         // four lanes per row: ds_t = (sum_c d ln g_t[c]) (1 - g_t) / d on every channel
@@ -1065,7 +1246,7 @@ __global__ __launch_bounds__(kST) void bwd_gate_kernel(BwdParams p) {
         ss += dpp<kDppXor1>(ss);
         ss += dpp<kDppXor2>(ss);
         const float ds = ss * sigmoidf_stable(-sk * (1.0f / D)) * (1.0f / D);
-        __syncthreads();
+        lds_barrier();
         for (int i = part; i < D; i += 4) sS[row * FP + i] = ds;
     } else {
         for (int idx = tid; idx < 64 * D; idx += kST) {
@@ -1076,7 +1257,7 @@ __global__ __launch_bounds__(kST) void bwd_gate_kernel(BwdParams p) {
             const float x = s / static_cast<float>(hi - lo);
             sS[t * FP + ch] *= sigmoidf_stable(-x) / static_cast<float>(hi - lo);
         }
-        __syncthreads();
+        lds_barrier();
         // pool transpose: channel c'' collects channels c'' - 2 .. c'' + 1
         for (int idx = tid; idx < 64 * D; idx += kST) {
             const int t = idx / D, ch = idx % D;
@@ -1087,7 +1268,7 @@ __global__ __launch_bounds__(kST) void bwd_gate_kernel(BwdParams p) {
             sK[t * FP + ch] = add;  // raw k no longer needed
         }
     }
-    __syncthreads();
+    lds_barrier();
     const float* add = GATE == 0 ? sS : sK;
     float* dk = p.dk + ((b * T + t0) * p.H_kv + hk) * D;
     constexpr int PPR = D / 4;

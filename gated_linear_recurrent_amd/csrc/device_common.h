@@ -123,6 +123,17 @@ __device__ __forceinline__ float group4_sum(float v) {
     return v + __shfl_xor(v, 32, 64);
 }
 
+// Workgroup barrier that orders LDS accesses only: the fences are restricted
+// to the local address space, so the barrier waits for outstanding LDS
+// operations but not for global stores in flight. For kernels whose barriers
+// protect LDS data only (no global value written and read back inside the
+// workgroup).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------- MFMA traits
 template <typename OT> struct Mfma;
 
