@@ -532,28 +532,44 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
         out[3] = __uint_as_float(h.y & 0xffff0000u) + __uint_as_float(l.y & 0xffff0000u);
     };
 
+    // Raw q rows (Q^ layout: 16 lanes per row, channel pairs 2 l + 32 i; a
+    // wave's four rows per instruction are 4 apart, so their LDS rows fall on
+    // disjoint banks) and raw dO pieces of the next head are loaded while the
+    // current head computes.
+    const int l16 = lane & 15, sub = lane >> 4;
+    auto q_row = [&](int pass) { return (w & 3) + 16 * ((w >> 2) + 2 * pass) + 4 * sub; };
+    constexpr int OPT = 64 * D / 8 / kBT;  // dO pieces (8 bf16) per thread
+    uint32_t qraw[2][D / 32];
+    uint4 oraw[OPT];
+    auto issue_head = [&](int hq) {
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int row = q_row(pass);
+            const bf16_t* qr = p.q + ((b * T + t0 + (row < nv ? row : 0)) * H_q + hq) * D + 2 * l16;
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) qraw[pass][i] = row < nv ? *reinterpret_cast<const uint32_t*>(qr + 32 * i) : 0u;
+        }
+        const bf16_t* og = p.dO + ((b * T + t0) * H_q + hq) * D;
+#pragma unroll
+        for (int e = 0; e < OPT; ++e) {
+            const int idx = tid + e * kBT, r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
+            oraw[e] = r < nv ? *reinterpret_cast<const uint4*>(og + r * qs + c8) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    issue_head(hk * p.n_rep);
+
     for (int h = 0; h < p.n_rep; ++h) {
         const int hq = hk * p.n_rep + h;
-        // Q^ = phi(q) 2^(b-m) (extreme channels: phi(q)) straight from the raw rows:
-        // 16 lanes per row, channel pairs 2 l + 32 i; a wave's four rows per
-        // instruction are 4 apart, so their LDS rows fall on disjoint banks
+        // Q^ = phi(q) 2^(b-m) (extreme channels: phi(q))
         {
-            const int l16 = lane & 15, sub = lane >> 4;
 #pragma unroll
             for (int pass = 0; pass < 2; ++pass) {
-                const int row = (w & 3) + 16 * ((w >> 2) + 2 * pass) + 4 * sub;
+                const int row = q_row(pass);
                 float v[D / 16];
-                if (row < nv) {
-                    const bf16_t* qr = p.q + ((b * T + t0 + row) * H_q + hq) * D + 2 * l16;
 #pragma unroll
-                    for (int i = 0; i < D / 32; ++i) {
-                        const uint32_t u = *reinterpret_cast<const uint32_t*>(qr + 32 * i);
-                        v[2 * i] = __uint_as_float(u << 16);
-                        v[2 * i + 1] = __uint_as_float(u & 0xffff0000u);
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < D / 16; ++i) v[i] = 0.f;
+                for (int i = 0; i < D / 32; ++i) {
+                    v[2 * i] = __uint_as_float(qraw[pass][i] << 16);
+                    v[2 * i + 1] = __uint_as_float(qraw[pass][i] & 0xffff0000u);
                 }
                 float mx = v[0];
 #pragma unroll
@@ -578,7 +594,12 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
                 }
             }
         }
-        stage_bf16<D, 64, kBT>(sO, VP, p.dO + ((b * T + t0) * H_q + hq) * D, qs, nv);
+#pragma unroll
+        for (int e = 0; e < OPT; ++e) {
+            const int idx = tid + e * kBT;
+            *reinterpret_cast<uint4*>(sO + (idx / (D / 8)) * VP + (idx % (D / 8)) * 8) = oraw[e];
+        }
+        if (h + 1 < p.n_rep) issue_head(hq + 1);
         lds_barrier();
         // A^h = alpha dO V^T, zero above the diagonal, as A^T tiles (rows t, columns s):
         // tiles w and w + 8 of the 4 x 4 grid; lane (s col, g) holds t = 16 it + 4 g + r
