@@ -36,8 +36,9 @@
 //   bwd_chunk_kernel   : GRM gradients of one chunk: dq, dk (feature-map
 //                        part), dv written; dL/dB rows and chunk sums stored
 //   bwd_swa_q_kernel   : window softmax per query; dq += ..; row statistics
-//   bwd_swa_k_kernel   : per key tile: dk += .., dv += ..
-//   bwd_gate_kernel    : suffix sums of dL/dB, sigmoid and pool transpose: dk += ..
+//   bwd_swa_k_kernel   : per key tile: dk += .., dv += ..; then the gate chain of
+//                        the chunk (suffix sums of dL/dB, sigmoid and pool
+//                        transpose) into the same dk update
 // Computed operands enter the bf16 MFMA as hi + lo bf16 pairs (fp32-accurate
 // products), raw bf16 inputs as they are. Barriers order LDS only: no kernel
 // here reads back a global value it wrote.
@@ -117,15 +118,23 @@ __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8_t& hi, bf16x
 
 // Rows 0..63 of a bf16 matrix (row stride `stride` elements) into LDS as
 // float32 (pitch in floats); rows >= nv are zero.
+// (Fixed trip counts, loads first: every global load of a thread is in
+// flight before the first LDS store.)
 template <int D, int NTH>
 __device__ __forceinline__ void stage_f32(float* dst, int pitch, const bf16_t* src, int64_t stride, int nv) {
-    constexpr int PPR = D / 8;
-    for (int idx = threadIdx.x; idx < 64 * PPR; idx += NTH) {
-        const int r = idx / PPR, c = (idx % PPR) * 8;
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (r < nv) u = *reinterpret_cast<const uint4*>(src + r * stride + c);
+    constexpr int PPR = D / 8, PER = 64 * PPR / NTH;
+    static_assert(PER * NTH == 64 * PPR, "pieces divide over the threads");
+    uint4 u[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int idx = threadIdx.x + e * NTH, r = idx / PPR, c = (idx % PPR) * 8;
+        u[e] = r < nv ? *reinterpret_cast<const uint4*>(src + r * stride + c) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int idx = threadIdx.x + e * NTH, r = idx / PPR, c = (idx % PPR) * 8;
         float f[8];
-        bf8_to_f32(u, f);
+        bf8_to_f32(u[e], f);
         float4* d4 = reinterpret_cast<float4*>(dst + r * pitch + c);
         d4[0] = make_float4(f[0], f[1], f[2], f[3]);
         d4[1] = make_float4(f[4], f[5], f[6], f[7]);
@@ -136,12 +145,18 @@ __device__ __forceinline__ void stage_f32(float* dst, int pitch, const bf16_t* s
 // rows >= nv are zero.
 template <int D, int ROWS, int NTH>
 __device__ __forceinline__ void stage_bf16(bf16_t* dst, int pitch, const bf16_t* src, int64_t stride, int nv) {
-    constexpr int PPR = D / 8;
-    for (int idx = threadIdx.x; idx < ROWS * PPR; idx += NTH) {
-        const int r = idx / PPR, c = (idx % PPR) * 8;
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (r < nv) u = *reinterpret_cast<const uint4*>(src + r * stride + c);
-        *reinterpret_cast<uint4*>(dst + r * pitch + c) = u;
+    constexpr int PPR = D / 8, PER = ROWS * PPR / NTH;
+    static_assert(PER * NTH == ROWS * PPR, "pieces divide over the threads");
+    uint4 u[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int idx = threadIdx.x + e * NTH, r = idx / PPR, c = (idx % PPR) * 8;
+        u[e] = r < nv ? *reinterpret_cast<const uint4*>(src + r * stride + c) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int idx = threadIdx.x + e * NTH, r = idx / PPR, c = (idx % PPR) * 8;
+        *reinterpret_cast<uint4*>(dst + r * pitch + c) = u[e];
     }
 }
 
@@ -926,6 +941,110 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
     }
 }
 
+// ---------------------------------------------------------------- gate chain
+// d ln g_u = sum_{t >= u} dL/dB_t (later chunks through their sums), then
+// dx = d ln g (1 - g) and the pool's transpose. Leaves the dk contribution of
+// the chunk's row t, channel c at add[t * FP + c] (either sK or sS) and ends
+// synchronised. sK, sS: fp32 [64][FP] scratch, sSuf: kST floats.
+template <int D, int GATE, int FP>
+__device__ __forceinline__ const float* gate_chain(const BwdParams& p, int c, int hk, int64_t b, float* sK, float* sS,
+                                                   float* sSuf) {
+    const int64_t n = p.n, T = p.T, t0 = 64 * static_cast<int64_t>(c);
+    const int nv = static_cast<int>(T - t0 < 64 ? T - t0 : 64);
+    const int64_t kvs = static_cast<int64_t>(p.H_kv) * D;
+    const int tid = threadIdx.x;
+    stage_f32<D, kST>(sK, FP, p.k + ((b * T + t0) * p.H_kv + hk) * D, kvs, nv);
+    {
+        const float* src = p.db + ((b * p.H_kv + hk) * T + t0) * D;
+        constexpr int PPR = D / 4, PER = 64 * PPR / kST;
+        float4 u[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int idx = tid + e * kST, t = idx / PPR, c4 = (idx % PPR) * 4;
+            u[e] = t < nv ? *reinterpret_cast<const float4*>(src + t * D + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int idx = tid + e * kST, t = idx / PPR, c4 = (idx % PPR) * 4;
+            *reinterpret_cast<float4*>(sS + t * FP + c4) = u[e];
+        }
+    }
+    {
+        // sum of the chunk sums after this chunk: thread (channel, part) takes
+        // every P-th later chunk, 16 loads in flight at a time
+        constexpr int P = kST / D, U = 16;
+        const int ch = tid % D, part = tid / D;
+        const float* tot = p.tot + (b * p.H_kv + hk) * n * D + ch;
+        float a[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) a[u] = 0.f;
+        for (int64_t j0 = c + 1 + part; j0 < n; j0 += U * P) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t j = j0 + u * P;
+                if (j < n) a[u] += tot[j * D];
+            }
+        }
+#pragma unroll
+        for (int u = 1; u < U; ++u) a[0] += a[u];
+        sSuf[part * D + ch] = a[0];
+    }
+    lds_barrier();
+    if (tid < D) {
+        // reverse inclusive scan down the chunk's rows, in registers
+        float run = 0.f;
+#pragma unroll
+        for (int j = 0; j < kST / D; ++j) run += sSuf[j * D + tid];
+        float r[64];
+#pragma unroll
+        for (int t = 0; t < 64; ++t) r[t] = sS[t * FP + tid];  // rows >= nv hold 0
+#pragma unroll
+        for (int t = 63; t >= 0; --t) {
+            run += r[t];
+            sS[t * FP + tid] = run;
+        }
+    }
+    lds_barrier();
+    if (GATE == 0) {
+        // four lanes per row: ds_t = (sum_c d ln g_t[c]) (1 - g_t) / d on every channel
+        const int row = tid >> 2, part = tid & 3;
+        float sk = 0.f, ss = 0.f;
+        for (int i = part; i < D; i += 4) {
+            sk += sK[row * FP + i];
+            ss += sS[row * FP + i];
+        }
+        sk += dpp<kDppXor1>(sk);
+        sk += dpp<kDppXor2>(sk);
+        ss += dpp<kDppXor1>(ss);
+        ss += dpp<kDppXor2>(ss);
+        const float ds = ss * sigmoidf_stable(-sk * (1.0f / D)) * (1.0f / D);
+        lds_barrier();
+        for (int i = part; i < D; i += 4) sS[row * FP + i] = ds;
+        lds_barrier();
+        return sS;
+    }
+    for (int idx = tid; idx < 64 * D; idx += kST) {
+        const int t = idx / D, ch = idx % D;
+        const int lo = ch > 0 ? ch - 1 : 0, hi = ch + 3 < D ? ch + 3 : D;
+        float sum = 0.f;
+        for (int j = lo; j < hi; ++j) sum += sK[t * FP + j];
+        const float x = sum / static_cast<float>(hi - lo);
+        sS[t * FP + ch] *= sigmoidf_stable(-x) / static_cast<float>(hi - lo);
+    }
+    lds_barrier();
+    // pool transpose: channel c'' collects channels c'' - 2 .. c'' + 1
+    for (int idx = tid; idx < 64 * D; idx += kST) {
+        const int t = idx / D, ch = idx % D;
+        float add = 0.f;
+#pragma unroll
+        for (int j = ch - 2; j <= ch + 1; ++j)
+            if (j >= 0 && j < D) add += sS[t * FP + j];
+        sK[t * FP + ch] = add;  // raw k no longer needed
+    }
+    lds_barrier();
+    return sK;
+}
+
 // ---------------------------------------------------------------- window: queries
 // One workgroup per (chunk, key/value head, sequence); wave i holds query
 // tile i of the chunk, all query heads of the group in turn. Keys of the
@@ -950,17 +1069,21 @@ __global__ __launch_bounds__(kST) void bwd_swa_q_kernel(BwdParams p) {
         const int64_t first = t0 - 64;
         const int lo = first < 0 ? 64 : 0;
         const int hi = static_cast<int>(T - first < 128 ? T - first : 128);
-        constexpr int PPR = D / 8;
-        for (int idx = tid; idx < 128 * PPR; idx += kST) {
-            const int r = idx / PPR, cpos = (idx % PPR) * 8;
-            uint4 ku = make_uint4(0, 0, 0, 0), vu = make_uint4(0, 0, 0, 0);
-            if (r >= lo && r < hi) {
-                const int64_t off = ((b * T + first + r) * p.H_kv + hk) * D + cpos;
-                ku = *reinterpret_cast<const uint4*>(p.k + off);
-                vu = *reinterpret_cast<const uint4*>(p.v + off);
-            }
-            *reinterpret_cast<uint4*>(sK + r * HP + cpos) = ku;
-            *reinterpret_cast<uint4*>(sV + r * HP + cpos) = vu;
+        constexpr int PPR = D / 8, PER = 128 * PPR / kST;
+        uint4 ku[PER], vu[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int idx = tid + e * kST, r = idx / PPR, cpos = (idx % PPR) * 8;
+            const bool ok = r >= lo && r < hi;
+            const int64_t off = ((b * T + first + (ok ? r : lo)) * p.H_kv + hk) * D + cpos;
+            ku[e] = ok ? *reinterpret_cast<const uint4*>(p.k + off) : make_uint4(0, 0, 0, 0);
+            vu[e] = ok ? *reinterpret_cast<const uint4*>(p.v + off) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int idx = tid + e * kST, r = idx / PPR, cpos = (idx % PPR) * 8;
+            *reinterpret_cast<uint4*>(sK + r * HP + cpos) = ku[e];
+            *reinterpret_cast<uint4*>(sV + r * HP + cpos) = vu[e];
         }
     }
     lds_barrier();
@@ -1075,13 +1198,14 @@ __global__ __launch_bounds__(kST) void bwd_swa_q_kernel(BwdParams p) {
 // i of the chunk. The queries that can see those keys are in this chunk and
 // the next, taken in aligned query-tile pairs (2G, 2G + 1); dk and dv are
 // summed over the query heads of the group.
-template <int D>
+template <int D, int GATE, bool WIN>
 __global__ __launch_bounds__(kST) __attribute__((amdgpu_waves_per_eu(2))) void bwd_swa_k_kernel(BwdParams p) {
     typedef Mfma<bf16_t> M;
     constexpr int HP = D + 16, KS = D / M::KSTEP, NCB = D / 16;
     __shared__ __align__(16) bf16_t sQ[128 * HP];
     __shared__ __align__(16) bf16_t sO[128 * HP];
-    __shared__ float sL[128], sDs[128];
+    __shared__ float sL[kST];  // window statistics: log2-sum-exp in [0, 128), sum p dp in [128, 256); gate scratch later
+    float* sDs = sL + 128;
 
     const int c = blockIdx.x, hk = blockIdx.y;
     const int64_t b = blockIdx.z, T = p.T, t0 = 64 * static_cast<int64_t>(c);
@@ -1115,7 +1239,7 @@ __global__ __launch_bounds__(kST) __attribute__((amdgpu_waves_per_eu(2))) void b
         adk[j] = zero4();
         adv[j] = zero4();
     }
-    for (int h = 0; h < p.n_rep; ++h) {
+    for (int h = 0; h < (WIN ? p.n_rep : 0); ++h) {
         const int hq = hk * p.n_rep + h;
         lds_barrier();
         stage_bf16<D, 128, kST>(sQ, HP, p.q + ((b * T + t0) * H_q + hq) * D, qs, nq);
@@ -1172,137 +1296,34 @@ __global__ __launch_bounds__(kST) __attribute__((amdgpu_waves_per_eu(2))) void b
             }
         }
     }
+    // the gate's share of dk for this chunk's keys, in the bytes of the q and dO tiles
+    constexpr int GFP = D + 4;
+    static_assert(64 * GFP * 4 <= 128 * HP * 2, "gate scratch fits a query tile");
+    lds_barrier();
+    const float* gadd = gate_chain<D, GATE, GFP>(p, c, hk, b, reinterpret_cast<float*>(sQ), reinterpret_cast<float*>(sO),
+                                                 sL);
     if (ktok < T) {
         const float rs = rsqrtf(static_cast<float>(D));
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
+            const float4 ga = *reinterpret_cast<const float4*>(gadd + kj * GFP + 16 * cb + 4 * g);
             float4* pk = reinterpret_cast<float4*>(p.dk + (b * T + ktok) * kvs + hk * D + 16 * cb + 4 * g);
-            float4* pv = reinterpret_cast<float4*>(p.dv + (b * T + ktok) * kvs + hk * D + 16 * cb + 4 * g);
-            float4 x = *pk, y = *pv;
-            x.x += adk[cb][0] * rs;
-            x.y += adk[cb][1] * rs;
-            x.z += adk[cb][2] * rs;
-            x.w += adk[cb][3] * rs;
-            y.x += adv[cb][0];
-            y.y += adv[cb][1];
-            y.z += adv[cb][2];
-            y.w += adv[cb][3];
+            float4 x = *pk;
+            x.x += adk[cb][0] * rs + ga.x;
+            x.y += adk[cb][1] * rs + ga.y;
+            x.z += adk[cb][2] * rs + ga.z;
+            x.w += adk[cb][3] * rs + ga.w;
             *pk = x;
-            *pv = y;
-        }
-    }
-}
-
-// ---------------------------------------------------------------- gate chain
-// d ln g_u = sum_{t >= u} dL/dB_t (later chunks through their sums), then
-// dx = d ln g (1 - g) and the pool's transpose: dk += ..
-template <int D, int GATE>
-__global__ __launch_bounds__(kST) void bwd_gate_kernel(BwdParams p) {
-    constexpr int FP = D + 4;
-    __shared__ __align__(16) float sK[64 * FP];
-    __shared__ __align__(16) float sS[64 * FP];
-    __shared__ float sSuf[kST];
-
-    const int c = blockIdx.x, hk = blockIdx.y;
-    const int64_t b = blockIdx.z, n = p.n, T = p.T, t0 = 64 * static_cast<int64_t>(c);
-    const int nv = static_cast<int>(T - t0 < 64 ? T - t0 : 64);
-    const int64_t kvs = static_cast<int64_t>(p.H_kv) * D;
-    const int tid = threadIdx.x;
-    stage_f32<D, kST>(sK, FP, p.k + ((b * T + t0) * p.H_kv + hk) * D, kvs, nv);
-    {
-        const float* src = p.db + ((b * p.H_kv + hk) * T + t0) * D;
-        for (int idx = tid; idx < 64 * D; idx += kST) {
-            const int t = idx / D, ch = idx % D;
-            sS[t * FP + ch] = t < nv ? src[t * D + ch] : 0.f;
-        }
-    }
-    lds_barrier();
-    {
-        // sum of the chunk sums after this chunk: thread (channel, part) takes
-        // every P-th later chunk, 16 loads in flight at a time
-        constexpr int P = kST / D, U = 16;
-        const int ch = tid % D, part = tid / D;
-        const float* tot = p.tot + (b * p.H_kv + hk) * n * D + ch;
-        float a[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) a[u] = 0.f;
-        for (int64_t j0 = c + 1 + part; j0 < n; j0 += U * P) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t j = j0 + u * P;
-                if (j < n) a[u] += tot[j * D];
+            if (WIN) {
+                float4* pv = reinterpret_cast<float4*>(p.dv + (b * T + ktok) * kvs + hk * D + 16 * cb + 4 * g);
+                float4 y = *pv;
+                y.x += adv[cb][0];
+                y.y += adv[cb][1];
+                y.z += adv[cb][2];
+                y.w += adv[cb][3];
+                *pv = y;
             }
         }
-#pragma unroll
-        for (int u = 1; u < U; ++u) a[0] += a[u];
-        sSuf[part * D + ch] = a[0];
-    }
-    lds_barrier();
-    if (tid < D) {
-        // reverse inclusive scan down the chunk's rows, in registers
-        float run = 0.f;
-#pragma unroll
-        for (int j = 0; j < kST / D; ++j) run += sSuf[j * D + tid];
-        float r[64];
-#pragma unroll
-        for (int t = 0; t < 64; ++t) r[t] = sS[t * FP + tid];  // rows >= nv hold 0
-#pragma unroll
-        for (int t = 63; t >= 0; --t) {
-            run += r[t];
-            sS[t * FP + tid] = run;
-        }
-    }
-    lds_barrier();
-    // sS[t][c] becomes the dk contribution of row t, channel c
-    if (GATE == 0) {
-        // four lanes per row: ds_t = (sum_c d ln g_t[c]) (1 - g_t) / d on every channel
-        const int row = tid >> 2, part = tid & 3;
-        float sk = 0.f, ss = 0.f;
-        for (int i = part; i < D; i += 4) {
-            sk += sK[row * FP + i];
-            ss += sS[row * FP + i];
-        }
-        sk += dpp<kDppXor1>(sk);
-        sk += dpp<kDppXor2>(sk);
-        ss += dpp<kDppXor1>(ss);
-        ss += dpp<kDppXor2>(ss);
-        const float ds = ss * sigmoidf_stable(-sk * (1.0f / D)) * (1.0f / D);
-        lds_barrier();
-        for (int i = part; i < D; i += 4) sS[row * FP + i] = ds;
-    } else {
-        for (int idx = tid; idx < 64 * D; idx += kST) {
-            const int t = idx / D, ch = idx % D;
-            const int lo = ch > 0 ? ch - 1 : 0, hi = ch + 3 < D ? ch + 3 : D;
-            float s = 0.f;
-            for (int j = lo; j < hi; ++j) s += sK[t * FP + j];
-            const float x = s / static_cast<float>(hi - lo);
-            sS[t * FP + ch] *= sigmoidf_stable(-x) / static_cast<float>(hi - lo);
-        }
-        lds_barrier();
-        // pool transpose: channel c'' collects channels c'' - 2 .. c'' + 1
-        for (int idx = tid; idx < 64 * D; idx += kST) {
-            const int t = idx / D, ch = idx % D;
-            float add = 0.f;
-#pragma unroll
-            for (int j = ch - 2; j <= ch + 1; ++j)
-                if (j >= 0 && j < D) add += sS[t * FP + j];
-            sK[t * FP + ch] = add;  // raw k no longer needed
-        }
-    }
-    lds_barrier();
-    const float* add = GATE == 0 ? sS : sK;
-    float* dk = p.dk + ((b * T + t0) * p.H_kv + hk) * D;
-    constexpr int PPR = D / 4;
-    for (int idx = tid; idx < nv * PPR; idx += kST) {
-        const int t = idx / PPR, c4 = (idx % PPR) * 4;
-        float4* dst = reinterpret_cast<float4*>(dk + t * kvs + c4);
-        const float4 a = *reinterpret_cast<const float4*>(add + t * FP + c4);
-        float4 o = *dst;
-        o.x += a.x;
-        o.y += a.y;
-        o.z += a.z;
-        o.w += a.w;
-        *dst = o;
     }
 }
 
@@ -1347,11 +1368,11 @@ hipError_t launch_bwd_t(const BackwardArgs& a) {
         hipLaunchKernelGGL((bwd_swa_q_kernel<D>), grid, dim3(kST), 0, st, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_swa_k_kernel<D>), grid, dim3(kST), 0, st, p);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_swa_k_kernel<D, GATE, true>), grid, dim3(kST), 0, st, p);
+    } else {
+        // no window part: only the gate's share of dk
+        hipLaunchKernelGGL((bwd_swa_k_kernel<D, GATE, false>), grid, dim3(kST), 0, st, p);
     }
-    hipLaunchKernelGGL((bwd_gate_kernel<D, GATE>), grid, dim3(kST), 0, st, p);
     return hipGetLastError();
 }
 
