@@ -1096,16 +1096,26 @@ __global__ __launch_bounds__(kST) void bwd_swa_q_kernel(BwdParams p) {
     const int ktlo = max(wi, (64 + 16 * wi - w + 1) >> 4);  // live key tiles: ktlo .. wi + 4
     const int64_t qrow = qtok < T ? qtok : T - 1;
 
-    for (int h = 0; h < p.n_rep; ++h) {
-        const int hq = hk * p.n_rep + h;
+    // this lane's query row of head hq: q and dO fragments; the next head's are
+    // loaded while the current one computes
+    M::frag qf[KS], of[KS];
+    auto load_frags = [&](int hq, M::frag* qd, M::frag* od) {
         const bf16_t* qr = p.q + (b * T + qrow) * qs + hq * D + 8 * g;
         const bf16_t* orow = p.dO + (b * T + qrow) * qs + hq * D + 8 * g;
-        M::frag qf[KS], of[KS];
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
-            qf[k] = M::load(qr + M::KSTEP * k);
-            of[k] = M::load(orow + M::KSTEP * k);
+            qd[k] = M::load(qr + M::KSTEP * k);
+            od[k] = M::load(orow + M::KSTEP * k);
         }
+    };
+    load_frags(hk * p.n_rep, qf, of);
+    for (int h = 0; h < p.n_rep; ++h) {
+        const int hq = hk * p.n_rep + h;
+        // this head's dq rows (added to below), in flight during the scores
+        float* dqrow = p.dq + (b * T + qrow) * qs + hq * D + 4 * g;
+        float4 dqv[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) dqv[cb] = *reinterpret_cast<const float4*>(dqrow + 16 * cb);
         // scores and value products on key tiles kt0 .. kt0 + 5: lane (query col, g) holds keys 16 kt + 4 g + r
         f32x4_t z[6], dp[6];
         float mx = -INFINITY;
@@ -1129,6 +1139,7 @@ __global__ __launch_bounds__(kST) void bwd_swa_q_kernel(BwdParams p) {
                 mx = fmaxf(mx, z[j][r]);
             }
         }
+        if (h + 1 < p.n_rep) load_frags(hq + 1, qf, of);  // the fragments of this head are consumed
         mx = group4_max(mx);
         float l = 0.f;
 #pragma unroll
@@ -1181,13 +1192,12 @@ __global__ __launch_bounds__(kST) void bwd_swa_q_kernel(BwdParams p) {
                 a = M::mma(kx, zl[G], a);
             }
             if (qtok < T) {
-                float4* dst = reinterpret_cast<float4*>(p.dq + (b * T + qtok) * qs + hq * D + 16 * cb + 4 * g);
-                float4 o = *dst;
+                float4 o = dqv[cb];
                 o.x += a[0] * rs;
                 o.y += a[1] * rs;
                 o.z += a[2] * rs;
                 o.w += a[3] * rs;
-                *dst = o;
+                *reinterpret_cast<float4*>(dqrow + 16 * cb) = o;
             }
         }
     }
