@@ -43,6 +43,9 @@ KERNELS = {
     "full_attn_kernel": ("liger::full_attn_kernel<128, 4>", "full_attn_8b_b1_t8192_d128",
                          ["gated_linear_recurrent_amd/csrc/full_attn.hip",
                           "gated_linear_recurrent_amd/csrc/device_common.h"]),
+    "bwd_chunk_kernel": ("liger::bwd_chunk_kernel<128, 0>", "prefill_8b_b1_t8192_d128",
+                         ["gated_linear_recurrent_amd/csrc/backward.hip",
+                          "gated_linear_recurrent_amd/csrc/device_common.h"]),
 }
 N_SIMD = 1024
 N_XCD = 8
