@@ -2,13 +2,14 @@
 float64 oracle's reverse pass, on bf16 inputs (the gradients are float32).
 
 Bar: for each of dq, dk, dv, max |gpu - ref| <= 1e-4 * max |ref| (the
-fp32 bar of the forward). Every product is taken in fp32 (raw bf16 operands
-exactly, computed operands unrounded), so the errors come from fp32
-rounding and the hardware exp2 (measured: below 1e-6, and below 1e-5 with
-extreme gate channels).
+fp32 bar of the forward). Every product is fp32-accurate (raw bf16 operands
+exactly, computed operands as hi + lo bf16 pairs with a residual below
+2^-17), so the errors come from fp32 rounding, the split residual and the
+hardware exp2 (measured: at most 1.6e-5 of max |ref|).
 
-Cases span one and many 64-token chunks, ragged tails, T = 1, windows
-1 .. 64, H_q / H_kv from 1 to 8, alpha = 0 and 1, both gates, and keys
+Cases span one and many 64-token chunks, ragged tails, T = 1 up to the
+full 8B shape (T = 8192, 32 query heads), windows 1 .. 64, H_q / H_kv
+from 1 to 8, alpha = 0 and 1, both gates, and keys
 scaled x40 so that gate channels become extreme (cumulative decay beyond
 2^96 inside a chunk: the pair-by-pair path).
 """
@@ -92,3 +93,19 @@ def test_backward_long_sequence():
     dO = grad_output(x["q"].shape, "bf16", seed=9)
     ref = oracle.prefill_backward(x["q"], x["k"], x["v"], dO, 1, 64, 0.5)
     _check(_run(x, dO, 1, 64, 0.5), ref, tag)
+
+
+@pytest.mark.timeout(600)
+def test_backward_8b_shape_full():
+    """The bench's backward workload in full: T = 8192, H_q = 32, H_kv = 8,
+    d = 128, scalar gate, window 64, alpha 0.5, dO from seed 23; every
+    element of dq, dk, dv against the float64 reverse pass (about a minute
+    of host time, 11 GB of host memory)."""
+    from synth import config_prefill_inputs
+    x = config_prefill_inputs("prefill_8b_b1_t8192_d128")
+    dO = grad_output(x["q"].shape, "bf16", seed=23)
+    say("[bwd] 8B shape: GPU")
+    got = _run(x, dO, 0, 64, 0.5)
+    say("[bwd] 8B shape: oracle")
+    ref = oracle.prefill_backward(x["q"], x["k"], x["v"], dO, 0, 64, 0.5)
+    _check(got, ref, "bwd 8B shape")
