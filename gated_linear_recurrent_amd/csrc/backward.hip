@@ -339,11 +339,35 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
     if (need_adj) {
 #pragma unroll
         for (int u = 0; u < NE; ++u) acc[u] = zero4();
+        // raw q and dO pieces (8 bf16) of a head; the next head's are loaded
+        // while the current one is contracted
+        constexpr int PPR = D / 8, PER = 64 * PPR / kBT;
+        uint4 qraw[PER], oraw[PER];
+        auto issue_head = [&](int hq) {
+            const bf16_t* qg = p.q + ((b * T + t0) * H_q + hq) * D;
+            const bf16_t* og = p.dO + ((b * T + t0) * H_q + hq) * D;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+                const int idx = tid + e * kBT, r = idx / PPR, c8 = (idx % PPR) * 8;
+                qraw[e] = r < nv ? *reinterpret_cast<const uint4*>(qg + r * qs + c8) : make_uint4(0, 0, 0, 0);
+                oraw[e] = r < nv ? *reinterpret_cast<const uint4*>(og + r * qs + c8) : make_uint4(0, 0, 0, 0);
+            }
+        };
+        issue_head(hk * p.n_rep);
         for (int h = 0; h < p.n_rep; ++h) {
             const int hq = hk * p.n_rep + h;
             lds_barrier();
-            stage_f32<D, kBT>(sQ, FP, p.q + ((b * T + t0) * H_q + hq) * D, qs, nv);
-            stage_bf16<D, 64, kBT>(sO, HP, p.dO + ((b * T + t0) * H_q + hq) * D, qs, nv);
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+                const int idx = tid + e * kBT, r = idx / PPR, c8 = (idx % PPR) * 8;
+                float f[8];
+                bf8_to_f32(qraw[e], f);
+                float4* d4 = reinterpret_cast<float4*>(sQ + r * FP + c8);
+                d4[0] = make_float4(f[0], f[1], f[2], f[3]);
+                d4[1] = make_float4(f[4], f[5], f[6], f[7]);
+                *reinterpret_cast<uint4*>(sO + r * HP + c8) = oraw[e];
+            }
+            if (h + 1 < p.n_rep) issue_head(hq + 1);
             lds_barrier();
             // Q~ = phi(q) (.) 2^(b), written as the split operand
             {
