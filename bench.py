@@ -113,6 +113,7 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-full", action="store_true", help="skip the full causal attention layer")
     ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy and GEMM peaks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-tokens", type=int, default=8192)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -427,6 +428,46 @@ def main() -> int:
         }
         log(f"[bench] decode kernel {k_ms * 1e3:.1f} us/step ({dach:.0f} GB/s); graph {graph_us:.1f} us/step; "
             f"cold {cold_us:.1f} us; wall {dwall * 1e6 / nsteps:.1f} us/step")
+
+    if not args.no_peaks:
+        # what the box reaches with plain library work, next to the datasheet peaks:
+        # a device-to-device copy of 1 GiB (read + write) and a bf16 GEMM (hipBLASLt) of 8192^3
+        n = 1 << 28
+        a = torch.empty(n, dtype=torch.float32, device=dev)
+        c = torch.empty_like(a)
+        for _ in range(3):
+            c.copy_(a)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            c.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_gbs = 2 * n * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del a, c
+        m = 8192
+        ga = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+        gb = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            gc = torch.matmul(ga, gb)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            gc = torch.matmul(ga, gb)
+        e1.record()
+        torch.cuda.synchronize()
+        gemm_tflops = 2 * m ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        del ga, gb, gc
+        result["measured_peaks"] = {"copy_gbs": copy_gbs, "bf16_gemm_tflops": gemm_tflops,
+                                    "note": "1 GiB fp32 device copy (read + write); 8192^3 bf16 torch.matmul"}
+        result["roofline"]["frac_of_measured_copy"] = result["roofline"]["achieved"] / copy_gbs
+        if "decode" in result:
+            result["decode"]["roofline"]["frac_of_measured_copy"] = result["decode"]["roofline"]["achieved"] / copy_gbs
+        if "full_attention" in result:
+            fr = result["full_attention"]["roofline"]
+            fr["frac_of_measured_gemm"] = fr["achieved"] / gemm_tflops
+        log(f"[bench] measured peaks: copy {copy_gbs:.0f} GB/s, bf16 GEMM {gemm_tflops:.0f} TFLOP/s")
 
     if args.copy_probe_mib > 0:
         # an elementwise kernel that reads and writes exactly n bytes each
