@@ -73,10 +73,6 @@ struct BwdParams {
     float alpha;
 };
 
-__device__ __forceinline__ f32x4_t mma4(float x, float y, f32x4_t acc) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, acc, 0, 0, 0);
-}
-
 __device__ __forceinline__ void bf8_to_f32(uint4 u, float* f) {
     f[0] = __uint_as_float(u.x << 16);
     f[1] = __uint_as_float(u.x & 0xffff0000u);
@@ -161,11 +157,9 @@ __device__ __forceinline__ void stage_bf16(bf16_t* dst, int pitch, const bf16_t*
 }
 
 // Softmax over the d channels of each of the 64 rows of x (fp32, in place),
-// eight lanes per row; rows >= nv become zero. With SCALE, element (t, c) is
-// then multiplied by 2^(e[t][c]) unless channel c is flagged in `keep`.
-template <int D, bool SCALE>
-__device__ __forceinline__ void row_softmax(float* x, int pitch, int nv, const float* e, const float* mref,
-                                            const uint32_t* keep) {
+// eight lanes per row; rows >= nv become zero.
+template <int D>
+__device__ __forceinline__ void row_softmax(float* x, int pitch, int nv) {
     const int row = threadIdx.x >> 3, part = threadIdx.x & 7;
     float* xr = x + row * pitch;
     float v[D / 8];
@@ -185,15 +179,7 @@ __device__ __forceinline__ void row_softmax(float* x, int pitch, int nv, const f
     s = group8_sum(s);
     const float inv = row < nv ? 1.0f / s : 0.0f;
 #pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
-        const int c = part + 8 * i;
-        float y = v[i] * inv;
-        if (SCALE) {
-            const bool ext = (keep[c >> 5] >> (c & 31)) & 1u;
-            if (!ext) y *= fast_exp2(e[row * D + c] - mref[c]);
-        }
-        xr[c] = y;
-    }
+    for (int i = 0; i < D / 8; ++i) xr[part + 8 * i] = v[i] * inv;
 }
 
 // Chunk set-up shared by the records and gradient kernels: raw k staged in
@@ -223,7 +209,7 @@ __device__ __forceinline__ void chunk_gate(float* sK, int FP, float* sBeta, floa
         }
     }
     lds_barrier();
-    row_softmax<D, false>(sK, FP, nv, nullptr, nullptr, nullptr);
+    row_softmax<D>(sK, FP, nv);
     // inclusive scan of the log2 gates over the 64 rows, per channel
     constexpr int P = kBT / D, TPP = 64 / P;
     const int c = threadIdx.x % D, pp = threadIdx.x / D;
@@ -409,12 +395,7 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- GRM gradients
-// x -> (hi, lo) bf16 at [idx] of two tiles; get_split returns hi + lo.
-__device__ __forceinline__ void put_split(bf16_t* hi, bf16_t* lo, int idx, float x) {
-    const bf16_t h = f32_to_bf16(x);
-    hi[idx] = h;
-    lo[idx] = f32_to_bf16(x - bf16_to_f32(h));
-}
+// Split values x = hi + lo kept in two bf16 tiles; get_split returns hi + lo.
 // Two adjacent elements (idx even) as one 32-bit store per tile.
 __device__ __forceinline__ void put_split2(bf16_t* hi, bf16_t* lo, int idx, float x0, float x1) {
     const uint32_t h = pack_bf16x2(x0, x1);
