@@ -51,7 +51,7 @@ def _check(got, ref, tag):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("gate", [0, 1])
 @pytest.mark.parametrize("B,T,n_rep,window", [(2, 100, 1, 64), (1, 300, 4, 64), (2, 130, 2, 7),
-                                              (1, 70, 8, 1), (1, 64, 4, 33), (1, 1, 2, 64)])
+                                              (1, 70, 8, 1), (1, 64, 4, 33), (1, 1, 2, 64), (1, 128, 3, 64)])
 def test_backward_matches_oracle(d, gate, B, T, n_rep, window):
     H_kv = 2
     tag = f"bwd d={d} gate={gate} B={B} T={T} n_rep={n_rep} w={window}"
