@@ -66,7 +66,7 @@ def _short(name: str) -> str:
 def trace(db: str, title: str, command: str) -> str:
     cur = sqlite3.connect(db).cursor()
     rows = list(cur.execute("select name,total_calls,total_duration,average,percentage from top_kernels"))
-    out = [f"# {title}\n", "Command (from the repository root on the GPU box):\n", f"```\n{command}\n```\n",
+    out = [f"# {title}\n", "Command (from the repository root, on the MI355X machine):\n", f"```\n{command}\n```\n",
            "| kernel | calls | total (us) | average (us) | % |", "|---|---|---|---|---|"]
     for n, c, t, a, p in rows:  # the view reports microseconds
         out.append(f"| `{_short(n)}` | {c} | {t:.1f} | {a:.2f} | {p:.1f} |")
