@@ -109,3 +109,15 @@ def test_backward_8b_shape_full():
     say("[bwd] 8B shape: oracle")
     ref = oracle.prefill_backward(x["q"], x["k"], x["v"], dO, 0, 64, 0.5)
     _check(got, ref, "bwd 8B shape")
+
+
+def test_backward_outlier_keys():
+    """The long-context recipe's key outliers (1% of key rows x8) with the
+    vector gate at T = 1024, H_q = 8, H_kv = 2, d = 128."""
+    tag = "bwd outlier keys"
+    say(f"[bwd] {tag}")
+    x = prefill_inputs(B=1, T=1024, H_q=8, H_kv=2, d=128, dtype="bf16", seed=55, outlier_frac=0.01,
+                       outlier_scale=8.0)
+    dO = grad_output(x["q"].shape, "bf16", seed=56)
+    ref = oracle.prefill_backward(x["q"], x["k"], x["v"], dO, 1, 64, 0.5)
+    _check(_run(x, dO, 1, 64, 0.5), ref, tag)
