@@ -29,16 +29,14 @@ __device__ __forceinline__ float dec_wave_max(float v) {
     v = fmaxf(v, dpp<kDppXor2>(v));
     v = fmaxf(v, dpp<kDppHalfMirror>(v));
     v = fmaxf(v, dpp<kDppMirror>(v));
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    return fmaxf(v, __shfl_xor(v, 32, 64));
+    return xor32_max(xor16_max(v));
 }
 __device__ __forceinline__ float dec_wave_sum(float v) {
     v += dpp<kDppXor1>(v);
     v += dpp<kDppXor2>(v);
     v += dpp<kDppHalfMirror>(v);
     v += dpp<kDppMirror>(v);
-    v += __shfl_xor(v, 16, 64);
-    return v + __shfl_xor(v, 32, 64);
+    return xor32_sum(xor16_sum(v));
 }
 
 // Per 4-lane block of a wave (lanes 4b .. 4b+3), register i of lane 4b+j
@@ -217,7 +215,7 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
             }
             mx = group8_max(mx);
             mx = fmaxf(mx, dpp<kDppMirror>(mx));
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = xor16_max(mx);
             float se = 0.f;
 #pragma unroll
             for (int e = 0; e < EPH; ++e) {
@@ -226,7 +224,7 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
             }
             se = group8_sum(se);
             se += dpp<kDppMirror>(se);
-            se += __shfl_xor(se, 16, 64);
+            se = xor16_sum(se);
             const float inv = fast_rcp(se) * (row == 0 ? 1.0f : alpha);
 #pragma unroll
             for (int e = 0; e < EPH; ++e) {
@@ -293,7 +291,7 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
                 dot[j] += dpp<kDppXor2>(dot[j]);
                 dot[j] += dpp<kDppHalfMirror>(dot[j]);
                 if constexpr (LPR >= 16) dot[j] += dpp<kDppMirror>(dot[j]);
-                if constexpr (LPR >= 32) dot[j] += __shfl_xor(dot[j], 16, 64);
+                if constexpr (LPR >= 32) dot[j] = xor16_sum(dot[j]);
                 dot[j] = valid ? dot[j] * scale : -INFINITY;
             }
             if (kl == 0) {

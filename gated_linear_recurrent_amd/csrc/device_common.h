@@ -113,15 +113,34 @@ __device__ __forceinline__ float wave_sum(float v) {
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
     return v;
 }
+// Cross-row lane exchanges in the VALU (gfx950 v_permlane16_swap /
+// v_permlane32_swap, no LDS round trip). Swapping a value with itself gives
+// each lane the pair {own, lane ^ 16} (or lane ^ 32) in an order that depends
+// on the lane; max and sum are commutative, so every lane of a pair ends
+// with the same bits. The pair's elements are copied out as scalars before
+// they are reinterpreted: a bit cast applied to an element of the returned
+// vector reads element 0 whatever the index.
+__device__ __forceinline__ void swap16(float v, float& a, float& b) {
+    const unsigned u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    a = __uint_as_float(r0);
+    b = __uint_as_float(r1);
+}
+__device__ __forceinline__ void swap32(float v, float& a, float& b) {
+    const unsigned u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    a = __uint_as_float(r0);
+    b = __uint_as_float(r1);
+}
+__device__ __forceinline__ float xor16_max(float v) { float a, b; swap16(v, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float xor32_max(float v) { float a, b; swap32(v, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float xor16_sum(float v) { float a, b; swap16(v, a, b); return a + b; }
+__device__ __forceinline__ float xor32_sum(float v) { float a, b; swap32(v, a, b); return a + b; }
 // Reduction over the four lane groups (L >> 4) that share a fragment row.
-__device__ __forceinline__ float group4_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    return fmaxf(v, __shfl_xor(v, 32, 64));
-}
-__device__ __forceinline__ float group4_sum(float v) {
-    v += __shfl_xor(v, 16, 64);
-    return v + __shfl_xor(v, 32, 64);
-}
+__device__ __forceinline__ float group4_max(float v) { return xor32_max(xor16_max(v)); }
+__device__ __forceinline__ float group4_sum(float v) { return xor32_sum(xor16_sum(v)); }
 
 // Workgroup barrier that orders LDS accesses only: the fences are restricted
 // to the local address space, so the barrier waits for outstanding LDS
