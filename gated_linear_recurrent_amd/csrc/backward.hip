@@ -229,6 +229,52 @@ __device__ __forceinline__ void chunk_gate(float* sK, int FP, float* sBeta, floa
     lds_barrier();
 }
 
+// Split values x = hi + lo kept in two bf16 tiles (|x - hi - lo| <= 2^-17 |x|).
+// Two adjacent elements (idx even) as one 32-bit store per tile.
+__device__ __forceinline__ void put_split2(bf16_t* hi, bf16_t* lo, int idx, float x0, float x1) {
+    const uint32_t h = pack_bf16x2(x0, x1);
+    *reinterpret_cast<uint32_t*>(hi + idx) = h;
+    *reinterpret_cast<uint32_t*>(lo + idx) =
+        pack_bf16x2(x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xffff0000u));
+}
+
+// Scalar-gate form of chunk_gate: the gate is one value per token, so the
+// cumulative log2 gate is kept per token (sB[64]) instead of broadcast over
+// the channels. The prefix is summed in the same order as chunk_gate's (runs
+// of 64 / (kBT / D) tokens, then the earlier runs' totals), so both give the
+// same bits. scratch needs kBT / D floats. Ends synchronised.
+template <int D>
+__device__ __forceinline__ void chunk_gate_scalar(float* sK, int FP, float* sB, float* scratch, int nv) {
+    const int row = threadIdx.x >> 3, part = threadIdx.x & 7;
+    const float* kr = sK + row * FP;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) s += kr[part + 8 * i];
+    s = group8_sum(s);
+    if (part == 0) sB[row] = row < nv ? log2_sigmoid(s * (1.0f / D)) : 0.f;
+    lds_barrier();
+    row_softmax<D>(sK, FP, nv);
+    constexpr int P = kBT / D, TPP = 64 / P;
+    if (threadIdx.x < P) {
+        const int pp = threadIdx.x;
+        float run = 0.f;
+#pragma unroll
+        for (int u = 0; u < TPP; ++u) {
+            run += sB[pp * TPP + u];
+            sB[pp * TPP + u] = run;
+        }
+        scratch[pp] = run;
+    }
+    lds_barrier();
+    if (threadIdx.x < 64) {
+        const int pp = threadIdx.x / TPP;
+        float off = 0.f;
+        for (int j = 0; j < pp; ++j) off += scratch[j];
+        sB[threadIdx.x] += off;
+    }
+    lds_barrier();
+}
+
 // ---------------------------------------------------------------- records
 // Forward record of chunk c (c < n-1): L = sum_t (phik_t (.) 2^(Delta-b_t))^T v_t, lg = Delta.
 // Adjoint record of chunk c (c > 0), stored at index n-1-c:
@@ -239,14 +285,16 @@ __device__ __forceinline__ void chunk_gate(float* sK, int FP, float* sBeta, floa
 template <int D, int GATE>
 __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
     typedef Mfma<bf16_t> M;
-    constexpr int FPK = D + 16, FP = D + 4, HP = D + 16;
+    constexpr int FPK = D + 16, HP = D + 16;
     constexpr int NCB = D / 16;
     constexpr int WPC = 8 / NCB;   // waves per channel block
     constexpr int NE = NCB / WPC;  // column tiles per wave
+    // Scalar gate: the cumulative gate is per token, and the workgroup fits
+    // twice in a compute unit's LDS.
+    constexpr bool SCAL = GATE == 0;
     // raw k -> phi(k) (fp32, pitch FPK); later the hi and lo bf16 tiles [64][HP] in the same bytes
     __shared__ __align__(16) float sK[64 * FPK];
-    __shared__ __align__(16) float sQ[64 * FP];
-    __shared__ __align__(16) float sBeta[64 * D];
+    __shared__ __align__(16) float sBeta[SCAL ? 64 : 64 * D];
     __shared__ __align__(16) bf16_t sV[64 * HP];
     __shared__ __align__(16) bf16_t sO[64 * HP];
     __shared__ float sScr[kBT];
@@ -269,8 +317,11 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
     stage_f32<D, kBT>(sK, FPK, p.k + ((b * T + t0) * p.H_kv + hk) * D, kvs, nv);
     stage_bf16<D, 64, kBT>(sV, HP, p.v + ((b * T + t0) * p.H_kv + hk) * D, kvs, nv);
     lds_barrier();
-    chunk_gate<D, GATE>(sK, FPK, sBeta, sScr, nv);
-    if (tid < D) sDelta[tid] = sBeta[63 * D + tid];
+    if constexpr (SCAL) chunk_gate_scalar<D>(sK, FPK, sBeta, sScr, nv);
+    else chunk_gate<D, GATE>(sK, FPK, sBeta, sScr, nv);
+    // cumulative log2 gate of token t on channel ch
+    auto beta = [&](int t, int ch) -> float { return SCAL ? sBeta[t] : sBeta[t * D + ch]; };
+    if (tid < D) sDelta[tid] = beta(63, tid);
     lds_barrier();
     const size_t rec = size_t(D) * D + D;
 
@@ -303,7 +354,7 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
             const int idx = tid + e * kBT, t = idx / D, ch = idx % D;
-            kt[e] = sK[t * FPK + ch] * fast_exp2(sDelta[ch] - sBeta[t * D + ch]);
+            kt[e] = sK[t * FPK + ch] * fast_exp2(sDelta[ch] - beta(t, ch));
         }
         lds_barrier();
 #pragma unroll
@@ -326,8 +377,11 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
 #pragma unroll
         for (int u = 0; u < NE; ++u) acc[u] = zero4();
         // raw q and dO pieces (8 bf16) of a head; the next head's are loaded
-        // while the current one is contracted
+        // while the current one is contracted. PPR consecutive lanes hold
+        // one token row, so the row softmax of q reduces over those lanes
+        // and Q~ = phi(q) (.) 2^(b) goes from registers to the split tiles.
         constexpr int PPR = D / 8, PER = 64 * PPR / kBT;
+        static_assert(PPR == 8 || PPR == 16, "a token row spans 8 or 16 lanes");
         uint4 qraw[PER], oraw[PER];
         auto issue_head = [&](int hq) {
             const bf16_t* qg = p.q + ((b * T + t0) * H_q + hq) * D;
@@ -342,45 +396,31 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
         issue_head(hk * p.n_rep);
         for (int h = 0; h < p.n_rep; ++h) {
             const int hq = hk * p.n_rep + h;
-            lds_barrier();
+            lds_barrier();  // the previous head's contraction has read the tiles
 #pragma unroll
             for (int e = 0; e < PER; ++e) {
                 const int idx = tid + e * kBT, r = idx / PPR, c8 = (idx % PPR) * 8;
                 float f[8];
                 bf8_to_f32(qraw[e], f);
-                float4* d4 = reinterpret_cast<float4*>(sQ + r * FP + c8);
-                d4[0] = make_float4(f[0], f[1], f[2], f[3]);
-                d4[1] = make_float4(f[4], f[5], f[6], f[7]);
+                float mx = f[0];
+#pragma unroll
+                for (int i = 1; i < 8; ++i) mx = fmaxf(mx, f[i]);
+                mx = PPR == 16 ? group16_max(mx) : group8_max(mx);
+                float sum = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    f[i] = fast_exp2((f[i] - mx) * kLog2e);
+                    sum += f[i];
+                }
+                sum = PPR == 16 ? group16_sum(sum) : group8_sum(sum);
+                const float inv = r < nv ? 1.0f / sum : 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; i += 2)
+                    put_split2(sXh, sXl, r * HP + c8 + i, f[i] * inv * fast_exp2(beta(r, c8 + i)),
+                               f[i + 1] * inv * fast_exp2(beta(r, c8 + i + 1)));
                 *reinterpret_cast<uint4*>(sO + r * HP + c8) = oraw[e];
             }
             if (h + 1 < p.n_rep) issue_head(hq + 1);
-            lds_barrier();
-            // Q~ = phi(q) (.) 2^(b), written as the split operand
-            {
-                const int row = tid >> 3, part = tid & 7;
-                const float* xr = sQ + row * FP;
-                float v[D / 8];
-                float mx = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < D / 8; ++i) {
-                    v[i] = xr[part + 8 * i];
-                    mx = fmaxf(mx, v[i]);
-                }
-                mx = group8_max(mx);
-                float s = 0.f;
-#pragma unroll
-                for (int i = 0; i < D / 8; ++i) {
-                    v[i] = fast_exp2((v[i] - mx) * kLog2e);
-                    s += v[i];
-                }
-                s = group8_sum(s);
-                const float inv = row < nv ? 1.0f / s : 0.0f;
-#pragma unroll
-                for (int i = 0; i < D / 8; ++i) {
-                    const int cc = part + 8 * i;
-                    put_split(row, cc, v[i] * inv * fast_exp2(sBeta[row * D + cc]));
-                }
-            }
             lds_barrier();
             contract(sO, acc);
         }
@@ -395,14 +435,6 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- GRM gradients
-// Split values x = hi + lo kept in two bf16 tiles; get_split returns hi + lo.
-// Two adjacent elements (idx even) as one 32-bit store per tile.
-__device__ __forceinline__ void put_split2(bf16_t* hi, bf16_t* lo, int idx, float x0, float x1) {
-    const uint32_t h = pack_bf16x2(x0, x1);
-    *reinterpret_cast<uint32_t*>(hi + idx) = h;
-    *reinterpret_cast<uint32_t*>(lo + idx) =
-        pack_bf16x2(x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xffff0000u));
-}
 // Sum of N (4 or 8) partials stored contiguously (16-byte aligned).
 template <int N>
 __device__ __forceinline__ float row_total(const float* p) {
@@ -414,6 +446,7 @@ __device__ __forceinline__ float row_total(const float* p) {
     }
     return s;
 }
+// A split value read back: hi + lo.
 __device__ __forceinline__ float get_split(const bf16_t* hi, const bf16_t* lo, int idx) {
     return bf16_to_f32(hi[idx]) + bf16_to_f32(lo[idx]);
 }
