@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 
 #include "kernels.h"
@@ -51,6 +52,42 @@ liger_status check_common(int32_t gate_mode, float alpha) {
 liger_status check_ptr(const void* p, const char* name) {
     if (!p) return fail(LIGER_E_INVALID_ARG, std::string(name) + " is NULL");
     if (!aligned16(p)) return fail(LIGER_E_INVALID_ARG, std::string(name) + " is not 16-byte aligned");
+    return LIGER_OK;
+}
+
+// Bytes of a [B, T, heads, d] tensor of `elem`-byte elements, saturating at
+// SIZE_MAX (a size that large cannot be a real buffer).
+size_t tensor_bytes(int64_t B, int64_t T, int64_t heads, int64_t d, size_t elem) {
+    size_t n = elem;
+    for (const int64_t f : {B, T, heads, d}) {
+        if (__builtin_mul_overflow(n, static_cast<size_t>(f), &n)) return SIZE_MAX;
+    }
+    return n;
+}
+
+// True when the byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y ? y - x < na : x - y < nb;
+}
+
+struct Span {
+    const void* p;
+    size_t n;
+    const char* name;
+};
+
+// Every output span must be disjoint from every input span and from the
+// other outputs.
+liger_status check_disjoint(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+    for (auto o = outs.begin(); o != outs.end(); ++o) {
+        for (const Span& i : ins)
+            if (overlaps(o->p, o->n, i.p, i.n))
+                return fail(LIGER_E_INVALID_ARG, std::string(o->name) + " must not overlap " + i.name);
+        for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlaps(o->p, o->n, o2->p, o2->n))
+                return fail(LIGER_E_INVALID_ARG, std::string(o->name) + " must not overlap " + o2->name);
+    }
     return LIGER_OK;
 }
 
@@ -112,7 +149,13 @@ liger_status prefill_impl(const void* q, const void* k, const void* v, const lig
     LIGER_TRY(check_ptr(v, "v"));
     LIGER_TRY(check_ptr(o, "o"));
     LIGER_TRY(check_ptr(S_T, "S_T"));
-    if (o == q || o == k || o == v) return fail(LIGER_E_INVALID_ARG, "o must not alias q, k or v");
+    {
+        const size_t es = shape->dtype == LIGER_BF16 ? 2 : 4;
+        const size_t qb = tensor_bytes(shape->B, shape->T, shape->H_q, shape->d, es);
+        const size_t kb = tensor_bytes(shape->B, shape->T, shape->H_kv, shape->d, es);
+        const size_t sb = tensor_bytes(shape->B, shape->H_kv, shape->d, shape->d, 4);
+        LIGER_TRY(check_disjoint({{o, qb, "o"}, {S_T, sb, "S_T"}}, {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}}));
+    }
     const liger::PrefillPlan pl = liger::make_prefill_plan(shape->B, shape->T, shape->H_kv, shape->d,
                                                            shape->dtype == LIGER_BF16, chunks_per_segment);
     if (pl.workspace_bytes > 0) {
@@ -210,11 +253,14 @@ liger_status continue_impl(const void* q, const void* k, const void* v, const fl
     LIGER_TRY(check_ptr(kv_ring->v, "kv_ring->v"));
     if (!kv_ring->pos) return fail(LIGER_E_INVALID_ARG, "kv_ring->pos is NULL");
     if (!kv_ring->sync) return fail(LIGER_E_INVALID_ARG, "kv_ring->sync is NULL");
-    if (o == q || o == k || o == v) return fail(LIGER_E_INVALID_ARG, "o must not alias q, k or v");
-    const size_t sbytes = size_t(shape->B) * shape->H_kv * shape->d * shape->d * sizeof(float);
-    const char* s0c = reinterpret_cast<const char*>(S0);
-    const char* stc = reinterpret_cast<const char*>(S_T);
-    if (s0c < stc + sbytes && stc < s0c + sbytes) return fail(LIGER_E_INVALID_ARG, "S_T must not overlap S0");
+    {
+        const size_t es = shape->dtype == LIGER_BF16 ? 2 : 4;
+        const size_t qb = tensor_bytes(shape->B, shape->T, shape->H_q, shape->d, es);
+        const size_t kb = tensor_bytes(shape->B, shape->T, shape->H_kv, shape->d, es);
+        const size_t sb = tensor_bytes(shape->B, shape->H_kv, shape->d, shape->d, 4);
+        LIGER_TRY(check_disjoint({{o, qb, "o"}, {S_T, sb, "S_T"}},
+                                 {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {S0, sb, "S0"}}));
+    }
     const liger::PrefillPlan pl = liger::make_prefill_plan(shape->B, shape->T, shape->H_kv, shape->d,
                                                            shape->dtype == LIGER_BF16, 0);
     if (pl.workspace_bytes > 0) {
@@ -315,7 +361,12 @@ liger_status decode_impl(const void* q, const void* k, const void* v, float* S, 
     LIGER_TRY(check_ptr(kv_ring->v, "kv_ring->v"));
     if (!kv_ring->pos) return fail(LIGER_E_INVALID_ARG, "kv_ring->pos is NULL");
     if (!kv_ring->sync) return fail(LIGER_E_INVALID_ARG, "kv_ring->sync is NULL");
-    if (o == q || o == k || o == v) return fail(LIGER_E_INVALID_ARG, "o must not alias q, k or v");
+    {
+        const size_t es = shape->dtype == LIGER_BF16 ? 2 : 4;
+        const size_t qb = tensor_bytes(shape->B, 1, shape->H_q, shape->d, es);
+        const size_t kb = tensor_bytes(shape->B, 1, shape->H_kv, shape->d, es);
+        LIGER_TRY(check_disjoint({{o, qb, "o"}}, {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}}));
+    }
     liger::DecodeArgs a;
     a.q = q;
     a.k = k;
@@ -372,7 +423,11 @@ liger_status liger_attn_full_causal(const void* q, const void* k, const void* v,
     LIGER_TRY(check_ptr(k, "k"));
     LIGER_TRY(check_ptr(v, "v"));
     LIGER_TRY(check_ptr(o, "o"));
-    if (o == q || o == k || o == v) return fail(LIGER_E_INVALID_ARG, "o must not alias q, k or v");
+    {
+        const size_t qb = tensor_bytes(shape->B, shape->T, shape->H_q, shape->d, 2);
+        const size_t kb = tensor_bytes(shape->B, shape->T, shape->H_kv, shape->d, 2);
+        LIGER_TRY(check_disjoint({{o, qb, "o"}}, {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}}));
+    }
     liger::FullAttnArgs a;
     a.q = q;
     a.k = k;
@@ -408,12 +463,14 @@ liger_status liger_attn_prefill_backward(const void* q, const void* k, const voi
     LIGER_TRY(check_ptr(dq, "dq"));
     LIGER_TRY(check_ptr(dk, "dk"));
     LIGER_TRY(check_ptr(dv, "dv"));
-    const void* outs[3] = {dq, dk, dv};
-    const void* ins[4] = {q, k, v, dO};
-    for (const void* o : outs)
-        for (const void* i : ins)
-            if (o == i) return fail(LIGER_E_INVALID_ARG, "dq, dk and dv must not alias the inputs");
-    if (dq == dk || dq == dv || dk == dv) return fail(LIGER_E_INVALID_ARG, "dq, dk and dv must be distinct");
+    {
+        const size_t qb = tensor_bytes(shape->B, shape->T, shape->H_q, shape->d, 2);
+        const size_t kb = tensor_bytes(shape->B, shape->T, shape->H_kv, shape->d, 2);
+        const size_t gqb = tensor_bytes(shape->B, shape->T, shape->H_q, shape->d, 4);
+        const size_t gkb = tensor_bytes(shape->B, shape->T, shape->H_kv, shape->d, 4);
+        LIGER_TRY(check_disjoint({{dq, gqb, "dq"}, {dk, gkb, "dk"}, {dv, gkb, "dv"}},
+                                 {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {dO, qb, "dO"}}));
+    }
     const size_t need = liger::backward_workspace_bytes(shape->B, shape->T, shape->H_kv, shape->H_q, shape->d);
     if (workspace_bytes < need) return fail(LIGER_E_WORKSPACE, "workspace smaller than liger_attn_prefill_backward_workspace_size");
     if (need > 0) LIGER_TRY(check_ptr(workspace, "workspace"));

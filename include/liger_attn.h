@@ -42,7 +42,9 @@
  *     caller has synchronised with the stream.
  *   - The caller owns every buffer. The library keeps no pointer after
  *     returning, allocates nothing and frees nothing. Device pointers must be
- *     16-byte aligned. Outputs must not alias inputs.
+ *     16-byte aligned. Output buffers must not overlap the input buffers
+ *     or each other (their byte ranges, from the shape, are checked:
+ *     LIGER_E_INVALID_ARG); inputs may overlap one another.
  *   - No global mutable state: calls on different streams may run
  *     concurrently as long as their buffers do not overlap.
  *   - Floating-point inputs are not sanitised: NaN or Inf propagate.
@@ -224,7 +226,7 @@ liger_status liger_kv_ring_fill(const void* k, const void* v,
  * for every query head h, which reads key/value head h / (H_q / H_kv).
  * q, o [B, T, H_q, d]; k, v [B, T, H_kv, d]; contiguous, device memory,
  * 16-byte aligned, bf16 only (fp32 is LIGER_E_UNSUPPORTED), d in {64, 128},
- * H_q / H_kv in {1, 2, 4, 8}. o must not alias the inputs. No workspace;
+ * H_q / H_kv in {1, 2, 4, 8}. o must not overlap the inputs. No workspace;
  * enqueued on `stream` (NULL: the default stream), nothing is synchronised.
  */
 liger_status liger_attn_full_causal(const void* q, const void* k, const void* v,
@@ -268,7 +270,7 @@ liger_status liger_attn_decode_step_sinks(const void* q, const void* k, const vo
  *   q, dO [B, T, H_q, d]; k, v [B, T, H_kv, d]: bf16 only (fp32 is
  *   LIGER_E_UNSUPPORTED), d in {64, 128}, any H_q / H_kv.
  *   dq [B, T, H_q, d], dk, dv [B, T, H_kv, d]: float32, written (not
- *   accumulated); distinct and not aliasing any input.
+ *   accumulated); pairwise disjoint and not overlapping any input.
  *   gate_mode, window (1..64) and alpha as given to the prefill.
  *   workspace: at least liger_attn_prefill_backward_workspace_size bytes of
  *   device memory (chunk-start states, chunk adjoints, per-row gate

@@ -16,6 +16,7 @@ import gated_linear_recurrent_amd as gla
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FAKE = 0x10000  # aligned, never dereferenced
+G = 1 << 32     # spacing of fake buffers whose byte ranges must not overlap
 
 
 @pytest.fixture(scope="module")
@@ -51,8 +52,8 @@ def _shape(**kw):
     return gla.liger_shape(**base)
 
 
-def _prefill(lib, shape, gate=1, window=64, alpha=0.5, q=FAKE, k=FAKE, v=FAKE, o=FAKE + 4096,
-             S=FAKE + 8192, ws=None, ws_bytes=0, cps=0):
+def _prefill(lib, shape, gate=1, window=64, alpha=0.5, q=FAKE, k=FAKE, v=FAKE, o=FAKE + G,
+             S=FAKE + 2 * G, ws=None, ws_bytes=0, cps=0):
     return lib.liger_attn_prefill_ex(q, k, v, gate, window, alpha, ctypes.byref(shape), o, S, ws,
                                      ws_bytes, cps, None)
 
@@ -82,6 +83,9 @@ def test_prefill_rejects_bad_shapes(lib, kw, code):
     (dict(q=None), gla.LIGER_E_INVALID_ARG),
     (dict(k=FAKE + 8), gla.LIGER_E_INVALID_ARG),
     (dict(o=FAKE), gla.LIGER_E_INVALID_ARG),      # aliases q
+    (dict(o=FAKE + 4096), gla.LIGER_E_INVALID_ARG),  # starts inside q
+    (dict(S=FAKE + G + 4096), gla.LIGER_E_INVALID_ARG),  # S_T starts inside o
+    (dict(S=FAKE + 256), gla.LIGER_E_INVALID_ARG),  # S_T starts inside q
     (dict(S=None), gla.LIGER_E_INVALID_ARG),
     (dict(cps=-1), gla.LIGER_E_INVALID_ARG),
 ])
@@ -96,6 +100,15 @@ def test_prefill_workspace_checks(lib):
     assert _prefill(lib, shp, ws=None) == gla.LIGER_E_WORKSPACE
     assert _prefill(lib, shp, ws=FAKE + 1 << 20, ws_bytes=need - 1) == gla.LIGER_E_WORKSPACE
     assert _prefill(lib, shp, ws=(FAKE + 1 << 20) + 4, ws_bytes=need) == gla.LIGER_E_INVALID_ARG
+
+
+def test_adjacent_buffers_are_accepted(lib):
+    """Byte ranges that touch without sharing a byte pass the overlap checks
+    (the call then stops at the missing workspace)."""
+    shp = _shape(T=64)
+    qbytes = 64 * 4 * 128 * 2
+    assert _prefill(lib, shp, o=FAKE + qbytes, S=FAKE + 2 * qbytes) == gla.LIGER_E_WORKSPACE
+    assert _prefill(lib, shp, o=FAKE + qbytes - 16, S=FAKE + 2 * qbytes) == gla.LIGER_E_INVALID_ARG
 
 
 def test_workspace_size_formula(lib):
@@ -143,9 +156,9 @@ def test_decode_rejects_null_ring_and_alias(lib):
     assert _decode(lib, _shape(), _ring(), gate=-1) == gla.LIGER_E_INVALID_ARG
 
 
-def _continue(lib, shape, ring, S0=FAKE + 131072, S_T=FAKE + 196608, o=FAKE + 4096, gate=1, alpha=0.5,
+def _continue(lib, shape, ring, S0=FAKE + 3 * G, S_T=FAKE + 4 * G, o=FAKE + 5 * G, gate=1, alpha=0.5,
               ws=FAKE << 8, ws_bytes=1 << 40):
-    return lib.liger_attn_prefill_continue(FAKE, FAKE + 65536, FAKE + 98304, S0,
+    return lib.liger_attn_prefill_continue(FAKE, FAKE + G, FAKE + 2 * G, S0,
                                            ctypes.byref(ring) if ring is not None else None, gate, alpha,
                                            ctypes.byref(shape), o, S_T, ws, ws_bytes, None)
 
@@ -156,8 +169,10 @@ def _continue(lib, shape, ring, S0=FAKE + 131072, S_T=FAKE + 196608, o=FAKE + 40
     (dict(), dict(window=65), dict(), gla.LIGER_E_INVALID_ARG),
     (dict(), dict(pos=None), dict(), gla.LIGER_E_INVALID_ARG),
     (dict(), dict(sync=None), dict(), gla.LIGER_E_INVALID_ARG),
-    (dict(), dict(), dict(S_T=FAKE + 131072 + 16), gla.LIGER_E_INVALID_ARG),   # S_T overlaps S0
+    (dict(), dict(), dict(S_T=FAKE + 3 * G + 16), gla.LIGER_E_INVALID_ARG),    # S_T overlaps S0
     (dict(), dict(), dict(o=FAKE), gla.LIGER_E_INVALID_ARG),                   # o aliases q
+    (dict(), dict(), dict(o=FAKE + 2 * G + 64), gla.LIGER_E_INVALID_ARG),      # o starts inside v
+    (dict(), dict(), dict(S_T=FAKE + 5 * G + 512), gla.LIGER_E_INVALID_ARG),   # S_T starts inside o
     (dict(), dict(), dict(ws=None), gla.LIGER_E_WORKSPACE),
     (dict(dtype=gla.LIGER_F32, d=128), dict(), dict(), gla.LIGER_E_UNSUPPORTED),
     (dict(T=0), dict(), dict(), gla.LIGER_E_INVALID_ARG),
@@ -212,9 +227,11 @@ def test_binding_refuses_host_tensors():
     ({}, dict(q=None), gla.LIGER_E_INVALID_ARG),
     ({}, dict(v=FAKE + 2), gla.LIGER_E_INVALID_ARG),
     ({}, dict(o=FAKE), gla.LIGER_E_INVALID_ARG),
+    ({}, dict(o=FAKE + G + 1024), gla.LIGER_E_INVALID_ARG),  # starts inside k
+    ({}, dict(o=FAKE - 1024), gla.LIGER_E_INVALID_ARG),      # ends inside q
 ])
 def test_full_causal_rejects_bad_arguments(lib, kw, ptrs, code):
-    p = dict(q=FAKE, k=FAKE + 4096, v=FAKE + 8192, o=FAKE + 12288)
+    p = dict(q=FAKE, k=FAKE + G, v=FAKE + 2 * G, o=FAKE + 3 * G)
     p.update(ptrs)
     st = lib.liger_attn_full_causal(p["q"], p["k"], p["v"], ctypes.byref(_shape(**kw)), p["o"], None)
     assert st == code, gla.liger_last_error()
@@ -258,13 +275,15 @@ def test_sinks_null_struct_rejected(lib):
     ({}, {}, dict(gate=2), gla.LIGER_E_INVALID_ARG),
     ({}, dict(dO=None), {}, gla.LIGER_E_INVALID_ARG),
     ({}, dict(dq=FAKE), {}, gla.LIGER_E_INVALID_ARG),
-    ({}, dict(dv=FAKE + 0x4000), {}, gla.LIGER_E_INVALID_ARG),
-    ({}, dict(dk=FAKE + 0x5008), {}, gla.LIGER_E_INVALID_ARG),
+    ({}, dict(dq=FAKE + 4096), {}, gla.LIGER_E_INVALID_ARG),       # starts inside q
+    ({}, dict(dv=FAKE + 4 * G), {}, gla.LIGER_E_INVALID_ARG),      # same as dq
+    ({}, dict(dk=FAKE + 4 * G + 2048), {}, gla.LIGER_E_INVALID_ARG),  # starts inside dq
+    ({}, dict(dk=FAKE + 5 * G + 8), {}, gla.LIGER_E_INVALID_ARG),  # misaligned
     ({}, {}, dict(ws_bytes=16), gla.LIGER_E_WORKSPACE),
 ])
 def test_backward_rejects_bad_arguments(lib, kw, ptrs, extra, code):
-    p = dict(q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, dO=FAKE + 0x3000, dq=FAKE + 0x4000, dk=FAKE + 0x5000,
-             dv=FAKE + 0x6000)
+    p = dict(q=FAKE, k=FAKE + G, v=FAKE + 2 * G, dO=FAKE + 3 * G, dq=FAKE + 4 * G, dk=FAKE + 5 * G,
+             dv=FAKE + 6 * G)
     p.update(ptrs)
     e = dict(gate=1, window=64, alpha=0.5, ws_bytes=1 << 40)
     e.update(extra)
