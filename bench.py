@@ -89,19 +89,25 @@ def decode_algorithmic(cfg: dict) -> float:
     return float(N * per_seq)
 
 
-def cpu_baseline(cfg: dict, x: dict, tokens: int) -> dict:
-    """The float64 oracle as it stands, on the host, BLAS limited to one thread."""
+def cpu_baseline(cfg: dict, x: dict, tokens: int, min_seconds: float = 10.0, max_runs: int = 20) -> dict:
+    """The float64 oracle as it stands, on the host, BLAS limited to one thread.
+    The sample is run repeatedly until about min_seconds of CPU work have been
+    timed; the value is the median rate over the runs."""
     import oracle
     from threadpoolctl import threadpool_limits
     gate = 0 if cfg["gate"] == "scalar" else 1
     q, k, v = (x[n][:, :tokens] for n in ("q", "k", "v"))
+    times = []
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        oracle.prefill(q, k, v, gate, cfg["window"], cfg["alpha"])
-        dt = time.perf_counter() - t0
+        while sum(times) < min_seconds and len(times) < max_runs:
+            t0 = time.perf_counter()
+            oracle.prefill(q, k, v, gate, cfg["window"], cfg["alpha"])
+            times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
     return {"value": cfg["B"] * tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{PREFILL_WORKLOAD}: first {tokens} of {cfg['T']} tokens (all heads), float64 "
-                      f"token loop, BLAS limited to 1 thread; {dt:.1f} s"}
+                      f"token loop, BLAS limited to 1 thread; {len(times)} runs, {sum(times):.1f} s in all, "
+                      f"median {dt:.2f} s per run"}
 
 
 def main() -> int:
