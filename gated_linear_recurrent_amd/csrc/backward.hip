@@ -325,7 +325,10 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
     lds_barrier();
     const size_t rec = size_t(D) * D + D;
 
-    // acc[u] += X Y over the 64 tokens, X = hi + lo tiles (channel-indexed rows), Y token-major bf16
+    // acc[u] += (X^T Y)^T over the 64 tokens, X = hi + lo tiles (channel-indexed
+    // record rows), Y token-major bf16. The tile is held transposed: lane
+    // (col, g) holds record row 16 cb + col, columns 16 (eb0 + u) + 4 g + r,
+    // so a row's four values leave with one 16-byte store.
     auto contract = [&](const bf16_t* Y, f32x4_t* acc) {
 #pragma unroll
         for (int G = 0; G < 2; ++G) {
@@ -334,10 +337,16 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
 #pragma unroll
             for (int u = 0; u < NE; ++u) {
                 const M::frag y = load_key_frag(Y, HP, 32 * G, 16 * (eb0 + u), lane);
-                acc[u] = M::mma(xh, y, acc[u]);
-                acc[u] = M::mma(xl, y, acc[u]);
+                acc[u] = M::mma(y, xh, acc[u]);
+                acc[u] = M::mma(y, xl, acc[u]);
             }
         }
+    };
+    auto store_record = [&](float* dst, const f32x4_t* acc, float scale) {
+#pragma unroll
+        for (int u = 0; u < NE; ++u)
+            *reinterpret_cast<float4*>(dst + (16 * cb + col) * D + 16 * (eb0 + u) + 4 * g) =
+                make_float4(scale * acc[u][0], scale * acc[u][1], scale * acc[u][2], scale * acc[u][3]);
     };
     // element (t, ch) of the split operand lives at [t][ch] of the hi and lo tiles
     auto put_split = [&](int t, int ch, float x) {
@@ -367,10 +376,7 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
         for (int u = 0; u < NE; ++u) acc[u] = zero4();
         contract(sV, acc);
         float* dst = p.fwd + ((b * p.H_kv + hk) * (n - 1) + c) * rec;
-#pragma unroll
-        for (int u = 0; u < NE; ++u)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(16 * cb + 4 * g + r) * D + 16 * (eb0 + u) + col] = acc[u][r];
+        store_record(dst, acc, 1.0f);
         if (tid < D) dst[size_t(D) * D + tid] = sDelta[tid];
     }
     if (need_adj) {
@@ -425,11 +431,7 @@ __global__ __launch_bounds__(kBT) void bwd_records_kernel(BwdParams p) {
             contract(sO, acc);
         }
         float* dst = p.adj + ((b * p.H_kv + hk) * (n - 1) + (n - 1 - c)) * rec;
-#pragma unroll
-        for (int u = 0; u < NE; ++u)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dst[(16 * cb + 4 * g + r) * D + 16 * (eb0 + u) + col] = p.alpha * acc[u][r];
+        store_record(dst, acc, p.alpha);
         if (tid < D) dst[size_t(D) * D + tid] = sDelta[tid];
     }
 }
