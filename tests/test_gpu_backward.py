@@ -8,7 +8,8 @@ exactly, computed operands as hi + lo bf16 pairs with a residual below
 hardware exp2 (measured: at most 1.6e-5 of max |ref|).
 
 Cases span one and many 64-token chunks, ragged tails, T = 1 up to the
-full 8B shape (T = 8192, 32 query heads), windows 1 .. 64, H_q / H_kv
+full 8B shape (T = 8192, 32 query heads) and the full 1B shape (B = 4,
+T = 2048, d = 64, vector gate), windows 1 .. 64, H_q / H_kv
 from 1 to 8, alpha = 0 and 1, both gates, and keys
 scaled x40 so that gate channels become extreme (cumulative decay beyond
 2^96 inside a chunk: the pair-by-pair path).
@@ -109,6 +110,22 @@ def test_backward_8b_shape_full():
     say("[bwd] 8B shape: oracle")
     ref = oracle.prefill_backward(x["q"], x["k"], x["v"], dO, 0, 64, 0.5)
     _check(got, ref, "bwd 8B shape")
+
+
+@pytest.mark.timeout(600)
+def test_backward_1b_shape_full():
+    """The 1B-shaped workload in full: B = 4, T = 2048, H_q = 32, H_kv = 8,
+    d = 64, vector gate, window 64, alpha 0.5, dO from seed 29; every element
+    of dq, dk, dv against the float64 reverse pass (about 15 s of host time,
+    3.3 GB of host memory)."""
+    from synth import config_prefill_inputs
+    x = config_prefill_inputs("prefill_1b_b4_t2048_d64")
+    dO = grad_output(x["q"].shape, "bf16", seed=29)
+    say("[bwd] 1B shape: GPU")
+    got = _run(x, dO, 1, 64, 0.5)
+    say("[bwd] 1B shape: oracle")
+    ref = oracle.prefill_backward(x["q"], x["k"], x["v"], dO, 1, 64, 0.5)
+    _check(got, ref, "bwd 1B shape")
 
 
 def test_backward_outlier_keys():
