@@ -11,7 +11,7 @@ import torch
 import gated_linear_recurrent_amd as gla
 import oracle
 from liger_testutil import DEV, TORCH_DT, abs_inf, check_prefill, rel_inf, say, to_dev, to_np
-from synth import prefill_inputs, round_to_bf16
+from synth import config_prefill_inputs, prefill_inputs, round_to_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -112,3 +112,18 @@ def test_gpu_prefill_hands_over_to_decode_with_sinks():
         torch.cuda.synchronize()
         assert abs_inf(to_np(o), o_full[:, t]) <= 2e-2, i
     assert rel_inf(to_np(S), S_full) <= 1e-2
+
+
+@pytest.mark.timeout(300)
+def test_prefill_with_sinks_8b_shape_full():
+    """The 8B prefill workload (T = 8192, H_q = 32, H_kv = 8, d = 128, scalar
+    gate) with 16 sink tokens per kv head, as timed by the benchmark, in the
+    default launch plan; every output and the final state against the oracle."""
+    say("[sinks] 8B shape, 16 sinks")
+    x = config_prefill_inputs("prefill_8b_b1_t8192_d128")
+    sk, sv = _sinks(8, 16, 128, "bf16", seed=404)
+    o_ref, S_ref = oracle.prefill(x["q"], x["k"], x["v"], 0, 64, 0.5, sink_k=sk, sink_v=sv)
+    q, k, v = (to_dev(x[m], "bf16") for m in ("q", "k", "v"))
+    o, S_T = gla.liger_attn_prefill(q, k, v, 0, 64, 0.5, sinks=(to_dev(sk, "bf16"), to_dev(sv, "bf16")))
+    torch.cuda.synchronize()
+    check_prefill("bf16", to_np(o), o_ref, to_np(S_T), S_ref, tag="sinks 8B shape")
