@@ -14,7 +14,7 @@ import torch
 import gated_linear_recurrent_amd as gla
 import oracle
 from liger_testutil import DEV, TORCH_DT, check_prefill, say, to_dev, to_np
-from synth import prefill_inputs
+from synth import config_prefill_inputs, prefill_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -137,3 +137,26 @@ def test_gpu_prefill_hands_over_to_continuation(gate):
     check_prefill(dtype, to_np(o2), o_full[:, T1:], to_np(S2), S_full, tag="hand-over")
     rk, rv, pos = oracle.ring_fill(k, v, window)
     _check_ring(ring, rk, rv, pos, dtype, "hand-over")
+
+
+@pytest.mark.timeout(300)
+def test_continuation_8b_shape_full():
+    """The 8B prefill workload (T = 8192, H_q = 32, H_kv = 8, d = 128, scalar
+    gate) split at a ragged boundary: GPU prefill of the first 4000 tokens,
+    GPU ring fill, GPU continuation over the other 4192; outputs, the final
+    state and the ring against one oracle prefill of all 8192 tokens."""
+    dtype, T1 = "bf16", 4000
+    say("[continue] 8B shape, 4000 + 4192")
+    x = config_prefill_inputs("prefill_8b_b1_t8192_d128")
+    q, k, v = x["q"], x["k"], x["v"]
+    o_full, S_full = oracle.prefill(q, k, v, 0, 64, 0.5)
+    q1, k1, v1 = (to_dev(a[:, :T1], dtype) for a in (q, k, v))
+    _, S1 = gla.liger_attn_prefill(q1, k1, v1, 0, 64, 0.5)
+    ring = gla.KVRing.empty(1, 8, 64, 128, TORCH_DT[dtype], DEV)
+    gla.liger_kv_ring_fill(k1, v1, ring)
+    q2, k2, v2 = (to_dev(a[:, T1:], dtype) for a in (q, k, v))
+    o2, S2 = gla.liger_attn_prefill_continue(q2, k2, v2, S1, ring, 0, 0.5)
+    torch.cuda.synchronize()
+    check_prefill(dtype, to_np(o2), o_full[:, T1:], to_np(S2), S_full, tag="continuation 8B shape")
+    rk, rv, pos = oracle.ring_fill(k, v, 64)
+    _check_ring(ring, rk, rv, pos, dtype, "continuation 8B shape")
