@@ -92,27 +92,6 @@ __device__ __forceinline__ float group8_sum(float v) {
     return v + dpp<kDppHalfMirror>(v);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const float y = __shfl_up(v, o, 64);
-        if (lane >= o) v += y;
-    }
-    return v;
-}
-
-// Wave-wide (64 lanes) butterfly reductions.
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
 // Cross-row lane exchanges in the VALU (gfx950 v_permlane16_swap /
 // v_permlane32_swap, no LDS round trip). Swapping a value with itself gives
 // each lane the pair {own, lane ^ 16} (or lane ^ 32) in an order that depends
