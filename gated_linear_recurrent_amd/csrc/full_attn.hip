@@ -14,6 +14,8 @@
 // end). Scores are formed as S^T = K Q^T, so a lane holds four keys of one
 // query and the probabilities pack straight into the key-indexed operand of
 // O^T += V^T P (V^T read from the token-major tile with transposing loads).
+// The key loop is software-pipelined: K runs one block ahead of V, so the
+// next block's scores (MFMA) are issued beside this block's softmax (VALU).
 // Query blocks are launched heaviest (last) first.
 #include <type_traits>
 
@@ -78,26 +80,41 @@ __global__ __launch_bounds__(128 * HPW) void full_attn_kernel(FullAttnArgs p) {
         for (int k = 0; k < KS; ++k) qf[s][k] = row < T ? M::load(qr + M::KSTEP * k) : M::zero();
     }
 
+    // K/V tiles staged through registers: K runs one key block ahead of V,
+    // so the scores of block j + 1 are formed while block j's probabilities
+    // are computed (independent MFMA and VALU work in one wave). During
+    // iteration j the waves read K(j + 1) and V(j); at its end K(j + 2) and
+    // V(j + 1) are stored into the buffers last read one iteration earlier.
     uint4 kr[NPC], vr[NPC];
-    auto issue = [&](int kb) {
+    auto issue_k = [&](int kb) {
 #pragma unroll
         for (int n = 0; n < NPC; ++n) {
             const int idx = tid + n * NTH;
             const int64_t row = 64 * static_cast<int64_t>(kb) + idx / PPR;
-            const int c0 = (idx % PPR) * 8;
-            kr[n] = make_uint4(0, 0, 0, 0);
-            vr[n] = make_uint4(0, 0, 0, 0);
-            if (row < T) {
-                kr[n] = *reinterpret_cast<const uint4*>(kg + row * kv_stride + c0);
-                vr[n] = *reinterpret_cast<const uint4*>(vg + row * kv_stride + c0);
-            }
+            kr[n] = row < T ? *reinterpret_cast<const uint4*>(kg + row * kv_stride + (idx % PPR) * 8)
+                            : make_uint4(0, 0, 0, 0);
         }
     };
-    auto commit = [&](int buf) {
+    auto issue_v = [&](int kb) {
+#pragma unroll
+        for (int n = 0; n < NPC; ++n) {
+            const int idx = tid + n * NTH;
+            const int64_t row = 64 * static_cast<int64_t>(kb) + idx / PPR;
+            vr[n] = row < T ? *reinterpret_cast<const uint4*>(vg + row * kv_stride + (idx % PPR) * 8)
+                            : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto commit_k = [&](int buf) {
 #pragma unroll
         for (int n = 0; n < NPC; ++n) {
             const int idx = tid + n * NTH;
             *reinterpret_cast<uint4*>(&sK[buf][(idx / PPR) * DP + (idx % PPR) * 8]) = kr[n];
+        }
+    };
+    auto commit_v = [&](int buf) {
+#pragma unroll
+        for (int n = 0; n < NPC; ++n) {
+            const int idx = tid + n * NTH;
             *reinterpret_cast<uint4*>(&sV[buf][(idx / PPR) * VP + (idx % PPR) * 8]) = vr[n];
         }
     };
@@ -111,25 +128,19 @@ __global__ __launch_bounds__(128 * HPW) void full_attn_kernel(FullAttnArgs p) {
     float l[2] = {0.f, 0.f};              // running sum of this lane's keys
     const float c = kLog2e * rsqrtf(static_cast<float>(D));
 
-    issue(0);
-    commit(0);
-    __syncthreads();
-    // one key block; the diagonal block (the last) is compiled on its own
-    auto block = [&](int kb, auto diag_c) {
+    // ---- S^T = K Q^T on the K tile in buffer kbuf: lane (col, g) holds keys
+    // 16 kt + 4 g + r of query col; on the diagonal block a key tile past a
+    // query tile is skipped whole
+    auto scores = [&](int kbuf, auto diag_c, f32x4_t (&sc)[2][4]) {
         constexpr bool diag = decltype(diag_c)::value;
-        const int cur = kb & 1;
-        if (!diag) issue(kb + 1);
-        // ---- S^T = K Q^T: lane (col, g) holds keys 16 kt + 4 g + r of query col
-        f32x4_t sc[2][4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             sc[0][kt] = zero4();
             sc[1][kt] = zero4();
-            // on the diagonal block a key tile past a query tile is masked whole
             const bool live0 = !diag || kt <= 2 * (wave & 1);
             const bool live1 = !diag || kt <= 2 * (wave & 1) + 1;
             if (!live1) continue;
-            const bf16_t* krow = &sK[cur][(16 * kt + col) * DP + 8 * g];
+            const bf16_t* krow = &sK[kbuf][(16 * kt + col) * DP + 8 * g];
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
                 const Frag a = M::load(krow + M::KSTEP * k);
@@ -137,8 +148,10 @@ __global__ __launch_bounds__(128 * HPW) void full_attn_kernel(FullAttnArgs p) {
                 sc[1][kt] = M::mma(a, qf[1][k], sc[1][kt]);
             }
         }
-        // ---- online softmax
-        Frag pf[2][2];
+    };
+    // ---- online softmax of one block's scores -> packed probabilities
+    auto softmax = [&](f32x4_t (&sc)[2][4], auto diag_c, Frag (&pf)[2][2]) {
+        constexpr bool diag = decltype(diag_c)::value;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             float mx = -INFINITY;
@@ -183,21 +196,60 @@ __global__ __launch_bounds__(128 * HPW) void full_attn_kernel(FullAttnArgs p) {
                 pf[s][G] = M::pack(v8);
             }
         }
-        // ---- O^T += V^T P over the two 32-key groups
+    };
+    // ---- O^T += V^T P over the two 32-key groups of the V tile in buffer vbuf
+    auto values = [&](int vbuf, const Frag (&pf)[2][2]) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int G = 0; G < 2; ++G) {
-                const Frag a = load_key_frag(sV[cur], VP, 32 * G, 16 * t, lane);
+                const Frag a = load_key_frag(sV[vbuf], VP, 32 * G, 16 * t, lane);
                 acc[0][t] = M::mma(a, pf[0][G], acc[0][t]);
                 acc[1][t] = M::mma(a, pf[1][G], acc[1][t]);
             }
-        // the next tile goes to the other buffer, last read one iteration ago
-        if (!diag) commit(cur ^ 1);
-        __syncthreads();
     };
-    for (int kb = 0; kb < qb; ++kb) block(kb, std::false_type{});
-    block(qb, std::true_type{});
+
+    // prologue: K(0), V(0) and K(1) in LDS, the scores of block 0
+    issue_k(0);
+    issue_v(0);
+    commit_k(0);
+    if (qb >= 1) issue_k(1);
+    commit_v(0);
+    if (qb >= 1) commit_k(1);
+    __syncthreads();
+    f32x4_t sc[2][4];
+    if (qb == 0) scores(0, std::true_type{}, sc);
+    else scores(0, std::false_type{}, sc);
+    // iteration 0 stores K(2) over K(0): every wave has read K(0) first
+    if (qb >= 1) __syncthreads();
+    // iteration j: K(j + 2) and V(j + 1) in flight, probabilities of block j,
+    // scores of block j + 1, values of block j, then the two stores
+    auto step = [&](int j, auto next_c) {
+        constexpr int NEXT = decltype(next_c)::value;  // 2: full next block, 1: diagonal next block
+        const bool issue_next_k = NEXT == 2 && j + 2 <= qb;
+        if (issue_next_k) issue_k(j + 2);
+        issue_v(j + 1);
+        Frag pf[2][2];
+        softmax(sc, std::false_type{}, pf);
+        f32x4_t scn[2][4];
+        if constexpr (NEXT == 2) scores((j + 1) & 1, std::false_type{}, scn);
+        else scores((j + 1) & 1, std::true_type{}, scn);
+        values(j & 1, pf);
+        if (issue_next_k) commit_k(j & 1);
+        commit_v((j + 1) & 1);
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) sc[s][kt] = scn[s][kt];
+    };
+    for (int j = 0; j + 1 < qb; ++j) step(j, std::integral_constant<int, 2>{});
+    if (qb >= 1) step(qb - 1, std::integral_constant<int, 1>{});
+    {
+        Frag pf[2][2];
+        softmax(sc, std::true_type{}, pf);
+        values(qb & 1, pf);
+    }
 
     // ---- normalise and store: lane (col, g) holds channels 16 t + 4 g + r of query col
     bf16_t* o = static_cast<bf16_t*>(p.o);
