@@ -8,6 +8,7 @@ from .liger_ref import (  # noqa: F401
     VECTOR_AVGPOOL4,
     decode_step,
     full_attention,
+    full_attention_rows,
     gate,
     pool_scalar_mean,
     pool_vector_avg4,

@@ -297,6 +297,35 @@ def full_attention(q, k, v):
     return o.reshape(B, T, H_q, d)
 
 
+def full_attention_rows(q, k, v, rows):
+    """The same causal softmax attention as full_attention, for chosen query
+    positions only: o[:, i] = sum_{j <= rows[i]} softmax_j(q_t . k_j / sqrt(d)) v_j
+    with t = rows[i], each from its whole causal prefix.
+
+    q: [B, T, H_q, d]; k, v: [B, T, H_kv, d]; rows: positions in [0, T).
+    Returns [B, len(rows), H_q, d]. This is the definition restricted to the
+    listed rows (sequences too long for the whole-sequence loop).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, H_q, d = q.shape
+    H_kv = k.shape[2]
+    if H_q % H_kv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    n_rep = H_q // H_kv
+    scale = 1.0 / np.sqrt(d)
+    rows = [int(t) for t in rows]
+    if any(t < 0 or t >= T for t in rows):
+        raise ValueError("rows must lie in [0, T)")
+    o = np.empty((B, len(rows), H_kv, n_rep, d))
+    for i, t in enumerate(rows):
+        qt = q[:, t].reshape(B, H_kv, n_rep, d)
+        kw = k[:, :t + 1].transpose(0, 2, 3, 1)            # [B, H_kv, d, t+1]
+        vw = v[:, :t + 1].transpose(0, 2, 1, 3)            # [B, H_kv, t+1, d]
+        p = softmax(np.matmul(qt, kw) * scale)             # [B, H_kv, n_rep, t+1]
+        o[:, i] = np.matmul(p, vw)
+    return o.reshape(B, len(rows), H_q, d)
+
+
 def prefill_backward(q, k, v, dO, gate_mode, window, alpha):
     """Gradients (dq, dk, dv) of sum(o * dO) for o = prefill(q, k, v, ...) from a zero state.
 

@@ -234,6 +234,31 @@ def test_full_attention_closed_forms():
         assert _close(o2[:, 0, h], v[:, 0, h // n_rep], rtol=1e-12)
 
 
+@pytest.mark.parametrize("n_rep", [1, 4])
+def test_full_attention_rows_pinned(n_rep):
+    """Row-sampled softmax layer: every listed row equals torch's causal
+    scaled_dot_product_attention (float64) at that position, and equals the
+    whole-sequence oracle there. Catches a prefix off by one (t vs t + 1
+    keys), rows taken from the wrong position, or a wrong head map."""
+    rng = np.random.default_rng(41 + n_rep)
+    B, T, H_kv, d = 2, 45, 2, 16
+    q = rng.standard_normal((B, T, H_kv * n_rep, d)) * 2.0
+    k = rng.standard_normal((B, T, H_kv, d))
+    v = rng.standard_normal((B, T, H_kv, d))
+    rows = [0, 1, 7, 31, 32, 44, 7]
+    o = oracle.full_attention_rows(q, k, v, rows)
+    assert o.shape == (B, len(rows), H_kv * n_rep, d)
+    tq = torch.from_numpy(q).transpose(1, 2)
+    tk = torch.from_numpy(k).transpose(1, 2).repeat_interleave(n_rep, dim=1)
+    tv = torch.from_numpy(v).transpose(1, 2).repeat_interleave(n_rep, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, is_causal=True, scale=1.0 / math.sqrt(d)).transpose(1, 2).numpy()
+    assert _close(o, ref[:, rows], rtol=1e-12)
+    assert _close(o, oracle.full_attention(q, k, v)[:, rows], rtol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.full_attention_rows(q, k, v, [T])
+
+
 def _sink_inputs(rng, B, T, H_kv, n_rep, d, n):
     q = rng.standard_normal((B, T, H_kv * n_rep, d))
     k = rng.standard_normal((B, T, H_kv, d))
