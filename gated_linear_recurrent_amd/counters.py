@@ -37,6 +37,17 @@ KERNELS = {
     "prefill_output_kernel": ("liger::prefill_output_kernel<unsigned short, 128, 0, false>", "prefill_8b_b1_t8192_d128",
                               ["gated_linear_recurrent_amd/csrc/prefill.hip",
                                "gated_linear_recurrent_amd/csrc/device_common.h"]),
+    "prefill_output_kernel_vector_d128": ("liger::prefill_output_kernel<unsigned short, 128, 1, false>",
+                                          "prefill_8b_b1_t32768_d128_outliers",
+                                          ["gated_linear_recurrent_amd/csrc/prefill.hip",
+                                           "gated_linear_recurrent_amd/csrc/device_common.h"]),
+    "prefill_output_kernel_vector_d64": ("liger::prefill_output_kernel<unsigned short, 64, 1, false>",
+                                         "prefill_1b_b4_t2048_d64",
+                                         ["gated_linear_recurrent_amd/csrc/prefill.hip",
+                                          "gated_linear_recurrent_amd/csrc/device_common.h"]),
+    "segment_state_kernel": ("liger::segment_state_kernel<unsigned short, 128, 0>", "prefill_8b_b1_t8192_d128",
+                             ["gated_linear_recurrent_amd/csrc/prefill.hip",
+                              "gated_linear_recurrent_amd/csrc/device_common.h"]),
     "decode_step_kernel": ("liger::decode_step_kernel<unsigned short, 128, 1, 4, false>", "decode_8b_n64_d128",
                            ["gated_linear_recurrent_amd/csrc/decode.hip",
                             "gated_linear_recurrent_amd/csrc/device_common.h"]),

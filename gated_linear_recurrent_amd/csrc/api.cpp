@@ -67,6 +67,7 @@ size_t tensor_bytes(int64_t B, int64_t T, int64_t heads, int64_t d, size_t elem)
 
 // True when the byte ranges [a, a + na) and [b, b + nb) share a byte.
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;  // absent optional buffer
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
     return x < y ? y - x < na : x - y < nb;
 }
@@ -149,13 +150,15 @@ liger_status prefill_impl(const void* q, const void* k, const void* v, const lig
     LIGER_TRY(check_ptr(v, "v"));
     LIGER_TRY(check_ptr(o, "o"));
     LIGER_TRY(check_ptr(S_T, "S_T"));
-    {
-        const size_t es = shape->dtype == LIGER_BF16 ? 2 : 4;
-        const size_t qb = tensor_bytes(shape->B, shape->T, shape->H_q, shape->d, es);
-        const size_t kb = tensor_bytes(shape->B, shape->T, shape->H_kv, shape->d, es);
-        const size_t sb = tensor_bytes(shape->B, shape->H_kv, shape->d, shape->d, 4);
-        LIGER_TRY(check_disjoint({{o, qb, "o"}, {S_T, sb, "S_T"}}, {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}}));
-    }
+    const size_t es = shape->dtype == LIGER_BF16 ? 2 : 4;
+    const size_t qb = tensor_bytes(shape->B, shape->T, shape->H_q, shape->d, es);
+    const size_t kb = tensor_bytes(shape->B, shape->T, shape->H_kv, shape->d, es);
+    const size_t sb = tensor_bytes(shape->B, shape->H_kv, shape->d, shape->d, 4);
+    const size_t skb = sinks ? tensor_bytes(shape->H_kv, sinks->n, 1, shape->d, es) : 0;
+    LIGER_TRY(check_disjoint({{o, qb, "o"}, {S_T, sb, "S_T"}},
+                             {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"},
+                              {sinks ? sinks->k : nullptr, skb, "sinks->k"},
+                              {sinks ? sinks->v : nullptr, skb, "sinks->v"}}));
     const liger::PrefillPlan pl = liger::make_prefill_plan(shape->B, shape->T, shape->H_kv, shape->d,
                                                            shape->dtype == LIGER_BF16, chunks_per_segment);
     if (pl.workspace_bytes > 0) {
@@ -164,6 +167,10 @@ liger_status prefill_impl(const void* q, const void* k, const void* v, const lig
         if (workspace_bytes < pl.workspace_bytes)
             return fail(LIGER_E_WORKSPACE, "workspace too small: " + std::to_string(workspace_bytes) + " < " +
                                                std::to_string(pl.workspace_bytes) + " bytes");
+        LIGER_TRY(check_disjoint({{workspace, pl.workspace_bytes, "workspace"}},
+                                 {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {o, qb, "o"}, {S_T, sb, "S_T"},
+                                  {sinks ? sinks->k : nullptr, skb, "sinks->k"},
+                                  {sinks ? sinks->v : nullptr, skb, "sinks->v"}}));
     }
     liger::PrefillArgs a;
     a.q = q;
@@ -253,14 +260,21 @@ liger_status continue_impl(const void* q, const void* k, const void* v, const fl
     LIGER_TRY(check_ptr(kv_ring->v, "kv_ring->v"));
     if (!kv_ring->pos) return fail(LIGER_E_INVALID_ARG, "kv_ring->pos is NULL");
     if (!kv_ring->sync) return fail(LIGER_E_INVALID_ARG, "kv_ring->sync is NULL");
-    {
-        const size_t es = shape->dtype == LIGER_BF16 ? 2 : 4;
-        const size_t qb = tensor_bytes(shape->B, shape->T, shape->H_q, shape->d, es);
-        const size_t kb = tensor_bytes(shape->B, shape->T, shape->H_kv, shape->d, es);
-        const size_t sb = tensor_bytes(shape->B, shape->H_kv, shape->d, shape->d, 4);
-        LIGER_TRY(check_disjoint({{o, qb, "o"}, {S_T, sb, "S_T"}},
-                                 {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {S0, sb, "S0"}}));
-    }
+    const size_t es = shape->dtype == LIGER_BF16 ? 2 : 4;
+    const size_t qb = tensor_bytes(shape->B, shape->T, shape->H_q, shape->d, es);
+    const size_t kb = tensor_bytes(shape->B, shape->T, shape->H_kv, shape->d, es);
+    const size_t sb = tensor_bytes(shape->B, shape->H_kv, shape->d, shape->d, 4);
+    const size_t rb = tensor_bytes(shape->B, shape->H_kv, window, shape->d, es);
+    const size_t pb = tensor_bytes(shape->B, 1, 1, 1, 8);
+    const size_t cb = tensor_bytes(shape->B, 1, 1, 1, 4);
+    const size_t skb = sinks ? tensor_bytes(shape->H_kv, sinks->n, 1, shape->d, es) : 0;
+    // written: o, S_T and the ring (k, v, pos, sync are updated in place)
+    LIGER_TRY(check_disjoint({{o, qb, "o"}, {S_T, sb, "S_T"}, {kv_ring->k, rb, "kv_ring->k"},
+                              {kv_ring->v, rb, "kv_ring->v"}, {kv_ring->pos, pb, "kv_ring->pos"},
+                              {kv_ring->sync, cb, "kv_ring->sync"}},
+                             {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {S0, sb, "S0"},
+                              {sinks ? sinks->k : nullptr, skb, "sinks->k"},
+                              {sinks ? sinks->v : nullptr, skb, "sinks->v"}}));
     const liger::PrefillPlan pl = liger::make_prefill_plan(shape->B, shape->T, shape->H_kv, shape->d,
                                                            shape->dtype == LIGER_BF16, 0);
     if (pl.workspace_bytes > 0) {
@@ -269,6 +283,12 @@ liger_status continue_impl(const void* q, const void* k, const void* v, const fl
         if (workspace_bytes < pl.workspace_bytes)
             return fail(LIGER_E_WORKSPACE, "workspace too small: " + std::to_string(workspace_bytes) + " < " +
                                                std::to_string(pl.workspace_bytes) + " bytes");
+        LIGER_TRY(check_disjoint({{workspace, pl.workspace_bytes, "workspace"}},
+                                 {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {S0, sb, "S0"}, {o, qb, "o"},
+                                  {S_T, sb, "S_T"}, {kv_ring->k, rb, "kv_ring->k"}, {kv_ring->v, rb, "kv_ring->v"},
+                                  {kv_ring->pos, pb, "kv_ring->pos"}, {kv_ring->sync, cb, "kv_ring->sync"},
+                                  {sinks ? sinks->k : nullptr, skb, "sinks->k"},
+                                  {sinks ? sinks->v : nullptr, skb, "sinks->v"}}));
     }
     liger::PrefillArgs a;
     a.q = q;
@@ -362,10 +382,21 @@ liger_status decode_impl(const void* q, const void* k, const void* v, float* S, 
     if (!kv_ring->pos) return fail(LIGER_E_INVALID_ARG, "kv_ring->pos is NULL");
     if (!kv_ring->sync) return fail(LIGER_E_INVALID_ARG, "kv_ring->sync is NULL");
     {
+        // written: o, and the decode state S, ring k/v, pos, sync (updated in place)
         const size_t es = shape->dtype == LIGER_BF16 ? 2 : 4;
         const size_t qb = tensor_bytes(shape->B, 1, shape->H_q, shape->d, es);
         const size_t kb = tensor_bytes(shape->B, 1, shape->H_kv, shape->d, es);
-        LIGER_TRY(check_disjoint({{o, qb, "o"}}, {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}}));
+        const size_t sb = tensor_bytes(shape->B, shape->H_kv, shape->d, shape->d, 4);
+        const size_t rb = tensor_bytes(shape->B, shape->H_kv, kv_ring->window, shape->d, es);
+        const size_t pb = tensor_bytes(shape->B, 1, 1, 1, 8);
+        const size_t cb = tensor_bytes(shape->B, 1, 1, 1, 4);
+        const size_t skb = sinks ? tensor_bytes(shape->H_kv, sinks->n, 1, shape->d, es) : 0;
+        LIGER_TRY(check_disjoint({{o, qb, "o"}, {S, sb, "S"}, {kv_ring->k, rb, "kv_ring->k"},
+                                  {kv_ring->v, rb, "kv_ring->v"}, {kv_ring->pos, pb, "kv_ring->pos"},
+                                  {kv_ring->sync, cb, "kv_ring->sync"}},
+                                 {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"},
+                                  {sinks ? sinks->k : nullptr, skb, "sinks->k"},
+                                  {sinks ? sinks->v : nullptr, skb, "sinks->v"}}));
     }
     liger::DecodeArgs a;
     a.q = q;
@@ -463,17 +494,17 @@ liger_status liger_attn_prefill_backward(const void* q, const void* k, const voi
     LIGER_TRY(check_ptr(dq, "dq"));
     LIGER_TRY(check_ptr(dk, "dk"));
     LIGER_TRY(check_ptr(dv, "dv"));
+    const size_t need = liger::backward_workspace_bytes(shape->B, shape->T, shape->H_kv, shape->H_q, shape->d);
+    if (workspace_bytes < need) return fail(LIGER_E_WORKSPACE, "workspace smaller than liger_attn_prefill_backward_workspace_size");
+    if (need > 0) LIGER_TRY(check_ptr(workspace, "workspace"));
     {
         const size_t qb = tensor_bytes(shape->B, shape->T, shape->H_q, shape->d, 2);
         const size_t kb = tensor_bytes(shape->B, shape->T, shape->H_kv, shape->d, 2);
         const size_t gqb = tensor_bytes(shape->B, shape->T, shape->H_q, shape->d, 4);
         const size_t gkb = tensor_bytes(shape->B, shape->T, shape->H_kv, shape->d, 4);
-        LIGER_TRY(check_disjoint({{dq, gqb, "dq"}, {dk, gkb, "dk"}, {dv, gkb, "dv"}},
+        LIGER_TRY(check_disjoint({{dq, gqb, "dq"}, {dk, gkb, "dk"}, {dv, gkb, "dv"}, {workspace, need, "workspace"}},
                                  {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {dO, qb, "dO"}}));
     }
-    const size_t need = liger::backward_workspace_bytes(shape->B, shape->T, shape->H_kv, shape->H_q, shape->d);
-    if (workspace_bytes < need) return fail(LIGER_E_WORKSPACE, "workspace smaller than liger_attn_prefill_backward_workspace_size");
-    if (need > 0) LIGER_TRY(check_ptr(workspace, "workspace"));
     liger::BackwardArgs a;
     a.q = q;
     a.k = k;
@@ -506,6 +537,16 @@ liger_status liger_kv_ring_fill(const void* k, const void* v, const liger_shape*
     LIGER_TRY(check_ptr(kv_ring->v, "kv_ring->v"));
     if (!kv_ring->pos) return fail(LIGER_E_INVALID_ARG, "kv_ring->pos is NULL");
     if (!kv_ring->sync) return fail(LIGER_E_INVALID_ARG, "kv_ring->sync is NULL");
+    {
+        const size_t es = shape->dtype == LIGER_BF16 ? 2 : 4;
+        const size_t kb = tensor_bytes(shape->B, shape->T, shape->H_kv, shape->d, es);
+        const size_t rb = tensor_bytes(shape->B, shape->H_kv, kv_ring->window, shape->d, es);
+        const size_t pb = tensor_bytes(shape->B, 1, 1, 1, 8);
+        const size_t cb = tensor_bytes(shape->B, 1, 1, 1, 4);
+        LIGER_TRY(check_disjoint({{kv_ring->k, rb, "kv_ring->k"}, {kv_ring->v, rb, "kv_ring->v"},
+                                  {kv_ring->pos, pb, "kv_ring->pos"}, {kv_ring->sync, cb, "kv_ring->sync"}},
+                                 {{k, kb, "k"}, {v, kb, "v"}}));
+    }
     liger::RingFillArgs a;
     a.k = k;
     a.v = v;

@@ -443,10 +443,19 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
     T* rvw = ring_v + ((static_cast<size_t>(n) * H_kv + h) * window + slot) * D;
     if (tid < D) *reinterpret_cast<Pair*>((tid < D / 2 ? rkw : rvw) + 2 * (tid % (D / 2))) = kvin;
 
-    // ---- the last of the H_kv workgroups of sequence n to arrive advances pos[n]
-    if (tid == 0 && prev == static_cast<uint32_t>(H_kv - 1)) {
-        sync[n] = 0u;
-        pos[n] = p + 1;
+    // ---- the last of the H_kv workgroups of sequence n to arrive advances
+    // pos[n] and clears the count. A count that was not zero on entry (a
+    // counter never reset, or a step that did not complete) shows up as an
+    // arrival numbered H_kv or more: that workgroup sets bit 31 of sync[n],
+    // which then stays set (every later arrival sees it and none advances
+    // pos[n]) until the caller resets the counter.
+    if (tid == 0) {
+        if (prev >= static_cast<uint32_t>(H_kv)) {
+            __hip_atomic_fetch_or(&sync[n], 0x80000000u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (prev == static_cast<uint32_t>(H_kv - 1)) {
+            __hip_atomic_fetch_and(&sync[n], 0x80000000u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            pos[n] = p + 1;
+        }
     }
 }
 

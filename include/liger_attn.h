@@ -97,6 +97,20 @@ typedef struct liger_kv_ring {
     uint32_t* sync; /* [N] arrival counters; zero before and after each call */
     int32_t window; /* 1 .. 64                                               */
 } liger_kv_ring;
+/*
+ * The decode state of sequence n is (S[n], ring k/v of sequence n, pos[n]);
+ * sync[n] holds nothing between calls: it is zero whenever no call on the
+ * sequence is in flight (liger_kv_ring_fill and liger_attn_prefill_continue
+ * set it to zero; a completed decode step leaves it zero). A snapshot of
+ * (S, ring k/v, pos) taken between calls, with sync set to zero, is a
+ * complete decode state. A decode step that finds sync[n] non-zero on entry
+ * (memory never cleared, a snapshot restored without clearing it, a step
+ * that did not complete) cannot tell when every workgroup of the sequence
+ * has read pos[n]: it sets bit 31 of sync[n], which stays set, and from then
+ * on pos[n] is not advanced. After synchronising, sync[n] != 0 reports this;
+ * restore (S, ring, pos) from a snapshot and clear sync (or rebuild the ring
+ * with liger_kv_ring_fill) to recover.
+ */
 
 /*
  * Meta-memory tokens ("attention sinks", Japanese summary page of Lizard,
@@ -112,6 +126,9 @@ typedef struct liger_sinks {
 } liger_sinks;
 
 /*
+ * Defined by: the chunked ("right-multiplication", linear in T) evaluation
+ * of the recurrence (news article on Liger, 手法の説明); the segments of
+ * that evaluation need the carried states below.
  * Bytes of device workspace liger_attn_prefill needs for `shape`: the state
  * carried into each segment of the chunked scan and a running-state slot per
  * segment. Returns 0 when the shape is invalid. `chunks_per_segment` selects the segment length
@@ -124,6 +141,11 @@ size_t liger_attn_prefill_workspace_size_ex(const liger_shape* shape,
 
 /*
  * Prefill: whole sequences from a zero state.
+ * Defined by: paper-notes page "Liger: Linearizing Large Language Models to
+ * Gated Recurrent Structures", sections 统一的门控线性循环框架 (the gated
+ * recurrence and its output), Liger Attention：层内混合注意力 (the alpha/beta
+ * mix with window-64 softmax attention) and 核心思想：Key 投影复用构建门控 (the
+ * gate pooled from the key); one of the two calls of this boundary.
  * Inputs q, k, v (layouts above). Outputs o [B, T, H_q, d] (dtype of q) and
  * S_T [B, H_kv, d, d] float32, the state after the last token.
  * window in 1..64, alpha in [0, 1] (beta = 1 - alpha).
@@ -139,7 +161,9 @@ liger_status liger_attn_prefill(const void* q, const void* k, const void* v,
                                 void* stream);
 
 /* As liger_attn_prefill with an explicit segment length (0 = automatic);
- * every segment length gives the same result up to float32 rounding. */
+ * every segment length gives the same result up to float32 rounding.
+ * Defined by: the same sections as liger_attn_prefill (a tuning extension
+ * of that call). */
 liger_status liger_attn_prefill_ex(const void* q, const void* k, const void* v,
                                    int32_t gate_mode, int32_t window, float alpha,
                                    const liger_shape* shape, void* o, float* S_T,
@@ -147,6 +171,8 @@ liger_status liger_attn_prefill_ex(const void* q, const void* k, const void* v,
                                    int32_t chunks_per_segment, void* stream);
 
 /*
+ * Defined by: the same sections as liger_attn_prefill (a profiling
+ * extension of that call: it computes nothing else).
  * Profiling aid: enqueue only the prefill kernels chosen by stage_mask, in
  * pipeline order: LIGER_STAGE_SEGMENT_STATES (local end state of every
  * segment but the last), LIGER_STAGE_CARRY_SCAN (states entering each
@@ -195,12 +221,21 @@ liger_status liger_attn_prefill_continue(const void* q, const void* k, const voi
 
 /*
  * Decode step: one new token for each of N = shape->B sequences.
+ * Defined by: paper-notes page "Liger: Linearizing Large Language Models to
+ * Gated Recurrent Structures", 统一的门控线性循环框架 (the recurrence taken
+ * one token at a time: S_t from S_{t-1}) and Liger Attention：层内混合注意力
+ * (the window of the most recent tokens); news article on Liger, 実験分析
+ * (decoding with a fixed-size state instead of a growing cache). The second
+ * call of this boundary.
  * q [N, H_q, d], k, v [N, H_kv, d] (dtype of the shape); o [N, H_q, d].
  * S [N, H_kv, d, d] float32 is updated in place to G (.) S + phi(k)^T v.
  * The ring is updated in place: the new k, v go to slot pos mod window, the
  * window of `window` most recent tokens (the new one included) is attended
  * to, and pos advances by one. gate_mode and alpha must be those of the
  * prefill that produced the state. shape->T is ignored.
+ * o, S, the ring's k, v, pos and sync are written: their byte ranges must be
+ * pairwise disjoint and must not overlap q, k, v or the sink tokens
+ * (LIGER_E_INVALID_ARG). sync must be zero on entry (see liger_kv_ring).
  */
 liger_status liger_attn_decode_step(const void* q, const void* k, const void* v,
                                     float* S, const liger_kv_ring* kv_ring,
@@ -209,10 +244,15 @@ liger_status liger_attn_decode_step(const void* q, const void* k, const void* v,
                                     void* stream);
 
 /*
+ * Defined by: paper-notes page "Liger: Linearizing Large Language Models to
+ * Gated Recurrent Structures", Liger Attention：层内混合注意力 (the softmax
+ * attention sees only the last `window` tokens, so only those are kept) and
+ * news article on Liger, 実験分析 (fixed-size decoding state).
  * Ring set-up after a prompt: copies the last min(T, window) tokens of
  * k, v [B, T, H_kv, d] to slots t mod window, zeroes the other slots,
  * sets pos = T and sync = 0. (Together with S_T from the prefill this is the
- * complete decode state.)
+ * complete decode state.) The ring's k, v, pos and sync must be pairwise
+ * disjoint and must not overlap k or v (LIGER_E_INVALID_ARG).
  */
 liger_status liger_kv_ring_fill(const void* k, const void* v,
                                 const liger_shape* shape,
@@ -286,7 +326,8 @@ liger_status liger_attn_prefill_backward(const void* q, const void* k, const voi
                                          void* workspace, size_t workspace_bytes,
                                          void* stream);
 
-/* Message of the last failed call on this thread ("" if none). */
+/* Message of the last failed call on this thread ("" if none). A helper of
+ * the boundary: it reports errors and computes nothing. */
 const char* liger_last_error(void);
 
 #ifdef __cplusplus

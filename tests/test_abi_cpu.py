@@ -126,12 +126,12 @@ def test_workspace_size_formula(lib):
     assert lib.liger_attn_prefill_workspace_size(None) == 0
 
 
-def _ring(window=64, k=FAKE, v=FAKE + 4096, pos=FAKE + 8192, sync=FAKE + 12288):
+def _ring(window=64, k=FAKE + 8 * G, v=FAKE + 9 * G, pos=FAKE + 10 * G, sync=FAKE + 11 * G):
     return gla.liger_kv_ring(k, v, pos, sync, window)
 
 
-def _decode(lib, shape, ring, gate=1, alpha=0.5, q=FAKE + 65536, k=FAKE + 69632, v=FAKE + 73728,
-            S=FAKE + 77824, o=FAKE + 81920):
+def _decode(lib, shape, ring, gate=1, alpha=0.5, q=FAKE + 12 * G, k=FAKE + 13 * G, v=FAKE + 14 * G,
+            S=FAKE + 15 * G, o=FAKE + 16 * G):
     return lib.liger_attn_decode_step(q, k, v, S, ctypes.byref(ring) if ring is not None else None,
                                       gate, alpha, ctypes.byref(shape), o, None)
 
@@ -152,8 +152,36 @@ def test_decode_rejects_bad_arguments(lib, kw, rkw, code):
 
 def test_decode_rejects_null_ring_and_alias(lib):
     assert _decode(lib, _shape(), None) == gla.LIGER_E_INVALID_ARG
-    assert _decode(lib, _shape(), _ring(), o=FAKE + 65536) == gla.LIGER_E_INVALID_ARG
+    assert _decode(lib, _shape(), _ring(), o=FAKE + 12 * G) == gla.LIGER_E_INVALID_ARG
     assert _decode(lib, _shape(), _ring(), gate=-1) == gla.LIGER_E_INVALID_ARG
+
+
+# decode writes o, S and the ring (k, v, pos, sync): each must be disjoint from
+# the inputs and from the others (shape: N = 1, H_q = 4, H_kv = 1, d = 128, bf16,
+# window 64: S 64 KiB, ring k and v 16 KiB each, pos 8 B, sync 4 B)
+@pytest.mark.parametrize("dkw,rkw,msg", [
+    (dict(S=FAKE + 12 * G + 512), {}, "S must not overlap q"),
+    (dict(S=FAKE + 16 * G - 4096), {}, "o must not overlap S"),
+    ({}, dict(k=FAKE + 13 * G), "kv_ring->k must not overlap k"),
+    ({}, dict(v=FAKE + 14 * G + 128), "kv_ring->v must not overlap v"),
+    ({}, dict(v=FAKE + 8 * G + 16384 - 16), "kv_ring->k must not overlap kv_ring->v"),
+    ({}, dict(pos=FAKE + 15 * G + 64), "S must not overlap kv_ring->pos"),
+    ({}, dict(sync=FAKE + 10 * G), "kv_ring->pos must not overlap kv_ring->sync"),
+    ({}, dict(sync=FAKE + 9 * G + 16), "kv_ring->v must not overlap kv_ring->sync"),
+    ({}, dict(pos=FAKE + 16 * G), "o must not overlap kv_ring->pos"),
+])
+def test_decode_rejects_overlapping_state(lib, dkw, rkw, msg):
+    assert _decode(lib, _shape(), _ring(**rkw), **dkw) == gla.LIGER_E_INVALID_ARG
+    assert gla.liger_last_error() == msg
+
+
+def test_decode_state_buffers_may_touch(lib):
+    """Buffers that touch without sharing a byte pass the overlap checks."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: the fake pointers of this test must not reach a kernel")
+    r = _ring(k=FAKE + 8 * G, v=FAKE + 8 * G + 16384, pos=FAKE + 8 * G + 32768, sync=FAKE + 8 * G + 32768 + 16)
+    assert _decode(lib, _shape(), r) == gla.LIGER_E_HIP, gla.liger_last_error()
 
 
 def _continue(lib, shape, ring, S0=FAKE + 3 * G, S_T=FAKE + 4 * G, o=FAKE + 5 * G, gate=1, alpha=0.5,
@@ -186,6 +214,42 @@ def test_continue_rejects_bad_arguments(lib, kw, rkw, ckw, code):
 
 def test_continue_rejects_null_ring(lib):
     assert _continue(lib, _shape(T=256), None) == gla.LIGER_E_INVALID_ARG
+
+
+@pytest.mark.parametrize("rkw,msg", [
+    (dict(k=FAKE + 256), "kv_ring->k must not overlap k"),
+    (dict(v=FAKE + G + 1024), "kv_ring->v must not overlap v"),
+    (dict(pos=FAKE + 8 * G + 64), "kv_ring->k must not overlap kv_ring->pos"),
+    (dict(sync=FAKE + 10 * G + 4), "kv_ring->pos must not overlap kv_ring->sync"),
+])
+def test_ring_fill_rejects_overlaps(lib, rkw, msg):
+    shp = _shape()
+    r = _ring(**rkw)
+    assert lib.liger_kv_ring_fill(FAKE, FAKE + G, ctypes.byref(shp), ctypes.byref(r), None) == gla.LIGER_E_INVALID_ARG
+    assert gla.liger_last_error() == msg
+
+
+@pytest.mark.parametrize("rkw,ckw,msg", [
+    (dict(k=FAKE + 5 * G), {}, "o must not overlap kv_ring->k"),
+    (dict(pos=FAKE + 3 * G + 8), {}, "kv_ring->pos must not overlap S0"),
+    ({}, dict(ws=FAKE + 64, ws_bytes=1 << 40), "workspace must not overlap q"),
+    ({}, dict(ws=FAKE + 4 * G - 1024, ws_bytes=1 << 40), "workspace must not overlap S_T"),
+])
+def test_continue_rejects_overlaps(lib, rkw, ckw, msg):
+    shp = _shape(T=256, H_q=4, H_kv=1)
+    assert _continue(lib, shp, _ring(**rkw), **ckw) == gla.LIGER_E_INVALID_ARG
+    assert gla.liger_last_error() == msg
+
+
+def test_prefill_rejects_workspace_overlap(lib):
+    shp = _shape(T=4096)
+    need = lib.liger_attn_prefill_workspace_size(ctypes.byref(shp))
+    assert _prefill(lib, shp, ws=FAKE + G - 4096, ws_bytes=need) == gla.LIGER_E_INVALID_ARG
+    assert gla.liger_last_error() == "workspace must not overlap o"
+    assert _prefill(lib, shp, ws=FAKE + 2 * G + 1024, ws_bytes=need) == gla.LIGER_E_INVALID_ARG
+    assert gla.liger_last_error() == "workspace must not overlap S_T"
+    assert _prefill(lib, shp, ws=FAKE + 4096, ws_bytes=need) == gla.LIGER_E_INVALID_ARG
+    assert gla.liger_last_error() == "workspace must not overlap q"
 
 
 def test_ring_fill_rejects_bad_arguments(lib):
@@ -280,6 +344,7 @@ def test_sinks_null_struct_rejected(lib):
     ({}, dict(dk=FAKE + 4 * G + 2048), {}, gla.LIGER_E_INVALID_ARG),  # starts inside dq
     ({}, dict(dk=FAKE + 5 * G + 8), {}, gla.LIGER_E_INVALID_ARG),  # misaligned
     ({}, {}, dict(ws_bytes=16), gla.LIGER_E_WORKSPACE),
+    ({}, dict(dv=(FAKE << 8) + 4096), {}, gla.LIGER_E_INVALID_ARG),  # inside the workspace
 ])
 def test_backward_rejects_bad_arguments(lib, kw, ptrs, extra, code):
     p = dict(q=FAKE, k=FAKE + G, v=FAKE + 2 * G, dO=FAKE + 3 * G, dq=FAKE + 4 * G, dk=FAKE + 5 * G,

@@ -55,7 +55,13 @@ def _run(dtype, d, gate, n_rep, window, T1, T2, alpha=0.5, B=2, H_kv=2, seed=0):
     S_T = torch.full_like(S0_dev, float("nan"))
     gla.liger_attn_prefill_continue(qd, kd, vd, S0_dev, ring, gate, alpha, o=o, S_T=S_T)
     torch.cuda.synchronize()
-    check_prefill(dtype, to_np(o), o_full[:, T1:], to_np(S_T), S_full, tag=tag)
+    if alpha == 1.0:
+        # the recurrent output alone: its own relative bar (the window output
+        # is ~25x larger and would hide a wrong recurrence under the mixed bar)
+        check_prefill(dtype, to_np(o), o1_full[:, T1:], to_np(S_T), S_full, o1_gpu=to_np(o),
+                      o1_ref=o1_full[:, T1:], tag=tag)
+    else:
+        check_prefill(dtype, to_np(o), o_full[:, T1:], to_np(S_T), S_full, tag=tag)
     assert np.array_equal(to_np(S0_dev), S0.astype(np.float32)), f"{tag}: S0 modified"
     rk_ref, rv_ref, pos_ref = oracle.ring_fill(k, v, window)
     _check_ring(ring, rk_ref, rv_ref, pos_ref, dtype, tag)
@@ -75,6 +81,26 @@ def _run(dtype, d, gate, n_rep, window, T1, T2, alpha=0.5, B=2, H_kv=2, seed=0):
 ])
 def test_continue_matches_oracle(dtype, d, gate, n_rep, window, T1, T2):
     _run(dtype, d, gate, n_rep, window, T1, T2)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("alpha", [0.0, 1.0])
+@pytest.mark.parametrize("n_rep,window,T1,T2", [
+    (4, 64, 30, 65),     # fewer than 64 tokens of history, a ragged chunk
+    (2, 64, 200, 130),   # several chunks on both sides
+    (2, 1, 5, 70),       # window 1
+])
+def test_continue_mixers_alone(dtype, d, gate, alpha, n_rep, window, T1, T2):
+    """alpha = 1 (recurrent output alone, relative bar) and alpha = 0 (window alone)."""
+    _run(dtype, d, gate, n_rep, window, T1, T2, alpha=alpha)
+
+
+@pytest.mark.parametrize("alpha", [0.0, 1.0])
+def test_continue_many_segments_mixers_alone(alpha):
+    """A long continuation (several segments, carried state in the carry scan)
+    with each mixer alone."""
+    _run("bf16", 128, 1, 4, 64, 150, 2100, B=1, H_kv=2, alpha=alpha)
 
 
 @pytest.mark.parametrize("gate", [0, 1])

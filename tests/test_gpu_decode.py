@@ -16,9 +16,14 @@ from synth import CONFIGS, GATE_MODES, decode_initial, decode_step_inputs, prefi
 pytestmark = pytest.mark.gpu
 
 
-def _bars(dtype, o_gpu, o_ref, tag):
+def _bars(dtype, o_gpu, o_ref, tag, alpha=0.5):
+    """fp32: relative 1e-4. bf16: max |error| <= 2e-2 on the mixed or window
+    output; the recurrent output alone (alpha = 1) is ~25x smaller than the
+    window output, so it is held to 2e-2 of its own largest magnitude."""
     if dtype == "f32":
         assert rel_inf(o_gpu, o_ref) <= 1e-4, (tag, rel_inf(o_gpu, o_ref))
+    elif alpha == 1.0:
+        assert rel_inf(o_gpu, o_ref) <= 2e-2, (tag, rel_inf(o_gpu, o_ref))
     else:
         assert abs_inf(o_gpu, o_ref) <= 2e-2, (tag, abs_inf(o_gpu, o_ref))
 
@@ -56,6 +61,43 @@ def test_prefill_then_decode_matches_oracle(dtype, d, gate, n_rep, window, T0):
                                        to_dev(x["v"][:, t], dtype), S, ring, gate, 0.5)
         torch.cuda.synchronize()
         _bars(dtype, to_np(o), o_full[:, t], f"{tag} step {i}")
+    assert rel_inf(to_np(S), S_full) <= 1e-5, rel_inf(to_np(S), S_full)
+    rk, rv, pos = oracle.ring_fill(x["k"], x["v"], window)
+    assert np.array_equal(_ring_bits(ring.k), _np_bits(rk, dtype))
+    assert np.array_equal(_ring_bits(ring.v), _np_bits(rv, dtype))
+    assert np.array_equal(ring.pos.cpu().numpy(), pos)
+    assert int(ring.sync.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("alpha", [0.0, 1.0])
+@pytest.mark.parametrize("n_rep,window,T0", [(4, 17, 3), (2, 1, 5), (1, 64, 70)])
+def test_decode_mixers_alone_match_oracle(dtype, d, gate, alpha, n_rep, window, T0):
+    """alpha = 1 (recurrent output alone) and alpha = 0 (window alone), so that
+    neither mixer can hide behind the other: an exclusive diagonal
+    (phi(q_t) S_{t-1}) or a transposed state fails the relative bar of the
+    alpha = 1 output by a wide margin."""
+    n_steps = 10
+    N, H_kv = 3, 2
+    H_q = H_kv * n_rep
+    tag = f"decode alpha={alpha} {dtype} d={d} gate={gate} n_rep={n_rep} w={window} T0={T0}"
+    say(f"[decode] {tag}")
+    x = prefill_inputs(B=N, T=T0 + n_steps, H_q=H_q, H_kv=H_kv, d=d, dtype=dtype, seed=T0 + 31 * n_rep + 5)
+    o_full, S_full = oracle.prefill(x["q"], x["k"], x["v"], gate, window, alpha)
+    _, S0 = oracle.prefill(x["q"][:, :T0], x["k"][:, :T0], x["v"][:, :T0], gate, window, alpha)
+    S = torch.from_numpy(S0.astype(np.float32)).to(DEV)
+    ring = gla.KVRing.empty(N, H_kv, window, d, TORCH_DT[dtype], DEV)
+    gla.liger_kv_ring_fill(to_dev(x["k"][:, :T0], dtype), to_dev(x["v"][:, :T0], dtype), ring)
+    worst = 0.0
+    for i in range(n_steps):
+        t = T0 + i
+        o = gla.liger_attn_decode_step(to_dev(x["q"][:, t], dtype), to_dev(x["k"][:, t], dtype),
+                                       to_dev(x["v"][:, t], dtype), S, ring, gate, alpha)
+        torch.cuda.synchronize()
+        _bars(dtype, to_np(o), o_full[:, t], f"{tag} step {i}", alpha)
+        worst = max(worst, rel_inf(to_np(o), o_full[:, t]))
+    say(f"  worst relative error of o over the steps: {worst:.3e}")
     assert rel_inf(to_np(S), S_full) <= 1e-5, rel_inf(to_np(S), S_full)
     rk, rv, pos = oracle.ring_fill(x["k"], x["v"], window)
     assert np.array_equal(_ring_bits(ring.k), _np_bits(rk, dtype))
@@ -137,36 +179,117 @@ def test_resume_from_host_snapshot():
     assert torch.equal(S3, S) and torch.equal(ring3.k, ring.k) and torch.equal(ring3.pos, ring.pos)
 
 
+def test_stale_arrival_counter_is_flagged():
+    """A sequence whose arrival counter is not zero on entry is reported: bit
+    31 of its sync word is set and stays set, and its pos is not advanced by
+    later steps. The other sequences are unaffected (outputs against the
+    oracle, pos advanced, sync zero). Clearing sync restores normal steps."""
+    N, H_kv, n_rep, d, w, gate = 3, 8, 4, 128, 64, 1
+    say("[decode] stale arrival counter")
+    init = decode_initial(N=N, H_kv=H_kv, d=d, window=w, dtype="bf16", seed=11, pos0=100)
+    S = torch.from_numpy(init["S"]).to(DEV)
+    ring = gla.KVRing(to_dev(init["ring_k"], "bf16"), to_dev(init["ring_v"], "bf16"),
+                      torch.from_numpy(init["pos"]).to(DEV), torch.zeros(N, dtype=torch.int32, device=DEV), w)
+    ring.sync[1] = 3
+    good = np.array([0, 2])
+    S_ref = init["S"][good].astype(np.float64)
+    rk, rv, pos = init["ring_k"][good], init["ring_v"][good], init["pos"][good]
+    for s in range(2):
+        x = decode_step_inputs(N=N, H_q=H_kv * n_rep, H_kv=H_kv, d=d, dtype="bf16", seed=11, step=s)
+        o = gla.liger_attn_decode_step(to_dev(x["q"], "bf16"), to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16"),
+                                       S, ring, gate, 0.5)
+        torch.cuda.synchronize()
+        o_ref, S_ref, rk, rv, pos = oracle.decode_step(x["q"][good], x["k"][good], x["v"][good], S_ref, rk, rv,
+                                                       pos, gate, 0.5)
+        assert abs_inf(to_np(o)[good], o_ref) <= 2e-2
+        sync = [int(c) & 0xFFFFFFFF for c in ring.sync.cpu().tolist()]
+        p = ring.pos.cpu().tolist()
+        assert sync[0] == 0 and sync[2] == 0, sync
+        assert p[0] == 101 + s and p[2] == 101 + s, p
+        assert sync[1] & 0x80000000, sync
+        if s == 0:
+            pos_after_first = p[1]
+        else:
+            assert p[1] == pos_after_first, (p, pos_after_first)
+    # recovery: the caller clears the counter; the next step advances pos again
+    ring.sync.zero_()
+    x = decode_step_inputs(N=N, H_q=H_kv * n_rep, H_kv=H_kv, d=d, dtype="bf16", seed=11, step=2)
+    gla.liger_attn_decode_step(to_dev(x["q"], "bf16"), to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16"),
+                               S, ring, gate, 0.5)
+    torch.cuda.synchronize()
+    assert int(ring.sync.abs().sum()) == 0
+    assert ring.pos.cpu().tolist() == [103, pos_after_first + 1, 103]
+
+
+@pytest.mark.timeout(600)
 def test_config_decode_8b_full():
-    """64 sequences x 1024 steps at Llama-3-8B geometry (all sequences on the
-    GPU; the oracle follows four of them, since sequences are independent)."""
+    """64 sequences x 1024 steps at Llama-3-8B geometry, every sequence
+    against the oracle: o at every step, and S, the ring bits and pos at the
+    end. Sequences are independent, so the oracle runs on blocks of sequences
+    in worker threads, each walking all the steps of its block."""
+    import queue
+    import threading
+
     name = "decode_8b_n64_d128"
     cfg = CONFIGS[name]
     N, H_q, H_kv, d, w = cfg["N"], cfg["H_q"], cfg["H_kv"], cfg["d"], cfg["window"]
     gate = GATE_MODES[cfg["gate"]]
-    follow = np.array([0, 17, 42, 63])
-    say(f"[decode] {name} steps={cfg['steps']} following sequences {follow.tolist()}")
+    n_steps = cfg["steps"]
+    say(f"[decode] {name} steps={n_steps}, all {N} sequences against the oracle")
     init = decode_initial(**cfg)
     S = torch.from_numpy(init["S"]).to(DEV)
     ring = gla.KVRing(to_dev(init["ring_k"], "bf16"), to_dev(init["ring_v"], "bf16"),
                       torch.from_numpy(init["pos"]).to(DEV), torch.zeros(N, dtype=torch.int32, device=DEV), w)
-    S_ref = init["S"][follow].astype(np.float64)
-    rk_ref, rv_ref, pos_ref = init["ring_k"][follow], init["ring_v"][follow], init["pos"][follow]
-    worst = 0.0
-    for s in range(cfg["steps"]):
+    n_blocks = 16
+    blocks = [np.arange(N)[i::n_blocks] for i in range(n_blocks)]
+    queues = [queue.Queue(maxsize=64) for _ in blocks]
+    result = [None] * n_blocks
+
+    def oracle_worker(bi):
+        sel = blocks[bi]
+        S_ref = init["S"][sel].astype(np.float64)
+        rk, rv, pos = init["ring_k"][sel], init["ring_v"][sel], init["pos"][sel]
+        worst = 0.0
+        try:
+            for s in range(n_steps):
+                x, o_gpu = queues[bi].get()
+                o_ref, S_ref, rk, rv, pos = oracle.decode_step(
+                    x["q"][sel], x["k"][sel], x["v"][sel], S_ref, rk, rv, pos, gate, cfg["alpha"])
+                worst = max(worst, abs_inf(o_gpu[sel], o_ref))
+            result[bi] = (worst, S_ref, rk, rv, pos)
+        except Exception as e:  # reported by the main thread
+            result[bi] = e
+
+    threads = [threading.Thread(target=oracle_worker, args=(bi,), daemon=True) for bi in range(n_blocks)]
+    for t in threads:
+        t.start()
+    for s in range(n_steps):
         x = decode_step_inputs(step=s, **cfg)
         o = gla.liger_attn_decode_step(to_dev(x["q"], "bf16"), to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16"),
                                        S, ring, gate, cfg["alpha"])
-        o_ref, S_ref, rk_ref, rv_ref, pos_ref = oracle.decode_step(
-            x["q"][follow], x["k"][follow], x["v"][follow], S_ref, rk_ref, rv_ref, pos_ref, gate, cfg["alpha"])
-        err = abs_inf(to_np(o)[follow], o_ref)
-        worst = max(worst, err)
-        assert err <= 2e-2, (s, err)
+        o_host = to_np(o)
+        for qu in queues:
+            qu.put((x, o_host))
         if s % 256 == 0:
-            say(f"  step {s}: max|o - ref| = {err:.3e}")
-    say(f"  worst max|o - ref| over all steps: {worst:.3e}")
-    assert rel_inf(to_np(S)[follow], S_ref) <= 1e-4
-    assert np.array_equal(_ring_bits(ring.k)[follow], _np_bits(rk_ref, "bf16"))
-    assert np.array_equal(_ring_bits(ring.v)[follow], _np_bits(rv_ref, "bf16"))
-    assert np.array_equal(ring.pos.cpu().numpy(), np.full(N, cfg["pos0"] + cfg["steps"]))
+            say(f"  GPU step {s} done")
+    for t in threads:
+        t.join()
+    for r in result:
+        assert not isinstance(r, Exception), r
+    worst = max(r[0] for r in result)
+    say(f"  worst max|o - ref| over all steps and sequences: {worst:.3e}")
+    assert worst <= 2e-2, worst
+    S_ref = np.empty((N, H_kv, d, d))
+    rk_ref = np.empty_like(init["ring_k"])
+    rv_ref = np.empty_like(init["ring_v"])
+    pos_ref = np.empty(N, np.int64)
+    for sel, r in zip(blocks, result):
+        S_ref[sel], rk_ref[sel], rv_ref[sel], pos_ref[sel] = r[1], r[2], r[3], r[4]
+    err_S = rel_inf(to_np(S), S_ref)
+    say(f"  state relative error {err_S:.3e}")
+    assert err_S <= 1e-4, err_S
+    assert np.array_equal(_ring_bits(ring.k), _np_bits(rk_ref, "bf16"))
+    assert np.array_equal(_ring_bits(ring.v), _np_bits(rv_ref, "bf16"))
+    assert np.array_equal(ring.pos.cpu().numpy(), pos_ref)
+    assert np.array_equal(pos_ref, np.full(N, cfg["pos0"] + n_steps))
     assert int(ring.sync.abs().sum()) == 0
