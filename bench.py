@@ -8,13 +8,20 @@ step is bracketed by HIP events on the stream the kernels run on; before
 each one an untimed 512 MiB write evicts the 256 MB last-level cache, so
 the inputs come from HBM ("cold", the headline `value`, median step). The
 same steps without the eviction are reported as "hot". The JSON line also
-carries the roofline of the dominant kernel (the fused output kernel), the
-float64 CPU oracle on the host as a reported baseline, the hybrid's full
-causal softmax attention layer on the same inputs (cold and hot, against
-the dense bf16 MFMA peak), the prefill's backward on the same inputs (cold
-and hot), and the decode workload (64 sequences,
-Llama-3-8B heads, one token per step: launched back to back, each between
-its own events, replayed from a captured HIP graph, and cold steps).
+carries:
+  - the roofline of the dominant kernel (the fused output kernel) and the
+    whole cold step's fraction of the same roofline;
+  - the other prefill workloads, each with its own roofline: the
+    Llama-3.2-1B-shaped batch (B=4, T=2048, d=64, vector gate) and the
+    long-context 8B shape (T=32768, vector gate, 1% of key rows x8);
+  - the decode workload (64 sequences, Llama-3-8B heads, 1024 single-token
+    steps: launched back to back, each between its own events, replayed from
+    a captured HIP graph, and cold steps after evicting the cache);
+  - the hybrid's full causal softmax attention layer, the prefill with sink
+    tokens, and the prefill's backward, on the 8B inputs;
+  - the float64 CPU oracle on the host as a reported baseline (prefill of
+    the 8B, 1B and long-context workloads and decode steps, each on a
+    bounded sample), with the CPU model and thread counts.
 
     python bench.py [--steps K] [--warmup W] [--decode-steps N]
 
@@ -34,7 +41,13 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 (vector or MFMA)
 PREFILL_WORKLOAD = "prefill_8b_b1_t8192_d128"
+PREFILL_1B_WORKLOAD = "prefill_1b_b4_t2048_d64"
+PREFILL_LONG_WORKLOAD = "prefill_8b_b1_t32768_d128_outliers"
+OUTPUT_KERNEL_RECORD = {PREFILL_WORKLOAD: "prefill_output_kernel",
+                        PREFILL_1B_WORKLOAD: "prefill_output_kernel_vector_d64",
+                        PREFILL_LONG_WORKLOAD: "prefill_output_kernel_vector_d128"}
 DECODE_WORKLOAD = "decode_8b_n64_d128"
 FULL_WORKLOAD = "full_attn_8b_b1_t8192_d128"
 N_SINKS = 16      # meta-memory tokens per key/value head in the sink measurements (synthetic, N(0, 1))
@@ -42,6 +55,9 @@ SINK_SEED = 17  # the softmax layer on the prefill workload's inputs
 BWD_SEED = 23   # upstream gradient of the backward measurement
 CHUNK = 64
 SCRUB_BYTES = 512 << 20        # larger than the 256 MB last-level cache
+# tokens of each other prefill workload that the CPU baseline times (a prefix:
+# the oracle is linear in T, so the prefix rate is the workload's rate)
+CPU_PREFIX_TOKENS = {PREFILL_1B_WORKLOAD: 512, PREFILL_LONG_WORKLOAD: 1024}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -89,25 +105,175 @@ def decode_algorithmic(cfg: dict) -> float:
     return float(N * per_seq)
 
 
-def cpu_baseline(cfg: dict, x: dict, tokens: int, min_seconds: float = 10.0, max_runs: int = 20) -> dict:
-    """The float64 oracle as it stands, on the host, BLAS limited to one thread.
-    The sample is run repeatedly until about min_seconds of CPU work have been
-    timed; the value is the median rate over the runs."""
+def cpu_info() -> dict:
+    """The host the CPU baseline ran on: CPU model, logical CPUs, CPUs this
+    process may use, and the BLAS thread pools the oracle's NumPy could use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    info = {"cpu_model": model, "cpu_count": os.cpu_count()}
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except AttributeError:
+        info["affinity_cpus"] = None
+    try:
+        from threadpoolctl import threadpool_info
+        info["blas_pools"] = [{"api": p.get("internal_api"), "threads": p.get("num_threads")}
+                              for p in threadpool_info()]
+    except Exception:  # report what is available
+        info["blas_pools"] = None
+    return info
+
+
+def _timed_runs(fn, min_seconds: float, max_runs: int) -> list:
+    times = []
+    while sum(times) < min_seconds and len(times) < max_runs:
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return times
+
+
+def cpu_baseline_prefill(name: str, x: dict, tokens: int, min_seconds: float, max_runs: int = 20) -> dict:
+    """The float64 oracle as it stands on the first `tokens` tokens of a
+    prefill workload (all batches and heads), BLAS limited to one thread, run
+    repeatedly until about min_seconds of CPU work are timed; the value is the
+    median rate over the runs (the oracle is linear in T, so a prefix rate is
+    the workload's rate)."""
     import oracle
+    from synth import CONFIGS
     from threadpoolctl import threadpool_limits
+    cfg = CONFIGS[name]
     gate = 0 if cfg["gate"] == "scalar" else 1
     q, k, v = (x[n][:, :tokens] for n in ("q", "k", "v"))
-    times = []
     with threadpool_limits(limits=1):
-        while sum(times) < min_seconds and len(times) < max_runs:
-            t0 = time.perf_counter()
-            oracle.prefill(q, k, v, gate, cfg["window"], cfg["alpha"])
-            times.append(time.perf_counter() - t0)
+        times = _timed_runs(lambda: oracle.prefill(q, k, v, gate, cfg["window"], cfg["alpha"]), min_seconds, max_runs)
     dt = sorted(times)[len(times) // 2]
     return {"value": cfg["B"] * tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{PREFILL_WORKLOAD}: first {tokens} of {cfg['T']} tokens (all heads), float64 "
-                      f"token loop, BLAS limited to 1 thread; {len(times)} runs, {sum(times):.1f} s in all, "
+            "sample": f"{name}: first {tokens} of {cfg['T']} tokens (all {cfg['B']} sequences and heads), "
+                      f"float64 token loop, BLAS limited to 1 thread; {len(times)} runs, {sum(times):.1f} s "
+                      f"in all, median {dt:.2f} s per run"}
+
+
+def cpu_baseline_decode(name: str, steps: int, min_seconds: float, max_runs: int = 20) -> dict:
+    """The float64 oracle's decode step over the first `steps` steps of the
+    decode workload (all sequences), BLAS limited to one thread; steps/s is
+    the median over repeated runs (inputs generated before the timing)."""
+    import oracle
+    from synth import CONFIGS, decode_initial, decode_step_inputs
+    from threadpoolctl import threadpool_limits
+    cfg = CONFIGS[name]
+    gate = 0 if cfg["gate"] == "scalar" else 1
+    init = decode_initial(**cfg)
+    xs = [decode_step_inputs(step=s, **cfg) for s in range(steps)]
+
+    def run():
+        S, rk, rv, pos = init["S"], init["ring_k"], init["ring_v"], init["pos"]
+        for x in xs:
+            _, S, rk, rv, pos = oracle.decode_step(x["q"], x["k"], x["v"], S, rk, rv, pos, gate, cfg["alpha"])
+
+    with threadpool_limits(limits=1):
+        times = _timed_runs(run, min_seconds, max_runs)
+    dt = sorted(times)[len(times) // 2]
+    return {"value": steps / dt, "unit": "steps/s", "tokens_per_s": cfg["N"] * steps / dt, "cores": 1,
+            "kind": "oracle",
+            "sample": f"{name}: first {steps} of {cfg['steps']} steps, all {cfg['N']} sequences, float64, "
+                      f"BLAS limited to 1 thread; {len(times)} runs, {sum(times):.1f} s in all, "
                       f"median {dt:.2f} s per run"}
+
+
+def stats(a) -> dict:
+    import numpy as np
+    return {"median_ms": float(np.median(a)), "min_ms": float(np.min(a)), "mean_ms": float(np.mean(a))}
+
+
+def measure_prefill(name: str, x: dict, steps: int, warmup: int, scrub, log_tag: str) -> dict:
+    """Cold and hot prefill steps of a named workload. Each step is two
+    enqueues on one stream (segment states + carry scan, then the output
+    kernel), bracketed by three HIP events, so the output kernel's launch
+    duration is measured on the stream it runs on. Returns the step times,
+    tokens/s at the cold median, and the roofline of the output kernel."""
+    import numpy as np
+    import torch
+
+    import gated_linear_recurrent_amd as gla
+    from synth import CONFIGS
+    cfg = CONFIGS[name]
+    dev = scrub.device
+    tdt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(tdt).contiguous() for n in ("q", "k", "v"))
+    B, T, H_q, d = q.shape
+    H_kv = k.shape[2]
+    gate = gla.LIGER_GATE_SCALAR_MEAN if cfg["gate"] == "scalar" else gla.LIGER_GATE_VECTOR_AVGPOOL4
+    o = torch.empty_like(q)
+    S_T = torch.empty((B, H_kv, d, d), dtype=torch.float32, device=dev)
+    code = gla.LIGER_BF16 if cfg["dtype"] == "bf16" else gla.LIGER_F32
+    ws = torch.empty(max(gla.liger_attn_prefill_workspace_size(B, T, H_q, H_kv, d, code), 16),
+                     dtype=torch.uint8, device=dev)
+
+    def prefill(mask):
+        gla.liger_attn_prefill(q, k, v, gate, cfg["window"], cfg["alpha"], o=o, S_T=S_T, workspace=ws,
+                               stage_mask=mask)
+
+    def timed(n: int, cold: bool):
+        """Per step: (segment states + carry scan, output kernel, total) in ms."""
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        torch.cuda.synchronize()
+        for i, e in enumerate(ev):
+            if cold:
+                scrub.fill_(float(i))
+            e[0].record()
+            prefill(gla.LIGER_STAGE_SEGMENT_STATES | gla.LIGER_STAGE_CARRY_SCAN)
+            e[1].record()
+            prefill(gla.LIGER_STAGE_OUTPUT)
+            e[2].record()
+        torch.cuda.synchronize()
+        return np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[0].elapsed_time(e[2])] for e in ev])
+
+    log(f"[bench] {log_tag}: warmup {warmup}, then {steps} cold + {steps} hot steps")
+    for _ in range(warmup):
+        prefill(7)
+    torch.cuda.synchronize()
+    cold = timed(steps, True)
+    hot = timed(steps, False)
+    ms_cold = float(np.median(cold[:, 2]))
+    byts, flops = prefill_algorithmic(cfg)
+    # the dominant kernel's average launch duration over every timed launch
+    out_ms = float(np.mean(np.concatenate([cold[:, 1], hot[:, 1]])))
+    achieved = byts / (out_ms * 1e-3) / 1e9
+    kname = OUTPUT_KERNEL_RECORD[name]
+    crec = counter_record(kname, name)
+    traffic = crec.get("hbm_bytes_per_launch")
+    peak_mfma = PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16" else PEAK_FP32_TFLOPS
+    log(f"[bench] {log_tag}: cold {ms_cold * 1e3:.1f} us/step (hot {np.median(hot[:, 2]) * 1e3:.1f}); "
+        f"output kernel {out_ms * 1e3:.1f} us ({achieved:.0f} GB/s); "
+        f"segment states + carry scan cold {np.median(cold[:, 0]) * 1e3:.1f} us")
+    return {
+        "workload": name, "B": B, "T": T, "H_q": H_q, "H_kv": H_kv, "d": d, "gate": cfg["gate"],
+        "window": cfg["window"], "alpha": cfg["alpha"], "steps": steps, "warmup": warmup,
+        "ms_per_step_cold": ms_cold,
+        "tokens_per_s": B * T / (ms_cold * 1e-3),
+        "tokens_per_s_hot": B * T / (float(np.median(hot[:, 2])) * 1e-3),
+        "cold": {"total": stats(cold[:, 2]), "segment_states_and_carry_scan": stats(cold[:, 0]),
+                 "output": stats(cold[:, 1])},
+        "hot": {"total": stats(hot[:, 2]), "segment_states_and_carry_scan": stats(hot[:, 0]),
+                "output": stats(hot[:, 1])},
+        # whole cold step against the same (HBM) roofline as the kernel below
+        "step_roofline_frac": byts / (ms_cold * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": kname, "kernel_ms": out_ms,
+                     "algorithmic_bytes": byts, "algorithmic_flops": flops,
+                     "mfma_frac_algorithmic": flops / (out_ms * 1e-3) / (peak_mfma * 1e12),
+                     "mfma_busy_frac_counters": crec.get("mfma_busy_frac"),
+                     "tcc_ea_gbs_counters": (traffic / (out_ms * 1e-3) / 1e9) if traffic else None},
+    }, (q, k, v, o, S_T, ws, gate)
 
 
 def main() -> int:
@@ -115,12 +281,14 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--decode-steps", type=int, default=512)
+    ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-full", action="store_true", help="skip the full causal attention layer")
     ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy and GEMM peaks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-prefill", action="store_true",
+                    help="skip the 1B-shaped and long-context prefill workloads")
     ap.add_argument("--cpu-baseline-tokens", type=int, default=8192)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
@@ -139,61 +307,19 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    scrub = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
     cfg = CONFIGS[PREFILL_WORKLOAD]
-    gate = gla.LIGER_GATE_SCALAR_MEAN if cfg["gate"] == "scalar" else gla.LIGER_GATE_VECTOR_AVGPOOL4
     log(f"[bench] generating {PREFILL_WORKLOAD}")
     x = config_prefill_inputs(PREFILL_WORKLOAD)
-    q, k, v = (torch.from_numpy(x[n]).to(dev).to(torch.bfloat16).contiguous() for n in ("q", "k", "v"))
+    head, bufs = measure_prefill(PREFILL_WORKLOAD, x, args.steps, args.warmup, scrub, "prefill 8B T=8192")
+    q, k, v, o, S_T, ws, gate = bufs
     B, T, H_q, d = q.shape
     H_kv = k.shape[2]
-    o = torch.empty_like(q)
-    S_T = torch.empty((B, H_kv, d, d), dtype=torch.float32, device=dev)
-    ws_bytes = gla.liger_attn_prefill_workspace_size(B, T, H_q, H_kv, d, gla.LIGER_BF16)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-
-    def prefill(mask):
-        gla.liger_attn_prefill(q, k, v, gate, cfg["window"], cfg["alpha"], o=o, S_T=S_T, workspace=ws,
-                               stage_mask=mask)
-
-    scrub = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
-
-    def timed_prefill(steps: int, cold: bool):
-        """Per step: (segment states + carry scan, output kernel, total) in ms."""
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-        torch.cuda.synchronize()
-        for i, e in enumerate(ev):
-            if cold:
-                scrub.fill_(float(i))
-            e[0].record()
-            prefill(gla.LIGER_STAGE_SEGMENT_STATES | gla.LIGER_STAGE_CARRY_SCAN)
-            e[1].record()
-            prefill(gla.LIGER_STAGE_OUTPUT)
-            e[2].record()
-        torch.cuda.synchronize()
-        return np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[0].elapsed_time(e[2])] for e in ev])
-
-    log(f"[bench] prefill warmup {args.warmup}")
-    for _ in range(args.warmup):
-        prefill(7)
-    torch.cuda.synchronize()
-    log(f"[bench] prefill timed {args.steps} cold + {args.steps} hot")
-    cold = timed_prefill(args.steps, True)
-    hot = timed_prefill(args.steps, False)
-    ms_per_step = float(np.median(cold[:, 2]))
-    tokens_per_s = B * T / (ms_per_step * 1e-3)
-    byts, flops = prefill_algorithmic(cfg)
-    # the dominant kernel's average launch duration over every timed launch
-    out_ms = float(np.mean(np.concatenate([cold[:, 1], hot[:, 1]])))
-    achieved = byts / (out_ms * 1e-3) / 1e9
-    crec = counter_record("prefill_output_kernel", PREFILL_WORKLOAD)
-    traffic = crec.get("hbm_bytes_per_launch")
-
-    def stats(a):
-        return {"median_ms": float(np.median(a)), "min_ms": float(np.min(a)), "mean_ms": float(np.mean(a))}
+    ms_per_step = head["ms_per_step_cold"]
 
     result = {
         "metric": "Liger Attention prefill tokens/s/GPU at 8B shapes; decode steps/s; % roofline",
-        "value": tokens_per_s,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -206,22 +332,25 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": PREFILL_WORKLOAD, "B": B, "T": T, "H_q": H_q, "H_kv": H_kv, "d": d,
                    "gate": cfg["gate"], "window": cfg["window"], "alpha": cfg["alpha"]},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "prefill_output_kernel", "kernel_ms": out_ms,
-                     "algorithmic_bytes": byts, "algorithmic_flops": flops,
-                     "mfma_frac_algorithmic": flops / (out_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
-                     "mfma_busy_frac_counters": crec.get("mfma_busy_frac"),
-                     "tcc_ea_gbs_counters": (traffic / (out_ms * 1e-3) / 1e9) if traffic else None},
-        "prefill_cold": {"total": stats(cold[:, 2]), "segment_states_and_carry_scan": stats(cold[:, 0]),
-                         "output": stats(cold[:, 1])},
-        "prefill_hot": {"total": stats(hot[:, 2]), "segment_states_and_carry_scan": stats(hot[:, 0]),
-                        "output": stats(hot[:, 1]), "tokens_per_s": B * T / (float(np.median(hot[:, 2])) * 1e-3)},
-        "prefill_op_roofline_frac": byts / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "roofline": dict(head["roofline"], step_frac=head["step_roofline_frac"]),
+        "prefill_cold": head["cold"],
+        "prefill_hot": dict(head["hot"], tokens_per_s=head["tokens_per_s_hot"]),
+        "prefill_op_roofline_frac": head["step_roofline_frac"],
     }
-    log(f"[bench] prefill cold {ms_per_step * 1e3:.1f} us/step (hot {np.median(hot[:, 2]) * 1e3:.1f}); "
-        f"output kernel {out_ms * 1e3:.1f} us ({achieved:.0f} GB/s); "
-        f"carries cold {np.median(cold[:, 0]) * 1e3:.1f} us")
+
+    # the other prefill workloads, each with its own roofline
+    cpu_prefix = {}  # the prefixes the CPU baseline times, kept from the same draws
+    if not args.no_other_prefill:
+        others = {}
+        for name, tag in ((PREFILL_1B_WORKLOAD, "prefill 1B B=4 T=2048"),
+                          (PREFILL_LONG_WORKLOAD, "prefill 8B T=32768 outliers")):
+            log(f"[bench] generating {name}")
+            xo = config_prefill_inputs(name)
+            others[name], _ = measure_prefill(name, xo, max(5, args.steps // 2), max(2, args.warmup // 2), scrub, tag)
+            cpu_prefix[name] = {n: np.ascontiguousarray(xo[n][:, :CPU_PREFIX_TOKENS[name]]) for n in ("q", "k", "v")}
+            del xo
+            torch.cuda.empty_cache()
+        result["prefill_other_workloads"] = others
 
     if not args.no_full:
         # the hybrid's softmax layer on the same 8B inputs (q, k, v in HBM)
@@ -426,11 +555,14 @@ def main() -> int:
             "with_sinks": {"n_sinks": N_SINKS, "kernel_us": sink_us},
             "roofline": {"bound": "hbm", "achieved": dach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": dach / PEAK_HBM_GBS, "traffic": dtraffic,
+                         "regime": "hot: back-to-back steps, the 48 MiB state + ring working set "
+                                   "stays in the 256 MB last-level cache",
                          "cold_frac": dbytes / (cold_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                         "cold_regime": "cold: median of single steps after evicting the last-level cache "
+                                        "(as in a multi-layer model, where each layer's state is evicted "
+                                        "between steps)",
                          "kernel": "decode_step_kernel", "algorithmic_bytes": dbytes,
-                         "tcc_ea_gbs_counters": (dtraffic / (k_ms * 1e-3) / 1e9) if dtraffic else None,
-                         "note": "state + ring working set (48 MiB) fits the 256 MB last-level cache; "
-                                 "cold_frac is measured after evicting it"},
+                         "tcc_ea_gbs_counters": (dtraffic / (k_ms * 1e-3) / 1e9) if dtraffic else None},
         }
         log(f"[bench] decode kernel {k_ms * 1e3:.1f} us/step ({dach:.0f} GB/s); graph {graph_us:.1f} us/step; "
             f"cold {cold_us:.1f} us; wall {dwall * 1e6 / nsteps:.1f} us/step")
@@ -486,8 +618,25 @@ def main() -> int:
         log(f"[bench] copy probe {args.copy_probe_mib} MiB x3 done")
 
     if not args.no_cpu_baseline:
+        # the oracle as it stands, on bounded samples of each workload (about
+        # 20 s of CPU work in all); GPU rates beside it for the ratio
         log("[bench] cpu baseline (float64 oracle)")
-        result["cpu_baseline"] = cpu_baseline(cfg, x, min(args.cpu_baseline_tokens, T))
+        cb = cpu_baseline_prefill(PREFILL_WORKLOAD, x, min(args.cpu_baseline_tokens, T), min_seconds=8.0)
+        cb["gpu_over_oracle"] = result["value"] / cb["value"]
+        cb["host"] = cpu_info()
+        legs = {}
+        for name in (PREFILL_1B_WORKLOAD, PREFILL_LONG_WORKLOAD):
+            xp = cpu_prefix.get(name) or config_prefill_inputs(name, T=CPU_PREFIX_TOKENS[name])
+            legs[name] = cpu_baseline_prefill(name, xp, CPU_PREFIX_TOKENS[name], min_seconds=4.0)
+        legs[DECODE_WORKLOAD] = cpu_baseline_decode(DECODE_WORKLOAD, 16, min_seconds=4.0)
+        other = result.get("prefill_other_workloads", {})
+        for name, leg in legs.items():
+            if name in other:
+                leg["gpu_over_oracle"] = other[name]["tokens_per_s"] / leg["value"]
+        if "decode" in result:
+            legs[DECODE_WORKLOAD]["gpu_over_oracle"] = result["decode"]["steps_per_s_kernel"] / legs[DECODE_WORKLOAD]["value"]
+        cb["other_workloads"] = legs
+        result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
     return 0
 
