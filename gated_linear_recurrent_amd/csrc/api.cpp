@@ -133,10 +133,12 @@ size_t liger_attn_prefill_workspace_size(const liger_shape* shape) {
 
 namespace {
 
-liger_status prefill_impl(const void* q, const void* k, const void* v, const liger_sinks* sinks, int32_t gate_mode,
-                          int32_t window, float alpha, const liger_shape* shape, void* o, float* S_T,
-                          void* workspace, size_t workspace_bytes, int32_t chunks_per_segment, int32_t stage_mask,
-                          void* stream) {
+// Checks of a prefill call that do not involve the workspace; fills `a`
+// (everything but a.workspace).
+liger_status prefill_validate(const void* q, const void* k, const void* v, const liger_sinks* sinks,
+                              int32_t gate_mode, int32_t window, float alpha, const liger_shape* shape, void* o,
+                              float* S_T, int32_t chunks_per_segment, int32_t stage_mask, void* stream,
+                              liger::PrefillArgs& a) {
     if (stage_mask < 1 || stage_mask > 7) return fail(LIGER_E_INVALID_ARG, "stage_mask must be in 1..7");
     LIGER_TRY(check_sinks(sinks));
     LIGER_TRY(check_shape(shape, true));
@@ -159,26 +161,12 @@ liger_status prefill_impl(const void* q, const void* k, const void* v, const lig
                              {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"},
                               {sinks ? sinks->k : nullptr, skb, "sinks->k"},
                               {sinks ? sinks->v : nullptr, skb, "sinks->v"}}));
-    const liger::PrefillPlan pl = liger::make_prefill_plan(shape->B, shape->T, shape->H_kv, shape->d,
-                                                           shape->dtype == LIGER_BF16, chunks_per_segment);
-    if (pl.workspace_bytes > 0) {
-        if (!workspace) return fail(LIGER_E_WORKSPACE, "workspace is NULL but " + std::to_string(pl.workspace_bytes) + " bytes are needed");
-        if (!aligned16(workspace)) return fail(LIGER_E_INVALID_ARG, "workspace is not 16-byte aligned");
-        if (workspace_bytes < pl.workspace_bytes)
-            return fail(LIGER_E_WORKSPACE, "workspace too small: " + std::to_string(workspace_bytes) + " < " +
-                                               std::to_string(pl.workspace_bytes) + " bytes");
-        LIGER_TRY(check_disjoint({{workspace, pl.workspace_bytes, "workspace"}},
-                                 {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {o, qb, "o"}, {S_T, sb, "S_T"},
-                                  {sinks ? sinks->k : nullptr, skb, "sinks->k"},
-                                  {sinks ? sinks->v : nullptr, skb, "sinks->v"}}));
-    }
-    liger::PrefillArgs a;
     a.q = q;
     a.k = k;
     a.v = v;
     a.o = o;
     a.S_T = S_T;
-    a.workspace = static_cast<float*>(workspace);
+    a.workspace = nullptr;
     a.B = shape->B;
     a.T = shape->T;
     a.H_kv = shape->H_kv;
@@ -188,7 +176,8 @@ liger_status prefill_impl(const void* q, const void* k, const void* v, const lig
     a.gate = gate_mode;
     a.bf16 = shape->dtype == LIGER_BF16;
     a.alpha = alpha;
-    a.plan = pl;
+    a.plan = liger::make_prefill_plan(shape->B, shape->T, shape->H_kv, shape->d, shape->dtype == LIGER_BF16,
+                                      chunks_per_segment);
     a.stage_mask = stage_mask;
     a.stream = stream;
     if (sinks) {
@@ -196,6 +185,34 @@ liger_status prefill_impl(const void* q, const void* k, const void* v, const lig
         a.sink_v = sinks->v;
         a.n_sink = sinks->n;
     }
+    return LIGER_OK;
+}
+
+liger_status prefill_impl(const void* q, const void* k, const void* v, const liger_sinks* sinks, int32_t gate_mode,
+                          int32_t window, float alpha, const liger_shape* shape, void* o, float* S_T,
+                          void* workspace, size_t workspace_bytes, int32_t chunks_per_segment, int32_t stage_mask,
+                          void* stream) {
+    liger::PrefillArgs a;
+    LIGER_TRY(prefill_validate(q, k, v, sinks, gate_mode, window, alpha, shape, o, S_T, chunks_per_segment,
+                               stage_mask, stream, a));
+    const liger::PrefillPlan& pl = a.plan;
+    if (pl.workspace_bytes > 0) {
+        if (!workspace) return fail(LIGER_E_WORKSPACE, "workspace is NULL but " + std::to_string(pl.workspace_bytes) + " bytes are needed");
+        if (!aligned16(workspace)) return fail(LIGER_E_INVALID_ARG, "workspace is not 16-byte aligned");
+        if (workspace_bytes < pl.workspace_bytes)
+            return fail(LIGER_E_WORKSPACE, "workspace too small: " + std::to_string(workspace_bytes) + " < " +
+                                               std::to_string(pl.workspace_bytes) + " bytes");
+        const size_t es = shape->dtype == LIGER_BF16 ? 2 : 4;
+        const size_t qb = tensor_bytes(shape->B, shape->T, shape->H_q, shape->d, es);
+        const size_t kb = tensor_bytes(shape->B, shape->T, shape->H_kv, shape->d, es);
+        const size_t sb = tensor_bytes(shape->B, shape->H_kv, shape->d, shape->d, 4);
+        const size_t skb = sinks ? tensor_bytes(shape->H_kv, sinks->n, 1, shape->d, es) : 0;
+        LIGER_TRY(check_disjoint({{workspace, pl.workspace_bytes, "workspace"}},
+                                 {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {o, qb, "o"}, {S_T, sb, "S_T"},
+                                  {sinks ? sinks->k : nullptr, skb, "sinks->k"},
+                                  {sinks ? sinks->v : nullptr, skb, "sinks->v"}}));
+    }
+    a.workspace = static_cast<float*>(workspace);
     return map_hip(liger::launch_prefill(a), "prefill launch");
 }
 
