@@ -41,6 +41,8 @@ EXPORTED = (
     "liger_attn_prefill",
     "liger_attn_prefill_ex",
     "liger_attn_prefill_stages",
+    "liger_attn_prefill_noalloc",
+    "liger_attn_prefill_noalloc_max_workspace",
     "liger_attn_prefill_continue",
     "liger_attn_decode_step",
     "liger_kv_ring_fill",
@@ -98,6 +100,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.liger_attn_prefill_ex.restype = i32
     lib.liger_attn_prefill_stages.argtypes = [vp, vp, vp, i32, i32, f32, shp, vp, vp, vp, sz, i32, i32, vp]
     lib.liger_attn_prefill_stages.restype = i32
+    lib.liger_attn_prefill_noalloc.argtypes = [vp, vp, vp, i32, i32, f32, shp, vp, vp, vp]
+    lib.liger_attn_prefill_noalloc.restype = i32
+    lib.liger_attn_prefill_noalloc_max_workspace.argtypes = []
+    lib.liger_attn_prefill_noalloc_max_workspace.restype = sz
     lib.liger_attn_prefill_continue.argtypes = [vp, vp, vp, vp, ring, i32, f32, shp, vp, vp, vp, sz, vp]
     lib.liger_attn_prefill_continue.restype = i32
     lib.liger_attn_decode_step.argtypes = [vp, vp, vp, vp, ring, i32, f32, shp, vp, vp]
@@ -216,6 +222,22 @@ def liger_attn_prefill(q, k, v, gate_mode: int, window: int, alpha: float, *, o=
                                          ctypes.byref(shp), _ptr(o), _ptr(S_T), _ptr(workspace),
                                          ws_bytes, chunks_per_segment, stage_mask, _stream(stream)))
     return o, S_T
+
+
+def liger_attn_prefill_noalloc(q, k, v, gate_mode: int, window: int, alpha: float, *, o, S_T, stream=None):
+    """liger_attn_prefill with the workspace in the library's static scratch
+    (no device allocation by the library). o and S_T are caller buffers."""
+    lib = load_library()
+    B, T, H_q, d = q.shape
+    H_kv = k.shape[2]
+    shp = make_shape(B, T, H_q, H_kv, d, _dtype_code(q))
+    _check(lib.liger_attn_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), gate_mode, window, alpha, ctypes.byref(shp),
+                                          _ptr(o), _ptr(S_T), _stream(stream)))
+    return o, S_T
+
+
+def liger_attn_prefill_noalloc_max_workspace() -> int:
+    return int(load_library().liger_attn_prefill_noalloc_max_workspace())
 
 
 @dataclass

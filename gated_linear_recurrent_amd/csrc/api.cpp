@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
@@ -109,6 +110,40 @@ liger_status check_sinks(const liger_sinks* sk) {
     if (sk->n < 1 || sk->n > 16) return fail(LIGER_E_INVALID_ARG, "sinks->n must be in 1..16");
     LIGER_TRY(check_ptr(sk->k, "sinks->k"));
     LIGER_TRY(check_ptr(sk->v, "sinks->v"));
+    return ok();
+}
+
+}  // namespace
+
+// Scratch memory of liger_attn_prefill_noalloc (the prefill workspace: carried
+// states and running-state slots), one copy on every GPU the library runs on,
+// held until the process ends. Host code never uses this name as an address:
+// it uses the per-device address from hipGetSymbolAddress below.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+liger_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return map_hip(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(LIGER_E_UNSUPPORTED, "device index beyond the scratch table");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return map_hip(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(LIGER_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return ok();
 }
 
@@ -249,6 +284,23 @@ liger_status liger_attn_prefill(const void* q, const void* k, const void* v, int
                                 size_t workspace_bytes, void* stream) {
     return liger_attn_prefill_ex(q, k, v, gate_mode, window, alpha, shape, o, S_T, workspace, workspace_bytes, 0,
                                  stream);
+}
+
+size_t liger_attn_prefill_noalloc_max_workspace(void) { return kScratchBytes; }
+
+liger_status liger_attn_prefill_noalloc(const void* q, const void* k, const void* v, int32_t gate_mode,
+                                        int32_t window, float alpha, const liger_shape* shape, void* o, float* S_T,
+                                        void* stream) {
+    liger::PrefillArgs a;
+    LIGER_TRY(prefill_validate(q, k, v, nullptr, gate_mode, window, alpha, shape, o, S_T, 0, 7, stream, a));
+    if (a.plan.workspace_bytes > kScratchBytes)
+        return fail(LIGER_E_WORKSPACE, "shape needs " + std::to_string(a.plan.workspace_bytes) +
+                                           " bytes of scratch; liger_attn_prefill_noalloc holds " +
+                                           std::to_string(kScratchBytes) + " (use liger_attn_prefill with a workspace)");
+    void* ws = nullptr;
+    LIGER_TRY(scratch_address(&ws));
+    a.workspace = static_cast<float*>(ws);
+    return map_hip(liger::launch_prefill(a), "prefill launch");
 }
 
 }  // extern "C"

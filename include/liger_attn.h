@@ -171,6 +171,31 @@ liger_status liger_attn_prefill_ex(const void* q, const void* k, const void* v,
                                    int32_t chunks_per_segment, void* stream);
 
 /*
+ * liger_attn_prefill for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and result as liger_attn_prefill, with
+ * the workspace taken from scratch memory the library holds instead of a
+ * caller buffer. The scratch is one static block of
+ * liger_attn_prefill_noalloc_max_workspace() bytes (32 MiB) on each GPU the
+ * library runs on, kept until the process ends; the call allocates and
+ * frees nothing. It runs on the current device (hipGetDevice), which must
+ * be the device of `stream`.
+ *   Shapes whose liger_attn_prefill_workspace_size exceeds that size are
+ *   rejected with LIGER_E_WORKSPACE before anything is launched.
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *   time on one GPU (different streams or threads, without ordering between
+ *   them) race and give undefined results. Calls ordered on one stream are
+ *   safe: nothing in the scratch needs to start at zero and every byte read
+ *   is written earlier in the same call.
+ * Other arguments, layouts and errors as for liger_attn_prefill.
+ */
+size_t liger_attn_prefill_noalloc_max_workspace(void);
+liger_status liger_attn_prefill_noalloc(const void* q, const void* k, const void* v,
+                                        int32_t gate_mode, int32_t window, float alpha,
+                                        const liger_shape* shape, void* o, float* S_T,
+                                        void* stream);
+
+/*
  * Defined by: the same sections as liger_attn_prefill (a profiling
  * extension of that call: it computes nothing else).
  * Profiling aid: enqueue only the prefill kernels chosen by stage_mask, in

@@ -367,3 +367,20 @@ def test_backward_workspace_size(lib):
     want = 4 * (2 * 2 * 2 * (n - 1) * (64 * 64 + 64) + 2 * 2 * 130 * 64 + 2 * 2 * n * 64 + 2 * 130 * 8 * 2)
     assert lib.liger_attn_prefill_backward_workspace_size(ctypes.byref(shp)) == want
     assert lib.liger_attn_prefill_backward_workspace_size(ctypes.byref(_shape(T=0))) == 0
+
+
+def test_noalloc_limit_and_rejection(lib):
+    """The allocation-free prefill states its scratch size and refuses larger
+    shapes (and invalid ones) before any HIP call."""
+    assert lib.liger_attn_prefill_noalloc_max_workspace() == 32 << 20
+    big = _shape(B=65, T=64, H_q=32, H_kv=8)
+    assert lib.liger_attn_prefill_workspace_size(ctypes.byref(big)) > 32 << 20
+    st = lib.liger_attn_prefill_noalloc(FAKE, FAKE + G, FAKE + 2 * G, 0, 64, 0.5, ctypes.byref(big),
+                                        FAKE + 3 * G, FAKE + 4 * G, None)
+    assert st == gla.LIGER_E_WORKSPACE and "32 MiB" not in gla.liger_last_error()
+    assert str(32 << 20) in gla.liger_last_error()
+    st = lib.liger_attn_prefill_noalloc(FAKE, FAKE, FAKE, 0, 64, 0.5, ctypes.byref(_shape()), FAKE, FAKE + G, None)
+    assert st == gla.LIGER_E_INVALID_ARG  # o aliases q
+    st = lib.liger_attn_prefill_noalloc(FAKE, FAKE, FAKE, 0, 0, 0.5, ctypes.byref(_shape()), FAKE + G, FAKE + 2 * G,
+                                        None)
+    assert st == gla.LIGER_E_INVALID_ARG  # window 0
