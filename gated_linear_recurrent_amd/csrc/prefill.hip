@@ -750,19 +750,17 @@ __device__ __forceinline__ void intra_key_operand(const Smem<T, D, GATE, FULL>& 
 template <typename T, int D>
 struct SegLayout {
     static constexpr int E = sizeof(T);
-    static constexpr int TB = E == 2 ? 256 : 128;      // tokens per block
+    static constexpr int TB = 128;                     // tokens per block
     static constexpr int P = D + 16;                   // row pitch (elements) of the K and V tiles
     static constexpr int VPL = 16 / E;                 // elements per 16-byte piece
     static constexpr int PPR = D / VPL;                // pieces per row
     static constexpr int NPT = TB * PPR / kPThreads;   // K (and V) pieces per thread
     static_assert(NPT * kPThreads == TB * PPR, "pieces per thread");
-    static constexpr int NPART = kPThreads / D;        // vector gate: token ranges per channel
-    static constexpr int TPP = TB / NPART;             // tokens per range
     static constexpr size_t K_OFF = 0;
     static constexpr size_t V_OFF = K_OFF + size_t(TB) * P * E;
     static constexpr size_t F_OFF = V_OFF + size_t(TB) * P * E;
-    // fp32: kmax[TB] kinv[TB] ell[TB] part[kPThreads] tot[D] lg[D]
-    static constexpr size_t TOTAL = F_OFF + (3 * size_t(TB) + kPThreads + 2 * D) * 4;
+    // fp32: kmax[TB] kinv[TB] ell[TB] tot[D] lg[D]
+    static constexpr size_t TOTAL = F_OFF + (3 * size_t(TB) + 2 * D) * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS budget of a gfx950 workgroup exceeded");
 };
 
@@ -780,8 +778,7 @@ __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams 
     float* kmax = reinterpret_cast<float*>(smem + SL::F_OFF);
     float* kinv = kmax + SL::TB;
     float* ell = kinv + SL::TB;     // scalar gate: log2 gate per token, then the sum after it
-    float* part = ell + SL::TB;     // vector gate: gate sums per (token range, channel)
-    float* tot = part + kPThreads;  // log2 decay of the whole block per channel
+    float* tot = ell + SL::TB;      // log2 decay of the whole block per channel
     float* lg = tot + D;            // log2 decay of the segment so far per channel
 
     const int s = blockIdx.x;
@@ -956,35 +953,78 @@ __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams 
                 }
             }
             __syncthreads();
-            // thread (c, range): channel c, tokens range*TPP .. +TPP-1; x_j[c] is
-            // the mean of k_j over the in-range channels c-1 .. c+2
-            const int c = ltid() % D;
-            const int rg = ltid() / D;
-            const int lo = c > 0 ? c - 1 : 0;
-            const int hi = c + 3 < D ? c + 3 : D;
-            const float inv_cnt = 1.0f / static_cast<float>(hi - lo);
-            float l[SL::TPP];
-            float own = 0.f;
+            // Piece layout: the LPP lanes of a group share one 16-byte channel
+            // piece (channels c0 .. c0 + VPL - 1); lane l owns tokens TPL l ..
+            // TPL l + TPL - 1. The pooled input x_j[c] is the mean of k_j over
+            // the in-range channels c-1 .. c+2, formed from the piece and its
+            // three neighbouring elements (one before, two after).
+            constexpr int TPL = SL::TB * SL::PPR / kPThreads;  // tokens per lane
+            constexpr int LPP = SL::TB / TPL;                    // lanes per piece
+            static_assert(LPP == 32 || LPP == 64, "a piece spans half a wave or a whole wave");
+            constexpr int VPL = SL::VPL;
+            const int tid = ltid();
+            const int c0 = (tid / LPP) * VPL;
+            const int l = tid % LPP;
+            float lg2[TPL][VPL];  // log2 gate per (token, channel)
 #pragma unroll
-            for (int jj = 0; jj < SL::TPP; ++jj) {
-                const int j = rg * SL::TPP + jj;
-                float x = 0.f;
-                for (int m = lo; m < hi; ++m) x += to_f32(Ks[j * SL::P + m]);
-                l[jj] = j < nb ? log2_sigmoid(x * inv_cnt) : 0.0f;
-                own += l[jj];
-            }
-            part[rg * D + c] = own;
-            __syncthreads();  // every pooled read is done before K is overwritten
-            float run = 0.f;
-            for (int r = rg + 1; r < SL::NPART; ++r) run += part[r * D + c];
+            for (int t = 0; t < TPL; ++t) {
+                const int j = TPL * l + t;
+                const T* row = Ks + j * SL::P;
+                const uint4 u = *reinterpret_cast<const uint4*>(row + c0);
+                const T* pe = reinterpret_cast<const T*>(&u);
+                float e[VPL + 3];  // channels c0 - 1 .. c0 + VPL + 1, zero outside the row
+                e[0] = c0 > 0 ? to_f32(row[c0 - 1]) : 0.0f;
 #pragma unroll
-            for (int jj = SL::TPP - 1; jj >= 0; --jj) {
-                const int j = rg * SL::TPP + jj;
-                T* e = Ks + j * SL::P + c;
-                *e = from_f32<T>(kinv[j] * fast_exp2((to_f32(*e) - kmax[j]) * kLog2e + run));
-                run += l[jj];
+                for (int i = 0; i < VPL; ++i) e[i + 1] = to_f32(pe[i]);
+                e[VPL + 1] = c0 + VPL < D ? to_f32(row[c0 + VPL]) : 0.0f;
+                e[VPL + 2] = c0 + VPL < D ? to_f32(row[c0 + VPL + 1]) : 0.0f;
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const int c = c0 + i;
+                    const float inv_cnt = (c == 0 || c == D - 2) ? (1.0f / 3.0f) : c == D - 1 ? 0.5f : 0.25f;
+                    const float x = (e[i] + e[i + 1]) + (e[i + 2] + e[i + 3]);
+                    lg2[t][i] = j < nb ? log2_sigmoid(x * inv_cnt) : 0.0f;
+                }
             }
-            if (rg == 0) tot[c] = run;
+            // sum of the gates after each token within the block: this lane's
+            // tokens, then the lanes after it (inclusive suffix over the group)
+            float after[VPL];
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                float own = 0.f;
+#pragma unroll
+                for (int t = 0; t < TPL; ++t) own += lg2[t][i];
+                float incl = own;
+#pragma unroll
+                for (int o = 1; o < LPP; o <<= 1) {
+                    const float y = __shfl_down(incl, o, LPP);
+                    if (l + o < LPP) incl += y;
+                }
+                after[i] = incl - own;
+                if (l == 0) tot[c0 + i] = incl;
+            }
+            __syncthreads();  // every pooled read of a neighbouring piece is done before K is overwritten
+            // key operand in place: phik_j (.) 2^(sum of the gates after j)
+#pragma unroll
+            for (int t = TPL - 1; t >= 0; --t) {
+                const int j = TPL * l + t;
+                T* row = Ks + j * SL::P + c0;
+                const uint4 u = *reinterpret_cast<const uint4*>(row);
+                const T* pe = reinterpret_cast<const T*>(&u);
+                const float m = kmax[j] * kLog2e, s = kinv[j];
+                float y[VPL];
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    y[i] = s * fast_exp2(fmaf(to_f32(pe[i]), kLog2e, after[i] - m));
+                    after[i] += lg2[t][i];
+                }
+                if constexpr (sizeof(T) == 2) {
+                    *reinterpret_cast<uint4*>(row) = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                                                                pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+                } else {
+                    *reinterpret_cast<float4*>(row) = make_float4(y[0], y[1], y[2], y[3]);
+                }
+            }
             __syncthreads();
         }
 
