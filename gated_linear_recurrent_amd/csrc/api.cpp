@@ -73,6 +73,13 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y ? y - x < na : x - y < nb;
 }
 
+// A shape whose buffers could not exist: some byte count saturated.
+liger_status check_sizes(std::initializer_list<size_t> sizes) {
+    for (const size_t n : sizes)
+        if (n == SIZE_MAX) return fail(LIGER_E_INVALID_ARG, "shape too large: a buffer size overflows");
+    return LIGER_OK;
+}
+
 struct Span {
     const void* p;
     size_t n;
@@ -157,7 +164,7 @@ size_t liger_attn_prefill_workspace_size_ex(const liger_shape* shape, int32_t ch
     if (check_shape(shape, true) != LIGER_OK || chunks_per_segment < 0) return 0;
     const liger::PrefillPlan pl = liger::make_prefill_plan(shape->B, shape->T, shape->H_kv, shape->d,
                                                            shape->dtype == LIGER_BF16, chunks_per_segment);
-    return pl.workspace_bytes;
+    return pl.workspace_bytes == SIZE_MAX ? 0 : pl.workspace_bytes;
 }
 
 size_t liger_attn_prefill_workspace_size(const liger_shape* shape) {
@@ -192,6 +199,7 @@ liger_status prefill_validate(const void* q, const void* k, const void* v, const
     const size_t kb = tensor_bytes(shape->B, shape->T, shape->H_kv, shape->d, es);
     const size_t sb = tensor_bytes(shape->B, shape->H_kv, shape->d, shape->d, 4);
     const size_t skb = sinks ? tensor_bytes(shape->H_kv, sinks->n, 1, shape->d, es) : 0;
+    LIGER_TRY(check_sizes({qb, kb, sb, skb}));
     LIGER_TRY(check_disjoint({{o, qb, "o"}, {S_T, sb, "S_T"}},
                              {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"},
                               {sinks ? sinks->k : nullptr, skb, "sinks->k"},
@@ -213,6 +221,7 @@ liger_status prefill_validate(const void* q, const void* k, const void* v, const
     a.alpha = alpha;
     a.plan = liger::make_prefill_plan(shape->B, shape->T, shape->H_kv, shape->d, shape->dtype == LIGER_BF16,
                                       chunks_per_segment);
+    LIGER_TRY(check_sizes({a.plan.workspace_bytes}));
     a.stage_mask = stage_mask;
     a.stream = stream;
     if (sinks) {
@@ -337,6 +346,7 @@ liger_status continue_impl(const void* q, const void* k, const void* v, const fl
     const size_t pb = tensor_bytes(shape->B, 1, 1, 1, 8);
     const size_t cb = tensor_bytes(shape->B, 1, 1, 1, 4);
     const size_t skb = sinks ? tensor_bytes(shape->H_kv, sinks->n, 1, shape->d, es) : 0;
+    LIGER_TRY(check_sizes({qb, kb, sb, rb, pb, cb, skb}));
     // written: o, S_T and the ring (k, v, pos, sync are updated in place)
     LIGER_TRY(check_disjoint({{o, qb, "o"}, {S_T, sb, "S_T"}, {kv_ring->k, rb, "kv_ring->k"},
                               {kv_ring->v, rb, "kv_ring->v"}, {kv_ring->pos, pb, "kv_ring->pos"},
@@ -346,6 +356,7 @@ liger_status continue_impl(const void* q, const void* k, const void* v, const fl
                               {sinks ? sinks->v : nullptr, skb, "sinks->v"}}));
     const liger::PrefillPlan pl = liger::make_prefill_plan(shape->B, shape->T, shape->H_kv, shape->d,
                                                            shape->dtype == LIGER_BF16, 0);
+    LIGER_TRY(check_sizes({pl.workspace_bytes}));
     if (pl.workspace_bytes > 0) {
         if (!workspace) return fail(LIGER_E_WORKSPACE, "workspace is NULL but " + std::to_string(pl.workspace_bytes) + " bytes are needed");
         if (!aligned16(workspace)) return fail(LIGER_E_INVALID_ARG, "workspace is not 16-byte aligned");
@@ -460,6 +471,7 @@ liger_status decode_impl(const void* q, const void* k, const void* v, float* S, 
         const size_t pb = tensor_bytes(shape->B, 1, 1, 1, 8);
         const size_t cb = tensor_bytes(shape->B, 1, 1, 1, 4);
         const size_t skb = sinks ? tensor_bytes(shape->H_kv, sinks->n, 1, shape->d, es) : 0;
+        LIGER_TRY(check_sizes({qb, kb, sb, rb, pb, cb, skb}));
         LIGER_TRY(check_disjoint({{o, qb, "o"}, {S, sb, "S"}, {kv_ring->k, rb, "kv_ring->k"},
                                   {kv_ring->v, rb, "kv_ring->v"}, {kv_ring->pos, pb, "kv_ring->pos"},
                                   {kv_ring->sync, cb, "kv_ring->sync"}},
@@ -526,6 +538,7 @@ liger_status liger_attn_full_causal(const void* q, const void* k, const void* v,
     {
         const size_t qb = tensor_bytes(shape->B, shape->T, shape->H_q, shape->d, 2);
         const size_t kb = tensor_bytes(shape->B, shape->T, shape->H_kv, shape->d, 2);
+        LIGER_TRY(check_sizes({qb, kb}));
         LIGER_TRY(check_disjoint({{o, qb, "o"}}, {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}}));
     }
     liger::FullAttnArgs a;
@@ -545,7 +558,8 @@ liger_status liger_attn_full_causal(const void* q, const void* k, const void* v,
 
 size_t liger_attn_prefill_backward_workspace_size(const liger_shape* shape) {
     if (check_shape(shape, true) != LIGER_OK) return 0;
-    return liger::backward_workspace_bytes(shape->B, shape->T, shape->H_kv, shape->H_q, shape->d);
+    const size_t n = liger::backward_workspace_bytes(shape->B, shape->T, shape->H_kv, shape->H_q, shape->d);
+    return n == SIZE_MAX ? 0 : n;
 }
 
 liger_status liger_attn_prefill_backward(const void* q, const void* k, const void* v, const void* dO,
@@ -564,6 +578,7 @@ liger_status liger_attn_prefill_backward(const void* q, const void* k, const voi
     LIGER_TRY(check_ptr(dk, "dk"));
     LIGER_TRY(check_ptr(dv, "dv"));
     const size_t need = liger::backward_workspace_bytes(shape->B, shape->T, shape->H_kv, shape->H_q, shape->d);
+    LIGER_TRY(check_sizes({need}));
     if (workspace_bytes < need) return fail(LIGER_E_WORKSPACE, "workspace smaller than liger_attn_prefill_backward_workspace_size");
     if (need > 0) LIGER_TRY(check_ptr(workspace, "workspace"));
     {
@@ -571,6 +586,7 @@ liger_status liger_attn_prefill_backward(const void* q, const void* k, const voi
         const size_t kb = tensor_bytes(shape->B, shape->T, shape->H_kv, shape->d, 2);
         const size_t gqb = tensor_bytes(shape->B, shape->T, shape->H_q, shape->d, 4);
         const size_t gkb = tensor_bytes(shape->B, shape->T, shape->H_kv, shape->d, 4);
+        LIGER_TRY(check_sizes({qb, kb, gqb, gkb}));
         LIGER_TRY(check_disjoint({{dq, gqb, "dq"}, {dk, gkb, "dk"}, {dv, gkb, "dv"}, {workspace, need, "workspace"}},
                                  {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {dO, qb, "dO"}}));
     }
@@ -612,6 +628,7 @@ liger_status liger_kv_ring_fill(const void* k, const void* v, const liger_shape*
         const size_t rb = tensor_bytes(shape->B, shape->H_kv, kv_ring->window, shape->d, es);
         const size_t pb = tensor_bytes(shape->B, 1, 1, 1, 8);
         const size_t cb = tensor_bytes(shape->B, 1, 1, 1, 4);
+        LIGER_TRY(check_sizes({kb, rb, pb, cb}));
         LIGER_TRY(check_disjoint({{kv_ring->k, rb, "kv_ring->k"}, {kv_ring->v, rb, "kv_ring->v"},
                                   {kv_ring->pos, pb, "kv_ring->pos"}, {kv_ring->sync, cb, "kv_ring->sync"}},
                                  {{k, kb, "k"}, {v, kb, "v"}}));

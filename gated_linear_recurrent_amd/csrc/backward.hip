@@ -1428,15 +1428,6 @@ hipError_t launch_bwd_t(const BackwardArgs& a) {
 
 }  // namespace
 
-size_t backward_workspace_bytes(int64_t B, int64_t T, int H_kv, int H_q, int d) {
-    if (T <= 0) return 0;
-    const int64_t n = (T + 63) / 64;
-    const size_t rec = size_t(d) * d + d;
-    const size_t floats = 2 * size_t(B) * H_kv * size_t(n - 1) * rec + size_t(B) * H_kv * T * d +
-                          size_t(B) * H_kv * n * d + size_t(B) * T * H_q * 2;
-    return floats * sizeof(float);
-}
-
 hipError_t launch_backward(const BackwardArgs& a) {
     if (a.T == 0 || a.B == 0) return hipSuccess;
     if (a.d == 64) return a.gate ? launch_bwd_t<64, 1>(a) : launch_bwd_t<64, 0>(a);

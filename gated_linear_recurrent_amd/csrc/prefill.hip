@@ -1810,29 +1810,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
 }
 
 // ------------------------------------------------------------------ host side
-PrefillPlan make_prefill_plan(int64_t B, int64_t T, int H_kv, int d, bool bf16, int64_t chunks_per_segment) {
-    PrefillPlan pl;
-    pl.n_chunks = (T + kChunk - 1) / kChunk;
-    int64_t cps = chunks_per_segment;
-    if (cps <= 0) {
-        // One output workgroup per compute unit (two when the LDS footprint allows).
-        const int64_t per_cu = (bf16 && d == 64) ? 2 : 1;
-        const int64_t target = 256 * per_cu;
-        const int64_t heads = B * H_kv;
-        int64_t want_seg = (target + heads - 1) / heads;
-        if (want_seg < 1) want_seg = 1;
-        cps = (pl.n_chunks + want_seg - 1) / want_seg;
-        if (cps < 2) cps = 2;
-    }
-    if (cps > pl.n_chunks) cps = pl.n_chunks;
-    pl.cps = cps;
-    pl.n_seg = (pl.n_chunks + cps - 1) / cps;
-    pl.carry_floats = size_t(d) * d + d;
-    pl.state_offset = size_t(B) * H_kv * size_t(pl.n_seg - 1) * pl.carry_floats;
-    pl.workspace_bytes = (pl.state_offset + size_t(B) * H_kv * size_t(pl.n_seg) * d * d) * sizeof(float);
-    return pl;
-}
-
 template <typename T, int D, int GATE>
 static hipError_t launch_prefill_t(const PrefillArgs& a) {
     PrefillParams p;
