@@ -5,9 +5,11 @@ A step is one prefill of the Llama-3-8B-shaped workload
 (B=1, T=8192, H_q=32, H_kv=8, d=128, bf16, scalar gate, window 64,
 alpha 0.5) with its inputs already resident in device memory. Each timed
 step is bracketed by HIP events on the stream the kernels run on; before
-each one an untimed 512 MiB write evicts the 256 MB last-level cache, so
-the inputs come from HBM ("cold", the headline `value`, median step). The
-same steps without the eviction are reported as "hot". The JSON line also
+each one an untimed 1 GiB read evicts the step's data from the 256 MB
+last-level cache, so the inputs come from HBM ("cold", the headline
+`value`, median step). The same steps without the eviction are reported as
+"hot", and steps after a 512 MiB write instead (whose dirty lines are
+written back during the step) as "cold_write_evicted". The JSON line also
 carries:
   - the roofline of the dominant kernel (the fused output kernel) and the
     whole cold step's fraction of the same roofline;
@@ -55,6 +57,7 @@ SINK_SEED = 17  # the softmax layer on the prefill workload's inputs
 BWD_SEED = 23   # upstream gradient of the backward measurement
 CHUNK = 64
 SCRUB_BYTES = 512 << 20        # larger than the 256 MB last-level cache
+READ_EVICT_BYTES = 1 << 30     # read through before each cold step
 # tokens of each other prefill workload that the CPU baseline times (a prefix:
 # the oracle is linear in T, so the prefix rate is the workload's rate)
 CPU_PREFIX_TOKENS = {PREFILL_1B_WORKLOAD: 512, PREFILL_LONG_WORKLOAD: 1024}
@@ -188,6 +191,31 @@ def cpu_baseline_decode(name: str, steps: int, min_seconds: float, max_runs: int
                       f"median {dt:.2f} s per run"}
 
 
+class Evictor:
+    """Empties the 256 MB last-level cache of the step's data before a cold step.
+
+    "read" (the default, used for every cold figure): sums a 1 GiB buffer, so
+    the cache is left holding clean lines of that buffer and the step's
+    inputs come from HBM. "write": fills a 512 MiB buffer, so the cache is left
+    full of dirty lines whose write-back to HBM then competes with the step;
+    reported beside the read-evicted figures for the prefill and decode
+    workloads, labelled."""
+
+    def __init__(self, dev):
+        import torch
+        self.rbuf = torch.ones(READ_EVICT_BYTES // 4, dtype=torch.float32, device=dev)
+        self.acc = torch.zeros((), dtype=torch.float32, device=dev)
+        self.wbuf = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
+        self.device = dev
+
+    def __call__(self, i: int, kind: str = "read"):
+        import torch
+        if kind == "read":
+            torch.sum(self.rbuf, dim=(0,), out=self.acc)
+        else:
+            self.wbuf.fill_(float(i))
+
+
 def stats(a) -> dict:
     import numpy as np
     return {"median_ms": float(np.median(a)), "min_ms": float(np.min(a)), "mean_ms": float(np.mean(a))}
@@ -221,13 +249,13 @@ def measure_prefill(name: str, x: dict, steps: int, warmup: int, scrub, log_tag:
         gla.liger_attn_prefill(q, k, v, gate, cfg["window"], cfg["alpha"], o=o, S_T=S_T, workspace=ws,
                                stage_mask=mask)
 
-    def timed(n: int, cold: bool):
+    def timed(n: int, cold, kind: str = "read"):
         """Per step: (segment states + carry scan, output kernel, total) in ms."""
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
         torch.cuda.synchronize()
         for i, e in enumerate(ev):
             if cold:
-                scrub.fill_(float(i))
+                scrub(i, kind)
             e[0].record()
             prefill(gla.LIGER_STAGE_SEGMENT_STATES | gla.LIGER_STAGE_CARRY_SCAN)
             e[1].record()
@@ -242,6 +270,7 @@ def measure_prefill(name: str, x: dict, steps: int, warmup: int, scrub, log_tag:
     torch.cuda.synchronize()
     cold = timed(steps, True)
     hot = timed(steps, False)
+    cold_w = timed(max(5, steps // 2), True, "write")
     ms_cold = float(np.median(cold[:, 2]))
     byts, flops = prefill_algorithmic(cfg)
     # the dominant kernel's average launch duration over every timed launch
@@ -264,6 +293,9 @@ def measure_prefill(name: str, x: dict, steps: int, warmup: int, scrub, log_tag:
                  "output": stats(cold[:, 1])},
         "hot": {"total": stats(hot[:, 2]), "segment_states_and_carry_scan": stats(hot[:, 0]),
                 "output": stats(hot[:, 1])},
+        "cold_write_evicted": {"total": stats(cold_w[:, 2]), "output": stats(cold_w[:, 1]),
+                               "note": "cache emptied by a 512 MiB write: its dirty lines are written back "
+                                       "during the step"},
         # whole cold step against the same (HBM) roofline as the kernel below
         "step_roofline_frac": byts / (ms_cold * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -307,7 +339,7 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    scrub = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
+    scrub = Evictor(dev)
     cfg = CONFIGS[PREFILL_WORKLOAD]
     log(f"[bench] generating {PREFILL_WORKLOAD}")
     x = config_prefill_inputs(PREFILL_WORKLOAD)
@@ -364,7 +396,7 @@ def main() -> int:
             ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nfull)]
             for i, (e0, e1) in enumerate(ev):
                 if cold_steps:
-                    scrub.fill_(float(i))
+                    scrub(i)
                 e0.record()
                 gla.liger_attn_full_causal(q, k, v, o=fo)
                 e1.record()
@@ -404,7 +436,7 @@ def main() -> int:
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         for i, (e0, e1) in enumerate(ev):
             if cold_steps:
-                scrub.fill_(float(i))
+                scrub(i)
             e0.record()
             prefill_sinks()
             e1.record()
@@ -439,7 +471,7 @@ def main() -> int:
             ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nb)]
             for i, (e0, e1) in enumerate(ev):
                 if cold_steps:
-                    scrub.fill_(float(i))
+                    scrub(i)
                 e0.record()
                 backward()
                 e1.record()
@@ -518,16 +550,24 @@ def main() -> int:
         g1.record()
         torch.cuda.synchronize()
         graph_us = g0.elapsed_time(g1) * 1e3 / (reps * glen)
-        # cold steps: the last-level cache is evicted before each one
+        # cold steps: the last-level cache is evicted before each one (read
+        # eviction; write eviction reported beside it), each step between its
+        # own pair of events like per_launch_events_us
         ncold = min(32, nsteps)
-        cold_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ncold)]
-        for s in range(ncold):
-            scrub.fill_(float(s))
-            cold_ev[s][0].record()
-            dstep(s)
-            cold_ev[s][1].record()
-        torch.cuda.synchronize()
-        cold_us = float(np.median([a.elapsed_time(b) for a, b in cold_ev])) * 1e3
+
+        def timed_cold(kind: str) -> float:
+            cold_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(ncold)]
+            for s in range(ncold):
+                scrub(s, kind)
+                cold_ev[s][0].record()
+                dstep(s)
+                cold_ev[s][1].record()
+            torch.cuda.synchronize()
+            return float(np.median([a.elapsed_time(b) for a, b in cold_ev])) * 1e3
+
+        cold_us = timed_cold("read")
+        cold_w_us = timed_cold("write")
         # the same steps with meta-memory sink tokens, back to back
         rng = np.random.default_rng(SINK_SEED + 1)
         dsinks = tuple(torch.from_numpy(rng.standard_normal((Hkv, N_SINKS, dd)).astype(np.float32)).to(dev)
@@ -552,20 +592,24 @@ def main() -> int:
             "steps_per_s_kernel": 1e3 / k_ms, "tokens_per_s_kernel": N * 1e3 / k_ms,
             "graph_us_per_step": graph_us, "graph_steps_per_s": 1e6 / graph_us,
             "cold_kernel_us_median": cold_us,
+            "cold_write_evicted_us_median": cold_w_us,
             "with_sinks": {"n_sinks": N_SINKS, "kernel_us": sink_us},
             "roofline": {"bound": "hbm", "achieved": dach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": dach / PEAK_HBM_GBS, "traffic": dtraffic,
                          "regime": "hot: back-to-back steps, the 48 MiB state + ring working set "
                                    "stays in the 256 MB last-level cache",
                          "cold_frac": dbytes / (cold_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                         "cold_regime": "cold: median of single steps after evicting the last-level cache "
-                                        "(as in a multi-layer model, where each layer's state is evicted "
-                                        "between steps)",
+                         "cold_regime": "cold: median of single steps, each between its own events (which add "
+                                        "about what per_launch_events_us adds to kernel_us), after evicting the "
+                                        "last-level cache with a 1 GiB read (as in a multi-layer model, where "
+                                        "each layer's state is evicted between steps); after a 512 MiB write "
+                                        "instead, the dirty lines' write-back adds to the step: "
+                                        "cold_write_evicted_us_median",
                          "kernel": "decode_step_kernel", "algorithmic_bytes": dbytes,
                          "tcc_ea_gbs_counters": (dtraffic / (k_ms * 1e-3) / 1e9) if dtraffic else None},
         }
         log(f"[bench] decode kernel {k_ms * 1e3:.1f} us/step ({dach:.0f} GB/s); graph {graph_us:.1f} us/step; "
-            f"cold {cold_us:.1f} us; wall {dwall * 1e6 / nsteps:.1f} us/step")
+            f"cold {cold_us:.1f} us (write-evicted {cold_w_us:.1f}); wall {dwall * 1e6 / nsteps:.1f} us/step")
 
     if not args.no_peaks:
         # what the box reaches with plain library work, next to the datasheet peaks:
