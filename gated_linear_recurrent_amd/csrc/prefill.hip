@@ -435,8 +435,6 @@ __device__ __forceinline__ void vector_gate_scan(const Smem<T, D, GATE, FULL>& s
 }
 
 // ------------------------------------------------------------ state update
-// Wave w owns TPW 16x16 tiles (rt, t) of the d x d state, held in fp32
-// accumulators: acc[u][r] = S[16 rt + 4 (L>>4) + r][16 t + (L&15)].
 template <int D>
 struct StateTiles {
     static constexpr int NTT = D / 16;
@@ -1150,6 +1148,35 @@ struct QFrags {
     typename Mfma<T>::frag f[2][D / Mfma<T>::KSTEP];
 };
 
+// The output block a wave computes after the current one: the next item of
+// this chunk, else the wave's first item of the next chunk. Its query
+// fragments are loaded as soon as the current block's are no longer needed,
+// so the load overlaps the rest of the current block and the chunk phases
+// in between.
+struct QNext {
+    int64_t row0;  // b * T + t0 of that block's chunk
+    int hq;
+    int pair;      // 0: query tiles (0, 3), 1: (1, 2)
+    int nvalid;
+    bool any;      // false: this wave has no further block
+};
+
+// Next block of a wave that is on item `it` of chunk `c` (chunks end at c_end).
+__device__ __forceinline__ QNext next_block(int it, int wave, int n_items, int n_rep, int h, int64_t b, int64_t T,
+                                            int64_t c, int64_t c_end) {
+    QNext nx;
+    const bool same = it + kPWaves < n_items;
+    const int itn = same ? it + kPWaves : wave;
+    const int64_t cn = same ? c : c + 1;
+    const int64_t tn = cn * kChunk;
+    nx.any = cn < c_end;
+    nx.row0 = b * T + tn;
+    nx.nvalid = T - tn < kChunk ? int(T - tn) : kChunk;
+    nx.hq = h * n_rep + itn % n_rep;
+    nx.pair = itn / n_rep;
+    return nx;
+}
+
 template <typename T, int D>
 __device__ __forceinline__ void load_q_block(QFrags<T, D>& qf, const T* q, int64_t row0, int H_q, int hq, int qa,
                                              int qb, int nvalid, int lane) {
@@ -1200,7 +1227,7 @@ __device__ __forceinline__ typename Mfma<T>::frag resident_frag(const Smem<T, D,
 
 template <typename T, int D, int GATE, int QA, int QB, bool SINK>
 __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, const ItemCtx<T, D, GATE>& x,
-                                             int lane, const QFrags<T, D>& qin) {
+                                             int lane, QFrags<T, D>& qin, const QNext& nx) {
     typedef Layout<T, D, GATE, true> L;
     typedef Mfma<T> M;
     typedef typename M::frag Frag;
@@ -1418,12 +1445,19 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
         }
         qinv[s] = (GATE ? 1.0f : x.alpha) * fast_rcp(group4_sum(sum));
     }
+    // the raw query fragments are dead: load the next block's into them
+    if (nx.any)
+        load_q_block<T, D>(qin, x.q, nx.row0, x.H_q, nx.hq, nx.pair == 0 ? 0 : 1, nx.pair == 0 ? 3 : 2, nx.nvalid, lane);
 
     // ---- intra-chunk scores on key tiles J = 0 .. I (query tile I), added into the same
     // per-key-tile operand. Tiles below the diagonal are whole; the diagonal
     // tile keeps j <= i. Scalar gate: the decay 2^(b_i - b_j) is split into
     // 2^(b_i - m) (here) and 2^(m - b_j) (in the key operand), or applied per
     // pair when the chunk's decay range is too wide to split.
+    // The two waves sharing a SIMD run blocks (0, 3) and (1, 2); the younger
+    // one, on (1, 2), loses issue arbitration and would finish alone, so it
+    // takes a higher issue priority from here to the end of the block.
+    if (QA == 1) __builtin_amdgcn_s_setprio(1);
     float bq[2] = {0.f, 0.f};
     float qsc[2];
     float4 bk[KTMAX + 1];
@@ -1653,12 +1687,22 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
         load_ring_issue<T, D>(cp, static_cast<const T*>(p.ring_k) + (size_t(b) * p.H_kv + h) * p.window * D,
                               static_cast<const T*>(p.ring_v) + (size_t(b) * p.H_kv + h) * p.window * D, pos_b,
                               p.window, npv0);
+    const int n_items = p.n_rep * 2;
+    // query fragments of this wave's first output block (resident state:
+    // each output block loads the next one's)
+    QFrags<T, D> qpre;
+    if (L::SLDS && wave < n_items) {
+        const int pair = wave / p.n_rep;
+        const int64_t t0 = c_begin * kChunk;
+        load_q_block<T, D>(qpre, static_cast<const T*>(p.q), b * p.T + t0, H_q, h * p.n_rep + (wave % p.n_rep),
+                           pair == 0 ? 0 : 1, pair == 0 ? 3 : 2, p.T - t0 < kChunk ? int(p.T - t0) : kChunk,
+                           threadIdx.x & 63);
+    }
     f32x4_t acc[StateTiles<D>::TPW];
     if constexpr (L::SLDS) load_state<D>(carry_in, acc);
     if (c_begin > 0 || npv0 > 0) load_chunk_commit(sm, int((c_begin + 1) & 1), cp);
     else zero_slot(sm, int((c_begin + 1) & 1));
     load_chunk_commit(sm, int(c_begin & 1), cr);
-    const int n_items = p.n_rep * 2;
     if constexpr (L::SLDS) {
         // Resident state: per chunk, gate statistics and the intra operand,
         // then the outputs (inter term from S entering the chunk), then the
@@ -1669,21 +1713,16 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
             const int cur = int(c & 1);
             const int64_t t0 = c * kChunk;
             const int nvalid = p.T - t0 < kChunk ? int(p.T - t0) : kChunk;
-            // query fragments of this wave's first output block, loaded now
-            // so their latency overlaps the gate phase
-            __builtin_amdgcn_sched_barrier(0);
-            QFrags<T, D> qpre;
-            if (wave < n_items) {
-                int lane = threadIdx.x & 63;
-                asm volatile("" : "+v"(lane));
-                const int pair = wave / p.n_rep;
-                load_q_block<T, D>(qpre, static_cast<const T*>(p.q), b * p.T + t0, H_q,
-                                   h * p.n_rep + (wave % p.n_rep), pair == 0 ? 0 : 1, pair == 0 ? 3 : 2, nvalid, lane);
+            // Scalar gate: no barrier is needed here. gate_stats first writes
+            // the key statistics, which the previous chunk no longer reads
+            // after its last barrier, and writes dec and exact only after two
+            // barriers of its own, which every wave reaches after finishing
+            // the previous state update.
+            if (GATE) {
+                if (threadIdx.x == 0) *sm.nbad = 0;
+                if (threadIdx.x < D / 32) sm.badmask[threadIdx.x] = 0u;
+                __syncthreads();
             }
-            __builtin_amdgcn_sched_barrier(0);
-            if (threadIdx.x == 0) *sm.nbad = 0;
-            if (threadIdx.x < D / 32) sm.badmask[threadIdx.x] = 0u;
-            __syncthreads();
             float b2[TPT];
             gate_stats<T, D, GATE, true, TPT>(sm, cur, nvalid, p.alpha, b2);
             __syncthreads();
@@ -1712,10 +1751,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
                 int lane = threadIdx.x & 63;
                 asm volatile("" : "+v"(lane));  // keep lane-derived addresses inside the loop
                 const int pair = it / p.n_rep;
-                if (it != wave)
-                    load_q_block<T, D>(qpre, x.q, x.row0, H_q, x.hq, pair == 0 ? 0 : 1, pair == 0 ? 3 : 2, nvalid, lane);
-                if (pair == 0) output_block<T, D, GATE, 0, 3, SINK>(sm, x, lane, qpre);
-                else output_block<T, D, GATE, 1, 2, SINK>(sm, x, lane, qpre);
+                const QNext nx = next_block(it, wave, n_items, p.n_rep, h, b, p.T, c, c_end);
+                if (pair == 0) output_block<T, D, GATE, 0, 3, SINK>(sm, x, lane, qpre, nx);
+                else output_block<T, D, GATE, 1, 2, SINK>(sm, x, lane, qpre, nx);
+                __builtin_amdgcn_s_setprio(0);
             }
             __syncthreads();
             if (c + 1 < c_end) load_chunk_commit(sm, cur ^ 1, cr);  // the previous chunk's slot is free now
@@ -1750,7 +1789,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
         __builtin_amdgcn_sched_barrier(0);
         if (c == c_begin) load_state<D>(carry_in, acc);
         else load_slot<D>(slot, acc);
-        QFrags<T, D> qpre;
         if (wave < n_items) {
             int lane = threadIdx.x & 63;
             asm volatile("" : "+v"(lane));
@@ -1798,8 +1836,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
             const int pair = it / p.n_rep;
             if (it != wave)
                 load_q_block<T, D>(qpre, x.q, x.row0, H_q, x.hq, pair == 0 ? 0 : 1, pair == 0 ? 3 : 2, nvalid, lane);
-            if (pair == 0) output_block<T, D, GATE, 0, 3, SINK>(sm, x, lane, qpre);
-            else output_block<T, D, GATE, 1, 2, SINK>(sm, x, lane, qpre);
+            QNext nx;
+            nx.any = false;  // without a resident state the registers are too few to load ahead
+            if (pair == 0) output_block<T, D, GATE, 0, 3, SINK>(sm, x, lane, qpre, nx);
+            else output_block<T, D, GATE, 1, 2, SINK>(sm, x, lane, qpre, nx);
+            __builtin_amdgcn_s_setprio(0);
         }
         __syncthreads();
         if (c + 1 < c_end) {
