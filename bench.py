@@ -304,6 +304,8 @@ def measure_prefill(name: str, x: dict, steps: int, warmup: int, scrub, log_tag:
                      "algorithmic_bytes": byts, "algorithmic_flops": flops,
                      "mfma_frac_algorithmic": flops / (out_ms * 1e-3) / (peak_mfma * 1e12),
                      "mfma_busy_frac_counters": crec.get("mfma_busy_frac"),
+                     "valu_busy_frac_counters": crec.get("valu_busy_frac"),
+                     "lds_bank_conflict_frac_counters": crec.get("lds_bank_conflict_frac"),
                      "tcc_ea_gbs_counters": (traffic / (out_ms * 1e-3) / 1e9) if traffic else None},
     }, (q, k, v, o, S_T, ws, gate)
 
@@ -606,7 +608,8 @@ def main() -> int:
                                         "instead, the dirty lines' write-back adds to the step: "
                                         "cold_write_evicted_us_median",
                          "kernel": "decode_step_kernel", "algorithmic_bytes": dbytes,
-                         "tcc_ea_gbs_counters": (dtraffic / (k_ms * 1e-3) / 1e9) if dtraffic else None},
+                         "tcc_ea_gbs_counters": (dtraffic / (k_ms * 1e-3) / 1e9) if dtraffic else None,
+                         "counters_by_regime": drec.get("regimes")},
         }
         log(f"[bench] decode kernel {k_ms * 1e3:.1f} us/step ({dach:.0f} GB/s); graph {graph_us:.1f} us/step; "
             f"cold {cold_us:.1f} us (write-evicted {cold_w_us:.1f}); wall {dwall * 1e6 / nsteps:.1f} us/step")

@@ -6,17 +6,31 @@ Kernel-time summary (from a `rocprofv3 --kernel-trace --stats` results database)
 
 Counter record read by bench.py (from `rocprofv3 --pmc ... --output-format csv`
 runs of `bench.py --copy-probe-mib MIB`: one run with FETCH_SIZE, one with
-WRITE_SIZE, one with SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE):
+WRITE_SIZE, one with the SQ busy counters and GRBM_GUI_ACTIVE, optionally one
+with the L2-to-fabric read request counters):
 
     python -m gated_linear_recurrent_amd.counters traffic --fetch DIR --write DIR --busy DIR \\
-        --copy-mib MIB --command "..." --out profiles/traffic_counters.json
+        [--tcc DIR] --copy-mib MIB --command "..." --out profiles/traffic_counters.json
 
 FETCH_SIZE and WRITE_SIZE are KiB per dispatch moved between the L2 and the
 memory fabric. Each is scaled by the ratio of the known size of a plain
 elementwise copy (torch.neg over MIB MiB of float32, reading and writing MIB
-MiB) to what the same counter reads for that copy. MFMA busy is
-SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE per XCD), with
-GRBM_GUI_ACTIVE summed over the 8 XCDs.
+MiB) to what the same counter reads for that copy. The busy fractions follow
+the derived metrics rocprofv3 lists for gfx950 (GRBM_GUI_ACTIVE per XCD being
+the csv value, summed over the 8 XCDs, divided by 8):
+  MFMA busy        SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE)   (MfmaUtil)
+  VALU busy        SQ_ACTIVE_INST_VALU / (256 CUs x GRBM_GUI_ACTIVE)           (VALUBusy)
+  LDS conflict     SQ_LDS_BANK_CONFLICT / (256 CUs x GRBM_GUI_ACTIVE)          (LDSBankConflict)
+  conflicts/access SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT)
+The read pass gives the mean time an L2 miss is outstanding, in cycles:
+TCC_EA0_RDREQ_LEVEL_sum / TCC_EA0_RDREQ_sum (requests in flight summed per
+cycle over requests, Little's law). The decode kernel's dispatches are also
+split by the dispatch that ran just before each one: the cache-evicting read
+(a reduction), the evicting write (a fill), or another decode step.
+
+Summary table of a record:
+
+    python -m gated_linear_recurrent_amd.counters summary profiles/traffic_counters.json
 """
 from __future__ import annotations
 
@@ -59,7 +73,11 @@ KERNELS = {
                           "gated_linear_recurrent_amd/csrc/device_common.h"]),
 }
 N_SIMD = 1024
+N_CU = 256
 N_XCD = 8
+# name fragments of the kernels that run right before a decode step in each regime
+DECODE_REGIMES = {"after_read_eviction": "reduce_kernel", "after_write_eviction": "FillFunctor",
+                  "back_to_back": "decode_step_kernel"}
 
 
 def source_sha(files) -> str:
@@ -84,15 +102,60 @@ def trace(db: str, title: str, command: str) -> str:
     return "\n".join(out) + "\n"
 
 
-def _counter_means(d: str) -> dict:
-    """{kernel name: {counter: mean value per dispatch}} over every csv under d."""
-    acc: dict = {}
+def _dispatches(d: str) -> list:
+    """[(dispatch id, kernel name, {counter: value})] over every csv under d, in dispatch order."""
+    by_id: dict = {}
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         with open(f) as fh:
             for r in csv.DictReader(fh):
-                k = acc.setdefault(r["Kernel_Name"], {})
-                k.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                key = (f, int(r["Dispatch_Id"]))
+                name, cs = by_id.setdefault(key, (r["Kernel_Name"], {}))
+                cs[r["Counter_Name"]] = float(r["Counter_Value"])
+    return [(i, n, cs) for (_, i), (n, cs) in sorted(by_id.items())]
+
+
+def _counter_means(d: str, after: str | None = None) -> dict:
+    """{kernel name: {counter: mean value per dispatch}} over every csv under d;
+    with `after`, only dispatches whose preceding dispatch's name contains it."""
+    acc: dict = {}
+    prev = None
+    for _, name, cs in _dispatches(d):
+        if after is None or (prev is not None and after in prev):
+            k = acc.setdefault(name, {})
+            for c, v in cs.items():
+                k.setdefault(c, []).append(v)
+        prev = name
     return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def busy_fracs(b: dict) -> dict:
+    """Derived busy fractions of one kernel's SQ pass (see the module docstring)."""
+    out = {}
+    gui = b.get("GRBM_GUI_ACTIVE")
+    if gui:
+        per_xcd = gui / N_XCD
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in b:
+            out["mfma_busy_frac"] = b["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * per_xcd)
+        if "SQ_ACTIVE_INST_VALU" in b:
+            out["valu_busy_frac"] = b["SQ_ACTIVE_INST_VALU"] / (N_CU * per_xcd)
+        if "SQ_LDS_BANK_CONFLICT" in b:
+            out["lds_bank_conflict_frac"] = b["SQ_LDS_BANK_CONFLICT"] / (N_CU * per_xcd)
+    act, conf = b.get("SQ_LDS_IDX_ACTIVE"), b.get("SQ_LDS_BANK_CONFLICT")
+    if act and conf is not None and act > conf:
+        out["lds_conflicts_per_access"] = conf / (act - conf)
+    return out
+
+
+def read_latency(t: dict) -> dict:
+    """Mean cycles an L2 read miss is outstanding, and the read requests per dispatch."""
+    out = {}
+    if t.get("TCC_EA0_RDREQ_sum"):
+        out["read_requests"] = t["TCC_EA0_RDREQ_sum"]
+        if "TCC_EA0_RDREQ_LEVEL_sum" in t:
+            out["read_latency_cycles"] = t["TCC_EA0_RDREQ_LEVEL_sum"] / t["TCC_EA0_RDREQ_sum"]
+        if "TCC_EA0_RDREQ_DRAM_sum" in t:
+            out["dram_read_requests"] = t["TCC_EA0_RDREQ_DRAM_sum"]
+    return out
 
 
 def _find(means: dict, prefix: str) -> dict:
@@ -102,9 +165,11 @@ def _find(means: dict, prefix: str) -> dict:
     raise KeyError(prefix)
 
 
-def traffic(fetch_dir: str, write_dir: str, busy_dir: str | None, copy_mib: int, command: str) -> dict:
+def traffic(fetch_dir: str, write_dir: str, busy_dir: str | None, copy_mib: int, command: str,
+            tcc_dir: str | None = None) -> dict:
     fetch, write = _counter_means(fetch_dir), _counter_means(write_dir)
     busy = _counter_means(busy_dir) if busy_dir else {}
+    tcc = _counter_means(tcc_dir) if tcc_dir else {}
     copy_kib = copy_mib * 1024.0
     f_copy = _find(fetch, "neg_kernel")["FETCH_SIZE"]
     w_copy = _find(write, "neg_kernel")["WRITE_SIZE"]
@@ -122,11 +187,63 @@ def traffic(fetch_dir: str, write_dir: str, busy_dir: str | None, copy_mib: int,
                "hbm_bytes_per_launch": (fk * sf + wk * sw) * 1024.0}
         try:
             b = _find(busy, prefix)
-            rec["mfma_busy_frac"] = b["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * b["GRBM_GUI_ACTIVE"] / N_XCD)
+            rec.update(busy_fracs(b))
+            rec["sq"] = b
         except KeyError:
             pass
+        try:
+            rec.update(read_latency(_find(tcc, prefix)))
+        except KeyError:
+            pass
+        if kern == "decode_step_kernel":
+            rec["regimes"] = {}
+            for regime, before in DECODE_REGIMES.items():
+                r = {}
+                try:
+                    fk = _find(_counter_means(fetch_dir, before), prefix)["FETCH_SIZE"]
+                    wk = _find(_counter_means(write_dir, before), prefix)["WRITE_SIZE"]
+                    r["hbm_bytes_per_launch"] = (fk * sf + wk * sw) * 1024.0
+                except KeyError:
+                    pass
+                for d, fn in ((busy_dir, busy_fracs), (tcc_dir, read_latency)):
+                    if d:
+                        try:
+                            r.update(fn(_find(_counter_means(d, before), prefix)))
+                        except KeyError:
+                            pass
+                rec["regimes"][regime] = r
         out[kern] = rec
     return out
+
+
+def summary(rec: dict) -> str:
+    """Markdown table of a traffic record."""
+    cal = rec["_calibration"]
+    lines = [f"Calibration: a plain elementwise copy of {cal['copy_mib']} MiB reads FETCH_SIZE = "
+             f"{cal['fetch_kib_read']:,.0f} KiB and WRITE_SIZE = {cal['write_kib_read']:,.0f} KiB per dispatch, "
+             f"so FETCH_SIZE is scaled by {cal['fetch_scale']:.3f} and WRITE_SIZE by {cal['write_scale']:.3f}.\n",
+             "| kernel (workload) | HBM bytes/launch | MFMA busy | VALU busy | LDS bank-conflict stall | "
+             "conflicts/access | L2 read miss latency (cycles) |",
+             "|---|---|---|---|---|---|---|"]
+
+    def pct(x):
+        return "" if x is None else f"{100 * x:.1f}%"
+
+    def row(name, r):
+        hb = r.get("hbm_bytes_per_launch")
+        lat = r.get("read_latency_cycles")
+        cpa = r.get("lds_conflicts_per_access")
+        return (f"| {name} | {'' if hb is None else f'{hb / 1e6:.1f} MB'} | {pct(r.get('mfma_busy_frac'))} | "
+                f"{pct(r.get('valu_busy_frac'))} | {pct(r.get('lds_bank_conflict_frac'))} | "
+                f"{'' if cpa is None else f'{cpa:.2f}'} | {'' if lat is None else f'{lat:.0f}'} |")
+
+    for kern, r in rec.items():
+        if kern.startswith("_"):
+            continue
+        lines.append(row(f"`{kern}` ({r['workload']})", r))
+        for regime, rr in r.get("regimes", {}).items():
+            lines.append(row(f"&nbsp;&nbsp;{kern}, {regime.replace('_', ' ')}", rr))
+    return "\n".join(lines) + "\n"
 
 
 def main(argv=None) -> int:
@@ -140,14 +257,20 @@ def main(argv=None) -> int:
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
     c.add_argument("--busy")
+    c.add_argument("--tcc")
     c.add_argument("--copy-mib", type=int, required=True)
     c.add_argument("--command", default="")
     c.add_argument("--out", required=True)
+    m = sub.add_parser("summary")
+    m.add_argument("record")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         sys.stdout.write(trace(a.db, a.title, a.command))
+    elif a.cmd == "summary":
+        with open(a.record) as f:
+            sys.stdout.write(summary(json.load(f)))
     else:
-        rec = traffic(a.fetch, a.write, a.busy, a.copy_mib, a.command)
+        rec = traffic(a.fetch, a.write, a.busy, a.copy_mib, a.command, a.tcc)
         with open(a.out, "w") as f:
             json.dump(rec, f, indent=1)
             f.write("\n")

@@ -71,3 +71,51 @@ def test_trace_table(tmp_path):
     text = counters.trace(db, "Kernel trace: test", "rocprofv3 --kernel-trace --stats -- python3 bench.py")
     assert text.startswith("# Kernel trace: test\n")
     assert "| `liger::prefill_output_kernel<unsigned short, 128, 0, false>` | 12 | 916.2 | 76.35 | 2.0 |" in text
+
+
+DEC = "void liger::decode_step_kernel<unsigned short, 128, 1, 4, false>(liger::DecodeParams)"
+RED = "void at::native::reduce_kernel<512, 1, at::native::ReduceOp<float, at::native::func_wrapper<float> > >(int)"
+FILL = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>, std::array<char*, 1ul> >(int)"
+
+
+def _write_dispatches(d, dispatches):
+    """dispatches: [(kernel, {counter: value})], one dispatch id each, several rows per dispatch."""
+    os.makedirs(os.path.join(d, "host", "1"), exist_ok=True)
+    with open(os.path.join(d, "host", "1", "p_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for i, (k, cs) in enumerate(dispatches):
+            for c, v in cs.items():
+                w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+
+
+def test_busy_fractions_follow_the_profiler_formulas():
+    # 8 XCDs at 1000 cycles each; 256 CUs, 1024 SIMDs
+    b = {"GRBM_GUI_ACTIVE": 8000.0, "SQ_VALU_MFMA_BUSY_CYCLES": 1024 * 250.0, "SQ_ACTIVE_INST_VALU": 256 * 400.0,
+         "SQ_LDS_BANK_CONFLICT": 256 * 50.0, "SQ_LDS_IDX_ACTIVE": 256 * 150.0}
+    f = counters.busy_fracs(b)
+    assert f["mfma_busy_frac"] == pytest.approx(0.25)
+    assert f["valu_busy_frac"] == pytest.approx(0.40)
+    assert f["lds_bank_conflict_frac"] == pytest.approx(0.05)
+    assert f["lds_conflicts_per_access"] == pytest.approx(0.5)
+    lat = counters.read_latency({"TCC_EA0_RDREQ_sum": 200.0, "TCC_EA0_RDREQ_LEVEL_sum": 200.0 * 700,
+                                 "TCC_EA0_RDREQ_DRAM_sum": 150.0})
+    assert lat == {"read_requests": 200.0, "read_latency_cycles": 700.0, "dram_read_requests": 150.0}
+
+
+def test_decode_dispatches_split_by_the_preceding_kernel(tmp_path):
+    d = str(tmp_path / "tcc")
+    seq = [(DEC, {"TCC_EA0_RDREQ_sum": 10.0, "TCC_EA0_RDREQ_LEVEL_sum": 1000.0}),   # first: no predecessor
+           (DEC, {"TCC_EA0_RDREQ_sum": 10.0, "TCC_EA0_RDREQ_LEVEL_sum": 2000.0}),   # back to back
+           (RED, {"TCC_EA0_RDREQ_sum": 5.0, "TCC_EA0_RDREQ_LEVEL_sum": 5.0}),
+           (DEC, {"TCC_EA0_RDREQ_sum": 10.0, "TCC_EA0_RDREQ_LEVEL_sum": 9000.0}),   # after the read eviction
+           (FILL, {"TCC_EA0_RDREQ_sum": 0.0, "TCC_EA0_RDREQ_LEVEL_sum": 0.0}),
+           (DEC, {"TCC_EA0_RDREQ_sum": 10.0, "TCC_EA0_RDREQ_LEVEL_sum": 12000.0})]  # after the write eviction
+    _write_dispatches(d, seq)
+    allm = counters._counter_means(d)[DEC]
+    assert allm["TCC_EA0_RDREQ_LEVEL_sum"] == pytest.approx((1000 + 2000 + 9000 + 12000) / 4)
+    for after, level in (("reduce_kernel", 9000.0), ("FillFunctor", 12000.0), ("decode_step_kernel", 2000.0)):
+        m = counters._counter_means(d, after)[DEC]
+        assert m["TCC_EA0_RDREQ_LEVEL_sum"] == level
+    assert counters.DECODE_REGIMES["after_read_eviction"] in RED
+    assert counters.DECODE_REGIMES["after_write_eviction"] in FILL
