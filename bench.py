@@ -58,6 +58,7 @@ BWD_SEED = 23   # upstream gradient of the backward measurement
 CHUNK = 64
 SCRUB_BYTES = 512 << 20        # larger than the 256 MB last-level cache
 READ_EVICT_BYTES = 1 << 30     # read through before each cold step
+DECODE_LAYERS = 8              # layers of decode state stepped in turn (8 x 48 MiB > 256 MB last-level cache)
 # tokens of each other prefill workload that the CPU baseline times (a prefix:
 # the oracle is linear in T, so the prefix rate is the workload's rate)
 CPU_PREFIX_TOKENS = {PREFILL_1B_WORKLOAD: 512, PREFILL_LONG_WORKLOAD: 1024}
@@ -570,6 +571,28 @@ def main() -> int:
 
         cold_us = timed_cold("read")
         cold_w_us = timed_cold("write")
+        # cold back to back, as in a multi-layer model: DECODE_LAYERS layers'
+        # states (more than the last-level cache holds together) stepped in
+        # turn, so each step finds its state evicted by the other layers' steps
+        lstate = [(S, ring)]
+        for _ in range(DECODE_LAYERS - 1):
+            lstate.append((S.clone(), gla.KVRing(ring.k.clone(), ring.v.clone(), ring.pos.clone(),
+                                                 torch.zeros(N, dtype=torch.int32, device=dev), w)))
+
+        def lstep(s):
+            Sl, rl = lstate[s % DECODE_LAYERS]
+            gla.liger_attn_decode_step(*steps_in[s], Sl, rl, dgate, dcfg["alpha"], o=do)
+
+        for s in range(2 * DECODE_LAYERS):
+            lstep(s)
+        torch.cuda.synchronize()
+        e0.record()
+        for s in range(nsteps):
+            lstep(s)
+        e1.record()
+        torch.cuda.synchronize()
+        multi_us = e0.elapsed_time(e1) * 1e3 / nsteps
+        del lstate
         # the same steps with meta-memory sink tokens, back to back
         rng = np.random.default_rng(SINK_SEED + 1)
         dsinks = tuple(torch.from_numpy(rng.standard_normal((Hkv, N_SINKS, dd)).astype(np.float32)).to(dev)
@@ -595,24 +618,29 @@ def main() -> int:
             "graph_us_per_step": graph_us, "graph_steps_per_s": 1e6 / graph_us,
             "cold_kernel_us_median": cold_us,
             "cold_write_evicted_us_median": cold_w_us,
+            "cold_multilayer_us": multi_us, "multilayer_layers": DECODE_LAYERS,
             "with_sinks": {"n_sinks": N_SINKS, "kernel_us": sink_us},
             "roofline": {"bound": "hbm", "achieved": dach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": dach / PEAK_HBM_GBS, "traffic": dtraffic,
                          "regime": "hot: back-to-back steps, the 48 MiB state + ring working set "
                                    "stays in the 256 MB last-level cache",
                          "cold_frac": dbytes / (cold_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                         "cold_multilayer_frac": dbytes / (multi_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
                          "cold_regime": "cold: median of single steps, each between its own events (which add "
                                         "about what per_launch_events_us adds to kernel_us), after evicting the "
                                         "last-level cache with a 1 GiB read (as in a multi-layer model, where "
                                         "each layer's state is evicted between steps); after a 512 MiB write "
                                         "instead, the dirty lines' write-back adds to the step: "
-                                        "cold_write_evicted_us_median",
+                                        "cold_write_evicted_us_median; cold_multilayer: steps back to back "
+                                        "over the states of several layers (384 MiB together), each layer's "
+                                        "state evicted by the others' steps",
                          "kernel": "decode_step_kernel", "algorithmic_bytes": dbytes,
                          "tcc_ea_gbs_counters": (dtraffic / (k_ms * 1e-3) / 1e9) if dtraffic else None,
                          "counters_by_regime": drec.get("regimes")},
         }
         log(f"[bench] decode kernel {k_ms * 1e3:.1f} us/step ({dach:.0f} GB/s); graph {graph_us:.1f} us/step; "
-            f"cold {cold_us:.1f} us (write-evicted {cold_w_us:.1f}); wall {dwall * 1e6 / nsteps:.1f} us/step")
+            f"cold {cold_us:.1f} us (write-evicted {cold_w_us:.1f}; {DECODE_LAYERS} layers back to back "
+            f"{multi_us:.1f}); wall {dwall * 1e6 / nsteps:.1f} us/step")
 
     if not args.no_peaks:
         # what the box reaches with plain library work, next to the datasheet peaks:
