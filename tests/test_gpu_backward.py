@@ -138,3 +138,37 @@ def test_backward_outlier_keys():
     dO = grad_output(x["q"].shape, "bf16", seed=56)
     ref = oracle.prefill_backward(x["q"], x["k"], x["v"], dO, 1, 64, 0.5)
     _check(_run(x, dO, 1, 64, 0.5), ref, tag)
+
+
+@pytest.mark.timeout(600)
+def test_backward_long_context_prefix():
+    """The long-context workload in full (T = 32768, H_q = 32, H_kv = 8,
+    d = 128, vector gate, 1% of key rows x8; workspace 680 MB) with dO zero
+    from token T0 = 2048 on. By causality only the first T0 outputs carry
+    loss, so the gradients of the first T0 tokens are those of the T0-token
+    prefix problem and every gradient from T0 on is zero. The prefix problem
+    is run through the same call and checked against the float64 reverse
+    pass; the long run must agree with it on the first T0 tokens (same chunk
+    records and scans there) and be exactly zero after."""
+    from synth import config_prefill_inputs
+    T0 = 2048
+    x = config_prefill_inputs("prefill_8b_b1_t32768_d128_outliers")
+    T = x["q"].shape[1]
+    dO = grad_output(x["q"].shape, "bf16", seed=31)
+    dO[:, T0:] = 0.0
+    assert gla.liger_attn_prefill_backward_workspace_size(1, T, 32, 8, 128) > 600e6
+    say(f"[bwd] long context T={T}: GPU")
+    got = _run(x, dO, 1, 64, 0.5)
+    xp = {n: np.ascontiguousarray(x[n][:, :T0]) for n in ("q", "k", "v")}
+    dOp = np.ascontiguousarray(dO[:, :T0])
+    say(f"[bwd] prefix T0={T0}: GPU")
+    pre = _run(xp, dOp, 1, 64, 0.5)
+    say(f"[bwd] prefix T0={T0}: oracle")
+    ref = oracle.prefill_backward(xp["q"], xp["k"], xp["v"], dOp, 1, 64, 0.5)
+    _check(pre, ref, "bwd long-context prefix")
+    for name, a, p in zip(("dq", "dk", "dv"), got, pre):
+        assert np.all(np.isfinite(a)), f"{name} has non-finite entries"
+        scale = max(float(np.max(np.abs(p))), 1e-30)
+        err = float(np.max(np.abs(a[:, :T0] - p))) / scale
+        assert err <= 1e-6, (name, err)
+        assert not np.any(a[:, T0:]), f"{name}: non-zero gradient after T0"
