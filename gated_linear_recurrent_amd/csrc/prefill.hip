@@ -748,7 +748,9 @@ __device__ __forceinline__ void intra_key_operand(const Smem<T, D, GATE, FULL>& 
 template <typename T, int D>
 struct SegLayout {
     static constexpr int E = sizeof(T);
-    static constexpr int TB = 128;                     // tokens per block
+    // tokens per block: at d = 128 a 256-token segment is four blocks, each
+    // block's loads in flight during the previous one; at d = 64 two
+    static constexpr int TB = D >= 128 ? 64 : 128;
     static constexpr int P = D + 16;                   // row pitch (elements) of the K and V tiles
     static constexpr int VPL = 16 / E;                 // elements per 16-byte piece
     static constexpr int PPR = D / VPL;                // pieces per row
