@@ -62,6 +62,7 @@ DECODE_LAYERS = 8              # layers of decode state stepped in turn (8 x 48 
 # tokens of each other prefill workload that the CPU baseline times (a prefix:
 # the oracle is linear in T, so the prefix rate is the workload's rate)
 CPU_PREFIX_TOKENS = {PREFILL_1B_WORKLOAD: 512, PREFILL_LONG_WORKLOAD: 1024}
+PREFILL_FP32_WORKLOAD = "prefill_fp32_b1_h2_t256_d64"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -704,6 +705,10 @@ def main() -> int:
             xp = cpu_prefix.get(name) or config_prefill_inputs(name, T=CPU_PREFIX_TOKENS[name])
             legs[name] = cpu_baseline_prefill(name, xp, CPU_PREFIX_TOKENS[name], min_seconds=4.0)
         legs[DECODE_WORKLOAD] = cpu_baseline_decode(DECODE_WORKLOAD, 16, min_seconds=4.0)
+        # the small fp32 workload (a correctness case, not timed on the GPU), whole
+        legs[PREFILL_FP32_WORKLOAD] = cpu_baseline_prefill(PREFILL_FP32_WORKLOAD,
+                                                           config_prefill_inputs(PREFILL_FP32_WORKLOAD),
+                                                           CONFIGS[PREFILL_FP32_WORKLOAD]["T"], min_seconds=1.0)
         other = result.get("prefill_other_workloads", {})
         for name, leg in legs.items():
             if name in other:
