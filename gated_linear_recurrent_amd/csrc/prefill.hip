@@ -1561,11 +1561,40 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
 #pragma unroll 1
     for (int t = 0; t < NT; ++t) {
         f32x4_t acc[2] = {zero4(), zero4()};
+        // Resident state, bf16, scalar gate: every LDS operand of this slice
+        // (the state pieces and the value fragments) is requested before the
+        // first MFMA, so the slice waits for LDS once instead of twice.
+        constexpr bool PRE = L::SLDS && BF && GATE == 0;
+        float4 sraw[PRE ? 2 * KS : 1];
+        Frag vfr[NG];
+        if constexpr (PRE) {
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                const float* src = sm.S32 + (16 * t + col) * L::SP + M::KSTEP * k + KPL * g;
+                sraw[2 * k] = *reinterpret_cast<const float4*>(src);
+                sraw[2 * k + 1] = *reinterpret_cast<const float4*>(src + 4);
+            }
+#pragma unroll
+            for (int G = 0; G < NG; ++G) {
+                const int kt = 2 * (GMIN + G);
+                if (!(inr(0, kt) || inr(0, kt + 1) || inr(1, kt) || inr(1, kt + 1))) continue;
+                vfr[G] = kt >= 0 ? load_key_frag(Vcur, L::VP, 16 * kt, 16 * t, lane)
+                                 : load_key_frag(Vprv, L::VP, 16 * (kt + 4), 16 * t, lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
             Frag a;
-            if constexpr (L::SLDS) a = resident_frag(sm, 16 * t + col, M::KSTEP * k + KPL * g);
-            else a = M::load(sm.St + (16 * t + col) * L::DP + M::KSTEP * k + KPL * g);
+            if constexpr (PRE) {
+                const float x[8] = {sraw[2 * k].x, sraw[2 * k].y, sraw[2 * k].z, sraw[2 * k].w,
+                                    sraw[2 * k + 1].x, sraw[2 * k + 1].y, sraw[2 * k + 1].z, sraw[2 * k + 1].w};
+                a = M::pack(x);
+            } else if constexpr (L::SLDS) {
+                a = resident_frag(sm, 16 * t + col, M::KSTEP * k + KPL * g);
+            } else {
+                a = M::load(sm.St + (16 * t + col) * L::DP + M::KSTEP * k + KPL * g);
+            }
             acc[0] = M::mma(a, qt[0][k], acc[0]);
             acc[1] = M::mma(a, qt[1][k], acc[1]);
         }
@@ -1592,8 +1621,10 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
 #pragma unroll
                 for (int s = 0; s < 2; ++s) gl[s] = inr(s, kt) || inr(s, kt + 1);
                 if (!gl[0] && !gl[1]) continue;
-                const Frag a = kt >= 0 ? load_key_frag(Vcur, L::VP, 16 * kt, 16 * t, lane)
-                                       : load_key_frag(Vprv, L::VP, 16 * (kt + 4), 16 * t, lane);
+                Frag a;
+                if constexpr (L::SLDS && GATE == 0) a = vfr[G];
+                else a = kt >= 0 ? load_key_frag(Vcur, L::VP, 16 * kt, 16 * t, lane)
+                                 : load_key_frag(Vprv, L::VP, 16 * (kt + 4), 16 * t, lane);
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
                     if (gl[s]) acc[s] = M::mma(a, pf[s][G], acc[s]);
