@@ -1307,9 +1307,21 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
         constexpr bool FAST = decltype(fast_c)::value;
         float lmax[2] = {-INFINITY, -INFINITY};
         const unsigned w = FAST ? 64u : static_cast<unsigned>(x.window);
+        // FAST (every tile in range is live): the next tile's key fragments
+        // are requested before this tile's MFMAs
+        Frag kbuf[2][KS];
+        auto load_tile = [&](int kt, Frag* dst) {
+            const T* krow = kt >= 0 ? Kcur + (16 * kt + col) * L::DP : Kprv + (16 * kt + 64 + col) * L::DP;
+#pragma unroll
+            for (int k = 0; k < KS; ++k) dst[k] = M::load(krow + M::KSTEP * k + KPL * g);
+        };
+        if constexpr (FAST) load_tile(KTMIN, kbuf[0]);
 #pragma unroll
         for (int u = 0; u < NKT; ++u) {
             const int kt = KTMIN + u;
+            if constexpr (FAST) {
+                if (u + 1 < NKT) load_tile(kt + 1, kbuf[(u + 1) & 1]);
+            }
             bool live[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s)
@@ -1320,7 +1332,7 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
                 f32x4_t d4[2] = {zero4(), zero4()};
 #pragma unroll
                 for (int k = 0; k < KS; ++k) {
-                    const Frag a = M::load(krow + M::KSTEP * k + KPL * g);
+                    const Frag a = FAST ? kbuf[u & 1][k] : M::load(krow + M::KSTEP * k + KPL * g);
 #pragma unroll
                     for (int s = 0; s < 2; ++s)
                         if (live[s]) d4[s] = M::mma(a, qr[s][k], d4[s]);
@@ -1354,7 +1366,7 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
                         for (int r = 0; r < 4; ++r) sc[s][u][r] = -INFINITY;
                     }
             }
-            __builtin_amdgcn_sched_barrier(0);  // bound the number of key fragments in flight
+            __builtin_amdgcn_sched_barrier(0);  // at most two key tiles' fragments in flight
         }
         if constexpr (SINK) {
             // sink scores: the sink keys (rows past n_sink repeat the last one
@@ -1472,12 +1484,20 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
 #pragma unroll
         for (int J = 0; J <= KTMAX; ++J) bk[J] = *reinterpret_cast<const float4*>(sm.b2s + 16 * J + 4 * g);
     }
+    // the next key tile's operand fragments are requested before this tile's MFMAs
+    Frag ibuf[2][KS];
+    auto load_itile = [&](int J, Frag* dst) {
+#pragma unroll
+        for (int k = 0; k < KS; ++k) dst[k] = M::load(sm.Kb + (16 * J + col) * L::DP + M::KSTEP * k + KPL * g);
+    };
+    load_itile(0, ibuf[0]);
 #pragma unroll
     for (int J = 0; J <= KTMAX; ++J) {
+        if (J + 1 <= KTMAX) load_itile(J + 1, ibuf[(J + 1) & 1]);
         f32x4_t d4[2] = {zero4(), zero4()};
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
-            const Frag a = M::load(sm.Kb + (16 * J + col) * L::DP + M::KSTEP * k + KPL * g);
+            const Frag a = ibuf[J & 1][k];
 #pragma unroll
             for (int s = 0; s < 2; ++s)
                 if (J <= QTS[s]) d4[s] = M::mma(a, qt[s][k], d4[s]);
