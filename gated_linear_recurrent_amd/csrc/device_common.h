@@ -80,6 +80,30 @@ constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8 lanes
 constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16 lanes
 constexpr int kDppRowShr1 = 0x111;
 
+constexpr int kDppRowShl1 = 0x101;    // lane i <- lane i+1 within its row (0 past the row end)
+constexpr int kDppRowShl2 = 0x102;
+constexpr int kDppRowShl4 = 0x104;
+constexpr int kDppRowShl8 = 0x108;
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Inclusive suffix sum over the 64 lanes of a wave: lane l gets the sum of v
+// over lanes l .. 63. Row shifts build the suffix inside each 16-lane row;
+// the totals of the later rows come from lane reads.
+__device__ __forceinline__ float wave_suffix_sum(float v) {
+    v += dpp<kDppRowShl1>(v);
+    v += dpp<kDppRowShl2>(v);
+    v += dpp<kDppRowShl4>(v);
+    v += dpp<kDppRowShl8>(v);
+    const float r1 = readlane_f(v, 16), r2 = readlane_f(v, 32), r3 = readlane_f(v, 48);
+    const float r23 = r2 + r3;
+    const int row = (threadIdx.x & 63) >> 4;
+    const float later = row == 0 ? r1 + r23 : row == 1 ? r23 : row == 2 ? r3 : 0.0f;
+    return v + later;
+}
+
 // All-reduce over aligned groups of 8 lanes.
 __device__ __forceinline__ float group8_max(float v) {
     v = fmaxf(v, dpp<kDppXor1>(v));

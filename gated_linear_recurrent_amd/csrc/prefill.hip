@@ -742,9 +742,10 @@ __device__ __forceinline__ void intra_key_operand(const Smem<T, D, GATE, FULL>& 
 // over the segment's tokens, in blocks of up to TB tokens held in LDS
 // token-major. Per block: key row statistics; the log2 gates and, per token,
 // the sum of the gates after it (computed as suffix sums, so every factor is
-// at most 1); the key operand phik_j (.) 2^(suffix after j) written over K in
-// place; then one MFMA contraction over the block's tokens added to the
-// running state rescaled by the block's decay.
+// at most 1); the key operand phik_j (.) 2^(suffix after j); then one MFMA
+// contraction over the block's tokens added to the running state rescaled by
+// the block's decay. The vector gate (a log2 gate per channel) and the scalar
+// gate (one per token) have a kernel each.
 template <typename T, int D>
 struct SegLayout {
     static constexpr int E = sizeof(T);
@@ -766,6 +767,7 @@ struct SegLayout {
 
 template <typename T, int D, int GATE>
 __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams p) {
+    static_assert(GATE == 1, "the scalar gate has its own segment-state kernel");
     typedef SegLayout<T, D> SL;
     typedef Mfma<T> M;
     typedef StateTiles<D> ST;
@@ -830,203 +832,110 @@ __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams 
             issue(blk0 + SL::TB, rest < SL::TB ? rest : SL::TB);
         }
 
-        if constexpr (GATE == 0) {
-            // Piece mapping of the loads: PPR consecutive lanes share a key
-            // row. Row statistics reduce over those lanes; the exponentials
-            // stay in registers until the gate suffix sums are known.
-            static_assert(SL::PPR == 8 || SL::PPR == 16, "a key row spans 8 or 16 lanes");
-            auto red_max = [](float v) {
-                v = group8_max(v);
-                if (SL::PPR == 16) v = fmaxf(v, dpp<kDppMirror>(v));
-                return v;
-            };
-            auto red_sum = [](float v) {
-                v = group8_sum(v);
-                if (SL::PPR == 16) v += dpp<kDppMirror>(v);
-                return v;
-            };
+        // key row statistics, eight lanes per row; rows past nb get 1/sum = 0
+        {
+            constexpr int NLD = D / (8 * SL::VPL);
             const int tid = ltid();
-            float ex[SL::NPT][SL::VPL];
-            float kiv[SL::NPT];
+            const int sub = tid & 7;
+            for (int r0 = 0; r0 < SL::TB; r0 += kPThreads / 8) {
+                const int j = r0 + (tid >> 3);
+                const T* row = Ks + j * SL::P + sub * SL::VPL;
+                float x[NLD * SL::VPL];
 #pragma unroll
-            for (int n = 0; n < SL::NPT; ++n) {
-                const int idx = tid + n * kPThreads;
-                const int j = idx / SL::PPR;
-                const uint4 u = *reinterpret_cast<const uint4*>(Ks + j * SL::P + (idx % SL::PPR) * SL::VPL);
-                const T* e = reinterpret_cast<const T*>(&u);
-                float mx = -INFINITY, sraw = 0.f;
+                for (int q = 0; q < NLD; ++q) {
+                    const uint4 u = *reinterpret_cast<const uint4*>(row + q * 8 * SL::VPL);
+                    const T* e = reinterpret_cast<const T*>(&u);
 #pragma unroll
-                for (int i = 0; i < SL::VPL; ++i) {
-                    ex[n][i] = to_f32(e[i]);
-                    mx = fmaxf(mx, ex[n][i]);
-                    sraw += ex[n][i];
+                    for (int i = 0; i < SL::VPL; ++i) x[q * SL::VPL + i] = to_f32(e[i]);
                 }
-                mx = red_max(mx) * kLog2e;
+                float mx = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < NLD * SL::VPL; ++i) mx = fmaxf(mx, x[i]);
+                mx = group8_max(mx);
                 float se = 0.f;
 #pragma unroll
-                for (int i = 0; i < SL::VPL; ++i) {
-                    ex[n][i] = fast_exp2(fmaf(ex[n][i], kLog2e, -mx));
-                    se += ex[n][i];
-                }
-                se = red_sum(se);
-                sraw = red_sum(sraw);
-                const bool ok = j < nb;
-                kiv[n] = ok ? fast_rcp(se) : 0.0f;
-                if (idx % SL::PPR == 0) ell[j] = ok ? log2_sigmoid(sraw * (1.0f / D)) : 0.0f;
-            }
-            __syncthreads();
-            // suffix sums over the block (one wave, TPL consecutive tokens per lane)
-            constexpr int TPL = SL::TB / 64;
-            if (ltid() < 64) {
-                const int lane = ltid();
-                float l[TPL];
-                float own = 0.f;
-#pragma unroll
-                for (int i = 0; i < TPL; ++i) {
-                    l[i] = ell[lane * TPL + i];
-                    own += l[i];
-                }
-                float incl = own;  // sum over lanes >= lane
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const float y = __shfl_down(incl, o, 64);
-                    if (lane + o < 64) incl += y;
-                }
-                float run = __shfl_down(incl, 1, 64);
-                if (lane == 63) run = 0.0f;
-#pragma unroll
-                for (int i = TPL - 1; i >= 0; --i) {
-                    ell[lane * TPL + i] = run;
-                    run += l[i];
-                }
-                const float total = __shfl(incl, 0, 64);
-                for (int c = lane; c < D; c += 64) tot[c] = total;
-            }
-            __syncthreads();
-            // key operand in place: phik_j 2^(sum of the gates after j)
-#pragma unroll
-            for (int n = 0; n < SL::NPT; ++n) {
-                const int idx = tid + n * kPThreads;
-                const int j = idx / SL::PPR;
-                T* e = Ks + j * SL::P + (idx % SL::PPR) * SL::VPL;
-                const float f = kiv[n] * fast_exp2(ell[j]);
-                float y[SL::VPL];
-#pragma unroll
-                for (int i = 0; i < SL::VPL; ++i) y[i] = f * ex[n][i];
-                if constexpr (sizeof(T) == 2) {
-                    *reinterpret_cast<uint4*>(e) = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
-                                                              pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
-                } else {
-                    *reinterpret_cast<float4*>(e) = make_float4(y[0], y[1], y[2], y[3]);
+                for (int i = 0; i < NLD * SL::VPL; ++i) se += fast_exp2((x[i] - mx) * kLog2e);
+                se = group8_sum(se);
+                if (sub == 0) {
+                    kmax[j] = mx;
+                    kinv[j] = j < nb ? fast_rcp(se) : 0.0f;
                 }
             }
-            __syncthreads();
-        } else {
-            // key row statistics, eight lanes per row; rows past nb get 1/sum = 0
-            {
-                constexpr int NLD = D / (8 * SL::VPL);
-                const int tid = ltid();
-                const int sub = tid & 7;
-                for (int r0 = 0; r0 < SL::TB; r0 += kPThreads / 8) {
-                    const int j = r0 + (tid >> 3);
-                    const T* row = Ks + j * SL::P + sub * SL::VPL;
-                    float x[NLD * SL::VPL];
+        }
+        __syncthreads();
+        // Piece layout: the LPP lanes of a group share one 16-byte channel
+        // piece (channels c0 .. c0 + VPL - 1); lane l owns tokens TPL l ..
+        // TPL l + TPL - 1. The pooled input x_j[c] is the mean of k_j over
+        // the in-range channels c-1 .. c+2, formed from the piece and its
+        // three neighbouring elements (one before, two after).
+        constexpr int TPL = SL::TB * SL::PPR / kPThreads;  // tokens per lane
+        constexpr int LPP = SL::TB / TPL;                    // lanes per piece
+        static_assert(LPP == 32 || LPP == 64, "a piece spans half a wave or a whole wave");
+        constexpr int VPL = SL::VPL;
+        const int tid = ltid();
+        const int c0 = (tid / LPP) * VPL;
+        const int l = tid % LPP;
+        float lg2[TPL][VPL];  // log2 gate per (token, channel)
 #pragma unroll
-                    for (int q = 0; q < NLD; ++q) {
-                        const uint4 u = *reinterpret_cast<const uint4*>(row + q * 8 * SL::VPL);
-                        const T* e = reinterpret_cast<const T*>(&u);
+        for (int t = 0; t < TPL; ++t) {
+            const int j = TPL * l + t;
+            const T* row = Ks + j * SL::P;
+            const uint4 u = *reinterpret_cast<const uint4*>(row + c0);
+            const T* pe = reinterpret_cast<const T*>(&u);
+            float e[VPL + 3];  // channels c0 - 1 .. c0 + VPL + 1, zero outside the row
+            e[0] = c0 > 0 ? to_f32(row[c0 - 1]) : 0.0f;
 #pragma unroll
-                        for (int i = 0; i < SL::VPL; ++i) x[q * SL::VPL + i] = to_f32(e[i]);
-                    }
-                    float mx = -INFINITY;
-#pragma unroll
-                    for (int i = 0; i < NLD * SL::VPL; ++i) mx = fmaxf(mx, x[i]);
-                    mx = group8_max(mx);
-                    float se = 0.f;
-#pragma unroll
-                    for (int i = 0; i < NLD * SL::VPL; ++i) se += fast_exp2((x[i] - mx) * kLog2e);
-                    se = group8_sum(se);
-                    if (sub == 0) {
-                        kmax[j] = mx;
-                        kinv[j] = j < nb ? fast_rcp(se) : 0.0f;
-                    }
-                }
-            }
-            __syncthreads();
-            // Piece layout: the LPP lanes of a group share one 16-byte channel
-            // piece (channels c0 .. c0 + VPL - 1); lane l owns tokens TPL l ..
-            // TPL l + TPL - 1. The pooled input x_j[c] is the mean of k_j over
-            // the in-range channels c-1 .. c+2, formed from the piece and its
-            // three neighbouring elements (one before, two after).
-            constexpr int TPL = SL::TB * SL::PPR / kPThreads;  // tokens per lane
-            constexpr int LPP = SL::TB / TPL;                    // lanes per piece
-            static_assert(LPP == 32 || LPP == 64, "a piece spans half a wave or a whole wave");
-            constexpr int VPL = SL::VPL;
-            const int tid = ltid();
-            const int c0 = (tid / LPP) * VPL;
-            const int l = tid % LPP;
-            float lg2[TPL][VPL];  // log2 gate per (token, channel)
-#pragma unroll
-            for (int t = 0; t < TPL; ++t) {
-                const int j = TPL * l + t;
-                const T* row = Ks + j * SL::P;
-                const uint4 u = *reinterpret_cast<const uint4*>(row + c0);
-                const T* pe = reinterpret_cast<const T*>(&u);
-                float e[VPL + 3];  // channels c0 - 1 .. c0 + VPL + 1, zero outside the row
-                e[0] = c0 > 0 ? to_f32(row[c0 - 1]) : 0.0f;
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) e[i + 1] = to_f32(pe[i]);
-                e[VPL + 1] = c0 + VPL < D ? to_f32(row[c0 + VPL]) : 0.0f;
-                e[VPL + 2] = c0 + VPL < D ? to_f32(row[c0 + VPL + 1]) : 0.0f;
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) {
-                    const int c = c0 + i;
-                    const float inv_cnt = (c == 0 || c == D - 2) ? (1.0f / 3.0f) : c == D - 1 ? 0.5f : 0.25f;
-                    const float x = (e[i] + e[i + 1]) + (e[i + 2] + e[i + 3]);
-                    lg2[t][i] = j < nb ? log2_sigmoid(x * inv_cnt) : 0.0f;
-                }
-            }
-            // sum of the gates after each token within the block: this lane's
-            // tokens, then the lanes after it (inclusive suffix over the group)
-            float after[VPL];
+            for (int i = 0; i < VPL; ++i) e[i + 1] = to_f32(pe[i]);
+            e[VPL + 1] = c0 + VPL < D ? to_f32(row[c0 + VPL]) : 0.0f;
+            e[VPL + 2] = c0 + VPL < D ? to_f32(row[c0 + VPL + 1]) : 0.0f;
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
-                float own = 0.f;
-#pragma unroll
-                for (int t = 0; t < TPL; ++t) own += lg2[t][i];
-                float incl = own;
-#pragma unroll
-                for (int o = 1; o < LPP; o <<= 1) {
-                    const float y = __shfl_down(incl, o, LPP);
-                    if (l + o < LPP) incl += y;
-                }
-                after[i] = incl - own;
-                if (l == 0) tot[c0 + i] = incl;
+                const int c = c0 + i;
+                const float inv_cnt = (c == 0 || c == D - 2) ? (1.0f / 3.0f) : c == D - 1 ? 0.5f : 0.25f;
+                const float x = (e[i] + e[i + 1]) + (e[i + 2] + e[i + 3]);
+                lg2[t][i] = j < nb ? log2_sigmoid(x * inv_cnt) : 0.0f;
             }
-            __syncthreads();  // every pooled read of a neighbouring piece is done before K is overwritten
-            // key operand in place: phik_j (.) 2^(sum of the gates after j)
-#pragma unroll
-            for (int t = TPL - 1; t >= 0; --t) {
-                const int j = TPL * l + t;
-                T* row = Ks + j * SL::P + c0;
-                const uint4 u = *reinterpret_cast<const uint4*>(row);
-                const T* pe = reinterpret_cast<const T*>(&u);
-                const float m = kmax[j] * kLog2e, s = kinv[j];
-                float y[VPL];
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) {
-                    y[i] = s * fast_exp2(fmaf(to_f32(pe[i]), kLog2e, after[i] - m));
-                    after[i] += lg2[t][i];
-                }
-                if constexpr (sizeof(T) == 2) {
-                    *reinterpret_cast<uint4*>(row) = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
-                                                                pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
-                } else {
-                    *reinterpret_cast<float4*>(row) = make_float4(y[0], y[1], y[2], y[3]);
-                }
-            }
-            __syncthreads();
         }
+        // sum of the gates after each token within the block: this lane's
+        // tokens, then the lanes after it (inclusive suffix over the group)
+        float after[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            float own = 0.f;
+#pragma unroll
+            for (int t = 0; t < TPL; ++t) own += lg2[t][i];
+            float incl = own;
+#pragma unroll
+            for (int o = 1; o < LPP; o <<= 1) {
+                const float y = __shfl_down(incl, o, LPP);
+                if (l + o < LPP) incl += y;
+            }
+            after[i] = incl - own;
+            if (l == 0) tot[c0 + i] = incl;
+        }
+        __syncthreads();  // every pooled read of a neighbouring piece is done before K is overwritten
+        // key operand in place: phik_j (.) 2^(sum of the gates after j)
+#pragma unroll
+        for (int t = TPL - 1; t >= 0; --t) {
+            const int j = TPL * l + t;
+            T* row = Ks + j * SL::P + c0;
+            const uint4 u = *reinterpret_cast<const uint4*>(row);
+            const T* pe = reinterpret_cast<const T*>(&u);
+            const float m = kmax[j] * kLog2e, s = kinv[j];
+            float y[VPL];
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                y[i] = s * fast_exp2(fmaf(to_f32(pe[i]), kLog2e, after[i] - m));
+                after[i] += lg2[t][i];
+            }
+            if constexpr (sizeof(T) == 2) {
+                *reinterpret_cast<uint4*>(row) = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                                                            pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+            } else {
+                *reinterpret_cast<float4*>(row) = make_float4(y[0], y[1], y[2], y[3]);
+            }
+        }
+        __syncthreads();
 
         // running state: acc <- diag(2^tot) acc + Kop^T V over the block;
         // wave w owns row tiles rt0 .. rt0+RTW-1 and column tiles ct0 .. ct0+CTW-1
@@ -1080,6 +989,211 @@ __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams 
                     dst[(16 * (rt0 + a) + 4 * g + r) * D + 16 * (ct0 + tt) + col] = acc[a * CTW + tt][r];
     }
     if (threadIdx.x < D) dst[size_t(D) * D + threadIdx.x] = lg[threadIdx.x];
+}
+
+// Scalar gate. Every channel of a token shares one log2 gate, so a block
+// needs one gate and one suffix sum per token, and the kernel takes two
+// barriers per block: the key operand and the value tile alternate between
+// two LDS buffers, so nothing written for block n+1 can overwrite what the
+// contraction of block n still reads.
+//   (a) from its loaded registers each thread commits its value pieces,
+//       converts its key pieces (the next block's loads then go into the same
+//       registers), forms the key-row softmax over the PPR lanes of the row and
+//       the token's log2 gate, and publishes the gate;          barrier
+//   (b) every wave forms the suffix sums of the block's gates itself (lane
+//       shifts and lane reads, no further barrier) and writes the key operand
+//       phik_j 2^(sum of the gates after j);                    barrier
+//   (c) acc <- 2^(block total) acc + Kop^T V; waves that finish early go on
+//       to (a) of the next block.
+// A segment is a whole number of chunks, so every block is a full chunk and
+// no load needs a bounds test.
+template <typename T, int D>
+struct SegLayoutScalar {
+    static constexpr int E = sizeof(T);
+    static constexpr int TB = kChunk;                  // tokens per block, one per lane of the gate scan
+    static constexpr int P = D + 16;                   // row pitch (elements) of the tiles
+    static constexpr int VPL = 16 / E;                 // elements per 16-byte piece
+    static constexpr int PPR = D / VPL;                // pieces per row
+    static constexpr int NPT = TB * PPR / kPThreads;   // key (and value) pieces per thread
+    static_assert(TB == 64 && NPT * kPThreads == TB * PPR, "block mapping");
+    static_assert(PPR == 8 || PPR == 16, "a key row spans 8 or 16 lanes");
+    static constexpr size_t TILE = size_t(TB) * P * E;
+    static constexpr size_t K_OFF = 0;         // key operand, two buffers
+    static constexpr size_t V_OFF = 2 * TILE;  // values, two buffers
+    static constexpr size_t G_OFF = 4 * TILE;  // log2 gates, two buffers of TB floats
+    static constexpr size_t TOTAL = G_OFF + 2 * size_t(TB) * 4;
+    static_assert(TOTAL <= 160 * 1024, "LDS budget of a gfx950 workgroup exceeded");
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kPThreads) void segment_state_scalar_kernel(PrefillParams p) {
+    typedef SegLayoutScalar<T, D> SL;
+    typedef Mfma<T> M;
+    typedef StateTiles<D> ST;
+    constexpr int RTW = ST::NTT >= 8 ? 2 : 1;  // state row tiles per wave
+    constexpr int CTW = ST::TPW / RTW;          // state column tiles per wave
+    static_assert(RTW * CTW == ST::TPW && (ST::NTT / RTW) * (ST::NTT / CTW) == kPWaves, "state tiling");
+    static_assert(SL::TB % M::KSTEP == 0, "whole MFMA steps per block");
+    __shared__ __align__(16) char smem[SL::TOTAL];
+
+    const int s = blockIdx.x;
+    const int h = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int64_t row_stride = int64_t(p.H_kv) * D;
+    const T* kbase = static_cast<const T*>(p.k) + (b * p.T * p.H_kv + h) * D;
+    const T* vbase = static_cast<const T*>(p.v) + (b * p.T * p.H_kv + h) * D;
+    const int64_t tok0 = int64_t(s) * p.cps * kChunk;  // never the last segment: whole chunks
+    const int ntok = int(p.cps) * kChunk;
+
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // a register quadruple, not a struct
+    u32x4 kr[SL::NPT], vr[SL::NPT];
+    auto issue = [&](int blk0) {
+        const int tid = ltid();
+#pragma unroll
+        for (int n = 0; n < SL::NPT; ++n) {
+            const int idx = tid + n * kPThreads;
+            const int64_t off = (tok0 + blk0 + idx / SL::PPR) * row_stride + (idx % SL::PPR) * SL::VPL;
+            kr[n] = *reinterpret_cast<const u32x4*>(kbase + off);
+            vr[n] = *reinterpret_cast<const u32x4*>(vbase + off);
+        }
+    };
+    auto red_max = [](float v) {
+        v = group8_max(v);
+        if (SL::PPR == 16) v = fmaxf(v, dpp<kDppMirror>(v));
+        return v;
+    };
+    auto red_sum = [](float v) {
+        v = group8_sum(v);
+        if (SL::PPR == 16) v += dpp<kDppMirror>(v);
+        return v;
+    };
+
+    f32x4_t acc[ST::TPW];
+#pragma unroll
+    for (int u = 0; u < ST::TPW; ++u) acc[u] = zero4();
+    float lgs = 0.0f;  // log2 decay of the segment so far (the same for every channel)
+    issue(0);
+    for (int blk0 = 0, buf = 0; blk0 < ntok; blk0 += SL::TB, buf ^= 1) {
+        T* Kop = reinterpret_cast<T*>(smem + SL::K_OFF + buf * SL::TILE);
+        T* Vs = reinterpret_cast<T*>(smem + SL::V_OFF + buf * SL::TILE);
+        float* ell = reinterpret_cast<float*>(smem + SL::G_OFF) + buf * SL::TB;
+        const int tid = ltid();
+
+        // (a) values committed, key pieces converted, next block's loads issued
+        float ex[SL::NPT][SL::VPL];
+#pragma unroll
+        for (int n = 0; n < SL::NPT; ++n) {
+            const int idx = tid + n * kPThreads;
+            *reinterpret_cast<u32x4*>(Vs + (idx / SL::PPR) * SL::P + (idx % SL::PPR) * SL::VPL) = vr[n];
+            const unsigned w[4] = {kr[n].x, kr[n].y, kr[n].z, kr[n].w};
+#pragma unroll
+            for (int i = 0; i < SL::VPL; ++i) {
+                if constexpr (sizeof(T) == 2)  // element i is the low (even i) or high half of word i / 2
+                    ex[n][i] = __uint_as_float(i % 2 == 0 ? w[i / 2] << 16 : w[i / 2] & 0xffff0000u);
+                else
+                    ex[n][i] = __uint_as_float(w[i]);
+            }
+        }
+        if (blk0 + SL::TB < ntok) issue(blk0 + SL::TB);
+        float kiv[SL::NPT];
+#pragma unroll
+        for (int n = 0; n < SL::NPT; ++n) {
+            const int idx = tid + n * kPThreads;
+            const int j = idx / SL::PPR;
+            float mx = -INFINITY, sraw = 0.f;
+#pragma unroll
+            for (int i = 0; i < SL::VPL; ++i) {
+                mx = fmaxf(mx, ex[n][i]);
+                sraw += ex[n][i];
+            }
+            mx = red_max(mx) * kLog2e;
+            float se = 0.f;
+#pragma unroll
+            for (int i = 0; i < SL::VPL; ++i) {
+                ex[n][i] = fast_exp2(fmaf(ex[n][i], kLog2e, -mx));
+                se += ex[n][i];
+            }
+            kiv[n] = fast_rcp(red_sum(se));
+            sraw = red_sum(sraw);
+            if (idx % SL::PPR == 0) ell[j] = log2_sigmoid(sraw * (1.0f / D));
+        }
+        lds_barrier();
+
+        // (b) suffix sums of the gates (each wave for itself), key operand
+        const int lane = tid & 63;
+        const float incl = wave_suffix_sum(ell[lane]);  // sum of the gates of tokens >= lane
+        const float tot = readlane_f(incl, 0);          // the whole block
+#pragma unroll
+        for (int n = 0; n < SL::NPT; ++n) {
+            const int idx = tid + n * kPThreads;
+            const int j = idx / SL::PPR;
+            float after = __shfl(incl, (j + 1) & 63, 64);  // the gates after token j
+            if (j == SL::TB - 1) after = 0.0f;
+            const float f = kiv[n] * fast_exp2(after);
+            float y[SL::VPL];
+#pragma unroll
+            for (int i = 0; i < SL::VPL; ++i) y[i] = f * ex[n][i];
+            T* e = Kop + j * SL::P + (idx % SL::PPR) * SL::VPL;
+            if constexpr (sizeof(T) == 2) {
+                *reinterpret_cast<uint4*>(e) = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                                                          pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+            } else {
+                *reinterpret_cast<float4*>(e) = make_float4(y[0], y[1], y[2], y[3]);
+            }
+        }
+        lds_barrier();
+
+        // (c) acc <- 2^tot acc + Kop^T V; wave w owns row tiles rt0 .. rt0+RTW-1
+        // and column tiles ct0 .. ct0+CTW-1
+        {
+            const int wave = tid >> 6;
+            const int col = lane & 15, g = lane >> 4;
+            const int rt0 = (wave % (ST::NTT / RTW)) * RTW;
+            const int ct0 = (wave / (ST::NTT / RTW)) * CTW;
+            const float f = fast_exp2(tot);
+#pragma unroll
+            for (int u = 0; u < ST::TPW; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[u][r] *= f;
+#pragma unroll
+            for (int ks = 0; ks < SL::TB / M::KSTEP; ++ks) {
+                typename M::frag af[RTW], bv[CTW];
+#pragma unroll
+                for (int a = 0; a < RTW; ++a) {
+                    if constexpr (sizeof(T) == 2) af[a] = load_key_frag(Kop, SL::P, M::KSTEP * ks, 16 * (rt0 + a), lane);
+                    else af[a] = Kop[(M::KSTEP * ks + g) * SL::P + 16 * (rt0 + a) + col];
+                }
+#pragma unroll
+                for (int tt = 0; tt < CTW; ++tt) {
+                    if constexpr (sizeof(T) == 2) bv[tt] = load_key_frag(Vs, SL::P, M::KSTEP * ks, 16 * (ct0 + tt), lane);
+                    else bv[tt] = Vs[(M::KSTEP * ks + g) * SL::P + 16 * (ct0 + tt) + col];
+                }
+#pragma unroll
+                for (int tt = 0; tt < CTW; ++tt)
+#pragma unroll
+                    for (int a = 0; a < RTW; ++a) acc[a * CTW + tt] = M::mma(af[a], bv[tt], acc[a * CTW + tt]);
+            }
+            lgs += tot;
+        }
+        // no barrier: the next block writes the other buffers, and the block
+        // after it writes these only after the next block's first barrier
+    }
+    const size_t rec = size_t(D) * D + D;
+    float* dst = p.carry + ((size_t(b) * p.H_kv + h) * size_t(p.n_seg - 1) + s) * rec;
+    {
+        const int lane = ltid() & 63, wave = ltid() >> 6;
+        const int col = lane & 15, g = lane >> 4;
+        const int rt0 = (wave % (ST::NTT / RTW)) * RTW;
+        const int ct0 = (wave / (ST::NTT / RTW)) * CTW;
+#pragma unroll
+        for (int a = 0; a < RTW; ++a)
+#pragma unroll
+            for (int tt = 0; tt < CTW; ++tt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dst[(16 * (rt0 + a) + 4 * g + r) * D + 16 * (ct0 + tt) + col] = acc[a * CTW + tt][r];
+    }
+    if (threadIdx.x < D) dst[size_t(D) * D + threadIdx.x] = lgs;
 }
 
 // ------------------------------------------------------------------ P2
@@ -1931,8 +2045,12 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     p.n_sink = a.n_sink;
     hipStream_t st = static_cast<hipStream_t>(a.stream);
     if (p.n_seg > 1 && (a.stage_mask & 1)) {
-        hipLaunchKernelGGL((segment_state_kernel<T, D, GATE>), dim3(unsigned(p.n_seg - 1), a.H_kv, unsigned(a.B)),
-                           dim3(kPThreads), 0, st, p);
+        if constexpr (GATE == 0)
+            hipLaunchKernelGGL((segment_state_scalar_kernel<T, D>), dim3(unsigned(p.n_seg - 1), a.H_kv, unsigned(a.B)),
+                               dim3(kPThreads), 0, st, p);
+        else
+            hipLaunchKernelGGL((segment_state_kernel<T, D, GATE>), dim3(unsigned(p.n_seg - 1), a.H_kv, unsigned(a.B)),
+                               dim3(kPThreads), 0, st, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
