@@ -994,17 +994,17 @@ __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams 
 // Scalar gate. Every channel of a token shares one log2 gate, so a block
 // needs one gate and one suffix sum per token, and the kernel takes two
 // barriers per block: the key operand and the value tile alternate between
-// two LDS buffers, so nothing written for block n+1 can overwrite what the
-// contraction of block n still reads.
+// two LDS buffers, so nothing written for one block can overwrite what the
+// contraction of the block before still reads. The blocks are taken from the
+// segment's end backwards.
 //   (a) from its loaded registers each thread commits its value pieces,
 //       converts its key pieces (the next block's loads then go into the same
 //       registers), forms the key-row softmax over the PPR lanes of the row and
 //       the token's log2 gate, and publishes the gate;          barrier
 //   (b) every wave forms the suffix sums of the block's gates itself (lane
 //       shifts and lane reads, no further barrier) and writes the key operand
-//       phik_j 2^(sum of the gates after j);                    barrier
-//   (c) acc <- 2^(block total) acc + Kop^T V; waves that finish early go on
-//       to (a) of the next block.
+//       phik_j 2^(gates after j, in this block and the later ones);  barrier
+//   (c) acc += Kop^T V, beside (a) of the next block.
 // A segment is a whole number of chunks, so every block is a full chunk and
 // no load needs a bounds test.
 template <typename T, int D>
@@ -1039,22 +1039,30 @@ __global__ __launch_bounds__(kPThreads) void segment_state_scalar_kernel(Prefill
     const int s = blockIdx.x;
     const int h = blockIdx.y;
     const int64_t b = blockIdx.z;
-    const int64_t row_stride = int64_t(p.H_kv) * D;
-    const T* kbase = static_cast<const T*>(p.k) + (b * p.T * p.H_kv + h) * D;
-    const T* vbase = static_cast<const T*>(p.v) + (b * p.T * p.H_kv + h) * D;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int64_t tok0 = int64_t(s) * p.cps * kChunk;  // never the last segment: whole chunks
-    const int ntok = int(p.cps) * kChunk;
+    const int nblk = int(p.cps);                        // blocks of one chunk each
+    const int64_t blk_stride = int64_t(SL::TB) * p.H_kv * D;  // elements between consecutive blocks
+    // this thread's pieces of the segment's first block (token row idx / PPR, piece idx % PPR)
+    const T* kp[SL::NPT];
+    const T* vp[SL::NPT];
+#pragma unroll
+    for (int n = 0; n < SL::NPT; ++n) {
+        const int idx = tid + n * kPThreads;
+        const int64_t off = ((b * p.T + tok0 + idx / SL::PPR) * p.H_kv + h) * D + (idx % SL::PPR) * SL::VPL;
+        kp[n] = static_cast<const T*>(p.k) + off;
+        vp[n] = static_cast<const T*>(p.v) + off;
+    }
 
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // a register quadruple, not a struct
     u32x4 kr[SL::NPT], vr[SL::NPT];
-    auto issue = [&](int blk0) {
-        const int tid = ltid();
+    auto issue = [&](int it) {  // the it-th block taken, counted from the segment's end
+        const int64_t o = int64_t(nblk - 1 - it) * blk_stride;
 #pragma unroll
         for (int n = 0; n < SL::NPT; ++n) {
-            const int idx = tid + n * kPThreads;
-            const int64_t off = (tok0 + blk0 + idx / SL::PPR) * row_stride + (idx % SL::PPR) * SL::VPL;
-            kr[n] = *reinterpret_cast<const u32x4*>(kbase + off);
-            vr[n] = *reinterpret_cast<const u32x4*>(vbase + off);
+            kr[n] = *reinterpret_cast<const u32x4*>(kp[n] + o);
+            vr[n] = *reinterpret_cast<const u32x4*>(vp[n] + o);
         }
     };
     auto red_max = [](float v) {
@@ -1067,24 +1075,20 @@ __global__ __launch_bounds__(kPThreads) void segment_state_scalar_kernel(Prefill
         if (SL::PPR == 16) v += dpp<kDppMirror>(v);
         return v;
     };
+    auto Kop = [&](int buf) { return reinterpret_cast<T*>(smem + SL::K_OFF + buf * SL::TILE); };
+    auto Vs = [&](int buf) { return reinterpret_cast<T*>(smem + SL::V_OFF + buf * SL::TILE); };
+    auto ell = [&](int buf) { return reinterpret_cast<float*>(smem + SL::G_OFF) + buf * SL::TB; };
 
-    f32x4_t acc[ST::TPW];
-#pragma unroll
-    for (int u = 0; u < ST::TPW; ++u) acc[u] = zero4();
-    float lgs = 0.0f;  // log2 decay of the segment so far (the same for every channel)
-    issue(0);
-    for (int blk0 = 0, buf = 0; blk0 < ntok; blk0 += SL::TB, buf ^= 1) {
-        T* Kop = reinterpret_cast<T*>(smem + SL::K_OFF + buf * SL::TILE);
-        T* Vs = reinterpret_cast<T*>(smem + SL::V_OFF + buf * SL::TILE);
-        float* ell = reinterpret_cast<float*>(smem + SL::G_OFF) + buf * SL::TB;
-        const int tid = ltid();
-
-        // (a) values committed, key pieces converted, next block's loads issued
-        float ex[SL::NPT][SL::VPL];
+    // (a) of a block whose loads are in kr/vr: values committed, key pieces
+    // converted, the block after it issued into the same registers, key-row
+    // statistics and the token gates (published to LDS)
+    float ex[SL::NPT][SL::VPL];
+    float kiv[SL::NPT];
+    auto convert_commit = [&](int it, int buf) {
 #pragma unroll
         for (int n = 0; n < SL::NPT; ++n) {
             const int idx = tid + n * kPThreads;
-            *reinterpret_cast<u32x4*>(Vs + (idx / SL::PPR) * SL::P + (idx % SL::PPR) * SL::VPL) = vr[n];
+            *reinterpret_cast<u32x4*>(Vs(buf) + (idx / SL::PPR) * SL::P + (idx % SL::PPR) * SL::VPL) = vr[n];
             const unsigned w[4] = {kr[n].x, kr[n].y, kr[n].z, kr[n].w};
 #pragma unroll
             for (int i = 0; i < SL::VPL; ++i) {
@@ -1094,12 +1098,12 @@ __global__ __launch_bounds__(kPThreads) void segment_state_scalar_kernel(Prefill
                     ex[n][i] = __uint_as_float(w[i]);
             }
         }
-        if (blk0 + SL::TB < ntok) issue(blk0 + SL::TB);
-        float kiv[SL::NPT];
+        if (it + 1 < nblk) issue(it + 1);
+    };
+    auto stats = [&](int buf) {
 #pragma unroll
         for (int n = 0; n < SL::NPT; ++n) {
             const int idx = tid + n * kPThreads;
-            const int j = idx / SL::PPR;
             float mx = -INFINITY, sraw = 0.f;
 #pragma unroll
             for (int i = 0; i < SL::VPL; ++i) {
@@ -1115,25 +1119,26 @@ __global__ __launch_bounds__(kPThreads) void segment_state_scalar_kernel(Prefill
             }
             kiv[n] = fast_rcp(red_sum(se));
             sraw = red_sum(sraw);
-            if (idx % SL::PPR == 0) ell[j] = log2_sigmoid(sraw * (1.0f / D));
+            // every lane of the row stores the same value: no branch splits the region
+            ell(buf)[idx / SL::PPR] = log2_sigmoid(sraw * (1.0f / D));
         }
-        lds_barrier();
-
-        // (b) suffix sums of the gates (each wave for itself), key operand
-        const int lane = tid & 63;
-        const float incl = wave_suffix_sum(ell[lane]);  // sum of the gates of tokens >= lane
-        const float tot = readlane_f(incl, 0);          // the whole block
+    };
+    // (b) suffix sums of the block's gates (each wave for itself), key operand
+    // phik_j 2^(gates after j in the block + later), later = the gates of the
+    // blocks after this one
+    auto scan_operand = [&](int buf, float later) {
+        const float incl = wave_suffix_sum(ell(buf)[lane]);  // sum of the gates of tokens >= lane
 #pragma unroll
         for (int n = 0; n < SL::NPT; ++n) {
             const int idx = tid + n * kPThreads;
             const int j = idx / SL::PPR;
             float after = __shfl(incl, (j + 1) & 63, 64);  // the gates after token j
             if (j == SL::TB - 1) after = 0.0f;
-            const float f = kiv[n] * fast_exp2(after);
+            const float f = kiv[n] * fast_exp2(after + later);
             float y[SL::VPL];
 #pragma unroll
             for (int i = 0; i < SL::VPL; ++i) y[i] = f * ex[n][i];
-            T* e = Kop + j * SL::P + (idx % SL::PPR) * SL::VPL;
+            T* e = Kop(buf) + j * SL::P + (idx % SL::PPR) * SL::VPL;
             if constexpr (sizeof(T) == 2) {
                 *reinterpret_cast<uint4*>(e) = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
                                                           pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
@@ -1141,59 +1146,71 @@ __global__ __launch_bounds__(kPThreads) void segment_state_scalar_kernel(Prefill
                 *reinterpret_cast<float4*>(e) = make_float4(y[0], y[1], y[2], y[3]);
             }
         }
-        lds_barrier();
-
-        // (c) acc <- 2^tot acc + Kop^T V; wave w owns row tiles rt0 .. rt0+RTW-1
-        // and column tiles ct0 .. ct0+CTW-1
-        {
-            const int wave = tid >> 6;
-            const int col = lane & 15, g = lane >> 4;
-            const int rt0 = (wave % (ST::NTT / RTW)) * RTW;
-            const int ct0 = (wave / (ST::NTT / RTW)) * CTW;
-            const float f = fast_exp2(tot);
+        return readlane_f(incl, 0);  // the whole block
+    };
+    // (c) acc += Kop^T V; wave w owns row tiles rt0 .. rt0+RTW-1 and column
+    // tiles ct0 .. ct0+CTW-1
+    f32x4_t acc[ST::TPW];
 #pragma unroll
-            for (int u = 0; u < ST::TPW; ++u)
+    for (int u = 0; u < ST::TPW; ++u) acc[u] = zero4();
+    const int col = lane & 15, g = lane >> 4;
+    const int rt0 = (wave % (ST::NTT / RTW)) * RTW;
+    const int ct0 = (wave / (ST::NTT / RTW)) * CTW;
+    auto contract = [&](int buf) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[u][r] *= f;
+        for (int ks = 0; ks < SL::TB / M::KSTEP; ++ks) {
+            typename M::frag af[RTW], bv[CTW];
 #pragma unroll
-            for (int ks = 0; ks < SL::TB / M::KSTEP; ++ks) {
-                typename M::frag af[RTW], bv[CTW];
-#pragma unroll
-                for (int a = 0; a < RTW; ++a) {
-                    if constexpr (sizeof(T) == 2) af[a] = load_key_frag(Kop, SL::P, M::KSTEP * ks, 16 * (rt0 + a), lane);
-                    else af[a] = Kop[(M::KSTEP * ks + g) * SL::P + 16 * (rt0 + a) + col];
-                }
-#pragma unroll
-                for (int tt = 0; tt < CTW; ++tt) {
-                    if constexpr (sizeof(T) == 2) bv[tt] = load_key_frag(Vs, SL::P, M::KSTEP * ks, 16 * (ct0 + tt), lane);
-                    else bv[tt] = Vs[(M::KSTEP * ks + g) * SL::P + 16 * (ct0 + tt) + col];
-                }
-#pragma unroll
-                for (int tt = 0; tt < CTW; ++tt)
-#pragma unroll
-                    for (int a = 0; a < RTW; ++a) acc[a * CTW + tt] = M::mma(af[a], bv[tt], acc[a * CTW + tt]);
+            for (int a = 0; a < RTW; ++a) {
+                if constexpr (sizeof(T) == 2) af[a] = load_key_frag(Kop(buf), SL::P, M::KSTEP * ks, 16 * (rt0 + a), lane);
+                else af[a] = Kop(buf)[(M::KSTEP * ks + g) * SL::P + 16 * (rt0 + a) + col];
             }
-            lgs += tot;
-        }
-        // no barrier: the next block writes the other buffers, and the block
-        // after it writes these only after the next block's first barrier
-    }
-    const size_t rec = size_t(D) * D + D;
-    float* dst = p.carry + ((size_t(b) * p.H_kv + h) * size_t(p.n_seg - 1) + s) * rec;
-    {
-        const int lane = ltid() & 63, wave = ltid() >> 6;
-        const int col = lane & 15, g = lane >> 4;
-        const int rt0 = (wave % (ST::NTT / RTW)) * RTW;
-        const int ct0 = (wave / (ST::NTT / RTW)) * CTW;
 #pragma unroll
-        for (int a = 0; a < RTW; ++a)
+            for (int tt = 0; tt < CTW; ++tt) {
+                if constexpr (sizeof(T) == 2) bv[tt] = load_key_frag(Vs(buf), SL::P, M::KSTEP * ks, 16 * (ct0 + tt), lane);
+                else bv[tt] = Vs(buf)[(M::KSTEP * ks + g) * SL::P + 16 * (ct0 + tt) + col];
+            }
 #pragma unroll
             for (int tt = 0; tt < CTW; ++tt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    dst[(16 * (rt0 + a) + 4 * g + r) * D + 16 * (ct0 + tt) + col] = acc[a * CTW + tt][r];
+                for (int a = 0; a < RTW; ++a) acc[a * CTW + tt] = M::mma(af[a], bv[tt], acc[a * CTW + tt]);
+        }
+    };
+
+    // The blocks are taken last to first, so the decay of the blocks after a
+    // block is already known when its key operand is formed and the running
+    // state is never rescaled. Block n's contraction (LDS and MFMA work)
+    // shares a region with the statistics of the block before it (VALU
+    // work): the two use different buffers, and the block after that
+    // overwrites block n's buffers only after the next first barrier.
+    float lgs = 0.0f;  // log2 decay of the blocks taken so far (the same for every channel)
+    issue(0);
+    convert_commit(0, 0);
+    stats(0);
+    for (int it = 0; it < nblk; ++it) {
+        const int buf = it & 1;
+        lds_barrier();  // this block's gates and values are visible
+        const float tot = scan_operand(buf, lgs);
+        lds_barrier();  // this block's key operand is visible
+        if (it + 1 < nblk) {
+            convert_commit(it + 1, buf ^ 1);
+            contract(buf);
+            stats(buf ^ 1);
+        } else {
+            contract(buf);
+        }
+        lgs += tot;
     }
-    if (threadIdx.x < D) dst[size_t(D) * D + threadIdx.x] = lgs;
+    const size_t rec = size_t(D) * D + D;
+    float* dst = p.carry + ((size_t(b) * p.H_kv + h) * size_t(p.n_seg - 1) + s) * rec;
+#pragma unroll
+    for (int a = 0; a < RTW; ++a)
+#pragma unroll
+        for (int tt = 0; tt < CTW; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[(16 * (rt0 + a) + 4 * g + r) * D + 16 * (ct0 + tt) + col] = acc[a * CTW + tt][r];
+    if (tid < D) dst[size_t(D) * D + tid] = lgs;
 }
 
 // ------------------------------------------------------------------ P2
