@@ -89,20 +89,28 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-// Inclusive suffix sum over the 64 lanes of a wave: lane l gets the sum of v
-// over lanes l .. 63. Row shifts build the suffix inside each 16-lane row;
-// the totals of the later rows come from lane reads.
-__device__ __forceinline__ float wave_suffix_sum(float v) {
+// Inclusive suffix sum over aligned groups of G (32 or 64) lanes: lane l
+// gets the sum of v over the lanes of its group from l on. Row shifts build
+// the suffix inside each 16-lane row; the totals of the later rows of the
+// group come from lane reads.
+template <int G = 64>
+__device__ __forceinline__ float group_suffix_sum(float v) {
+    static_assert(G == 32 || G == 64, "a group is half a wave or a wave");
     v += dpp<kDppRowShl1>(v);
     v += dpp<kDppRowShl2>(v);
     v += dpp<kDppRowShl4>(v);
     v += dpp<kDppRowShl8>(v);
-    const float r1 = readlane_f(v, 16), r2 = readlane_f(v, 32), r3 = readlane_f(v, 48);
-    const float r23 = r2 + r3;
     const int row = (threadIdx.x & 63) >> 4;
-    const float later = row == 0 ? r1 + r23 : row == 1 ? r23 : row == 2 ? r3 : 0.0f;
-    return v + later;
+    if constexpr (G == 64) {
+        const float r1 = readlane_f(v, 16), r2 = readlane_f(v, 32), r3 = readlane_f(v, 48);
+        const float r23 = r2 + r3;
+        return v + (row == 0 ? r1 + r23 : row == 1 ? r23 : row == 2 ? r3 : 0.0f);
+    } else {
+        const float r1 = readlane_f(v, 16), r3 = readlane_f(v, 48);
+        return v + (row == 0 ? r1 : row == 2 ? r3 : 0.0f);
+    }
 }
+__device__ __forceinline__ float wave_suffix_sum(float v) { return group_suffix_sum<64>(v); }
 
 // All-reduce over aligned groups of 8 lanes.
 __device__ __forceinline__ float group8_max(float v) {

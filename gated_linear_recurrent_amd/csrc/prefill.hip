@@ -904,12 +904,7 @@ __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams 
             float own = 0.f;
 #pragma unroll
             for (int t = 0; t < TPL; ++t) own += lg2[t][i];
-            float incl = own;
-#pragma unroll
-            for (int o = 1; o < LPP; o <<= 1) {
-                const float y = __shfl_down(incl, o, LPP);
-                if (l + o < LPP) incl += y;
-            }
+            const float incl = group_suffix_sum<LPP>(own);
             after[i] = incl - own;
             if (l == 0) tot[c0 + i] = incl;
         }
