@@ -80,6 +80,9 @@ constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8 lanes
 constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16 lanes
 constexpr int kDppRowShr1 = 0x111;
 
+constexpr int kDppRowShr2 = 0x112;    // lane i <- lane i-2 within its row (0 before the row start)
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
 constexpr int kDppRowShl1 = 0x101;    // lane i <- lane i+1 within its row (0 past the row end)
 constexpr int kDppRowShl2 = 0x102;
 constexpr int kDppRowShl4 = 0x104;
@@ -111,6 +114,20 @@ __device__ __forceinline__ float group_suffix_sum(float v) {
     }
 }
 __device__ __forceinline__ float wave_suffix_sum(float v) { return group_suffix_sum<64>(v); }
+
+// Inclusive prefix sum over the 64 lanes of a wave: lane l gets the sum of v
+// over lanes 0 .. l (row shifts inside each 16-lane row, then the totals of
+// the earlier rows from lane reads).
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+    v += dpp<kDppRowShr1>(v);
+    v += dpp<kDppRowShr2>(v);
+    v += dpp<kDppRowShr4>(v);
+    v += dpp<kDppRowShr8>(v);
+    const float r0 = readlane_f(v, 15), r1 = readlane_f(v, 31), r2 = readlane_f(v, 47);
+    const float r01 = r0 + r1;
+    const int row = (threadIdx.x & 63) >> 4;
+    return v + (row == 0 ? 0.0f : row == 1 ? r0 : row == 2 ? r01 : r01 + r2);
+}
 
 // All-reduce over aligned groups of 8 lanes.
 __device__ __forceinline__ float group8_max(float v) {

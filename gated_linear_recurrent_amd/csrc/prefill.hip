@@ -67,9 +67,9 @@ struct Layout {
     static constexpr size_t VT_OFF = K_OFF + size_t(NSLOT) * 64 * DP * E;     // V [slot][V_ELEMS]
     static constexpr size_t KB_OFF = VT_OFF + size_t(NSLOT) * V_ELEMS * E;    // K~ (state^T or intra)
     static constexpr size_t ST_OFF = KB_OFF + size_t(KB_ELEMS) * E;           // state region
-    // small persistent arrays: kmax[64] kinv[64] b2s[64] dec[D] mref[D] emref[D]
-    // blast[D] badlist[D] badmask[D/32] nbad, exact
-    static constexpr size_t SMALL_WORDS = 64 * 3 + D * 5 + D / 32 + 4;
+    // small persistent arrays: kmax[64] kinv[64] b2s[64] b2e[64] dec[D] mref[D]
+    // emref[D] blast[D] badlist[D] badmask[D/32] nbad, exact
+    static constexpr size_t SMALL_WORDS = 64 * 4 + D * 5 + D / 32 + 4;
     static constexpr size_t F_BYTES = (FULL && GATE) ? size_t(64) * FP * 4 : 0;
     static constexpr size_t TMP_FLOATS = size_t(kPThreads) + 3 * D;
     // Output kernels keep the running state in LDS as fp32 S^T [D][SP] when
@@ -109,7 +109,8 @@ struct Smem {
     float* b0;    // [D]
     float* kmax;  // [64]
     float* kinv;  // [64]
-    float* b2s;   // [64] scalar-gate cumulative log2 gate / scalar ell2 before the scan
+    float* b2s;   // [64] scalar-gate cumulative log2 gate
+    float* b2e;   // [64] scalar-gate log2 gate per token (the scan's input)
     float* dec;   // [D] 2^(b_last) per d_k row
     float* mref;  // [D] log2 reference per channel (0 for bad channels)
     float* emref; // [D] 2^mref
@@ -136,7 +137,8 @@ struct Smem {
         kmax = sm;
         kinv = sm + 64;
         b2s = sm + 128;
-        dec = sm + 192;
+        b2e = sm + 192;
+        dec = sm + 256;
         mref = dec + D;
         emref = mref + D;
         blast = emref + D;
@@ -375,22 +377,7 @@ __device__ __forceinline__ void key_row_stats(const Smem<T, D, GATE, FULL>& sm, 
         const bool ok = j < nvalid;
         sm.kmax[j] = mx;
         sm.kinv[j] = ok ? fast_rcp(se) : 0.0f;
-        if (GATE == 0) sm.b2s[j] = ok ? log2_sigmoid(sraw * (1.0f / D)) : 0.0f;
-    }
-}
-
-// Scalar gate: inclusive prefix sum of ell2 over the chunk (one wave).
-template <typename T, int D, int GATE, bool FULL>
-__device__ __forceinline__ void scalar_gate_scan(const Smem<T, D, GATE, FULL>& sm) {
-    if (ltid() < 64) {
-        const int lane = ltid();
-        float x = sm.b2s[lane];
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const float y = __shfl_up(x, o, 64);
-            if (lane >= o) x += y;
-        }
-        sm.b2s[lane] = x;
+        if (GATE == 0) sm.b2e[j] = ok ? log2_sigmoid(sraw * (1.0f / D)) : 0.0f;
     }
 }
 
@@ -597,12 +584,17 @@ __device__ __forceinline__ void gate_stats(const Smem<T, D, GATE, FULL>& sm, int
     key_row_stats(sm, slot, nvalid);
     __syncthreads();
     if (GATE == 0) {
-        scalar_gate_scan(sm);
-        __syncthreads();
-        const float bl = sm.b2s[nvalid - 1];
+        // Every wave forms the inclusive prefix of the chunk's gates itself
+        // (lane shifts and lane reads); wave 0 publishes it. With the resident
+        // state, b2s is next read after the caller's barrier; gate_prep reads
+        // it right away and keeps the barrier.
+        const float pre = wave_prefix_sum(sm.b2e[ltid() & 63]);
+        if (ltid() < 64) sm.b2s[ltid()] = pre;
+        if constexpr (!(FULL && L::SLDS)) __syncthreads();
+        const float bl = readlane_f(pre, nvalid - 1);
         // reference for the factorised intra-chunk decay: the middle token
-        const float m = sm.b2s[nvalid - 1 < 31 ? nvalid - 1 : 31];
-        const bool ex = fmaxf(sm.b2s[0] - m, m - bl) > kEmax2;
+        const float m = readlane_f(pre, nvalid - 1 < 31 ? nvalid - 1 : 31);
+        const bool ex = fmaxf(readlane_f(pre, 0) - m, m - bl) > kEmax2;
         if (ltid() < D) {
             sm.dec[ltid()] = fast_exp2(bl);
             sm.mref[ltid()] = ex ? 0.0f : m;
