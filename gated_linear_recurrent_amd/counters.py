@@ -59,9 +59,9 @@ KERNELS = {
                                          "prefill_1b_b4_t2048_d64",
                                          ["gated_linear_recurrent_amd/csrc/prefill.hip",
                                           "gated_linear_recurrent_amd/csrc/device_common.h"]),
-    "segment_state_kernel": ("liger::segment_state_kernel<unsigned short, 128, 0>", "prefill_8b_b1_t8192_d128",
-                             ["gated_linear_recurrent_amd/csrc/prefill.hip",
-                              "gated_linear_recurrent_amd/csrc/device_common.h"]),
+    "segment_state_scalar_kernel": ("liger::segment_state_scalar_kernel<unsigned short, 128>", "prefill_8b_b1_t8192_d128",
+                                    ["gated_linear_recurrent_amd/csrc/prefill.hip",
+                                     "gated_linear_recurrent_amd/csrc/device_common.h"]),
     "decode_step_kernel": ("liger::decode_step_kernel<unsigned short, 128, 1, 4, false>", "decode_8b_n64_d128",
                            ["gated_linear_recurrent_amd/csrc/decode.hip",
                             "gated_linear_recurrent_amd/csrc/device_common.h"]),
