@@ -1201,33 +1201,39 @@ __global__ __launch_bounds__(kPThreads) void segment_state_scalar_kernel(Prefill
 }
 
 // ------------------------------------------------------------------ P2
-// One thread per state element; the carries of up to BATCH segments are
-// loaded before the first multiply-add so their latencies overlap.
+// One thread per state element. The decays of up to BATCH segment records
+// come with one load per wave (lane u holds record u's, exponentiated once
+// and read out with a lane read); the record elements are all loaded, in
+// order, before the first multiply-add, so each step waits only for its own
+// record while the stores of the steps before it drain.
 template <int D>
 __global__ __launch_bounds__(256) void carry_scan_kernel(float* __restrict__ carry, const float* __restrict__ S0,
                                                           int64_t n_seg, int H_kv) {
     constexpr int BATCH = 32;
+    static_assert(D % 64 == 0, "a wave covers one row of the state, or half of it");
     const int e = blockIdx.x * 256 + threadIdx.x;  // D*D is a multiple of 256
+    const int lane = threadIdx.x & 63;
     const int h = blockIdx.y;
     const int64_t b = blockIdx.z;
     const size_t rec = size_t(D) * D + D;
     float* base = carry + (size_t(b) * H_kv + h) * size_t(n_seg - 1) * rec;
-    const int r = e / D;
+    const int r = e / D;  // the same for every lane of a wave
+    const int64_t last = n_seg - 2;
     float acc = S0 ? S0[(size_t(b) * H_kv + h) * D * D + e] : 0.f;
     for (int64_t s0 = 0; s0 < n_seg - 1; s0 += BATCH) {
-        float Ls[BATCH], lg[BATCH];
+        const int64_t sl = s0 + lane < last ? s0 + lane : last;
+        const float dec = fast_exp2(base[sl * rec + size_t(D) * D + r]);  // lane u: record s0 + u
+        float Ls[BATCH];
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
-            if (s0 + u < n_seg - 1) {
-                const float* recp = base + (s0 + u) * rec;
-                Ls[u] = recp[e];
-                lg[u] = recp[size_t(D) * D + r];
-            }
+            const int64_t sr = s0 + u < last ? s0 + u : last;  // past the last record it is read again
+            Ls[u] = base[sr * rec + e];
+            __builtin_amdgcn_sched_barrier(0);  // issue order = record order
         }
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
             if (s0 + u < n_seg - 1) {
-                acc = fast_exp2(lg[u]) * acc + Ls[u];
+                acc = readlane_f(dec, u) * acc + Ls[u];
                 base[(s0 + u) * rec + e] = acc;
             }
         }
