@@ -20,7 +20,7 @@
 // the same K/V tiles: the current chunk plus the previous one.
 //
 // Three kernels (sequence parallelism over segments of `cps` chunks):
-//   P1 segment_state_kernel : local end state L_s (from zero) and total log2
+//   P1 segment_state_*_kernel: local end state L_s (from zero) and total log2
 //                             decay of every segment but the last
 //   P2 carry_scan_kernel    : S_in[s+1] = 2^(lg_s) (.) S_in[s] + L_s, in place
 //   P3 prefill_output_kernel: per segment, walks its chunks from S_in[s],
@@ -738,140 +738,149 @@ __device__ __forceinline__ void intra_key_operand(const Smem<T, D, GATE, FULL>& 
 // contraction over the block's tokens added to the running state rescaled by
 // the block's decay. The vector gate (a log2 gate per channel) and the scalar
 // gate (one per token) have a kernel each.
+// Vector gate. The gate differs per channel, so each block needs a suffix
+// sum per (token, channel): the lanes of a group share one 16-byte channel
+// piece over a run of tokens (thread tid: piece tid / LPP, tokens
+// TPL (tid % LPP) ..), the 4-tap pooled input comes from the piece and three
+// neighbouring elements of the raw key row, and the suffix sums run over
+// the lane group with DPP row shifts. Two barriers per block: the raw key
+// tile, the value tile and the key operand alternate between two LDS
+// buffers, and the operand has a buffer of its own, so it can be written
+// while other lanes still read raw keys for their pooled inputs.
+//   (a) each thread commits its raw key and value pieces, and forms the
+//       softmax statistics of its key rows from its loaded registers (PPR
+//       lanes per row); the next block's loads go into the same
+//       registers;                                              barrier
+//   (b) pooled gates, suffix sums over the group and the key operand
+//       phik_j[c] 2^(gates after j in the block + later[c]), later = the
+//       gates of the blocks after this one (blocks are taken from the
+//       segment's end backwards, so the state is never rescaled);  barrier
+//   (c) acc += Kop^T V, beside (a) of the next block.
+// A segment is a whole number of chunks, so every block is a full chunk.
 template <typename T, int D>
-struct SegLayout {
+struct SegLayoutVector {
     static constexpr int E = sizeof(T);
-    // tokens per block: at d = 128 a 256-token segment is four blocks, each
-    // block's loads in flight during the previous one; at d = 64 two
-    static constexpr int TB = D >= 128 ? 64 : 128;
-    static constexpr int P = D + 16;                   // row pitch (elements) of the K and V tiles
+    static constexpr int TB = kChunk;                  // tokens per block
+    static constexpr int P = D + 16;                   // row pitch (elements) of the tiles
     static constexpr int VPL = 16 / E;                 // elements per 16-byte piece
     static constexpr int PPR = D / VPL;                // pieces per row
-    static constexpr int NPT = TB * PPR / kPThreads;   // K (and V) pieces per thread
-    static_assert(NPT * kPThreads == TB * PPR, "pieces per thread");
-    static constexpr size_t K_OFF = 0;
-    static constexpr size_t V_OFF = K_OFF + size_t(TB) * P * E;
-    static constexpr size_t F_OFF = V_OFF + size_t(TB) * P * E;
-    // fp32: kmax[TB] kinv[TB] ell[TB] tot[D] lg[D]
-    static constexpr size_t TOTAL = F_OFF + (3 * size_t(TB) + 2 * D) * 4;
+    static constexpr int NPT = TB * PPR / kPThreads;   // key (and value) pieces per thread
+    static constexpr int TPL = TB * PPR / kPThreads;   // tokens per lane in the gate phase
+    static constexpr int LPP = TB / TPL;               // lanes per channel piece in the gate phase
+    static_assert(TB == 64 && NPT * kPThreads == TB * PPR, "block mapping");
+    static_assert(PPR == 8 || PPR == 16, "a key row spans 8 or 16 lanes");
+    static_assert(LPP == 32 || LPP == 64, "a piece spans half a wave or a whole wave");
+    static constexpr size_t TILE = size_t(TB) * P * E;
+    static constexpr size_t K_OFF = 0;         // raw keys, two buffers
+    static constexpr size_t V_OFF = 2 * TILE;  // values, two buffers
+    static constexpr size_t O_OFF = 4 * TILE;  // key operand, two buffers
+    static constexpr size_t F_OFF = 6 * TILE;  // fp32: kmx[TB] kiv[TB]
+    static constexpr size_t TOTAL = F_OFF + 2 * size_t(TB) * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS budget of a gfx950 workgroup exceeded");
 };
 
-template <typename T, int D, int GATE>
-__global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams p) {
-    static_assert(GATE == 1, "the scalar gate has its own segment-state kernel");
-    typedef SegLayout<T, D> SL;
+template <typename T, int D>
+__global__ __launch_bounds__(kPThreads) void segment_state_vector_kernel(PrefillParams p) {
+    typedef SegLayoutVector<T, D> SL;
     typedef Mfma<T> M;
     typedef StateTiles<D> ST;
     constexpr int RTW = ST::NTT >= 8 ? 2 : 1;  // state row tiles per wave
     constexpr int CTW = ST::TPW / RTW;          // state column tiles per wave
     static_assert(RTW * CTW == ST::TPW && (ST::NTT / RTW) * (ST::NTT / CTW) == kPWaves, "state tiling");
+    static_assert(SL::TB % M::KSTEP == 0, "whole MFMA steps per block");
+    constexpr int VPL = SL::VPL, TPL = SL::TPL, LPP = SL::LPP;
     __shared__ __align__(16) char smem[SL::TOTAL];
-    T* Ks = reinterpret_cast<T*>(smem + SL::K_OFF);
-    T* Vs = reinterpret_cast<T*>(smem + SL::V_OFF);
-    float* kmax = reinterpret_cast<float*>(smem + SL::F_OFF);
-    float* kinv = kmax + SL::TB;
-    float* ell = kinv + SL::TB;     // scalar gate: log2 gate per token, then the sum after it
-    float* tot = ell + SL::TB;      // log2 decay of the whole block per channel
-    float* lg = tot + D;            // log2 decay of the segment so far per channel
+    float* kmx = reinterpret_cast<float*>(smem + SL::F_OFF);  // row max times log2 e
+    float* kiv = kmx + SL::TB;                                 // 1 / row sum of exponentials
 
     const int s = blockIdx.x;
     const int h = blockIdx.y;
     const int64_t b = blockIdx.z;
-    const int64_t row_stride = int64_t(p.H_kv) * D;
-    const T* kbase = static_cast<const T*>(p.k) + (b * p.T * p.H_kv + h) * D;
-    const T* vbase = static_cast<const T*>(p.v) + (b * p.T * p.H_kv + h) * D;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int64_t tok0 = int64_t(s) * p.cps * kChunk;  // never the last segment: whole chunks
-    const int ntok = int(p.cps) * kChunk;
+    const int nblk = int(p.cps);
+    const int64_t blk_stride = int64_t(SL::TB) * p.H_kv * D;
+    const T* kp[SL::NPT];
+    const T* vp[SL::NPT];
+#pragma unroll
+    for (int n = 0; n < SL::NPT; ++n) {
+        const int idx = tid + n * kPThreads;
+        const int64_t off = ((b * p.T + tok0 + idx / SL::PPR) * p.H_kv + h) * D + (idx % SL::PPR) * VPL;
+        kp[n] = static_cast<const T*>(p.k) + off;
+        vp[n] = static_cast<const T*>(p.v) + off;
+    }
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // a register quadruple, not a struct
+    u32x4 kr[SL::NPT], vr[SL::NPT];
+    auto issue = [&](int it) {  // the it-th block taken, counted from the segment's end
+        const int64_t o = int64_t(nblk - 1 - it) * blk_stride;
+#pragma unroll
+        for (int n = 0; n < SL::NPT; ++n) {
+            kr[n] = *reinterpret_cast<const u32x4*>(kp[n] + o);
+            vr[n] = *reinterpret_cast<const u32x4*>(vp[n] + o);
+        }
+    };
+    auto Kraw = [&](int buf) { return reinterpret_cast<T*>(smem + SL::K_OFF + buf * SL::TILE); };
+    auto Vs = [&](int buf) { return reinterpret_cast<T*>(smem + SL::V_OFF + buf * SL::TILE); };
+    auto Kop = [&](int buf) { return reinterpret_cast<T*>(smem + SL::O_OFF + buf * SL::TILE); };
 
-    uint4 kr[SL::NPT], vr[SL::NPT];
-    auto issue = [&](int blk0, int nb) {
-        const int tid = ltid();
+    // (a) raw pieces to LDS; row statistics from the registers
+    auto commit_stats = [&](int it, int buf) {
+        float mxs[SL::NPT], ses[SL::NPT];
 #pragma unroll
         for (int n = 0; n < SL::NPT; ++n) {
             const int idx = tid + n * kPThreads;
-            const int j = idx / SL::PPR;
-            const int64_t off = (tok0 + blk0 + j) * row_stride + (idx % SL::PPR) * SL::VPL;
-            kr[n] = make_uint4(0, 0, 0, 0);
-            vr[n] = make_uint4(0, 0, 0, 0);
-            if (j < nb) {
-                kr[n] = *reinterpret_cast<const uint4*>(kbase + off);
-                vr[n] = *reinterpret_cast<const uint4*>(vbase + off);
+            const int o = (idx / SL::PPR) * SL::P + (idx % SL::PPR) * VPL;
+            *reinterpret_cast<u32x4*>(Kraw(buf) + o) = kr[n];
+            *reinterpret_cast<u32x4*>(Vs(buf) + o) = vr[n];
+            const unsigned w[4] = {kr[n].x, kr[n].y, kr[n].z, kr[n].w};
+            float x[VPL];
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                if constexpr (sizeof(T) == 2)  // element i is the low (even i) or high half of word i / 2
+                    x[i] = __uint_as_float(i % 2 == 0 ? w[i / 2] << 16 : w[i / 2] & 0xffff0000u);
+                else
+                    x[i] = __uint_as_float(w[i]);
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) mx = fmaxf(mx, x[i]);
+            mx = group8_max(mx);
+            if (SL::PPR == 16) mx = fmaxf(mx, dpp<kDppMirror>(mx));
+            mx *= kLog2e;
+            float se = 0.f;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) se += fast_exp2(fmaf(x[i], kLog2e, -mx));
+            se = group8_sum(se);
+            if (SL::PPR == 16) se += dpp<kDppMirror>(se);
+            mxs[n] = mx;
+            ses[n] = se;
+        }
+        if (it + 1 < nblk) issue(it + 1);
+#pragma unroll
+        for (int n = 0; n < SL::NPT; ++n) {
+            const int idx = tid + n * kPThreads;
+            if (idx % SL::PPR == 0) {
+                kmx[idx / SL::PPR] = mxs[n];
+                kiv[idx / SL::PPR] = fast_rcp(ses[n]);
             }
         }
     };
 
-    f32x4_t acc[ST::TPW];
+    // (b) pooled gates, suffix sums, key operand; later[] carries the
+    // per-channel gates of the blocks already taken
+    const int c0 = (tid / LPP) * VPL;
+    const int l = tid % LPP;
+    float later[VPL];
 #pragma unroll
-    for (int u = 0; u < ST::TPW; ++u) acc[u] = zero4();
-    if (threadIdx.x < D) lg[threadIdx.x] = 0.0f;
-    issue(0, ntok < SL::TB ? ntok : SL::TB);
-    for (int blk0 = 0; blk0 < ntok; blk0 += SL::TB) {
-        const int nb = ntok - blk0 < SL::TB ? ntok - blk0 : SL::TB;  // a multiple of 64
-        {
-            const int tid = ltid();
-#pragma unroll
-            for (int n = 0; n < SL::NPT; ++n) {
-                const int idx = tid + n * kPThreads;
-                const int o = (idx / SL::PPR) * SL::P + (idx % SL::PPR) * SL::VPL;
-                *reinterpret_cast<uint4*>(Ks + o) = kr[n];
-                *reinterpret_cast<uint4*>(Vs + o) = vr[n];
-            }
-        }
-        __syncthreads();
-        if (blk0 + SL::TB < ntok) {  // next block in flight while this one is processed
-            const int rest = ntok - blk0 - SL::TB;
-            issue(blk0 + SL::TB, rest < SL::TB ? rest : SL::TB);
-        }
-
-        // key row statistics, eight lanes per row; rows past nb get 1/sum = 0
-        {
-            constexpr int NLD = D / (8 * SL::VPL);
-            const int tid = ltid();
-            const int sub = tid & 7;
-            for (int r0 = 0; r0 < SL::TB; r0 += kPThreads / 8) {
-                const int j = r0 + (tid >> 3);
-                const T* row = Ks + j * SL::P + sub * SL::VPL;
-                float x[NLD * SL::VPL];
-#pragma unroll
-                for (int q = 0; q < NLD; ++q) {
-                    const uint4 u = *reinterpret_cast<const uint4*>(row + q * 8 * SL::VPL);
-                    const T* e = reinterpret_cast<const T*>(&u);
-#pragma unroll
-                    for (int i = 0; i < SL::VPL; ++i) x[q * SL::VPL + i] = to_f32(e[i]);
-                }
-                float mx = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < NLD * SL::VPL; ++i) mx = fmaxf(mx, x[i]);
-                mx = group8_max(mx);
-                float se = 0.f;
-#pragma unroll
-                for (int i = 0; i < NLD * SL::VPL; ++i) se += fast_exp2((x[i] - mx) * kLog2e);
-                se = group8_sum(se);
-                if (sub == 0) {
-                    kmax[j] = mx;
-                    kinv[j] = j < nb ? fast_rcp(se) : 0.0f;
-                }
-            }
-        }
-        __syncthreads();
-        // Piece layout: the LPP lanes of a group share one 16-byte channel
-        // piece (channels c0 .. c0 + VPL - 1); lane l owns tokens TPL l ..
-        // TPL l + TPL - 1. The pooled input x_j[c] is the mean of k_j over
-        // the in-range channels c-1 .. c+2, formed from the piece and its
-        // three neighbouring elements (one before, two after).
-        constexpr int TPL = SL::TB * SL::PPR / kPThreads;  // tokens per lane
-        constexpr int LPP = SL::TB / TPL;                    // lanes per piece
-        static_assert(LPP == 32 || LPP == 64, "a piece spans half a wave or a whole wave");
-        constexpr int VPL = SL::VPL;
-        const int tid = ltid();
-        const int c0 = (tid / LPP) * VPL;
-        const int l = tid % LPP;
+    for (int i = 0; i < VPL; ++i) later[i] = 0.0f;
+    auto gate_operand = [&](int buf) {
+        const T* Kr = Kraw(buf);
         float lg2[TPL][VPL];  // log2 gate per (token, channel)
 #pragma unroll
         for (int t = 0; t < TPL; ++t) {
             const int j = TPL * l + t;
-            const T* row = Ks + j * SL::P;
+            const T* row = Kr + j * SL::P;
             const uint4 u = *reinterpret_cast<const uint4*>(row + c0);
             const T* pe = reinterpret_cast<const T*>(&u);
             float e[VPL + 3];  // channels c0 - 1 .. c0 + VPL + 1, zero outside the row
@@ -885,97 +894,102 @@ __global__ __launch_bounds__(kPThreads) void segment_state_kernel(PrefillParams 
                 const int c = c0 + i;
                 const float inv_cnt = (c == 0 || c == D - 2) ? (1.0f / 3.0f) : c == D - 1 ? 0.5f : 0.25f;
                 const float x = (e[i] + e[i + 1]) + (e[i + 2] + e[i + 3]);
-                lg2[t][i] = j < nb ? log2_sigmoid(x * inv_cnt) : 0.0f;
+                lg2[t][i] = log2_sigmoid(x * inv_cnt);
             }
         }
-        // sum of the gates after each token within the block: this lane's
-        // tokens, then the lanes after it (inclusive suffix over the group)
-        float after[VPL];
+        // the gates after each token: this lane's later tokens, then the
+        // lanes after it (inclusive suffix over the group), then later blocks
+        float after[VPL], tot[VPL];
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
             float own = 0.f;
 #pragma unroll
             for (int t = 0; t < TPL; ++t) own += lg2[t][i];
             const float incl = group_suffix_sum<LPP>(own);
-            after[i] = incl - own;
-            if (l == 0) tot[c0 + i] = incl;
+            after[i] = incl - own + later[i];
+            // the block's total: the group's first lane
+            tot[i] = LPP == 64 ? readlane_f(incl, 0) : (lane < 32 ? readlane_f(incl, 0) : readlane_f(incl, 32));
         }
-        __syncthreads();  // every pooled read of a neighbouring piece is done before K is overwritten
-        // key operand in place: phik_j (.) 2^(sum of the gates after j)
+        T* Ko = Kop(buf);
 #pragma unroll
         for (int t = TPL - 1; t >= 0; --t) {
             const int j = TPL * l + t;
-            T* row = Ks + j * SL::P + c0;
-            const uint4 u = *reinterpret_cast<const uint4*>(row);
+            const uint4 u = *reinterpret_cast<const uint4*>(Kr + j * SL::P + c0);
             const T* pe = reinterpret_cast<const T*>(&u);
-            const float m = kmax[j] * kLog2e, s = kinv[j];
+            const float m = kmx[j], sc = kiv[j];
             float y[VPL];
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
-                y[i] = s * fast_exp2(fmaf(to_f32(pe[i]), kLog2e, after[i] - m));
+                y[i] = sc * fast_exp2(fmaf(to_f32(pe[i]), kLog2e, after[i] - m));
                 after[i] += lg2[t][i];
             }
+            T* dst = Ko + j * SL::P + c0;
             if constexpr (sizeof(T) == 2) {
-                *reinterpret_cast<uint4*>(row) = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
                                                             pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
             } else {
-                *reinterpret_cast<float4*>(row) = make_float4(y[0], y[1], y[2], y[3]);
+                *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
             }
         }
-        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) later[i] += tot[i];
+    };
 
-        // running state: acc <- diag(2^tot) acc + Kop^T V over the block;
-        // wave w owns row tiles rt0 .. rt0+RTW-1 and column tiles ct0 .. ct0+CTW-1
-        {
-            const int lane = ltid() & 63, wave = ltid() >> 6;
-            const int col = lane & 15, g = lane >> 4;
-            const int rt0 = (wave % (ST::NTT / RTW)) * RTW;
-            const int ct0 = (wave / (ST::NTT / RTW)) * CTW;
+    // (c) acc += Kop^T V
+    f32x4_t acc[ST::TPW];
 #pragma unroll
-            for (int a = 0; a < RTW; ++a)
+    for (int u = 0; u < ST::TPW; ++u) acc[u] = zero4();
+    const int col = lane & 15, g = lane >> 4;
+    const int rt0 = (wave % (ST::NTT / RTW)) * RTW;
+    const int ct0 = (wave / (ST::NTT / RTW)) * CTW;
+    auto contract = [&](int buf) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float f = fast_exp2(tot[16 * (rt0 + a) + 4 * g + r]);
+        for (int ks = 0; ks < SL::TB / M::KSTEP; ++ks) {
+            typename M::frag af[RTW], bv[CTW];
 #pragma unroll
-                    for (int tt = 0; tt < CTW; ++tt) acc[a * CTW + tt][r] *= f;
-                }
-            for (int ks = 0; ks < nb / M::KSTEP; ++ks) {
-                typename M::frag af[RTW];
-#pragma unroll
-                for (int a = 0; a < RTW; ++a) {
-                    if constexpr (sizeof(T) == 2) af[a] = load_key_frag(Ks, SL::P, M::KSTEP * ks, 16 * (rt0 + a), lane);
-                    else af[a] = Ks[(M::KSTEP * ks + g) * SL::P + 16 * (rt0 + a) + col];
-                }
-#pragma unroll
-                for (int tt = 0; tt < CTW; ++tt) {
-                    const int t = ct0 + tt;
-                    typename M::frag bv;
-                    if constexpr (sizeof(T) == 2) bv = load_key_frag(Vs, SL::P, M::KSTEP * ks, 16 * t, lane);
-                    else bv = Vs[(M::KSTEP * ks + g) * SL::P + 16 * t + col];
-#pragma unroll
-                    for (int a = 0; a < RTW; ++a) acc[a * CTW + tt] = M::mma(af[a], bv, acc[a * CTW + tt]);
-                }
+            for (int a = 0; a < RTW; ++a) {
+                if constexpr (sizeof(T) == 2) af[a] = load_key_frag(Kop(buf), SL::P, M::KSTEP * ks, 16 * (rt0 + a), lane);
+                else af[a] = Kop(buf)[(M::KSTEP * ks + g) * SL::P + 16 * (rt0 + a) + col];
             }
-            if (ltid() < D) lg[ltid()] += tot[ltid()];
-        }
-        __syncthreads();  // the next block's commit overwrites K and V
-    }
-    const size_t rec = size_t(D) * D + D;
-    float* dst = p.carry + ((size_t(b) * p.H_kv + h) * size_t(p.n_seg - 1) + s) * rec;
-    {
-        const int lane = ltid() & 63, wave = ltid() >> 6;
-        const int col = lane & 15, g = lane >> 4;
-        const int rt0 = (wave % (ST::NTT / RTW)) * RTW;
-        const int ct0 = (wave / (ST::NTT / RTW)) * CTW;
 #pragma unroll
-        for (int a = 0; a < RTW; ++a)
+            for (int tt = 0; tt < CTW; ++tt) {
+                if constexpr (sizeof(T) == 2) bv[tt] = load_key_frag(Vs(buf), SL::P, M::KSTEP * ks, 16 * (ct0 + tt), lane);
+                else bv[tt] = Vs(buf)[(M::KSTEP * ks + g) * SL::P + 16 * (ct0 + tt) + col];
+            }
 #pragma unroll
             for (int tt = 0; tt < CTW; ++tt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    dst[(16 * (rt0 + a) + 4 * g + r) * D + 16 * (ct0 + tt) + col] = acc[a * CTW + tt][r];
+                for (int a = 0; a < RTW; ++a) acc[a * CTW + tt] = M::mma(af[a], bv[tt], acc[a * CTW + tt]);
+        }
+    };
+
+    issue(0);
+    commit_stats(0, 0);
+    for (int it = 0; it < nblk; ++it) {
+        const int buf = it & 1;
+        lds_barrier();  // this block's raw keys, values and row statistics are visible
+        gate_operand(buf);
+        lds_barrier();  // this block's key operand is visible
+        if (it + 1 < nblk) {
+            commit_stats(it + 1, buf ^ 1);
+            contract(buf);
+        } else {
+            contract(buf);
+        }
     }
-    if (threadIdx.x < D) dst[size_t(D) * D + threadIdx.x] = lg[threadIdx.x];
+    const size_t rec = size_t(D) * D + D;
+    float* dst = p.carry + ((size_t(b) * p.H_kv + h) * size_t(p.n_seg - 1) + s) * rec;
+#pragma unroll
+    for (int a = 0; a < RTW; ++a)
+#pragma unroll
+        for (int tt = 0; tt < CTW; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[(16 * (rt0 + a) + 4 * g + r) * D + 16 * (ct0 + tt) + col] = acc[a * CTW + tt][r];
+    if (l == 0) {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) dst[size_t(D) * D + c0 + i] = later[i];
+    }
 }
 
 // Scalar gate. Every channel of a token shares one log2 gate, so a block
@@ -2059,7 +2073,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
             hipLaunchKernelGGL((segment_state_scalar_kernel<T, D>), dim3(unsigned(p.n_seg - 1), a.H_kv, unsigned(a.B)),
                                dim3(kPThreads), 0, st, p);
         else
-            hipLaunchKernelGGL((segment_state_kernel<T, D, GATE>), dim3(unsigned(p.n_seg - 1), a.H_kv, unsigned(a.B)),
+            hipLaunchKernelGGL((segment_state_vector_kernel<T, D>), dim3(unsigned(p.n_seg - 1), a.H_kv, unsigned(a.B)),
                                dim3(kPThreads), 0, st, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
