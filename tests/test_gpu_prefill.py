@@ -93,6 +93,22 @@ def test_scalar_gate_extreme_decay(dtype, d):
     _run_case(x, dtype, 0, 64, 0.5, 1, tag=f"extreme scalar decay {dtype}")
 
 
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("cps", [1, 3, 10])
+def test_slow_decay_across_segments(dtype, d, gate, cps):
+    """Keys shifted by +6: phi(k) is unchanged (a softmax over the channels)
+    while every gate becomes sigma(~6) ~ 0.9975, so the state keeps hundreds
+    of tokens and the chunk-to-chunk, block-to-block and segment-to-segment
+    decays all reach the output (T = 640: ten chunks in segments of 1, 3 or
+    10 chunks)."""
+    x = prefill_inputs(B=1, T=640, H_q=4, H_kv=1, d=d, dtype=dtype, seed=23 + d + gate)
+    x["k"] = x["k"] + 6.0
+    if dtype == "bf16":  # keep the canonical inputs bf16-exact on both sides
+        x["k"] = round_to_bf16(x["k"])
+    _run_case(x, dtype, gate, 64, 0.5, cps, tag=f"slow decay {dtype} d={d} gate={gate} cps={cps}")
+
+
 def test_deterministic_and_fully_written():
     x = prefill_inputs(B=1, T=700, H_q=8, H_kv=2, d=128, dtype="bf16", seed=5)
     say("[prefill] determinism bf16 d=128 T=700")
