@@ -14,7 +14,7 @@ import torch
 import gated_linear_recurrent_amd as gla
 import oracle
 from liger_testutil import DEV, TORCH_DT, check_prefill, say, to_dev, to_np
-from synth import config_prefill_inputs, prefill_inputs
+from synth import config_prefill_inputs, prefill_inputs, round_to_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -163,6 +163,28 @@ def test_gpu_prefill_hands_over_to_continuation(gate):
     check_prefill(dtype, to_np(o2), o_full[:, T1:], to_np(S2), S_full, tag="hand-over")
     rk, rv, pos = oracle.ring_fill(k, v, window)
     _check_ring(ring, rk, rv, pos, dtype, "hand-over")
+
+
+@pytest.mark.parametrize("gate", [0, 1])
+def test_slow_decay_hands_over_to_continuation(gate):
+    """Keys shifted by +6 (gates ~0.9975, phi(k) unchanged): the state the GPU
+    prefill hands over still weighs on every continued token. alpha = 1: the
+    recurrent output alone, held to its relative bar."""
+    dtype, d, window, alpha, T1, T2 = "bf16", 128, 64, 1.0, 330, 200
+    x = prefill_inputs(B=2, T=T1 + T2, H_q=8, H_kv=2, d=d, dtype=dtype, seed=79 + gate)
+    x["k"] = round_to_bf16(x["k"] + 6.0)
+    q, k, v = x["q"], x["k"], x["v"]
+    o_full, S_full = oracle.prefill(q, k, v, gate, window, alpha)
+    say(f"[continue] slow-decay hand-over gate={gate}")
+    q1, k1, v1 = (to_dev(a[:, :T1], dtype) for a in (q, k, v))
+    _, S1 = gla.liger_attn_prefill(q1, k1, v1, gate, window, alpha)
+    ring = gla.KVRing.empty(2, 2, window, d, TORCH_DT[dtype], DEV)
+    gla.liger_kv_ring_fill(k1, v1, ring)
+    q2, k2, v2 = (to_dev(a[:, T1:], dtype) for a in (q, k, v))
+    o2, S2 = gla.liger_attn_prefill_continue(q2, k2, v2, S1, ring, gate, alpha)
+    torch.cuda.synchronize()
+    check_prefill(dtype, to_np(o2), o_full[:, T1:], to_np(S2), S_full, to_np(o2), o_full[:, T1:],
+                  tag="slow-decay hand-over")
 
 
 @pytest.mark.timeout(300)

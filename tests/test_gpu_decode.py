@@ -11,7 +11,7 @@ import torch
 import gated_linear_recurrent_amd as gla
 import oracle
 from liger_testutil import DEV, TORCH_DT, abs_inf, rel_inf, say, to_dev, to_np
-from synth import CONFIGS, GATE_MODES, decode_initial, decode_step_inputs, prefill_inputs
+from synth import CONFIGS, GATE_MODES, decode_initial, decode_step_inputs, prefill_inputs, round_to_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -123,6 +123,29 @@ def test_gpu_prefill_hands_over_to_decode(gate):
                                        to_dev(x["v"][:, t], "bf16"), S, ring, gate, 0.5)
         torch.cuda.synchronize()
         assert abs_inf(to_np(o), o_full[:, t]) <= 2e-2
+    assert rel_inf(to_np(S), S_full) <= 1e-2
+
+
+@pytest.mark.parametrize("gate", [0, 1])
+def test_slow_decay_prefill_hands_over_to_decode(gate):
+    """Keys shifted by +6: phi(k) is unchanged and every gate is ~0.9975, so
+    the state the GPU prefill hands over still weighs on every decode step.
+    alpha = 1: the recurrent output alone, held to its relative bar."""
+    N, H_kv, n_rep, d, T0, n = 2, 2, 4, 128, 300, 20
+    say(f"[decode] slow-decay prefill hand-over gate={gate}")
+    x = prefill_inputs(B=N, T=T0 + n, H_q=H_kv * n_rep, H_kv=H_kv, d=d, dtype="bf16", seed=78)
+    x["k"] = round_to_bf16(x["k"] + 6.0)
+    o_full, S_full = oracle.prefill(x["q"], x["k"], x["v"], gate, 64, 1.0)
+    _, S = gla.liger_attn_prefill(to_dev(x["q"][:, :T0], "bf16"), to_dev(x["k"][:, :T0], "bf16"),
+                                  to_dev(x["v"][:, :T0], "bf16"), gate, 64, 1.0)
+    ring = gla.KVRing.empty(N, H_kv, 64, d, torch.bfloat16, DEV)
+    gla.liger_kv_ring_fill(to_dev(x["k"][:, :T0], "bf16"), to_dev(x["v"][:, :T0], "bf16"), ring)
+    for i in range(n):
+        t = T0 + i
+        o = gla.liger_attn_decode_step(to_dev(x["q"][:, t], "bf16"), to_dev(x["k"][:, t], "bf16"),
+                                       to_dev(x["v"][:, t], "bf16"), S, ring, gate, 1.0)
+        torch.cuda.synchronize()
+        _bars("bf16", to_np(o), o_full[:, t], f"slow decay gate={gate} step {i}", alpha=1.0)
     assert rel_inf(to_np(S), S_full) <= 1e-2
 
 
