@@ -86,6 +86,22 @@ def test_backward_extreme_gate_channels(d):
     _check(_run(x, dO, 1, 64, 0.5), ref, tag)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("gate", [0, 1])
+def test_backward_slow_decay(d, gate):
+    """Keys shifted by +6: phi(k) is unchanged and every gate is ~0.9975, so
+    the chunk-start states and the adjoints flowing back from later tokens
+    carry over hundreds of tokens through both scans (T = 400, alpha = 1:
+    the recurrence alone)."""
+    tag = f"bwd slow decay d={d} gate={gate}"
+    say(f"[bwd] {tag}")
+    x = prefill_inputs(B=1, T=400, H_q=8, H_kv=2, d=d, dtype="bf16", seed=401 + d + gate)
+    x["k"] = round_to_bf16(x["k"] + 6.0)
+    dO = grad_output(x["q"].shape, "bf16", seed=11)
+    ref = oracle.prefill_backward(x["q"], x["k"], x["v"], dO, gate, 64, 1.0)
+    _check(_run(x, dO, gate, 64, 1.0), ref, tag)
+
+
 def test_backward_long_sequence():
     """32 chunks through both scans: T = 2048, H_q = 8, H_kv = 2, d = 128."""
     tag = "bwd long"
