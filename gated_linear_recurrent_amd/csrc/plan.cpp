@@ -32,9 +32,9 @@ PrefillPlan make_prefill_plan(int64_t B, int64_t T, int H_kv, int d, bool bf16, 
     pl.n_chunks = (T + kChunk - 1) / kChunk;
     int64_t cps = chunks_per_segment;
     if (cps <= 0) {
-        // One output workgroup per compute unit (two when the LDS footprint allows).
-        const int64_t per_cu = (bf16 && d == 64) ? 2 : 1;
-        const int64_t target = 256 * per_cu;
+        // One output workgroup per compute unit (each keeps its running state
+        // resident in LDS when it fits, which beats two smaller ones per unit).
+        const int64_t target = 256;
         const int64_t heads = B * H_kv;
         int64_t want_seg = (target + heads - 1) / heads;
         if (want_seg < 1) want_seg = 1;

@@ -77,8 +77,7 @@ struct Layout {
     // operand-type copy S'^T [D][DP] and the fp32 state lives in registers and
     // a per-workgroup global slot between chunks.
     static constexpr size_t S32_BYTES = size_t(D) * SP * 4;
-    // bf16 d = 64 output kernels run two workgroups per compute unit
-    static constexpr size_t BUDGET = (FULL && E == 2 && D == 64) ? 80 * 1024 : 160 * 1024;
+    static constexpr size_t BUDGET = 160 * 1024;  // one output workgroup per compute unit
     static constexpr bool SLDS = FULL && (ST_OFF + S32_BYTES + F_BYTES + SMALL_WORDS * 4 <= BUDGET) &&
                                  (size_t(KB_ELEMS) * E >= TMP_FLOATS * 4);
     static constexpr size_t ST_BYTES = !FULL ? 0 : SLDS ? S32_BYTES : size_t(D) * DP * E;
