@@ -685,6 +685,82 @@ __device__ __forceinline__ void gate_prep(const Smem<T, D, GATE, FULL>& sm, int 
     state_key_operand<T, D, GATE, FULL, TPT>(sm, slot, nvalid, sm.bl2, b2);
 }
 
+// Scalar gate with the resident state: key row statistics, the chunk's gate
+// prefix and the intra operand Kb[j][c] = phik_j[c] 2^(mref - b_j) in one
+// phase with one barrier. Thread (j, part) keeps the exponentials of its
+// pieces of key row j in registers for the operand, and takes b_j, the
+// reference and the exact flag from its own wave's scan (every wave scans
+// the same 64 gates), so nothing it writes to Kb depends on another wave's
+// LDS stores after the barrier. Leaves in LDS what gate_stats leaves and the
+// same operand as intra_key_operand.
+template <typename T, int D>
+__device__ __forceinline__ void scalar_gate_intra(const Smem<T, D, 0, true>& sm, int slot, int nvalid) {
+    typedef Layout<T, D, 0, true> L;
+    static_assert(kPThreads == 64 * 8, "eight lanes per key row");
+    constexpr int VPL = 16 / sizeof(T);
+    constexpr int NLD = D / (8 * VPL);  // pieces of VPL elements per lane: part * VPL + 8 VPL q
+    const int tid = ltid();
+    const int j = tid >> 3, part = tid & 7;
+    const T* row = sm.K + slot * 64 * L::DP + j * L::DP + part * VPL;
+    float x[NLD * VPL];
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) {
+        const uint4 u = *reinterpret_cast<const uint4*>(row + q * 8 * VPL);
+        const T* e = reinterpret_cast<const T*>(&u);
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) x[q * VPL + i] = to_f32(e[i]);
+    }
+    float mx = -INFINITY, sraw = 0.f;
+#pragma unroll
+    for (int i = 0; i < NLD * VPL; ++i) {
+        mx = fmaxf(mx, x[i]);
+        sraw += x[i];
+    }
+    mx = group8_max(mx);
+    float se = 0.f;
+#pragma unroll
+    for (int i = 0; i < NLD * VPL; ++i) {
+        x[i] = fast_exp2((x[i] - mx) * kLog2e);
+        se += x[i];
+    }
+    se = group8_sum(se);
+    sraw = group8_sum(sraw);
+    const bool ok = j < nvalid;
+    const float kinv = ok ? fast_rcp(se) : 0.0f;
+    if (part == 0) {
+        sm.kmax[j] = mx;
+        sm.kinv[j] = kinv;
+        sm.b2e[j] = ok ? log2_sigmoid(sraw * (1.0f / D)) : 0.0f;
+    }
+    __syncthreads();
+    const float pre = wave_prefix_sum(sm.b2e[tid & 63]);
+    if (tid < 64) sm.b2s[tid] = pre;
+    const float bl = readlane_f(pre, nvalid - 1);
+    // reference for the factorised intra-chunk decay: the middle token
+    const float m = readlane_f(pre, nvalid - 1 < 31 ? nvalid - 1 : 31);
+    const bool ex = fmaxf(readlane_f(pre, 0) - m, m - bl) > kEmax2;
+    if (tid < D) {
+        sm.dec[tid] = fast_exp2(bl);
+        sm.mref[tid] = ex ? 0.0f : m;
+        sm.blast[tid] = bl;
+    }
+    if (tid == 0) *sm.exact = ex ? 1 : 0;
+    const float bj = __shfl(pre, j, 64);
+    const float sc = kinv * (ex ? 1.0f : fast_exp2(m - bj));
+    T* dst = sm.Kb + j * L::DP + part * VPL;
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) {
+        const float* y = x + q * VPL;
+        if constexpr (sizeof(T) == 2) {
+            *reinterpret_cast<uint4*>(dst + q * 8 * VPL) =
+                make_uint4(pack_bf16x2(sc * y[0], sc * y[1]), pack_bf16x2(sc * y[2], sc * y[3]),
+                           pack_bf16x2(sc * y[4], sc * y[5]), pack_bf16x2(sc * y[6], sc * y[7]));
+        } else {
+            *reinterpret_cast<float4*>(dst + q * 8 * VPL) = make_float4(sc * y[0], sc * y[1], sc * y[2], sc * y[3]);
+        }
+    }
+}
+
 // Intra operand Kb[j][c] = phik_j[c] 2^(mref[c] - b_j[c]) (vector, good
 // channels), 0 (bad channels), phik_j[c] (scalar gate).
 template <typename T, int D, int GATE, bool FULL, int TPT>
@@ -1903,20 +1979,24 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
             const int cur = int(c & 1);
             const int64_t t0 = c * kChunk;
             const int nvalid = p.T - t0 < kChunk ? int(p.T - t0) : kChunk;
-            // Scalar gate: no barrier is needed here. gate_stats first writes
-            // the key statistics, which the previous chunk no longer reads
-            // after its last barrier, and writes dec and exact only after two
-            // barriers of its own, which every wave reaches after finishing
-            // the previous state update.
+            // Scalar gate: no barrier is needed here. scalar_gate_intra first
+            // writes the key statistics, which the previous chunk no longer
+            // reads after its last barrier, and writes dec, exact and the
+            // intra operand only after a barrier of its own, which every wave
+            // reaches after finishing the previous state update.
             if (GATE) {
                 if (threadIdx.x == 0) *sm.nbad = 0;
                 if (threadIdx.x < D / 32) sm.badmask[threadIdx.x] = 0u;
                 __syncthreads();
             }
             float b2[TPT];
-            gate_stats<T, D, GATE, true, TPT>(sm, cur, nvalid, p.alpha, b2);
-            __syncthreads();
-            intra_key_operand<T, D, GATE, true, TPT>(sm, cur, b2);
+            if constexpr (GATE == 0) {
+                scalar_gate_intra<T, D>(sm, cur, nvalid);
+            } else {
+                gate_stats<T, D, GATE, true, TPT>(sm, cur, nvalid, p.alpha, b2);
+                __syncthreads();
+                intra_key_operand<T, D, GATE, true, TPT>(sm, cur, b2);
+            }
             __syncthreads();
             ItemCtx<T, D, GATE> x;
             x.q = static_cast<const T*>(p.q);
