@@ -187,8 +187,6 @@ liger_status prefill_validate(const void* q, const void* k, const void* v, const
     LIGER_TRY(check_common(gate_mode, alpha));
     if (window < 1 || window > 64) return fail(LIGER_E_INVALID_ARG, "window must be in 1..64");
     if (chunks_per_segment < 0) return fail(LIGER_E_INVALID_ARG, "chunks_per_segment must be >= 0");
-    if (shape->dtype == LIGER_F32 && shape->d != 64)
-        return fail(LIGER_E_UNSUPPORTED, "fp32 prefill is built for d = 64 only");
     LIGER_TRY(check_ptr(q, "q"));
     LIGER_TRY(check_ptr(k, "k"));
     LIGER_TRY(check_ptr(v, "v"));
@@ -326,8 +324,6 @@ liger_status continue_impl(const void* q, const void* k, const void* v, const fl
     if (!kv_ring) return fail(LIGER_E_INVALID_ARG, "kv_ring is NULL");
     const int32_t window = kv_ring->window;
     if (window < 1 || window > 64) return fail(LIGER_E_INVALID_ARG, "ring window must be in 1..64");
-    if (shape->dtype == LIGER_F32 && shape->d != 64)
-        return fail(LIGER_E_UNSUPPORTED, "fp32 prefill is built for d = 64 only");
     LIGER_TRY(check_ptr(q, "q"));
     LIGER_TRY(check_ptr(k, "k"));
     LIGER_TRY(check_ptr(v, "v"));

@@ -77,7 +77,9 @@ struct PrefillPlan {
     int64_t n_seg;           // ceil(n_chunks / cps)
     size_t carry_floats;     // floats per carry record: d*d + d
     size_t state_offset;     // floats before the state slots: B * H_kv * (n_seg - 1) * carry_floats
-    size_t workspace_bytes;  // (state_offset + B * H_kv * n_seg * d*d) * 4
+    size_t op_offset;        // floats before the state-operand slots (fp32, d = 128): state_offset + slots
+    size_t halo_offset;      // floats before the halo rows (fp32, d = 128): op_offset + operand slots
+    size_t workspace_bytes;  // (halo_offset + [fp32, d = 128] B * H_kv * 2 * 64 * d) * 4
 };
 
 struct PrefillArgs {

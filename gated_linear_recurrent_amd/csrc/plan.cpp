@@ -47,7 +47,16 @@ PrefillPlan make_prefill_plan(int64_t B, int64_t T, int H_kv, int d, bool bf16, 
     pl.carry_floats = size_t(d) * d + d;
     pl.state_offset = sat_mul({size_t(B), size_t(H_kv), size_t(pl.n_seg - 1), pl.carry_floats});
     const size_t slots = sat_mul({size_t(B), size_t(H_kv), size_t(pl.n_seg), size_t(d) * d});
-    pl.workspace_bytes = sat_mul({sat_add({pl.state_offset, slots}), sizeof(float)});
+    // fp32 at d = 128: the output kernel also keeps each chunk's state operand
+    // in global memory (same size as the state slots)
+    // and, for a continuation, the 64 tokens before it as contiguous K and V
+    // rows per (b, kv head) (the window halo of the first chunk)
+    pl.op_offset = sat_add({pl.state_offset, slots});
+    const bool hg = !bf16 && d == 128;
+    const size_t ops = hg ? slots : 0;
+    pl.halo_offset = sat_add({pl.op_offset, ops});
+    const size_t halo = hg ? sat_mul({size_t(B), size_t(H_kv), 2 * 64, size_t(d)}) : 0;
+    pl.workspace_bytes = sat_mul({sat_add({pl.halo_offset, halo}), sizeof(float)});
     return pl;
 }
 

@@ -53,7 +53,11 @@ struct Layout {
     static constexpr int DP = D + PAD;   // pitch of token-major [64][D] tiles
     static constexpr int JP = 64 + PAD;  // pitch of channel-major [D][64] tiles
     static constexpr int FP = D + 4;     // pitch of the fp32 gate-factor tile
-    static constexpr int NSLOT = FULL ? 2 : 1;
+    // fp32 at d = 128 ("global halo"): the output kernel keeps only the current
+    // chunk's K/V in LDS; the previous chunk's keys and values (the window
+    // halo) and the state operand are read from global memory.
+    static constexpr bool HG = FULL && E == 4 && D == 128;
+    static constexpr int NSLOT = FULL && !HG ? 2 : 1;
     static constexpr int KB_ELEMS = (64 * DP > D * JP) ? 64 * DP : D * JP;
     // bf16 keeps V token-major ([64][VP], rows 8 banks apart) and reads it with
     // transposing loads; fp32 stores V^T ([D][JP], keys at key_pos).
@@ -78,9 +82,9 @@ struct Layout {
     // a per-workgroup global slot between chunks.
     static constexpr size_t S32_BYTES = size_t(D) * SP * 4;
     static constexpr size_t BUDGET = 160 * 1024;  // one output workgroup per compute unit
-    static constexpr bool SLDS = FULL && (ST_OFF + S32_BYTES + F_BYTES + SMALL_WORDS * 4 <= BUDGET) &&
+    static constexpr bool SLDS = FULL && !HG && (ST_OFF + S32_BYTES + F_BYTES + SMALL_WORDS * 4 <= BUDGET) &&
                                  (size_t(KB_ELEMS) * E >= TMP_FLOATS * 4);
-    static constexpr size_t ST_BYTES = !FULL ? 0 : SLDS ? S32_BYTES : size_t(D) * DP * E;
+    static constexpr size_t ST_BYTES = (!FULL || HG) ? 0 : SLDS ? S32_BYTES : size_t(D) * DP * E;
     static constexpr size_t F_OFF = ST_OFF + ST_BYTES;                        // fp32 [64][FP]
     static constexpr size_t TMP_OFF = F_OFF + F_BYTES;                        // gate-scan scratch
     // The scan scratch (part sums, raw references) shares a region that is
@@ -156,6 +160,8 @@ struct PrefillParams {
     float* S_T;
     float* carry;
     float* state_slots;
+    float* op_slots;  // global halo: state operand [D][D] per output workgroup
+    float* halo;      // global halo, continuation: K then V rows [64][D] per (b, kv head)
     int64_t T;
     int64_t n_chunks;
     int64_t cps;
@@ -174,6 +180,10 @@ struct PrefillParams {
     const void* sink_k;
     const void* sink_v;
     int n_sink;
+    // global halo (fp32, d = 128) only: the output kernel computes the
+    // segment-state records instead of outputs (no segment-state kernel is
+    // built for that tile shape)
+    int rec_mode;
 };
 
 // ------------------------------------------------------------ chunk loading
@@ -517,6 +527,25 @@ __device__ __forceinline__ void publish_state(const Smem<T, D, GATE, FULL>& sm,
         } else {
             *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
         }
+    }
+}
+
+// The same operand in global memory as fp32 [D][D] (global halo): read back
+// by the other waves of the workgroup after a barrier.
+template <typename T, int D, int GATE, bool FULL>
+__device__ __forceinline__ void publish_state_global(const Smem<T, D, GATE, FULL>& sm, float* dst,
+                                                     const f32x4_t (&acc)[StateTiles<D>::TPW]) {
+    typedef StateTiles<D> ST;
+    const int lane = ltid() & 63, wave = ltid() >> 6;
+    const int col = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < ST::TPW; ++u) {
+        const int rt = ST::rt(wave, u), t = ST::ct(wave, u);
+        const int r0 = 16 * rt + 4 * g;
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = GATE ? acc[u][r] * fast_exp2(sm.mref[r0 + r]) : acc[u][r];
+        *reinterpret_cast<float4*>(dst + (16 * t + col) * D + r0) = make_float4(x[0], x[1], x[2], x[3]);
     }
 }
 
@@ -1345,6 +1374,13 @@ struct ItemCtx {
     const T* sink_k;  // this key/value head's sink tokens [n_sink][D]
     const T* sink_v;
     int n_sink;
+    // global halo (fp32, d = 128): the previous chunk's K and V rows in
+    // global memory (row j at kprv[j * prv_stride]) and the state operand
+    // S'^T [D][D] of this chunk
+    const T* kprv;
+    const T* vprv;
+    int64_t prv_stride;
+    const float* opg;
 };
 
 // One wave computes the outputs of 32 query rows (query tiles QA and QB of the
@@ -1461,9 +1497,15 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
     const int col = lane & 15, g = lane >> 4;
     const int dl = col - 4 * g;         // i - j = 16 (I - kt) + dl - r inside a tile pair
     const T* Kcur = sm.K + x.cur * 64 * L::DP;
-    const T* Kprv = sm.K + (x.cur ^ 1) * 64 * L::DP;
+    const T* Kprv = sm.K + (L::NSLOT == 2 ? x.cur ^ 1 : 0) * 64 * L::DP;
     const T* Vcur = sm.Vt + x.cur * L::V_ELEMS;
-    const T* Vprv = sm.Vt + (x.cur ^ 1) * L::V_ELEMS;
+    const T* Vprv = sm.Vt + (L::NSLOT == 2 ? x.cur ^ 1 : 0) * L::V_ELEMS;
+    // row of the previous chunk's key tile kt (kt < 0): LDS, or global memory
+    // with the global halo
+    auto prev_krow = [&](int kt) -> const T* {
+        if constexpr (L::HG) return x.kprv + (16 * kt + 64 + col) * x.prv_stride;
+        else return Kprv + (16 * kt + 64 + col) * L::DP;
+    };
     const int nbad = GATE ? *sm.nbad : 0;
     const bool exact = GATE ? false : (*sm.exact != 0);
     const bool full_window = x.window >= 64;
@@ -1524,7 +1566,7 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
         // are requested before this tile's MFMAs
         Frag kbuf[2][KS];
         auto load_tile = [&](int kt, Frag* dst) {
-            const T* krow = kt >= 0 ? Kcur + (16 * kt + col) * L::DP : Kprv + (16 * kt + 64 + col) * L::DP;
+            const T* krow = kt >= 0 ? Kcur + (16 * kt + col) * L::DP : prev_krow(kt);
 #pragma unroll
             for (int k = 0; k < KS; ++k) dst[k] = M::load(krow + M::KSTEP * k + KPL * g);
         };
@@ -1541,7 +1583,7 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
                 live[s] = inr(s, kt) &&
                           (FAST || ((kt >= 0 || x.npv > 0) && (16 * kt + 15 > 16 * QTS[s] - x.window)));
             if (live[0] || live[1]) {
-                const T* krow = kt >= 0 ? Kcur + (16 * kt + col) * L::DP : Kprv + (16 * kt + 64 + col) * L::DP;
+                const T* krow = kt >= 0 ? Kcur + (16 * kt + col) * L::DP : prev_krow(kt);
                 f32x4_t d4[2] = {zero4(), zero4()};
 #pragma unroll
                 for (int k = 0; k < KS; ++k) {
@@ -1825,6 +1867,8 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
                 a = M::pack(x);
             } else if constexpr (L::SLDS) {
                 a = resident_frag(sm, 16 * t + col, M::KSTEP * k + KPL * g);
+            } else if constexpr (L::HG) {
+                a = M::load(reinterpret_cast<const T*>(x.opg) + (16 * t + col) * D + M::KSTEP * k + KPL * g);
             } else {
                 a = M::load(sm.St + (16 * t + col) * L::DP + M::KSTEP * k + KPL * g);
             }
@@ -1842,6 +1886,7 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     acc[s][r] += bad_q * (L::SLDS ? sm.S32[(16 * t + 4 * g + r) * L::SP + c]
+                                          : L::HG ? x.opg[(16 * t + 4 * g + r) * D + c]
                                                   : to_f32(sm.St[(16 * t + 4 * g + r) * L::DP + c]));
             }
         }
@@ -1869,9 +1914,21 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
             for (int u = 0; u < NKT; ++u) {
                 const int kt = KTMIN + u;
                 const int kk = kt >= 0 ? kt : kt + 4;
-                const T* base = kt >= 0 ? vrow_c : vrow_p;
-                const float4 pv = *reinterpret_cast<const float4*>(base + 32 * (kk >> 1) + 8 * g + 4 * (kk & 1));
-                const float pr[4] = {pv.x, pv.y, pv.z, pv.w};
+                float pr[4];
+                if (L::HG && kt < 0) {
+                    // keys 16 kk + 4 g + r of the previous chunk, channel 16 t + col
+                    const T* vg = x.vprv + (16 * kk + 4 * g) * x.prv_stride + 16 * t + col;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        pr[r] = (x.npv > 0 && (inr(0, kt) || inr(1, kt))) ? to_f32(vg[r * x.prv_stride]) : 0.0f;
+                } else {
+                    const T* base = kt >= 0 ? vrow_c : vrow_p;
+                    const float4 pv = *reinterpret_cast<const float4*>(base + 32 * (kk >> 1) + 8 * g + 4 * (kk & 1));
+                    pr[0] = pv.x;
+                    pr[1] = pv.y;
+                    pr[2] = pv.z;
+                    pr[3] = pv.w;
+                }
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
                     if (inr(s, kt)) {
@@ -1930,7 +1987,48 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
     const int H_q = p.H_kv * p.n_rep;
     const size_t rec = size_t(D) * D + D;
 
+    if constexpr (L::HG) {
+        if (p.rec_mode) {
+            // Segment-state record of segment s (every segment but the last):
+            // the state reached from zero over its chunks and the log2 decay
+            // of the whole segment per d_k row, as the segment-state kernels
+            // write them for the other configurations.
+            const int64_t cb = int64_t(s) * p.cps;
+            const int64_t ce = cb + p.cps < p.n_chunks ? cb + p.cps : p.n_chunks;
+            ChunkRegs<T, D> cr;
+            load_chunk_issue<T, D>(cr, kbase, vbase, row_stride, cb * kChunk,
+                                   p.T - cb * kChunk < kChunk ? int(p.T - cb * kChunk) : kChunk);
+            f32x4_t acc[StateTiles<D>::TPW];
+#pragma unroll
+            for (int u = 0; u < StateTiles<D>::TPW; ++u) acc[u] = zero4();
+            float lg = 0.f;
+            load_chunk_commit(sm, 0, cr);
+            for (int64_t c = cb; c < ce; ++c) {
+                const int64_t t0 = c * kChunk;
+                const int nvalid = p.T - t0 < kChunk ? int(p.T - t0) : kChunk;
+                if (c + 1 < ce) {
+                    const int64_t t1 = t0 + kChunk;
+                    load_chunk_issue<T, D>(cr, kbase, vbase, row_stride, t1, p.T - t1 < kChunk ? int(p.T - t1) : kChunk);
+                }
+                if (threadIdx.x == 0) *sm.nbad = 0;
+                if (threadIdx.x < D / 32) sm.badmask[threadIdx.x] = 0u;
+                __syncthreads();
+                float b2[TPT];
+                gate_prep<T, D, GATE, true, TPT>(sm, 0, nvalid, p.alpha, b2);
+                __syncthreads();
+                state_advance(sm, 0, acc);
+                if (threadIdx.x < D) lg += sm.blast[threadIdx.x];
+                __syncthreads();
+                if (c + 1 < ce) load_chunk_commit(sm, 0, cr);
+            }
+            float* dst = p.carry + ((size_t(b) * p.H_kv + h) * size_t(p.n_seg - 1) + s) * rec;
+            store_state<D>(dst, acc);
+            if (threadIdx.x < D) dst[size_t(D) * D + threadIdx.x] = lg;
+            return;
+        }
+    }
     float* slot = p.state_slots + ((size_t(b) * p.H_kv + h) * size_t(p.n_seg) + s) * size_t(D) * D;
+    float* opg = L::HG ? p.op_slots + ((size_t(b) * p.H_kv + h) * size_t(p.n_seg) + s) * size_t(D) * D : nullptr;
     const float* carry_in = s > 0 ? p.carry + ((size_t(b) * p.H_kv + h) * size_t(p.n_seg - 1) + (s - 1)) * rec
                             : p.S0 ? p.S0 + (size_t(b) * p.H_kv + h) * D * D : nullptr;
     // continuation: tokens already consumed, and how many of the 64 before the
@@ -1948,7 +2046,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
     ChunkRegs<T, D> cr, cp;
     load_chunk_issue<T, D>(cr, kbase, vbase, row_stride, c_begin * kChunk,
                            p.T - c_begin * kChunk < kChunk ? int(p.T - c_begin * kChunk) : kChunk);
-    if (c_begin > 0) load_chunk_issue<T, D>(cp, kbase, vbase, row_stride, (c_begin - 1) * kChunk, kChunk);
+    if (L::HG) {
+        // the previous chunk stays in global memory
+    } else if (c_begin > 0) load_chunk_issue<T, D>(cp, kbase, vbase, row_stride, (c_begin - 1) * kChunk, kChunk);
     else if (npv0 > 0)
         load_ring_issue<T, D>(cp, static_cast<const T*>(p.ring_k) + (size_t(b) * p.H_kv + h) * p.window * D,
                               static_cast<const T*>(p.ring_v) + (size_t(b) * p.H_kv + h) * p.window * D, pos_b,
@@ -1966,9 +2066,32 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
     }
     f32x4_t acc[StateTiles<D>::TPW];
     if constexpr (L::SLDS) load_state<D>(carry_in, acc);
-    if (c_begin > 0 || npv0 > 0) load_chunk_commit(sm, int((c_begin + 1) & 1), cp);
-    else zero_slot(sm, int((c_begin + 1) & 1));
-    load_chunk_commit(sm, int(c_begin & 1), cr);
+    // global halo, continuation: the ring's tokens before the first chunk as
+    // contiguous rows (zero before the sequence start), read after the
+    // barrier below like the previous chunk of a later chunk
+    T* halo_k = nullptr;
+    T* halo_v = nullptr;
+    if constexpr (L::HG) {
+        if (c_begin == 0 && npv0 > 0) {
+            halo_k = reinterpret_cast<T*>(p.halo) + (size_t(b) * p.H_kv + h) * 2 * 64 * D;
+            halo_v = halo_k + 64 * D;
+            const T* rk = static_cast<const T*>(p.ring_k) + (size_t(b) * p.H_kv + h) * p.window * D;
+            const T* rv = static_cast<const T*>(p.ring_v) + (size_t(b) * p.H_kv + h) * p.window * D;
+            for (int idx = threadIdx.x; idx < 64 * D; idx += kPThreads) {
+                const int j = idx / D;
+                const int64_t rr = j < 64 - npv0 ? -1 : (pos_b - 64 + j) % p.window;
+                halo_k[idx] = rr >= 0 ? rk[rr * D + idx % D] : T(0);
+                halo_v[idx] = rr >= 0 ? rv[rr * D + idx % D] : T(0);
+            }
+        }
+    }
+    if (L::HG) {
+        load_chunk_commit(sm, 0, cr);
+    } else {
+        if (c_begin > 0 || npv0 > 0) load_chunk_commit(sm, int((c_begin + 1) & 1), cp);
+        else zero_slot(sm, int((c_begin + 1) & 1));
+        load_chunk_commit(sm, int(c_begin & 1), cr);
+    }
     if constexpr (L::SLDS) {
         // Resident state: per chunk, gate statistics and the intra operand,
         // then the outputs (inter term from S entering the chunk), then the
@@ -2050,7 +2173,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
     }
     __syncthreads();
     for (int64_t c = c_begin; c < c_end; ++c) {
-        const int cur = int(c & 1);
+        const int cur = L::NSLOT == 2 ? int(c & 1) : 0;
         const int64_t t0 = c * kChunk;
         const int nvalid = p.T - t0 < kChunk ? int(p.T - t0) : kChunk;
         // running state (entering this chunk) and the query fragments of this
@@ -2074,7 +2197,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
         gate_prep<T, D, GATE, true, TPT>(sm, cur, nvalid, p.alpha, b2);
         __syncthreads();
         // state operand for this chunk (S entering it), then advance the state
-        publish_state(sm, acc);
+        if constexpr (L::HG) publish_state_global(sm, opg, acc);
+        else publish_state(sm, acc);
         state_advance(sm, cur, acc);
         if (c + 1 < c_end) store_slot<D>(slot, acc);
         else if (last_seg) store_state<D>(p.S_T + (size_t(b) * p.H_kv + h) * D * D, acc);
@@ -2094,6 +2218,15 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
         x.sink_v = SINK ? static_cast<const T*>(p.sink_v) + size_t(h) * p.n_sink * D : nullptr;
         x.n_sink = SINK ? p.n_sink : 0;
         x.cur = cur;
+        if constexpr (L::HG) {
+            // previous chunk in global memory (read when x.npv > 0): the
+            // sequence, or the continuation's halo rows
+            const bool from_ring = c == 0 && npv0 > 0;
+            x.kprv = from_ring ? halo_k : c > 0 ? kbase + (t0 - kChunk) * row_stride : kbase;
+            x.vprv = from_ring ? halo_v : c > 0 ? vbase + (t0 - kChunk) * row_stride : vbase;
+            x.prv_stride = from_ring ? D : row_stride;
+            x.opg = opg;
+        }
         // next chunk's K/V: in flight during the output phase, stored after it
         if (c + 1 < c_end) {
             const int64_t t1 = t0 + kChunk;
@@ -2114,7 +2247,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
         }
         __syncthreads();
         if (c + 1 < c_end) {
-            load_chunk_commit(sm, cur ^ 1, cr);  // the previous chunk's slot is free now
+            // the previous chunk's slot is free now (global halo: this chunk's)
+            load_chunk_commit(sm, L::NSLOT == 2 ? cur ^ 1 : 0, cr);
             __syncthreads();
         }
     }
@@ -2131,6 +2265,8 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     p.S_T = a.S_T;
     p.carry = a.workspace;
     p.state_slots = a.workspace + a.plan.state_offset;
+    p.op_slots = a.workspace + a.plan.op_offset;
+    p.halo = a.workspace + a.plan.halo_offset;
     p.T = a.T;
     p.n_chunks = a.plan.n_chunks;
     p.cps = a.plan.cps;
@@ -2146,8 +2282,20 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     p.sink_k = a.sink_k;
     p.sink_v = a.sink_v;
     p.n_sink = a.n_sink;
+    p.rec_mode = 0;
     hipStream_t st = static_cast<hipStream_t>(a.stream);
-    if (p.n_seg > 1 && (a.stage_mask & 1)) {
+    // fp32 at d = 128: the output kernel in record mode writes the segment
+    // records (the segment-state kernels are built for the other tile shapes)
+    constexpr bool HG = Layout<T, D, GATE, true>::HG;
+    if (HG && p.n_seg > 1 && (a.stage_mask & 1)) {
+        PrefillParams pr = p;
+        pr.rec_mode = 1;
+        hipLaunchKernelGGL((prefill_output_kernel<T, D, GATE, false>), dim3(unsigned(p.n_seg - 1), a.H_kv, unsigned(a.B)),
+                           dim3(kPThreads), 0, st, pr);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if constexpr (!HG) if (p.n_seg > 1 && (a.stage_mask & 1)) {
         if constexpr (GATE == 0)
             hipLaunchKernelGGL((segment_state_scalar_kernel<T, D>), dim3(unsigned(p.n_seg - 1), a.H_kv, unsigned(a.B)),
                                dim3(kPThreads), 0, st, p);
@@ -2193,7 +2341,7 @@ hipError_t launch_prefill(const PrefillArgs& a) {
         return a.gate ? launch_prefill_t<bf16_t, 128, 1>(a) : launch_prefill_t<bf16_t, 128, 0>(a);
     }
     if (a.d == 64) return a.gate ? launch_prefill_t<float, 64, 1>(a) : launch_prefill_t<float, 64, 0>(a);
-    return hipErrorInvalidValue;  // fp32 with d = 128 exceeds the LDS budget of this kernel
+    return a.gate ? launch_prefill_t<float, 128, 1>(a) : launch_prefill_t<float, 128, 0>(a);
 }
 
 }  // namespace liger

@@ -152,7 +152,7 @@ size_t liger_attn_prefill_workspace_size_ex(const liger_shape* shape,
  * workspace: device memory of at least liger_attn_prefill_workspace_size
  * bytes (may be NULL when that size is 0); its contents on entry are
  * ignored and on return are unspecified.
- * Supported: d in {64, 128} for bf16, d = 64 for fp32.
+ * Supported: d in {64, 128} for bf16 and for fp32.
  */
 liger_status liger_attn_prefill(const void* q, const void* k, const void* v,
                                 int32_t gate_mode, int32_t window, float alpha,

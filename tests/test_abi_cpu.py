@@ -66,7 +66,6 @@ def _prefill(lib, shape, gate=1, window=64, alpha=0.5, q=FAKE, k=FAKE, v=FAKE, o
     (dict(d=96), gla.LIGER_E_UNSUPPORTED),
     (dict(d=256), gla.LIGER_E_UNSUPPORTED),
     (dict(dtype=7), gla.LIGER_E_INVALID_ARG),
-    (dict(dtype=gla.LIGER_F32, d=128), gla.LIGER_E_UNSUPPORTED),
 ])
 def test_prefill_rejects_bad_shapes(lib, kw, code):
     assert _prefill(lib, _shape(**kw)) == code
@@ -122,6 +121,14 @@ def test_workspace_size_formula(lib):
         assert size == 2 * 2 * ((n_seg - 1) * (128 * 128 + 128) + n_seg * 128 * 128) * 4
     size0 = lib.liger_attn_prefill_workspace_size(ctypes.byref(_shape(T=8192, H_q=32, H_kv=8)))
     assert size0 > 0 and size0 % 16 == 0
+    # fp32 at d = 128: a state-operand slot beside each running-state slot,
+    # and 64 halo K and V rows per (b, kv head)
+    for T, cps in [(64, 1), (65, 1), (1000, 3)]:
+        shp = _shape(B=2, T=T, H_q=8, H_kv=2, dtype=gla.LIGER_F32)
+        n_chunks = -(-T // 64)
+        size = lib.liger_attn_prefill_workspace_size_ex(ctypes.byref(shp), cps)
+        n_seg = -(-n_chunks // min(cps, n_chunks))
+        assert size == 2 * 2 * ((n_seg - 1) * (128 * 128 + 128) + 2 * n_seg * 128 * 128 + 2 * 64 * 128) * 4
     assert lib.liger_attn_prefill_workspace_size(ctypes.byref(_shape(d=96))) == 0
     assert lib.liger_attn_prefill_workspace_size(None) == 0
 
@@ -202,7 +209,6 @@ def _continue(lib, shape, ring, S0=FAKE + 3 * G, S_T=FAKE + 4 * G, o=FAKE + 5 * 
     (dict(), dict(), dict(o=FAKE + 2 * G + 64), gla.LIGER_E_INVALID_ARG),      # o starts inside v
     (dict(), dict(), dict(S_T=FAKE + 5 * G + 512), gla.LIGER_E_INVALID_ARG),   # S_T starts inside o
     (dict(), dict(), dict(ws=None), gla.LIGER_E_WORKSPACE),
-    (dict(dtype=gla.LIGER_F32, d=128), dict(), dict(), gla.LIGER_E_UNSUPPORTED),
     (dict(T=0), dict(), dict(), gla.LIGER_E_INVALID_ARG),
     (dict(), dict(), dict(gate=5), gla.LIGER_E_INVALID_ARG),
 ])

@@ -68,7 +68,7 @@ def _run(dtype, d, gate, n_rep, window, T1, T2, alpha=0.5, B=2, H_kv=2, seed=0):
     return x
 
 
-@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
 @pytest.mark.parametrize("gate", [0, 1])
 @pytest.mark.parametrize("n_rep,window,T1,T2", [
     (1, 64, 0, 100),     # from a zero state and an empty ring: a plain prefill
@@ -83,7 +83,7 @@ def test_continue_matches_oracle(dtype, d, gate, n_rep, window, T1, T2):
     _run(dtype, d, gate, n_rep, window, T1, T2)
 
 
-@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
 @pytest.mark.parametrize("gate", [0, 1])
 @pytest.mark.parametrize("alpha", [0.0, 1.0])
 @pytest.mark.parametrize("n_rep,window,T1,T2", [

@@ -49,6 +49,17 @@ def test_fp32_edges(gate, n_rep, T, window):
     _run_case(x, "f32", gate, window, 0.5, cps=1, tag=f"fp32 T={T} w={window} n_rep={n_rep}")
 
 
+@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("n_rep", [1, 4])
+@pytest.mark.parametrize("T,cps", [(1, 0), (64, 0), (65, 1), (200, 0), (200, 1), (450, 3)])
+@pytest.mark.parametrize("window", [1, 17, 64])
+def test_fp32_d128(gate, n_rep, T, cps, window):
+    """fp32 at d = 128: the window halo and the state operand come from global
+    memory, and the output kernel also writes the segment records."""
+    x = prefill_inputs(B=2, T=T, H_q=2 * n_rep, H_kv=2, d=128, dtype="f32", seed=T * 11 + window + n_rep)
+    _run_case(x, "f32", gate, window, 0.5, cps=cps, tag=f"fp32 d=128 T={T} w={window} n_rep={n_rep} cps={cps}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("gate", [0, 1])
 @pytest.mark.parametrize("T,n_rep,cps", [(1, 4, 0), (100, 1, 0), (300, 4, 1), (513, 4, 2), (1000, 2, 0)])
@@ -76,7 +87,7 @@ def _strong_decay_keys(x, rng, d):
     return x
 
 
-@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
 def test_vector_gate_extreme_decay_channels(dtype, d):
     rng = np.random.default_rng(3)
     x = prefill_inputs(B=1, T=200, H_q=4, H_kv=1, d=d, dtype=dtype, seed=17)
@@ -84,7 +95,7 @@ def test_vector_gate_extreme_decay_channels(dtype, d):
     _run_case(x, dtype, 1, 64, 0.5, 1, tag=f"extreme vector decay {dtype} d={d}")
 
 
-@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 128)])
 def test_scalar_gate_extreme_decay(dtype, d):
     x = prefill_inputs(B=1, T=200, H_q=4, H_kv=1, d=d, dtype=dtype, seed=19)
     x["k"][:, 50:120] -= 30.0   # mean key ~ -30: gate ~ e^-30 on these tokens
@@ -93,7 +104,7 @@ def test_scalar_gate_extreme_decay(dtype, d):
     _run_case(x, dtype, 0, 64, 0.5, 1, tag=f"extreme scalar decay {dtype}")
 
 
-@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
 @pytest.mark.parametrize("gate", [0, 1])
 @pytest.mark.parametrize("cps", [1, 3, 10])
 def test_slow_decay_across_segments(dtype, d, gate, cps):

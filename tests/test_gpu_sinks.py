@@ -32,7 +32,7 @@ def _o_bar(dtype, o_gpu, o_ref, tag):
         assert abs_inf(o_gpu, o_ref) <= 2e-2, (tag, abs_inf(o_gpu, o_ref))
 
 
-@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
 @pytest.mark.parametrize("gate", [0, 1])
 @pytest.mark.parametrize("n_rep,window,T,n", [(1, 64, 100, 1), (4, 64, 300, 16), (4, 7, 130, 5), (2, 1, 70, 3)])
 def test_prefill_with_sinks(dtype, d, gate, n_rep, window, T, n):
