@@ -448,6 +448,12 @@ __device__ __forceinline__ float row_total(const float* p) {
     }
     return s;
 }
+// The lane index as a value the compiler cannot move: code derived from it
+// stays where it is written (a rare path inside a loop is not hoisted).
+__device__ __forceinline__ int opaque_lane(int lane) {
+    asm volatile("" : "+v"(lane));
+    return lane;
+}
 // A split value read back: hi + lo.
 __device__ __forceinline__ float get_split(const bf16_t* hi, const bf16_t* lo, int idx) {
     return bf16_to_f32(hi[idx]) + bf16_to_f32(lo[idx]);
@@ -723,12 +729,15 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
             }
         }
         if (any_ext && extr) {
+            // lane indices re-derived here, so that the addresses of this rare
+            // path are not hoisted out of the head loop (and spilled) with it
+            const int lo = opaque_lane(lane), col_o = lo & 15, ch0_o = 16 * jb + 4 * (lo >> 4);
 #pragma unroll
             for (int u = 0; u < NTI; ++u)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     if (!((extr >> r) & 1u)) continue;
-                    const int s = 16 * (i0 + u) + col, ch = ch0 + r;
+                    const int s = 16 * (i0 + u) + col_o, ch = ch0_o + r;
                     const float bs = sBeta[s * BP + ch];
                     float sum = 0.f;
                     for (int t = 0; t <= s; ++t)
@@ -791,12 +800,13 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
             }
         }
         if (any_ext && extr) {
+            const int lo = opaque_lane(lane), col_o = lo & 15, ch0_o = 16 * jb + 4 * (lo >> 4);
 #pragma unroll
             for (int u = 0; u < NTI; ++u)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     if (!((extr >> r) & 1u)) continue;
-                    const int t = 16 * (i0 + u) + col, ch = ch0 + r;
+                    const int t = 16 * (i0 + u) + col_o, ch = ch0_o + r;
                     const float bt = sBeta[t * BP + ch];
                     float sum = 0.f;
                     for (int s = t; s < 64; ++s)
@@ -832,20 +842,22 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdParams p) {
             }
             const int s = 16 * is0 + col, tb0 = 16 * it0 + 4 * g, tb1 = 16 * it1 + 4 * g;
             if (any_ext) {
+                const int lo = opaque_lane(lane);
+                const int s_o = 16 * is0 + (lo & 15), tb0_o = 16 * it0 + 4 * (lo >> 4), tb1_o = 16 * it1 + 4 * (lo >> 4);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
 #pragma unroll
                     for (int tl = 0; tl < 2; ++tl) {
-                        const int t = (tl ? tb1 : tb0) + r;
-                        if (s < t) continue;
+                        const int t = (tl ? tb1_o : tb0_o) + r;
+                        if (s_o < t) continue;
                         float sum = 0.f;
                         for (int wd = 0; wd < D / 32; ++wd) {
                             uint32_t bits = sExt[wd];
                             while (bits) {
                                 const int ch = 32 * wd + __builtin_ctz(bits);
                                 bits &= bits - 1;
-                                sum += get_split(sKh, sKl, t * XP + ch) * get_split(sQh, sQl, s * XP + ch) *
-                                       fast_exp2(sBeta[s * BP + ch] - sBeta[t * BP + ch]);
+                                sum += get_split(sKh, sKl, t * XP + ch) * get_split(sQh, sQl, s_o * XP + ch) *
+                                       fast_exp2(sBeta[s_o * BP + ch] - sBeta[t * BP + ch]);
                             }
                         }
                         if (tl) a1[r] += sum;

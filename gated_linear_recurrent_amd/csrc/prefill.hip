@@ -36,6 +36,13 @@ constexpr int kPThreads = 512;
 constexpr int kPWaves = kPThreads / 64;
 constexpr float kEmax2 = 96.0f;  // largest log2 factor admitted to the MFMA path
 
+// The lane index as a value the compiler cannot move: code derived from it
+// stays where it is written (a rare path inside a loop is not hoisted).
+__device__ __forceinline__ int opaque_lane(int lane) {
+    asm volatile("" : "+v"(lane));
+    return lane;
+}
+
 // Thread index hidden from loop-invariant code motion: values derived from it
 // are recomputed where they are used instead of being held in registers
 // across the whole chunk loop.
@@ -1512,13 +1519,29 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
 
     int i_loc[2];
     bool row_ok[2];
-    const T* qrow[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
         i_loc[s] = 16 * QTS[s] + col;
         row_ok[s] = i_loc[s] < x.nvalid;
-        qrow[s] = x.q + ((x.row0 + (row_ok[s] ? i_loc[s] : 0)) * x.H_q + x.hq) * D;
     }
+    // Per-lane values of the rare bad-channel paths, re-derived inside them
+    // from a lane index the compiler cannot move, so that they are not
+    // computed at the top of the block and kept live (or spilled) through it.
+    struct RareLane {
+        int il;       // query row of tile s
+        bool ok;
+        const T* qr;  // its raw query row
+        int g;
+    };
+    auto rare_lane = [&](int s) -> RareLane {
+        RareLane rl;
+        const int lo = opaque_lane(lane);
+        rl.il = 16 * QTS[s] + (lo & 15);
+        rl.ok = rl.il < x.nvalid;
+        rl.qr = x.q + ((x.row0 + (rl.ok ? rl.il : 0)) * x.H_q + x.hq) * D;
+        rl.g = lo >> 4;
+        return rl;
+    };
 
     // ---- query rows: raw fragments (window operand). The recurrence operand
     // (built below) is e^(q - max) times the gate factor; the softmax
@@ -1762,17 +1785,20 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
             if (J > QTS[s]) continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r) d4[s][r] *= qsc[s];
-            for (int nb = 0; nb < nbad; ++nb) {
-                const int c = sm.badlist[nb];
-                const float qc = row_ok[s] ? to_f32(qrow[s][c]) : 0.0f;
-                const float coef = x.alpha * fast_exp2((qc - qmax[s]) * kLog2e) * qinv[s];
-                const float b2i = sm.F[i_loc[s] * L::FP + c];
+            if (nbad) {
+                const RareLane rl = rare_lane(s);
+                for (int nb = 0; nb < nbad; ++nb) {
+                    const int c = sm.badlist[nb];
+                    const float qc = rl.ok ? to_f32(rl.qr[c]) : 0.0f;
+                    const float coef = x.alpha * fast_exp2((qc - qmax[s]) * kLog2e) * qinv[s];
+                    const float b2i = sm.F[rl.il * L::FP + c];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = 16 * J + 4 * g + r;
-                    const float phik = sm.kinv[j] * fast_exp2((to_f32(Kcur[j * L::DP + c]) - sm.kmax[j]) * kLog2e);
-                    const float term = coef * phik * fast_exp2(fminf(b2i - sm.F[j * L::FP + c], 0.0f));
-                    d4[s][r] += j <= i_loc[s] ? term : 0.0f;
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 16 * J + 4 * rl.g + r;
+                        const float phik = sm.kinv[j] * fast_exp2((to_f32(Kcur[j * L::DP + c]) - sm.kmax[j]) * kLog2e);
+                        const float term = coef * phik * fast_exp2(fminf(b2i - sm.F[j * L::FP + c], 0.0f));
+                        d4[s][r] += j <= rl.il ? term : 0.0f;
+                    }
                 }
             }
             if (GATE == 0 && exact) {
@@ -1878,16 +1904,19 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             acc[s] *= inter_scale[s];
-            for (int nb = 0; nb < nbad; ++nb) {
-                const int c = sm.badlist[nb];
-                const float qc = row_ok[s] ? to_f32(qrow[s][c]) : 0.0f;
-                const float bad_q =
-                    x.alpha * fast_exp2((qc - qmax[s]) * kLog2e) * qinv[s] * fast_exp2(sm.F[i_loc[s] * L::FP + c]);
+            if (nbad) {
+                const RareLane rl = rare_lane(s);
+                for (int nb = 0; nb < nbad; ++nb) {
+                    const int c = sm.badlist[nb];
+                    const float qc = rl.ok ? to_f32(rl.qr[c]) : 0.0f;
+                    const float bad_q =
+                        x.alpha * fast_exp2((qc - qmax[s]) * kLog2e) * qinv[s] * fast_exp2(sm.F[rl.il * L::FP + c]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[s][r] += bad_q * (L::SLDS ? sm.S32[(16 * t + 4 * g + r) * L::SP + c]
-                                          : L::HG ? x.opg[(16 * t + 4 * g + r) * D + c]
-                                                  : to_f32(sm.St[(16 * t + 4 * g + r) * L::DP + c]));
+                    for (int r = 0; r < 4; ++r)
+                        acc[s][r] += bad_q * (L::SLDS ? sm.S32[(16 * t + 4 * rl.g + r) * L::SP + c]
+                                              : L::HG ? x.opg[(16 * t + 4 * rl.g + r) * D + c]
+                                                      : to_f32(sm.St[(16 * t + 4 * rl.g + r) * L::DP + c]));
+                }
             }
         }
         if constexpr (BF) {
