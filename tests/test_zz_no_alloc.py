@@ -33,7 +33,7 @@ def _both(x, dtype, gate, window, alpha):
 def test_noalloc_matches_prefill_on_consecutive_calls():
     """First the 8B workload (T = 8192, 32 query heads, 8 key/value heads,
     d = 128: 31.6 MiB of the 32 MiB scratch), then a smaller, ragged vector-gate
-    case, then an fp32 case: each bit-identical to liger_attn_prefill and
+    case, then fp32 cases at d = 64 and d = 128: each bit-identical to liger_attn_prefill and
     within the parity bars against the oracle."""
     assert gla.liger_attn_prefill_noalloc_max_workspace() == 32 << 20
     say("[noalloc] 8B workload")
@@ -49,7 +49,8 @@ def test_noalloc_matches_prefill_on_consecutive_calls():
 
     for dtype, d, gate, (B, T, H_q, H_kv), window, alpha in [
             ("bf16", 128, 1, (2, 300, 8, 2), 64, 0.5),
-            ("f32", 64, 0, (1, 200, 4, 1), 17, 1.0)]:
+            ("f32", 64, 0, (1, 200, 4, 1), 17, 1.0),
+            ("f32", 128, 1, (1, 330, 8, 2), 64, 0.5)]:
         say(f"[noalloc] {dtype} d={d} gate={gate} B={B} T={T} H_q={H_q} H_kv={H_kv} w={window} alpha={alpha}")
         x = prefill_inputs(B=B, T=T, H_q=H_q, H_kv=H_kv, d=d, dtype=dtype, seed=T + d)
         o, S, o_ref, S_ref = _both(x, dtype, gate, window, alpha)
