@@ -131,7 +131,9 @@ typedef struct liger_sinks {
  * that evaluation need the carried states below.
  * Bytes of device workspace liger_attn_prefill needs for `shape`: the state
  * carried into each segment of the chunked scan and a running-state slot per
- * segment. Returns 0 when the shape is invalid. `chunks_per_segment` selects the segment length
+ * segment (fp32 at d = 128 also a state-operand slot per segment and 64
+ * window-halo key and value rows per (b, kv head)). Returns 0 when the shape
+ * is invalid. `chunks_per_segment` selects the segment length
  * in 64-token chunks; 0 picks it from the shape (the same choice the
  * prefill call makes when given 0).
  */

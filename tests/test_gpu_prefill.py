@@ -60,6 +60,13 @@ def test_fp32_d128(gate, n_rep, T, cps, window):
     _run_case(x, "f32", gate, window, 0.5, cps=cps, tag=f"fp32 d=128 T={T} w={window} n_rep={n_rep} cps={cps}")
 
 
+@pytest.mark.parametrize("gate", [0, 1])
+def test_fp32_d128_eight_query_heads_per_kv_head(gate):
+    """Sixteen output blocks per chunk for eight waves, three sequences."""
+    x = prefill_inputs(B=3, T=260, H_q=8, H_kv=1, d=128, dtype="f32", seed=91 + gate)
+    _run_case(x, "f32", gate, 64, 0.5, cps=1, tag=f"fp32 d=128 n_rep=8 gate={gate}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("gate", [0, 1])
 @pytest.mark.parametrize("T,n_rep,cps", [(1, 4, 0), (100, 1, 0), (300, 4, 1), (513, 4, 2), (1000, 2, 0)])
