@@ -406,25 +406,38 @@ template <typename T, int D, int GATE, bool FULL, int TPT>
 __device__ __forceinline__ void vector_gate_scan(const Smem<T, D, GATE, FULL>& sm, int slot,
                                                  int nvalid, float (&b2)[TPT]) {
     typedef Layout<T, D, GATE, FULL> L;
+    constexpr int NPART = kPThreads / D;
     const int c = ltid() % D;
     const int part = ltid() / D;
     const T* Ks = sm.K + slot * 64 * L::DP;
-    const int lo = c > 0 ? c - 1 : 0;
-    const int hi = c + 3 < D ? c + 3 : D;
-    const float inv_cnt = 1.0f / static_cast<float>(hi - lo);
+    // Taps c-1 .. c+2 of the pool; a tap past either edge reads channel c and
+    // is replaced by zero, so every token takes four independent reads with
+    // no branch, summed in channel order.
+    const bool hm = c > 0, h1 = c + 1 < D, h2 = c + 2 < D;
+    const int om = hm ? -1 : 0, o1 = h1 ? 1 : 0, o2 = h2 ? 2 : 0;
+    const float inv_cnt = 1.0f / static_cast<float>(1 + int(hm) + int(h1) + int(h2));
+    float xs[TPT];
+#pragma unroll
+    for (int jj = 0; jj < TPT; ++jj) {
+        const T* r = Ks + (part * TPT + jj) * L::DP + c;
+        const float tm = to_f32(r[om]), t0 = to_f32(r[0]), t1 = to_f32(r[o1]), t2 = to_f32(r[o2]);
+        xs[jj] = (((hm ? tm : 0.0f) + t0) + (h1 ? t1 : 0.0f)) + (h2 ? t2 : 0.0f);
+    }
     float run = 0.f;
 #pragma unroll
     for (int jj = 0; jj < TPT; ++jj) {
-        const int j = part * TPT + jj;
-        float x = 0.f;
-        for (int m = lo; m < hi; ++m) x += to_f32(Ks[j * L::DP + m]);
-        run += j < nvalid ? log2_sigmoid(x * inv_cnt) : 0.0f;
+        const float l = log2_sigmoid(xs[jj] * inv_cnt);
+        run += part * TPT + jj < nvalid ? l : 0.0f;
         b2[jj] = run;
     }
     sm.part[part * D + c] = run;
     __syncthreads();
     float off = 0.f;
-    for (int p = 0; p < part; ++p) off += sm.part[p * D + c];
+#pragma unroll
+    for (int p = 0; p < NPART - 1; ++p) {
+        const float s = sm.part[p * D + c];
+        off += p < part ? s : 0.0f;
+    }
     const int ref = nvalid - 1 < 31 ? nvalid - 1 : 31;
     const int last = nvalid - 1;
 #pragma unroll
