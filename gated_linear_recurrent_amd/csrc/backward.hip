@@ -202,10 +202,9 @@ __device__ __forceinline__ void chunk_gate(float* sK, int FP, float* sBeta, floa
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) {
             const int c = part + 8 * i;
-            const int lo = c > 0 ? c - 1 : 0, hi = c + 3 < D ? c + 3 : D;
-            float s = 0.f;
-            for (int j = lo; j < hi; ++j) s += kr[j];
-            sBeta[row * BP + c] = row < nv ? log2_sigmoid(s / static_cast<float>(hi - lo)) : 0.f;
+            int n;
+            const float s = pool4_taps<D>(kr, c, n);
+            sBeta[row * BP + c] = row < nv ? log2_sigmoid(s / static_cast<float>(n)) : 0.f;
         }
     }
     lds_barrier();
@@ -1077,11 +1076,10 @@ __device__ __forceinline__ const float* gate_chain(const BwdParams& p, int c, in
     }
     for (int idx = tid; idx < 64 * D; idx += kST) {
         const int t = idx / D, ch = idx % D;
-        const int lo = ch > 0 ? ch - 1 : 0, hi = ch + 3 < D ? ch + 3 : D;
-        float sum = 0.f;
-        for (int j = lo; j < hi; ++j) sum += sK[t * FP + j];
-        const float x = sum / static_cast<float>(hi - lo);
-        sS[t * FP + ch] *= sigmoidf_stable(-x) / static_cast<float>(hi - lo);
+        int n;
+        const float sum = pool4_taps<D>(sK + t * FP, ch, n);
+        const float x = sum / static_cast<float>(n);
+        sS[t * FP + ch] *= sigmoidf_stable(-x) / static_cast<float>(n);
     }
     lds_barrier();
     // pool transpose: channel c'' collects channels c'' - 2 .. c'' + 1

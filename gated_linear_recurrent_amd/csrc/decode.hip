@@ -246,10 +246,8 @@ __global__ __launch_bounds__(kDecThreads, (NREP >= 8 || sizeof(T) == 4) ? 1 : 2)
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) {
                     const int c = lane + 64 * e;
-                    const int lo = c > 0 ? c - 1 : 0;
-                    const int hi = c + 3 < D ? c + 3 : D;
-                    float sm = 0.f;
-                    for (int m = lo; m < hi; ++m) sm += s_k[m];
+                    int n;
+                    const float sm = pool4_taps<D>(s_k, c, n);
                     s_g[c] = sigmoidf_stable(sm * (c == 0 || c == D - 2 ? (1.0f / 3.0f) : c == D - 1 ? 0.5f : 0.25f));
                 }
             }

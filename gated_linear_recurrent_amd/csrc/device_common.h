@@ -69,6 +69,19 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f32_to_bf16(x); }
 
+// Numerator of the vector gate's 4-tap pool at channel c of a key row of D
+// channels: the sum of the in-range taps c-1 .. c+2 in channel order, with
+// the tap count in n. Always four independent reads with no branch: a tap
+// past either edge reads channel c and is replaced by zero.
+template <int D, typename T>
+__device__ __forceinline__ float pool4_taps(const T* row, int c, int& n) {
+    const bool hm = c > 0, h1 = c + 1 < D, h2 = c + 2 < D;
+    const float tm = to_f32(row[hm ? c - 1 : c]), t0 = to_f32(row[c]);
+    const float t1 = to_f32(row[h1 ? c + 1 : c]), t2 = to_f32(row[h2 ? c + 2 : c]);
+    n = 1 + int(hm) + int(h1) + int(h2);
+    return (((hm ? tm : 0.0f) + t0) + (h1 ? t1 : 0.0f)) + (h2 ? t2 : 0.0f);
+}
+
 // DPP lane exchanges (no LDS traffic). Row = 16 lanes.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {

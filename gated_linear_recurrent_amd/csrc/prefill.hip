@@ -410,19 +410,11 @@ __device__ __forceinline__ void vector_gate_scan(const Smem<T, D, GATE, FULL>& s
     const int c = ltid() % D;
     const int part = ltid() / D;
     const T* Ks = sm.K + slot * 64 * L::DP;
-    // Taps c-1 .. c+2 of the pool; a tap past either edge reads channel c and
-    // is replaced by zero, so every token takes four independent reads with
-    // no branch, summed in channel order.
-    const bool hm = c > 0, h1 = c + 1 < D, h2 = c + 2 < D;
-    const int om = hm ? -1 : 0, o1 = h1 ? 1 : 0, o2 = h2 ? 2 : 0;
-    const float inv_cnt = 1.0f / static_cast<float>(1 + int(hm) + int(h1) + int(h2));
+    int cnt = 0;
     float xs[TPT];
 #pragma unroll
-    for (int jj = 0; jj < TPT; ++jj) {
-        const T* r = Ks + (part * TPT + jj) * L::DP + c;
-        const float tm = to_f32(r[om]), t0 = to_f32(r[0]), t1 = to_f32(r[o1]), t2 = to_f32(r[o2]);
-        xs[jj] = (((hm ? tm : 0.0f) + t0) + (h1 ? t1 : 0.0f)) + (h2 ? t2 : 0.0f);
-    }
+    for (int jj = 0; jj < TPT; ++jj) xs[jj] = pool4_taps<D>(Ks + (part * TPT + jj) * L::DP, c, cnt);
+    const float inv_cnt = 1.0f / static_cast<float>(cnt);
     float run = 0.f;
 #pragma unroll
     for (int jj = 0; jj < TPT; ++jj) {
