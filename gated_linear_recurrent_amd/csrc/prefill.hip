@@ -423,7 +423,7 @@ __device__ __forceinline__ void vector_gate_scan(const Smem<T, D, GATE, FULL>& s
         b2[jj] = run;
     }
     sm.part[part * D + c] = run;
-    __syncthreads();
+    lds_barrier();
     float off = 0.f;
 #pragma unroll
     for (int p = 0; p < NPART - 1; ++p) {
@@ -622,7 +622,7 @@ __device__ __forceinline__ void gate_stats(const Smem<T, D, GATE, FULL>& sm, int
                                            float alpha, float (&b2)[TPT]) {
     typedef Layout<T, D, GATE, FULL> L;
     key_row_stats(sm, slot, nvalid);
-    __syncthreads();
+    lds_barrier();
     if (GATE == 0) {
         // Every wave forms the inclusive prefix of the chunk's gates itself
         // (lane shifts and lane reads); wave 0 publishes it. With the resident
@@ -630,7 +630,7 @@ __device__ __forceinline__ void gate_stats(const Smem<T, D, GATE, FULL>& sm, int
         // it right away and keeps the barrier.
         const float pre = wave_prefix_sum(sm.b2e[ltid() & 63]);
         if (ltid() < 64) sm.b2s[ltid()] = pre;
-        if constexpr (!(FULL && L::SLDS)) __syncthreads();
+        if constexpr (!(FULL && L::SLDS)) lds_barrier();
         const float bl = readlane_f(pre, nvalid - 1);
         // reference for the factorised intra-chunk decay: the middle token
         const float m = readlane_f(pre, nvalid - 1 < 31 ? nvalid - 1 : 31);
@@ -643,7 +643,7 @@ __device__ __forceinline__ void gate_stats(const Smem<T, D, GATE, FULL>& sm, int
         if (ltid() == 0) *sm.exact = ex ? 1 : 0;
     } else {
         vector_gate_scan<T, D, GATE, FULL, TPT>(sm, slot, nvalid, b2);
-        __syncthreads();
+        lds_barrier();
         const int c = ltid() % D;
         const int part = ltid() / D;
         const float m2 = sm.m2raw[c];
@@ -2205,31 +2205,46 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
         }
         return;
     }
+    // the state entering the segment goes to this workgroup's slot, which
+    // every chunk then reloads (each lane reads back its own stores)
+    load_state<D>(carry_in, acc);
+    store_slot<D>(slot, acc);
     __syncthreads();
     for (int64_t c = c_begin; c < c_end; ++c) {
         const int cur = L::NSLOT == 2 ? int(c & 1) : 0;
         const int64_t t0 = c * kChunk;
         const int nvalid = p.T - t0 < kChunk ? int(p.T - t0) : kChunk;
-        // running state (entering this chunk) and the query fragments of this
-        // wave's first output block, loaded now so their latency overlaps the
-        // gate and state phases
+        // Running state (entering this chunk), loaded now so its latency
+        // overlaps the gate phase: nothing waits on it before the state phase
+        // (the barriers up to there order LDS only, and vector memory
+        // counters drain in order, so any earlier wait would include it).
         __builtin_amdgcn_sched_barrier(0);
-        if (c == c_begin) load_state<D>(carry_in, acc);
-        else load_slot<D>(slot, acc);
-        if (wave < n_items) {
-            int lane = threadIdx.x & 63;
-            asm volatile("" : "+v"(lane));
-            const int pair = wave / p.n_rep;
-            load_q_block<T, D>(qpre, static_cast<const T*>(p.q), b * p.T + t0, H_q, h * p.n_rep + (wave % p.n_rep),
-                               pair == 0 ? 0 : 1, pair == 0 ? 3 : 2, nvalid, lane);
-        }
+        load_slot<D>(slot, acc);
         __builtin_amdgcn_sched_barrier(0);
+        // Query fragments of this wave's first output block, in flight during
+        // the state phases. bf16 issues them after the gate phase: their
+        // address code waits on the vector memory counter (register reuse, a
+        // spill reload), which at the chunk top would wait for the state.
+        // fp32 issues them here (its fragment registers would otherwise be
+        // live through the gate phase).
+        constexpr bool LATE_Q = sizeof(T) == 2;
+        auto issue_q = [&]() {
+            if (wave < n_items) {
+                int lane = threadIdx.x & 63;
+                asm volatile("" : "+v"(lane));
+                const int pair = wave / p.n_rep;
+                load_q_block<T, D>(qpre, static_cast<const T*>(p.q), b * p.T + t0, H_q,
+                                   h * p.n_rep + (wave % p.n_rep), pair == 0 ? 0 : 1, pair == 0 ? 3 : 2, nvalid, lane);
+            }
+        };
+        if (!LATE_Q) issue_q();
         if (threadIdx.x == 0) *sm.nbad = 0;
         if (threadIdx.x < D / 32) sm.badmask[threadIdx.x] = 0u;
-        __syncthreads();
+        lds_barrier();
         float b2[TPT];
         gate_prep<T, D, GATE, true, TPT>(sm, cur, nvalid, p.alpha, b2);
-        __syncthreads();
+        if (LATE_Q) issue_q();
+        lds_barrier();
         // state operand for this chunk (S entering it), then advance the state
         if constexpr (L::HG) publish_state_global(sm, opg, acc);
         else publish_state(sm, acc);
