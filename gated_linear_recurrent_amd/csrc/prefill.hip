@@ -1440,7 +1440,11 @@ __device__ __forceinline__ QNext next_block(int it, int wave, int n_items, int n
     return nx;
 }
 
-template <typename T, int D>
+// UNCOND: rows past the end read row 0 of the chunk (always a token) and
+// are zeroed where they are used, so the loads carry no branch: the compiler
+// then counts them exactly, and waits on the vector memory counter for
+// earlier loads do not also wait for these.
+template <typename T, int D, bool UNCOND = false>
 __device__ __forceinline__ void load_q_block(QFrags<T, D>& qf, const T* q, int64_t row0, int H_q, int hq, int qa,
                                              int qb, int nvalid, int lane) {
     typedef Mfma<T> M;
@@ -1452,7 +1456,11 @@ __device__ __forceinline__ void load_q_block(QFrags<T, D>& qf, const T* q, int64
         const T* qrow = q + ((row0 + (ok ? i : 0)) * H_q + hq) * D;
 #pragma unroll
         for (int k = 0; k < D / M::KSTEP; ++k) {
-            if constexpr (sizeof(T) == 2) {
+            if constexpr (UNCOND) {
+                static_assert(sizeof(T) == 2, "unconditional query loads are bf16 only");
+                qf.f[s][k] = __builtin_bit_cast(typename M::frag,
+                                                *reinterpret_cast<const uint4*>(qrow + M::KSTEP * k + M::KPL * g));
+            } else if constexpr (sizeof(T) == 2) {
                 const uint4 u = ok ? *reinterpret_cast<const uint4*>(qrow + M::KSTEP * k + M::KPL * g)
                                    : make_uint4(0, 0, 0, 0);
                 qf.f[s][k] = __builtin_bit_cast(typename M::frag, u);
@@ -1556,7 +1564,12 @@ __device__ __forceinline__ void output_block(const Smem<T, D, GATE, true>& sm, c
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int k = 0; k < KS; ++k) qr[s][k] = qin.f[s][k];
+        for (int k = 0; k < KS; ++k) {
+            // without a resident state, bf16 query rows past the end arrive
+            // unconditionally loaded (row 0) and are zeroed here
+            if constexpr (L::SLDS || !BF) qr[s][k] = qin.f[s][k];
+            else qr[s][k] = row_ok[s] ? qin.f[s][k] : M::zero();
+        }
     auto qval = [&](int s, int k, int i) -> float {
         if constexpr (BF) {
             const uint4 u = __builtin_bit_cast(uint4, qr[s][k]);
@@ -2229,9 +2242,17 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
         // live through the gate phase).
         constexpr bool LATE_Q = sizeof(T) == 2;
         auto issue_q = [&]() {
-            if (wave < n_items) {
-                int lane = threadIdx.x & 63;
-                asm volatile("" : "+v"(lane));
+            int lane = threadIdx.x & 63;
+            asm volatile("" : "+v"(lane));
+            if constexpr (LATE_Q) {
+                // every wave loads (a wave without an item loads item 0's
+                // rows and never uses them), so no branch joins here
+                const int it0 = wave < n_items ? wave : 0;
+                const int pair = it0 / p.n_rep;
+                load_q_block<T, D, true>(qpre, static_cast<const T*>(p.q), b * p.T + t0, H_q,
+                                         h * p.n_rep + (it0 % p.n_rep), pair == 0 ? 0 : 1, pair == 0 ? 3 : 2, nvalid,
+                                         lane);
+            } else if (wave < n_items) {
                 const int pair = wave / p.n_rep;
                 load_q_block<T, D>(qpre, static_cast<const T*>(p.q), b * p.T + t0, H_q,
                                    h * p.n_rep + (wave % p.n_rep), pair == 0 ? 0 : 1, pair == 0 ? 3 : 2, nvalid, lane);
@@ -2287,7 +2308,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_output_kernel(PrefillParams
             asm volatile("" : "+v"(lane));  // keep lane-derived addresses inside the loop
             const int pair = it / p.n_rep;
             if (it != wave)
-                load_q_block<T, D>(qpre, x.q, x.row0, H_q, x.hq, pair == 0 ? 0 : 1, pair == 0 ? 3 : 2, nvalid, lane);
+                load_q_block<T, D, LATE_Q>(qpre, x.q, x.row0, H_q, x.hq, pair == 0 ? 0 : 1, pair == 0 ? 3 : 2, nvalid,
+                                           lane);
             QNext nx;
             nx.any = false;  // without a resident state the registers are too few to load ahead
             if (pair == 0) output_block<T, D, GATE, 0, 3, SINK>(sm, x, lane, qpre, nx);
